@@ -1,0 +1,187 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 library.
+ *
+ * NVFP4 is a two-level microscaled 4-bit format: E2M1 elements (1 sign,
+ * 2 exponent, 1 mantissa bit), one FP8 E4M3 scale per micro-block of 16
+ * elements and one FP32 scale per tensor.  Sources: guiahardware.es
+ * "NVFP4: cos'e e come supera FP8 e BF16 nell'intelligenza artificiale",
+ * section "Cos'e NVFP4"; chaitex.ru "FP4", section on the mathematical
+ * structure of FP4 (bullets and numbered items 1-2); "Mastering Low-Precision
+ * AI" (ai-news pages.dev), first paragraph.  The training recipe (readjensen.com
+ * NVFP4 news page, recipe paragraph) quantizes activations and gradients in
+ * 1x16 blocks, weights in 16x16 blocks (so fprop and dgrad see the same
+ * values), applies a random Hadamard transform to the wgrad inputs, rounds
+ * gradients stochastically, and runs the three MLP GEMMs on NVFP4 inputs
+ * with BF16 outputs.
+ *
+ * Arithmetic convention (the pages give no formulas; every step is one
+ * IEEE FP32 operation rounded to nearest-even, in this order):
+ *     amax = max |x|  (over the Hadamard-transformed values when rht = 1)
+ *     s_g  = amax / 2688                          (2688 = 6 * 448)
+ *     per block: a_B = max |x| over the block;  t = a_B / (6 * s_g);
+ *                e = E4M3 round-to-nearest-even of t, saturating at 448;
+ *                d = e * s_g
+ *     per element: y = x / d;  q = E2M1 of y (RNE, or stochastic), saturating at 6
+ *     a block with a_B = 0, e = 0 or d = 0 stores e = 0 and q = 0.
+ * Stochastic rounding rounds |y| up to the next E2M1 magnitude when
+ * r < frac * 2^32 (frac = the position of |y| between its two neighbours),
+ * with r the 32-bit word of Philox4x32-10 (Salmon et al., SC'11) at
+ * key = (seed mod 2^32, seed >> 32), counter = (g mod 2^32, g >> 32,
+ * stream_id, 0), g = idx >> 2, word idx & 3, idx = row * cols + col.
+ *
+ * Storage (all dense, row-major, caller-owned device memory):
+ *   codes   uint8 [rows, cols/2]: byte j of a row holds element 2j in its
+ *           low nibble and element 2j+1 in its high nibble.
+ *   scales  uint8 E4M3 codes:  1D, axis 1 (blocks along a row):  [rows, cols/16]
+ *                              1D, axis 0 (blocks down a column): [rows/16, cols]
+ *                              2D (16x16 blocks):                  [rows/16, cols/16]
+ *   tensor_scale  one float (s_g) in device memory.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are device pointers unless stated; `stream` is a
+ *     hipStream_t (NULL = the default stream).  Work is enqueued on `stream`
+ *     and the call returns without synchronizing.  The library allocates no
+ *     memory and keeps no state between calls.
+ *   - Argument errors are reported before anything is enqueued, so nothing
+ *     is written on error.  Launch failures return NVFP4_ERR_HIP.
+ *   - Inputs must be finite.  With the environment variable NVFP4_DEBUG=1
+ *     nvfp4_quantize synchronizes `stream` and returns NVFP4_ERR_NONFINITE
+ *     when the tensor amax is not finite.
+ *   - Device pointers must be 16-byte aligned, and leading dimensions must
+ *     keep every row 16-byte aligned (NVFP4_ERR_ALIGN otherwise).
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_INVALID_ARG = 1, /* null pointer, bad enum value, negative size */
+    NVFP4_ERR_SHAPE = 2,       /* a dimension breaks the block or packing rules */
+    NVFP4_ERR_ALIGN = 3,       /* pointer or leading dimension not 16-byte aligned */
+    NVFP4_ERR_LAYOUT = 4,      /* a GEMM operand's blocks do not run along K */
+    NVFP4_ERR_UNSUPPORTED = 5, /* a valid but unimplemented combination */
+    NVFP4_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+    NVFP4_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */
+    NVFP4_ERR_NONFINITE = 8    /* NVFP4_DEBUG=1 only: amax is Inf or NaN */
+} nvfp4_status;
+
+typedef enum { NVFP4_DTYPE_BF16 = 0, NVFP4_DTYPE_FP32 = 1 } nvfp4_dtype;
+typedef enum { NVFP4_BLOCK_1D = 0, NVFP4_BLOCK_2D = 1 } nvfp4_block;
+typedef enum { NVFP4_ROUND_RNE = 0, NVFP4_ROUND_SR = 1 } nvfp4_round;
+typedef enum { NVFP4_LAYOUT_NT = 0, NVFP4_LAYOUT_NN = 1, NVFP4_LAYOUT_TN = 2 } nvfp4_layout;
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int nvfp4_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* nvfp4_status_string(nvfp4_status status);
+
+/*
+ * Bytes of device workspace nvfp4_quantize needs for a rows x cols tensor
+ * when it computes the tensor amax itself (amax_in == NULL).  The workspace
+ * holds per-workgroup partial maxima and the reduced amax; it needs no
+ * initialisation and may be reused by later calls on the same stream.
+ */
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
+
+/*
+ * Quantize a rows x cols tensor to NVFP4.
+ * Sources: two-level scaling -- guiahardware.es "Cos'e NVFP4"; chaitex.ru
+ * "FP4" items 1-2.  2D weight blocks, RHT on wgrad inputs and stochastic
+ * rounding of gradients -- readjensen.com recipe paragraph.
+ *
+ *   x, x_dtype, ld_x   input (BF16 or FP32), row r starts at x + r*ld_x elements
+ *   block, axis        NVFP4_BLOCK_1D with axis 1 (16 consecutive columns of a
+ *                      row) or axis 0 (16 consecutive rows of a column);
+ *                      NVFP4_BLOCK_2D: 16x16 tiles, axis ignored
+ *   rounding, seed, stream_id
+ *                      NVFP4_ROUND_RNE, or NVFP4_ROUND_SR with the Philox
+ *                      stream keyed by seed and stream_id (see above)
+ *   rht, rht_sign_mask rht = 1 applies y = 1/4 * H16 * D * x to each block of
+ *                      16 along `axis` before quantizing (1D only), where
+ *                      D = diag(d_i), d_i = -1 iff bit i of the mask is set,
+ *                      computed in FP32 as four butterfly stages at
+ *                      distances 1, 2, 4, 8 followed by the 1/4 scaling
+ *   amax_in            NULL: the library computes amax (needs the workspace);
+ *                      else a device float used as amax as-is (it must be the
+ *                      amax of exactly what is quantized, i.e. after the RHT)
+ *   amax_out           NULL, or a device float that receives amax
+ *   codes, scales, tensor_scale
+ *                      outputs in the storage layout above
+ *   workspace, workspace_bytes
+ *                      device scratch of nvfp4_quantize_workspace_size bytes
+ *                      (may be NULL/0 when amax_in != NULL)
+ * Shape rules: rows, cols >= 0; cols % 16 == 0; rows % 16 == 0 for axis 0
+ * and for 2D.  ld_x >= cols.  An empty tensor writes s_g = 0 (and amax 0).
+ */
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                            int64_t ld_x, nvfp4_block block, int axis, nvfp4_round rounding,
+                            uint64_t seed, uint32_t stream_id, int rht, uint32_t rht_sign_mask,
+                            const float* amax_in, float* amax_out, uint8_t* codes,
+                            uint8_t* scales, float* tensor_scale, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * Standalone 16-point random Hadamard transform (the wgrad-input transform
+ * of the recipe paragraph, readjensen.com; "Hadamard transforms" in
+ * "Mastering Low-Precision AI", third paragraph).
+ * y[r*ld_y + c] = (1/4 * H16 * D * x) over each group of 16 along `axis`,
+ * in FP32 exactly as nvfp4_quantize computes it with rht = 1.
+ * Shape rules: cols % 16 == 0 (axis 1) / rows % 16 == 0 (axis 0); cols % 8 == 0.
+ */
+nvfp4_status nvfp4_rht16(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                         int64_t ld_x, int axis, uint32_t sign_mask, float* y, int64_t ld_y,
+                         void* stream);
+
+/*
+ * Dequantize: out[r*ld_out + c] = RN32(val(q) * e * s_g), then (for BF16
+ * output) rounded to nearest-even BF16.  The element value times its block
+ * scale is exact in FP32; s_g is the product's only rounding.
+ * Source: the two-level decode implied by "Cos'e NVFP4" (guiahardware.es)
+ * and chaitex.ru "FP4" items 1-2.
+ * codes/scales/tensor_scale follow the storage layout above with the given
+ * block mode and axis.  Shape rules as for nvfp4_quantize.
+ */
+nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
+                              const float* tensor_scale, int64_t rows, int64_t cols,
+                              nvfp4_block block, int axis, nvfp4_dtype out_dtype, void* out,
+                              int64_t ld_out, void* stream);
+
+/*
+ * NVFP4 GEMM with FP32 accumulation: C = s_A * s_B * sum_k (q*e)_A (q*e)_B.
+ * Source: the three MLP GEMMs (fprop, dgrad, wgrad) with NVFP4 inputs and
+ * BF16 outputs, readjensen.com recipe paragraph.
+ *   NVFP4_LAYOUT_NT (fprop):  A stored [M, K], B stored [N, K];  C = A * B^T
+ *   NVFP4_LAYOUT_NN (dgrad):  A stored [M, K], B stored [K, N];  C = A * B
+ *   NVFP4_LAYOUT_TN (wgrad):  A stored [K, M], B stored [K, N];  C = A^T * B
+ * Each operand is an NVFP4 tensor (codes, scales, device tensor scale) in the
+ * storage layout above.  Its scale blocks must run along K: a 1D operand
+ * stored with K along its columns uses axis 1, one stored with K along its
+ * rows uses axis 0 (the axis is implied by the layout); a 2D operand is
+ * accepted in any position (NVFP4_ERR_LAYOUT is returned for 2D operands
+ * whose dims are not multiples of 16).
+ *   c, ldc, out_dtype  C[m*ldc + n], BF16 (recipe output) or FP32; c needs only
+ *                      element alignment and ldc >= N is free
+ * Shape rules: M, N, K >= 0; K % 16 == 0; a dimension along which codes are
+ * packed but which is not K (N for NN, M and N for TN) must be a multiple of
+ * 16.  K == 0 writes zeros.
+ */
+nvfp4_status nvfp4_gemm(nvfp4_layout layout, int64_t M, int64_t N, int64_t K,
+                        const uint8_t* a_codes, const uint8_t* a_scales,
+                        const float* a_tensor_scale, nvfp4_block a_block,
+                        const uint8_t* b_codes, const uint8_t* b_scales,
+                        const float* b_tensor_scale, nvfp4_block b_block, nvfp4_dtype out_dtype,
+                        void* c, int64_t ldc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */

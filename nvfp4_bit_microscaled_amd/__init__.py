@@ -1,0 +1,233 @@
+"""Python binding of the MI355X NVFP4 library (libnvfp4.so, C ABI in include/nvfp4.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current HIP stream.  The library
+must be built (``python -m nvfp4_bit_microscaled_amd.build``); importing
+this package without it raises ImportError -- there is no fallback.
+
+NVFP4 (guiahardware.es "NVFP4: cos'e e come supera FP8 e BF16", section
+"Cos'e NVFP4"): E2M1 codes, an E4M3 scale per 16 elements and an FP32 tensor
+scale.  Recipe (readjensen.com NVFP4 training-recipe page, recipe paragraph):
+1x16 blocks for activations and gradients, 16x16 for weights, RHT on wgrad
+inputs, stochastic rounding of gradients, NVFP4 GEMMs with BF16 output.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+# enums (include/nvfp4.h)
+OK = 0
+STATUS_NAMES = {0: "NVFP4_OK", 1: "NVFP4_ERR_INVALID_ARG", 2: "NVFP4_ERR_SHAPE",
+                3: "NVFP4_ERR_ALIGN", 4: "NVFP4_ERR_LAYOUT", 5: "NVFP4_ERR_UNSUPPORTED",
+                6: "NVFP4_ERR_WORKSPACE", 7: "NVFP4_ERR_HIP", 8: "NVFP4_ERR_NONFINITE"}
+DTYPE_BF16, DTYPE_FP32 = 0, 1
+BLOCK_1D, BLOCK_2D = 0, 1
+ROUND_RNE, ROUND_SR = 0, 1
+LAYOUT = {"NT": 0, "NN": 1, "TN": 2}
+
+EXPORTS = ("nvfp4_version", "nvfp4_status_string", "nvfp4_quantize_workspace_size",
+           "nvfp4_quantize", "nvfp4_rht16", "nvfp4_dequantize", "nvfp4_gemm")
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s returned %s" % (fn, STATUS_NAMES.get(status, status)))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libnvfp4.so is not built: run `python -m nvfp4_bit_microscaled_amd.build`"
+                          " (expected at %s)" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i64, u64, u32, vp, ci = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
+    L.nvfp4_version.restype = ci
+    L.nvfp4_version.argtypes = []
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_status_string.argtypes = [ci]
+    L.nvfp4_quantize_workspace_size.restype = ctypes.c_size_t
+    L.nvfp4_quantize_workspace_size.argtypes = [i64, i64]
+    L.nvfp4_quantize.restype = ci
+    L.nvfp4_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, u64, u32, ci, u32, vp, vp, vp,
+                                 vp, vp, vp, ctypes.c_size_t, vp]
+    L.nvfp4_rht16.restype = ci
+    L.nvfp4_rht16.argtypes = [vp, ci, i64, i64, i64, ci, u32, vp, i64, vp]
+    L.nvfp4_dequantize.restype = ci
+    L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, ci, ci, ci, vp, i64, vp]
+    L.nvfp4_gemm.restype = ci
+    L.nvfp4_gemm.argtypes = [ci, i64, i64, i64, vp, vp, vp, ci, vp, vp, vp, ci, ci, vp, i64, vp]
+    return L
+
+
+lib = _load()
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise NVFP4Error(fn, status)
+
+
+def version() -> int:
+    return lib.nvfp4_version()
+
+
+def status_string(status: int) -> str:
+    return lib.nvfp4_status_string(status).decode()
+
+
+# ---------------------------------------------------------------- raw ABI calls
+# Same names and argument order as include/nvfp4.h; tensors stand for device
+# pointers, None for NULL.  They return the status code unchanged.
+
+def nvfp4_quantize_workspace_size(rows: int, cols: int) -> int:
+    return lib.nvfp4_quantize_workspace_size(rows, cols)
+
+
+def nvfp4_quantize(x, x_dtype, rows, cols, ld_x, block, axis, rounding, seed, stream_id, rht,
+                   rht_sign_mask, amax_in, amax_out, codes, scales, tensor_scale, workspace,
+                   workspace_bytes, stream=None) -> int:
+    return lib.nvfp4_quantize(_p(x), x_dtype, rows, cols, ld_x, block, axis, rounding, seed,
+                              stream_id, rht, rht_sign_mask, _p(amax_in), _p(amax_out),
+                              _p(codes), _p(scales), _p(tensor_scale), _p(workspace),
+                              workspace_bytes, _stream(stream))
+
+
+def nvfp4_rht16(x, x_dtype, rows, cols, ld_x, axis, sign_mask, y, ld_y, stream=None) -> int:
+    return lib.nvfp4_rht16(_p(x), x_dtype, rows, cols, ld_x, axis, sign_mask, _p(y), ld_y,
+                           _stream(stream))
+
+
+def nvfp4_dequantize(codes, scales, tensor_scale, rows, cols, block, axis, out_dtype, out, ld_out,
+                     stream=None) -> int:
+    return lib.nvfp4_dequantize(_p(codes), _p(scales), _p(tensor_scale), rows, cols, block, axis,
+                                out_dtype, _p(out), ld_out, _stream(stream))
+
+
+def nvfp4_gemm(layout, M, N, K, a_codes, a_scales, a_tensor_scale, a_block, b_codes, b_scales,
+               b_tensor_scale, b_block, out_dtype, c, ldc, stream=None) -> int:
+    return lib.nvfp4_gemm(layout, M, N, K, _p(a_codes), _p(a_scales), _p(a_tensor_scale), a_block,
+                          _p(b_codes), _p(b_scales), _p(b_tensor_scale), b_block, out_dtype,
+                          _p(c), ldc, _stream(stream))
+
+
+# ---------------------------------------------------------------- tensor-level helpers
+
+@dataclass
+class NVFP4Tensor:
+    """codes uint8 [R, C/2], scales uint8 (layout by block/axis), tensor_scale float32 [1]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: torch.Tensor
+    amax: torch.Tensor
+    rows: int
+    cols: int
+    block2d: bool
+    axis: int
+
+
+def scale_shape(rows: int, cols: int, block2d: bool, axis: int):
+    if block2d:
+        return (rows // 16, cols // 16)
+    return (rows, cols // 16) if axis == 1 else (rows // 16, cols)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    raise TypeError("NVFP4 input must be bfloat16 or float32, got %s" % t.dtype)
+
+
+_workspaces = {}
+
+
+def _workspace(device, rows, cols):
+    n = nvfp4_quantize_workspace_size(rows, cols)
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < n:
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def quantize(x: torch.Tensor, block2d: bool = False, axis: int = 1, sr: bool = False,
+             seed: int = 0, stream_id: int = 0, rht: bool = False, mask: int = 0,
+             amax_in: torch.Tensor | None = None, out: NVFP4Tensor | None = None) -> NVFP4Tensor:
+    """Quantize a 2-D BF16/FP32 CUDA tensor (row stride may exceed its width)."""
+    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1
+    rows, cols = x.shape
+    dev = x.device
+    if out is None:
+        out = NVFP4Tensor(
+            codes=torch.empty(rows, cols // 2, dtype=torch.uint8, device=dev),
+            scales=torch.empty(scale_shape(rows, cols, block2d, axis), dtype=torch.uint8,
+                               device=dev),
+            tensor_scale=torch.empty(1, dtype=torch.float32, device=dev),
+            amax=torch.empty(1, dtype=torch.float32, device=dev),
+            rows=rows, cols=cols, block2d=block2d, axis=axis)
+    ws = None if amax_in is not None else _workspace(dev, rows, cols)
+    st = nvfp4_quantize(x, _dtype_code(x), rows, cols, x.stride(0),
+                        BLOCK_2D if block2d else BLOCK_1D, axis, ROUND_SR if sr else ROUND_RNE,
+                        seed, stream_id, int(rht), mask, amax_in, out.amax, out.codes, out.scales,
+                        out.tensor_scale, ws, 0 if ws is None else ws.numel())
+    _check("nvfp4_quantize", st)
+    return out
+
+
+def rht16(x: torch.Tensor, axis: int, mask: int) -> torch.Tensor:
+    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1
+    rows, cols = x.shape
+    y = torch.empty(rows, cols, dtype=torch.float32, device=x.device)
+    _check("nvfp4_rht16", nvfp4_rht16(x, _dtype_code(x), rows, cols, x.stride(0), axis, mask, y,
+                                      cols))
+    return y
+
+
+def dequantize(t: NVFP4Tensor, out_dtype=torch.bfloat16) -> torch.Tensor:
+    out = torch.empty(t.rows, t.cols, dtype=out_dtype, device=t.codes.device)
+    _check("nvfp4_dequantize", nvfp4_dequantize(
+        t.codes, t.scales, t.tensor_scale, t.rows, t.cols, BLOCK_2D if t.block2d else BLOCK_1D,
+        t.axis, _dtype_code(out), out, t.cols))
+    return out
+
+
+def gemm(layout: str, a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """NT: a [M,K], b [N,K]; NN: a [M,K], b [K,N]; TN: a [K,M], b [K,N]."""
+    if layout == "NT":
+        M, K = a.rows, a.cols
+        N = b.rows
+    elif layout == "NN":
+        M, K = a.rows, a.cols
+        N = b.cols
+    elif layout == "TN":
+        K, M = a.rows, a.cols
+        N = b.cols
+    else:
+        raise ValueError(layout)
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=a.codes.device)
+    _check("nvfp4_gemm", nvfp4_gemm(
+        LAYOUT[layout], M, N, K, a.codes, a.scales, a.tensor_scale,
+        BLOCK_2D if a.block2d else BLOCK_1D, b.codes, b.scales, b.tensor_scale,
+        BLOCK_2D if b.block2d else BLOCK_1D, _dtype_code(out), out, out.stride(0)))
+    return out

@@ -1,0 +1,213 @@
+// C ABI of the NVFP4 library (declared in include/nvfp4.h): argument
+// validation and dispatch to the HIP launchers.  Every check happens before
+// anything is enqueued, so a call that returns an error has written nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "launch.h"
+#include "nvfp4.h"
+
+using namespace nvfp4;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool debug_mode()
+{
+    const char* v = std::getenv("NVFP4_DEBUG");
+    return v && v[0] == '1';
+}
+
+nvfp4_status from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+constexpr uint64_t kMaxItems = 0xFFFFFFFFull;  // kernels index work items in 32 bits
+
+// Workspace layout: [0, kMaxAmaxPartials) partial maxima, then the amax slot.
+constexpr size_t kWorkspaceFloats = kMaxAmaxPartials + 64;
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_version(void) { return 100; }
+
+const char* nvfp4_status_string(nvfp4_status s)
+{
+    switch (s) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_INVALID_ARG: return "NVFP4_ERR_INVALID_ARG";
+    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE";
+    case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN";
+    case NVFP4_ERR_LAYOUT: return "NVFP4_ERR_LAYOUT";
+    case NVFP4_ERR_UNSUPPORTED: return "NVFP4_ERR_UNSUPPORTED";
+    case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE";
+    case NVFP4_ERR_HIP: return "NVFP4_ERR_HIP";
+    case NVFP4_ERR_NONFINITE: return "NVFP4_ERR_NONFINITE";
+    }
+    return "NVFP4_ERR_UNKNOWN";
+}
+
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols)
+{
+    (void)rows;
+    (void)cols;
+    return kWorkspaceFloats * sizeof(float);
+}
+
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                            int64_t ld_x, nvfp4_block block, int axis, nvfp4_round rounding,
+                            uint64_t seed, uint32_t stream_id, int rht, uint32_t rht_sign_mask,
+                            const float* amax_in, float* amax_out, uint8_t* codes,
+                            uint8_t* scales, float* tensor_scale, void* workspace,
+                            size_t workspace_bytes, void* stream)
+{
+    if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (block != NVFP4_BLOCK_1D && block != NVFP4_BLOCK_2D) return NVFP4_ERR_INVALID_ARG;
+    if (rounding != NVFP4_ROUND_RNE && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_INVALID_ARG;
+    if (block == NVFP4_BLOCK_1D && axis != 0 && axis != 1) return NVFP4_ERR_INVALID_ARG;
+    if (rht != 0 && rht != 1) return NVFP4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0) return NVFP4_ERR_INVALID_ARG;
+    if (!tensor_scale) return NVFP4_ERR_INVALID_ARG;
+    if (rht && block == NVFP4_BLOCK_2D) return NVFP4_ERR_UNSUPPORTED;
+    if (cols % 16) return NVFP4_ERR_SHAPE;
+    bool along_rows = (block == NVFP4_BLOCK_2D) || axis == 0;
+    if (along_rows && rows % 16) return NVFP4_ERR_SHAPE;
+    if (ld_x < cols) return NVFP4_ERR_SHAPE;
+    if ((uint64_t)rows * (uint64_t)(cols / 8) > kMaxItems) return NVFP4_ERR_UNSUPPORTED;
+    size_t esz = x_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (rows == 0 || cols == 0) return from_hip(launch_write_zero_scale(tensor_scale, amax_out, s));
+    if (!x || !codes || !scales) return NVFP4_ERR_INVALID_ARG;
+    if (!aligned16(x) || ((size_t)ld_x * esz) % 16) return NVFP4_ERR_ALIGN;
+    if (!aligned16(codes) || !aligned16(scales)) return NVFP4_ERR_ALIGN;
+    if (!amax_in) {
+        if (!workspace || workspace_bytes < nvfp4_quantize_workspace_size(rows, cols))
+            return NVFP4_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return NVFP4_ERR_ALIGN;
+    }
+
+    QuantArgs a;
+    a.x = x;
+    a.bf16 = x_dtype == NVFP4_DTYPE_BF16;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld_x;
+    a.block2d = block == NVFP4_BLOCK_2D;
+    a.axis = axis;
+    a.sr = rounding == NVFP4_ROUND_SR;
+    a.seed = seed;
+    a.stream_id = stream_id;
+    a.rht = rht != 0;
+    a.mask = rht_sign_mask & 0xFFFFu;
+    a.codes = codes;
+    a.scales = scales;
+    a.tensor_scale = tensor_scale;
+    a.amax_out = amax_out;
+
+    const float* amax_src = amax_in;
+    if (!amax_in) {
+        float* ws = static_cast<float*>(workspace);
+        float* amax_slot = ws + kMaxAmaxPartials;
+        hipError_t e = launch_amax(a, ws, amax_slot, s);
+        if (e != hipSuccess) return NVFP4_ERR_HIP;
+        amax_src = amax_slot;
+    }
+    if (debug_mode()) {
+        float h = 0.0f;
+        if (hipMemcpyAsync(&h, amax_src, sizeof(float), hipMemcpyDeviceToHost, s) != hipSuccess)
+            return NVFP4_ERR_HIP;
+        if (hipStreamSynchronize(s) != hipSuccess) return NVFP4_ERR_HIP;
+        if (!std::isfinite(h)) return NVFP4_ERR_NONFINITE;
+    }
+    return from_hip(launch_quantize(a, amax_src, amax_in != nullptr, s));
+}
+
+nvfp4_status nvfp4_rht16(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                         int64_t ld_x, int axis, uint32_t sign_mask, float* y, int64_t ld_y,
+                         void* stream)
+{
+    if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (axis != 0 && axis != 1) return NVFP4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0) return NVFP4_ERR_INVALID_ARG;
+    if (axis == 1 && cols % 16) return NVFP4_ERR_SHAPE;
+    if (axis == 0 && (rows % 16 || cols % 8)) return NVFP4_ERR_SHAPE;
+    if (ld_x < cols || ld_y < cols) return NVFP4_ERR_SHAPE;
+    if ((uint64_t)rows * (uint64_t)(cols / 8) > kMaxItems) return NVFP4_ERR_UNSUPPORTED;
+    if (rows == 0 || cols == 0) return NVFP4_OK;
+    if (!x || !y) return NVFP4_ERR_INVALID_ARG;
+    size_t esz = x_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    if (!aligned16(x) || ((size_t)ld_x * esz) % 16) return NVFP4_ERR_ALIGN;
+    if (!aligned16(y) || ((size_t)ld_y * 4) % 16) return NVFP4_ERR_ALIGN;
+    return from_hip(launch_rht16(x, x_dtype == NVFP4_DTYPE_BF16, rows, cols, ld_x, axis,
+                                 sign_mask & 0xFFFFu, y, ld_y, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
+                              const float* tensor_scale, int64_t rows, int64_t cols,
+                              nvfp4_block block, int axis, nvfp4_dtype out_dtype, void* out,
+                              int64_t ld_out, void* stream)
+{
+    if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (block != NVFP4_BLOCK_1D && block != NVFP4_BLOCK_2D) return NVFP4_ERR_INVALID_ARG;
+    if (block == NVFP4_BLOCK_1D && axis != 0 && axis != 1) return NVFP4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0) return NVFP4_ERR_INVALID_ARG;
+    if (cols % 16) return NVFP4_ERR_SHAPE;
+    bool along_rows = (block == NVFP4_BLOCK_2D) || axis == 0;
+    if (along_rows && rows % 16) return NVFP4_ERR_SHAPE;
+    if (ld_out < cols) return NVFP4_ERR_SHAPE;
+    if ((uint64_t)rows * (uint64_t)(cols / 8) > kMaxItems) return NVFP4_ERR_UNSUPPORTED;
+    if (rows == 0 || cols == 0) return NVFP4_OK;
+    if (!codes || !scales || !tensor_scale || !out) return NVFP4_ERR_INVALID_ARG;
+    size_t esz = out_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(out) ||
+        ((size_t)ld_out * esz) % 16)
+        return NVFP4_ERR_ALIGN;
+    return from_hip(launch_dequantize(codes, scales, tensor_scale, rows, cols,
+                                      block == NVFP4_BLOCK_2D, axis,
+                                      out_dtype == NVFP4_DTYPE_BF16, out, ld_out,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_gemm(nvfp4_layout layout, int64_t M, int64_t N, int64_t K,
+                        const uint8_t* a_codes, const uint8_t* a_scales,
+                        const float* a_tensor_scale, nvfp4_block a_block,
+                        const uint8_t* b_codes, const uint8_t* b_scales,
+                        const float* b_tensor_scale, nvfp4_block b_block, nvfp4_dtype out_dtype,
+                        void* c, int64_t ldc, void* stream)
+{
+    if (layout != NVFP4_LAYOUT_NT && layout != NVFP4_LAYOUT_NN && layout != NVFP4_LAYOUT_TN)
+        return NVFP4_ERR_INVALID_ARG;
+    if (a_block != NVFP4_BLOCK_1D && a_block != NVFP4_BLOCK_2D) return NVFP4_ERR_INVALID_ARG;
+    if (b_block != NVFP4_BLOCK_1D && b_block != NVFP4_BLOCK_2D) return NVFP4_ERR_INVALID_ARG;
+    if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_INVALID_ARG;
+    if (ldc < N) return NVFP4_ERR_SHAPE;
+    if (K % 16) return NVFP4_ERR_SHAPE;
+    const bool a_kmajor = layout != NVFP4_LAYOUT_TN;  // A stored [M, K] unless TN
+    const bool b_kmajor = layout == NVFP4_LAYOUT_NT;  // B stored [N, K] only for NT
+    // dims along which codes are packed but which are not K
+    if (!a_kmajor && M % 16) return NVFP4_ERR_SHAPE;
+    if (!b_kmajor && N % 16) return NVFP4_ERR_SHAPE;
+    // 2D operands need both dims divisible by 16
+    if (a_block == NVFP4_BLOCK_2D && M % 16) return NVFP4_ERR_LAYOUT;
+    if (b_block == NVFP4_BLOCK_2D && N % 16) return NVFP4_ERR_LAYOUT;
+    if (M == 0 || N == 0) return NVFP4_OK;
+    if (!c) return NVFP4_ERR_INVALID_ARG;
+    size_t esz = out_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    if ((reinterpret_cast<uintptr_t>(c) & (esz - 1)) != 0) return NVFP4_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) return from_hip(launch_fill_zero(c, out_dtype == NVFP4_DTYPE_BF16, M, N, ldc, s));
+    if (!a_codes || !a_scales || !a_tensor_scale || !b_codes || !b_scales || !b_tensor_scale)
+        return NVFP4_ERR_INVALID_ARG;
+    if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) || !aligned16(b_scales))
+        return NVFP4_ERR_ALIGN;
+    GemmOperand A{a_codes, a_scales, a_tensor_scale, a_block == NVFP4_BLOCK_2D, a_kmajor};
+    GemmOperand B{b_codes, b_scales, b_tensor_scale, b_block == NVFP4_BLOCK_2D, b_kmajor};
+    return from_hip(launch_gemm(M, N, K, A, B, out_dtype == NVFP4_DTYPE_BF16, c, ldc, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,218 @@
+// Device helpers shared by the NVFP4 kernels (gfx950 / CDNA4).
+//
+// Format (guiahardware.es "NVFP4: cos'e e come supera FP8 e BF16", section
+// "Cos'e NVFP4"; chaitex.ru "FP4", mathematical-structure section): E2M1
+// elements, one E4M3 scale per 16 elements, one FP32 tensor scale.
+//
+// Every helper here is exact with respect to the IEEE FP32 convention the
+// C ABI documents (include/nvfp4.h): each step is one FP32 operation rounded
+// to nearest-even.  The hardware conversions used were checked to round to
+// nearest-even: FP32->E2M1 (v_cvt_scalef32_pk_fp4_f32, saturating, sign
+// kept) and FP32->E4M3 (v_cvt_pk_fp8_f32, which gives NaN from 464 on, so
+// inputs are clamped to 448 first).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 6 * 448: largest E2M1 magnitude times largest E4M3 magnitude.
+constexpr float kGlobalDivisor = 2688.0f;
+
+// ---------------------------------------------------------------- loads
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight consecutive input values (BF16 or FP32) starting at p (16-byte aligned).
+template <bool kBF16>
+__device__ __forceinline__ void load8(const void* p, float v[8])
+{
+    if (kBF16) {
+        u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_lo(w[i]);
+            v[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+        u32x4 a = reinterpret_cast<const u32x4*>(p)[0];
+        u32x4 b = reinterpret_cast<const u32x4*>(p)[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = __uint_as_float(a[i]);
+            v[4 + i] = __uint_as_float(b[i]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- E4M3
+
+// E4M3 code of t >= 0 (RNE, saturating at 448; +inf also gives 448).
+__device__ __forceinline__ uint32_t e4m3_encode(float t)
+{
+    float c = __builtin_fminf(t, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+
+// FP32 value of the E4M3 code held in the low byte of `code`.
+__device__ __forceinline__ float e4m3_decode(uint32_t code)
+{
+    return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
+
+// ---------------------------------------------------------------- division
+
+// Correctly rounded |x| / d for a block: r = RN(1/d) comes from one IEEE
+// division per block; two FMA refinement steps (Markstein) then give
+// RN(|x|/d) per element.  The first step turns q0 = RN(|x| r) into an
+// approximation within one ulp; the second is Markstein's theorem
+// (correct rounding from a faithful quotient and a correctly rounded
+// reciprocal, with exact FMA remainders).  Valid when no intermediate
+// underflows or overflows; callers route the rest through IEEE division.
+__device__ __forceinline__ float div_markstein(float ax, float d, float r)
+{
+    float q0 = ax * r;
+    float e0 = __builtin_fmaf(-q0, d, ax);
+    float q1 = __builtin_fmaf(e0, r, q0);
+    float e1 = __builtin_fmaf(-q1, d, ax);
+    return __builtin_fmaf(e1, r, q1);
+}
+
+// Per-block quotient context: d = RN(e * s_g) and r = RN(1/d).
+struct BlockDiv {
+    float d, r;
+    bool fast;  // d far from the FP32 range ends: Markstein applies when |x| is not tiny
+};
+
+__device__ __forceinline__ BlockDiv make_block_div(float d)
+{
+    BlockDiv b;
+    b.d = d;
+    b.r = 1.0f / d;
+    b.fast = (d >= 0x1p-60f) && (d <= 0x1p60f);
+    return b;
+}
+
+// RN(x / d) with the sign of x (so -0 stays -0).
+__device__ __forceinline__ float quotient(float x, const BlockDiv& b)
+{
+    float ax = __builtin_fabsf(x);
+    float y;
+    if (b.fast && ax >= 0x1p-60f) {
+        y = div_markstein(ax, b.d, b.r);
+    } else {
+        y = ax / b.d;  // IEEE division (tiny or extreme operands)
+    }
+    return __uint_as_float(__float_as_uint(y) | (__float_as_uint(x) & 0x80000000u));
+}
+
+// ---------------------------------------------------------------- E2M1
+
+// Two E2M1 codes (RNE, saturating, sign kept) packed into byte `sel` of `old`:
+// low nibble = a, high nibble = b.
+template <int sel>
+__device__ __forceinline__ uint32_t fp4_pack2(uint32_t old, float a, float b)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, sel);
+}
+
+// Magnitude of E2M1 code c (0..7) as FP32.
+__device__ __forceinline__ float e2m1_mag(uint32_t c)
+{
+    // 0, 0.5, 1, 1.5 for c < 4; (1 + (c & 1)/2) * 2^((c >> 1) - 1) above
+    float small = 0.5f * (float)c;
+    float big = __builtin_ldexpf(1.0f + 0.5f * (float)(c & 1u), (int)(c >> 1) - 1);
+    return c < 4 ? small : big;
+}
+
+// Stochastic rounding of |y| (y already RN(x/d), sign carried separately) to an
+// E2M1 magnitude code using the uniform word r: round up from the lower
+// neighbour lo to hi when r < frac * 2^32, frac = (|y| - lo) / (hi - lo).
+// `rne` is the RNE magnitude code of |y| (0..7).
+__device__ __forceinline__ uint32_t e2m1_sr_mag(float ay, uint32_t rne, uint32_t r)
+{
+    if (ay >= 6.0f) return 7u;
+    uint32_t lo = (e2m1_mag(rne) > ay) ? rne - 1u : rne;
+    float vlo = e2m1_mag(lo);
+    float inv_step = lo < 4u ? 2.0f : (lo < 6u ? 1.0f : 0.5f);
+    float frac = (ay - vlo) * inv_step;        // exact (Sterbenz, power-of-two step)
+    float thr = __builtin_ceilf(frac * 4294967296.0f);  // exact; < 2^32
+    uint32_t t = (uint32_t)thr;
+    return (r < t) ? lo + 1u : lo;
+}
+
+// ---------------------------------------------------------------- Philox
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): multipliers
+// 0xD2511F53 / 0xCD9E8D57, Weyl key increments 0x9E3779B9 / 0xBB67AE85.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+        u32x4 n;
+        n[0] = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+        n[1] = (uint32_t)p1;
+        n[2] = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        n[3] = (uint32_t)p0;
+        c = n;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// The four stochastic-rounding words for flat element indices 4g .. 4g+3.
+__device__ __forceinline__ u32x4 sr_words(uint64_t seed, uint32_t stream_id, uint64_t g)
+{
+    u32x4 c;
+    c[0] = (uint32_t)g;
+    c[1] = (uint32_t)(g >> 32);
+    c[2] = stream_id;
+    c[3] = 0u;
+    return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+// ---------------------------------------------------------------- RHT16
+
+// y = 1/4 * H16 * D * x on 16 values in registers: sign flips from `mask`
+// (bit i set -> element i negated), butterflies at distances 1, 2, 4, 8,
+// then the 1/4 scaling.  Same FP32 operation order as the documented
+// convention.
+__device__ __forceinline__ void rht16_inplace(float v[16], uint32_t mask)
+{
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((mask >> i) & 1u) << 31));
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j & h) continue;
+            float a = v[j], b = v[j + h];
+            v[j] = a + b;
+            v[j + h] = a - b;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0.25f * v[i];
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,64 @@
+// Internal launchers behind the C ABI (include/nvfp4.h).  Arguments have
+// already been validated by api.cpp; every launcher enqueues on `stream` and
+// returns the hipError_t of the last launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+struct QuantArgs {
+    const void* x;
+    bool bf16;
+    int64_t rows, cols, ld;
+    int block2d;     // 0: 1x16, 1: 16x16
+    int axis;        // 1D only: 1 along columns, 0 along rows
+    bool sr;
+    uint64_t seed;
+    uint32_t stream_id;
+    bool rht;
+    uint32_t mask;
+    uint8_t* codes;
+    uint8_t* scales;
+    float* tensor_scale;
+    float* amax_out;
+};
+
+// Number of per-workgroup partial maxima the amax pass writes (<= this).
+constexpr int kMaxAmaxPartials = 2048;
+
+// Pass 1: partial maxima of |x| (after the RHT when enabled) into partials[],
+// then reduce them into *amax_dst (and *amax_out when non-null).
+hipError_t launch_amax(const QuantArgs& a, float* partials, float* amax_dst, hipStream_t s);
+
+// Pass 2: quantize using the amax at *amax_src; writes codes, scales,
+// tensor_scale (and amax_out when amax_src is the caller's amax_in).
+hipError_t launch_quantize(const QuantArgs& a, const float* amax_src, bool write_amax_out,
+                           hipStream_t s);
+
+// Empty tensor: s_g = 0 and amax = 0.
+hipError_t launch_write_zero_scale(float* tensor_scale, float* amax_out, hipStream_t s);
+
+hipError_t launch_rht16(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                        int axis, uint32_t mask, float* y, int64_t ld_y, hipStream_t s);
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts,
+                             int64_t rows, int64_t cols, int block2d, int axis, bool out_bf16,
+                             void* out, int64_t ld_out, hipStream_t s);
+
+struct GemmOperand {
+    const uint8_t* codes;
+    const uint8_t* scales;
+    const float* ts;
+    int block2d;
+    bool k_major;  // true: codes packed along K (storage [MN, K]); false: storage [K, MN]
+};
+
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
+                       const GemmOperand& B, bool out_bf16, void* c, int64_t ldc, hipStream_t s);
+
+hipError_t launch_fill_zero(void* c, bool bf16, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
+
+}  // namespace nvfp4

@@ -1,0 +1,687 @@
+// NVFP4 quantization, 16-point RHT and dequantization kernels for gfx950.
+//
+// Two-level microscaling (guiahardware.es "NVFP4: cos'e e come supera FP8 e
+// BF16", section "Cos'e NVFP4"; chaitex.ru "FP4", items 1-2 of the
+// mathematical-structure section): per 16-element block an E4M3 scale, per
+// tensor an FP32 scale.  Recipe (readjensen.com NVFP4 training-recipe page,
+// recipe paragraph): 1x16 blocks for activations/gradients, 16x16 blocks for
+// weights, a random Hadamard transform on wgrad inputs, stochastic rounding
+// of gradients.
+//
+// All kernels stream HBM once: 16-byte loads, every value kept in registers
+// from load to packed store.  The global amax is a separate pass (the tensor
+// scale depends on every element) that writes per-workgroup partial maxima;
+// a one-workgroup kernel reduces them.  No atomics, so results do not depend
+// on scheduling.
+#include "device_common.h"
+#include "launch.h"
+
+namespace nvfp4 {
+
+// ------------------------------------------------------------ fast division
+
+// Unsigned 32-bit division by a runtime constant (Granlund & Montgomery,
+// "Division by invariant integers using multiplication", PLDI'94): with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, n / d equals
+// (umulhi(n, m) + n) >> l for every 32-bit n.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+static FastDiv make_fastdiv(uint32_t d)
+{
+    FastDiv f;
+    f.d = d;
+    uint32_t l = 0;
+    while (((uint64_t)1 << l) < d) ++l;
+    f.l = l;
+    f.m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f)
+{
+    uint64_t t = (uint64_t)__umulhi(n, f.m) + n;
+    return (uint32_t)(t >> f.l);
+}
+
+// ------------------------------------------------------------ block logic
+
+struct QuantParams {
+    const uint8_t* x;  // bytes
+    int64_t rows, cols, ld;  // ld in elements
+    uint8_t* codes;
+    uint8_t* scales;
+    const float* amax_src;
+    float* tensor_scale;
+    float* amax_out;
+    float* partials;
+    uint64_t seed;
+    uint32_t stream_id;
+    uint32_t mask;
+    uint32_t items;  // work items of the kernel's mapping (< 2^32)
+    FastDiv div;     // items per row-group, for the item -> (row, col) split
+    int write_amax_out;
+};
+
+struct TensorScale {
+    float s_g;
+    BlockDiv d6;  // division by RN(6 * s_g)
+};
+
+__device__ __forceinline__ TensorScale make_tensor_scale(float amax)
+{
+    TensorScale t;
+    t.s_g = amax / kGlobalDivisor;
+    t.d6 = make_block_div(6.0f * t.s_g);
+    return t;
+}
+
+// Block scale from the block amax.  Returns the E4M3 code (0 for a zero
+// block) and fills bd with d = RN(e * s_g) and its reciprocal.
+__device__ __forceinline__ uint32_t block_scale(float aB, const TensorScale& ts, BlockDiv& bd,
+                                                bool& zero)
+{
+    zero = true;
+    bd.d = 1.0f;
+    bd.r = 1.0f;
+    bd.fast = true;
+    if (!(aB > 0.0f)) return 0u;
+    float t = quotient(aB, ts.d6);  // RN(a_B / RN(6 s_g))
+    uint32_t e = e4m3_encode(t);
+    float d = e4m3_decode(e) * ts.s_g;
+    if (e == 0u || d == 0.0f) return 0u;
+    zero = false;
+    bd = make_block_div(d);
+    return e;
+}
+
+// Codes for n consecutive elements (n = 8) packed low-nibble-first into
+// n/2 bytes of `out` words.  y[] are RN(x/d) with the sign of x.
+__device__ __forceinline__ uint32_t pack8_rne(const float y[8])
+{
+    uint32_t w = 0u;
+    w = fp4_pack2<0>(w, y[0], y[1]);
+    w = fp4_pack2<1>(w, y[2], y[3]);
+    w = fp4_pack2<2>(w, y[4], y[5]);
+    w = fp4_pack2<3>(w, y[6], y[7]);
+    return w;
+}
+
+// Stochastic rounding of 8 quotients with their 8 uniform words.
+__device__ __forceinline__ uint32_t pack8_sr(const float y[8], const uint32_t r[8])
+{
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_fabsf(y[i]);
+    uint32_t rne = pack8_rne(a);  // RNE magnitudes of |y|
+    uint32_t w = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t mag = e2m1_sr_mag(a[i], (rne >> (4 * i)) & 7u, r[i]);
+        uint32_t sgn = __float_as_uint(y[i]) >> 31;
+        w |= ((sgn << 3) | mag) << (4 * i);
+    }
+    return w;
+}
+
+// Quantize 8 values sharing one block scale.
+template <bool kSR>
+__device__ __forceinline__ uint32_t encode8(const float v[8], const BlockDiv& bd, bool zero,
+                                            const uint32_t r[8])
+{
+    if (zero) return 0u;
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = quotient(v[i], bd);
+    return kSR ? pack8_sr(y, r) : pack8_rne(y);
+}
+
+__device__ __forceinline__ void block_reduce_max_store(float m, float* dst)
+{
+    __shared__ float red[16];
+    m = wave_max(m);
+    int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float r = red[0];
+        for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = __builtin_fmaxf(r, red[i]);
+        *dst = r;
+    }
+}
+
+__device__ __forceinline__ void write_scale_outputs(const QuantParams& p, const TensorScale& ts)
+{
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *p.tensor_scale = ts.s_g;
+        if (p.write_amax_out) *p.amax_out = *p.amax_src;
+    }
+}
+
+// ------------------------------------------------------------ 1x16 along rows
+
+// One thread per 16-element block of a row (axis 1).  Work item b is block
+// cb = b % (cols/16) of row b / (cols/16); its flat element index is 16 b.
+template <bool kBF16, bool kSR, bool kRHT, bool kAmaxOnly, bool kDense>
+__global__ __launch_bounds__(256) void k_quant_rows(QuantParams p)
+{
+    constexpr int esz = kBF16 ? 2 : 4;
+    float amax_local = 0.0f;
+    TensorScale ts;
+    if (!kAmaxOnly) {
+        ts = make_tensor_scale(*p.amax_src);
+        write_scale_outputs(p, ts);
+    }
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t b = blockIdx.x * blockDim.x + threadIdx.x; b < p.items; b += stride) {
+        const uint8_t* src;
+        if (kDense) {
+            src = p.x + (int64_t)b * 16 * esz;
+        } else {
+            uint32_t row = fdiv(b, p.div);
+            uint32_t cb = b - row * p.div.d;
+            src = p.x + ((int64_t)row * p.ld + (int64_t)cb * 16) * esz;
+        }
+        float v[16];
+        load8<kBF16>(src, v);
+        load8<kBF16>(src + 8 * esz, v + 8);
+        if (kRHT) rht16_inplace(v, p.mask);
+        float aB = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) aB = __builtin_fmaxf(aB, __builtin_fabsf(v[i]));
+        if (kAmaxOnly) {
+            amax_local = __builtin_fmaxf(amax_local, aB);
+            continue;
+        }
+        BlockDiv bd;
+        bool zero;
+        uint32_t e = block_scale(aB, ts, bd, zero);
+        uint32_t r[16];
+        if (kSR) {
+            uint64_t g = (uint64_t)b * 4;  // flat index 16 b, four words per Philox call
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x4 w = sr_words(p.seed, p.stream_id, g + q);
+                r[4 * q] = w[0]; r[4 * q + 1] = w[1]; r[4 * q + 2] = w[2]; r[4 * q + 3] = w[3];
+            }
+        }
+        u32x2 out;
+        out[0] = encode8<kSR>(v, bd, zero, r);
+        out[1] = encode8<kSR>(v + 8, bd, zero, r + 8);
+        *reinterpret_cast<u32x2*>(p.codes + (int64_t)b * 8) = out;
+        p.scales[b] = (uint8_t)e;
+    }
+    if (kAmaxOnly) block_reduce_max_store(amax_local, p.partials + blockIdx.x);
+}
+
+// ------------------------------------------------------------ 1x16 along columns
+
+// One thread per 16-row x 8-column tile (axis 0): 8 column blocks.  Work item
+// t is column group cg = t % (cols/8) of row block rb = t / (cols/8).  Each
+// row of the tile is one 16-byte (BF16) load; a wave reads 1 KB per row.
+template <bool kBF16, bool kSR, bool kRHT, bool kAmaxOnly>
+__global__ __launch_bounds__(256) void k_quant_cols(QuantParams p)
+{
+    constexpr int esz = kBF16 ? 2 : 4;
+    float amax_local = 0.0f;
+    TensorScale ts;
+    if (!kAmaxOnly) {
+        ts = make_tensor_scale(*p.amax_src);
+        write_scale_outputs(p, ts);
+    }
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < p.items; t += stride) {
+        uint32_t rb = fdiv(t, p.div);
+        uint32_t cg = t - rb * p.div.d;
+        int64_t r0 = (int64_t)rb * 16, c0 = (int64_t)cg * 8;
+        float v[16][8];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) load8<kBF16>(p.x + ((r0 + i) * p.ld + c0) * esz, v[i]);
+        if (kRHT) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float col[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) col[i] = v[i][j];
+                rht16_inplace(col, p.mask);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i][j] = col[i];
+            }
+        }
+        float aB[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            aB[j] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) aB[j] = __builtin_fmaxf(aB[j], __builtin_fabsf(v[i][j]));
+        }
+        if (kAmaxOnly) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax_local = __builtin_fmaxf(amax_local, aB[j]);
+            continue;
+        }
+        BlockDiv bd[8];
+        bool zero[8];
+        uint32_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = block_scale(aB[j], ts, bd[j], zero[j]);
+        u32x2 sc;
+        sc[0] = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
+        sc[1] = e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24);
+        *reinterpret_cast<u32x2*>(p.scales + rb * p.cols + c0) = sc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float y[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] = zero[j] ? 0.0f : quotient(v[i][j], bd[j]);
+            uint32_t w;
+            if (kSR) {
+                uint64_t g = (uint64_t)((r0 + i) * p.cols + c0) >> 2;
+                u32x4 w0 = sr_words(p.seed, p.stream_id, g);
+                u32x4 w1 = sr_words(p.seed, p.stream_id, g + 1);
+                uint32_t r[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+                w = pack8_sr(y, r);
+                // zero blocks give code 0 regardless of the word
+                uint32_t keep = 0u;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) keep |= zero[j] ? 0u : (0xFu << (4 * j));
+                w &= keep;
+            } else {
+                w = pack8_rne(y);
+            }
+            *reinterpret_cast<uint32_t*>(p.codes + (r0 + i) * (p.cols / 2) + c0 / 2) = w;
+        }
+    }
+    if (kAmaxOnly) block_reduce_max_store(amax_local, p.partials + blockIdx.x);
+}
+
+// ------------------------------------------------------------ 16x16 blocks
+
+// One wave per 16-row x 256-column strip; lane l covers columns
+// 16 (l % 16) .. +15 of rows (l / 16) + 4k, k = 0..3, so the four lanes
+// holding one 16x16 block combine their maxima with two lane swaps.
+// Work item w (a wave) is column strip w % strips of row block w / strips.
+template <bool kBF16, bool kSR>
+__global__ __launch_bounds__(256) void k_quant_2d(QuantParams p)
+{
+    constexpr int esz = kBF16 ? 2 : 4;
+    TensorScale ts = make_tensor_scale(*p.amax_src);
+    write_scale_outputs(p, ts);
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t waves = gridDim.x * (blockDim.x >> 6);
+    const uint32_t cg = lane & 15, rq = lane >> 4;
+    for (uint32_t w = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); w < p.items;
+         w += waves) {
+        uint32_t rb = fdiv(w, p.div);
+        uint32_t strip = w - rb * p.div.d;
+        int64_t c0 = (int64_t)strip * 256 + cg * 16;
+        bool valid = c0 < p.cols;
+        int64_t rbase = (int64_t)rb * 16 + rq;
+        float v[4][16];
+        float aB = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (valid) {
+                const uint8_t* src = p.x + ((rbase + 4 * k) * p.ld + c0) * esz;
+                load8<kBF16>(src, v[k]);
+                load8<kBF16>(src + 8 * esz, v[k] + 8);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[k][i] = 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) aB = __builtin_fmaxf(aB, __builtin_fabsf(v[k][i]));
+        }
+        aB = __builtin_fmaxf(aB, __shfl_xor(aB, 16, 64));
+        aB = __builtin_fmaxf(aB, __shfl_xor(aB, 32, 64));
+        if (!valid) continue;
+        BlockDiv bd;
+        bool zero;
+        uint32_t e = block_scale(aB, ts, bd, zero);
+        if (rq == 0) p.scales[(int64_t)rb * (p.cols / 16) + c0 / 16] = (uint8_t)e;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int64_t row = rbase + 4 * k;
+            uint32_t r[16];
+            if (kSR) {
+                uint64_t g = (uint64_t)(row * p.cols + c0) >> 2;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u32x4 ww = sr_words(p.seed, p.stream_id, g + q);
+                    r[4 * q] = ww[0]; r[4 * q + 1] = ww[1]; r[4 * q + 2] = ww[2]; r[4 * q + 3] = ww[3];
+                }
+            }
+            u32x2 out;
+            out[0] = encode8<kSR>(v[k], bd, zero, r);
+            out[1] = encode8<kSR>(v[k] + 8, bd, zero, r + 8);
+            *reinterpret_cast<u32x2*>(p.codes + row * (p.cols / 2) + c0 / 2) = out;
+        }
+    }
+}
+
+// ------------------------------------------------------------ amax reduce
+
+__global__ __launch_bounds__(256) void k_amax_finalize(const float* partials, int n,
+                                                       float* amax_dst, float* amax_out)
+{
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) m = __builtin_fmaxf(m, partials[i]);
+    __shared__ float red[4];
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float r = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+        *amax_dst = r;
+        if (amax_out) *amax_out = r;
+    }
+}
+
+__global__ void k_write_zero_scale(float* ts, float* amax_out)
+{
+    *ts = 0.0f;
+    if (amax_out) *amax_out = 0.0f;
+}
+
+// ------------------------------------------------------------ RHT16 standalone
+
+// axis 1: one thread per 16-element group of a row; axis 0: one thread per
+// 16-row x 8-column tile.  FP32 output.
+template <bool kBF16>
+__global__ __launch_bounds__(256) void k_rht16_rows(const uint8_t* x, int64_t ld, uint32_t items,
+                                                    FastDiv div, uint32_t mask, float* y,
+                                                    int64_t ld_y)
+{
+    constexpr int esz = kBF16 ? 2 : 4;
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t b = blockIdx.x * blockDim.x + threadIdx.x; b < items; b += stride) {
+        uint32_t row = fdiv(b, div);
+        uint32_t cb = b - row * div.d;
+        const uint8_t* src = x + ((int64_t)row * ld + (int64_t)cb * 16) * esz;
+        float v[16];
+        load8<kBF16>(src, v);
+        load8<kBF16>(src + 8 * esz, v + 8);
+        rht16_inplace(v, mask);
+        float* dst = y + (int64_t)row * ld_y + (int64_t)cb * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u32x4 w;
+            w[0] = __float_as_uint(v[4 * i]); w[1] = __float_as_uint(v[4 * i + 1]);
+            w[2] = __float_as_uint(v[4 * i + 2]); w[3] = __float_as_uint(v[4 * i + 3]);
+            reinterpret_cast<u32x4*>(dst)[i] = w;
+        }
+    }
+}
+
+template <bool kBF16>
+__global__ __launch_bounds__(256) void k_rht16_cols(const uint8_t* x, int64_t ld, uint32_t items,
+                                                    FastDiv div, uint32_t mask, float* y,
+                                                    int64_t ld_y)
+{
+    constexpr int esz = kBF16 ? 2 : 4;
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < items; t += stride) {
+        uint32_t rb = fdiv(t, div);
+        uint32_t cg = t - rb * div.d;
+        int64_t r0 = (int64_t)rb * 16, c0 = (int64_t)cg * 8;
+        float v[16][8];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) load8<kBF16>(x + ((r0 + i) * ld + c0) * esz, v[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float col[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) col[i] = v[i][j];
+            rht16_inplace(col, mask);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i][j] = col[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float* dst = y + (r0 + i) * ld_y + c0;
+            u32x4 a, b;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[j] = __float_as_uint(v[i][j]);
+                b[j] = __float_as_uint(v[i][4 + j]);
+            }
+            reinterpret_cast<u32x4*>(dst)[0] = a;
+            reinterpret_cast<u32x4*>(dst)[1] = b;
+        }
+    }
+}
+
+// ------------------------------------------------------------ dequantize
+
+// One thread per 8 consecutive elements of a row (one 32-bit code word).
+// v = RN32((val * e) * s_g); val * e is exact in FP32.
+template <bool kOutBF16, int kMode>  // kMode: 0 = 1D axis 1, 1 = 1D axis 0, 2 = 2D
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* codes, const uint8_t* scales,
+                                                 const float* ts, int64_t cols, uint32_t items,
+                                                 FastDiv div, uint8_t* out, int64_t ld_out)
+{
+    const float s_g = *ts;
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < items; t += stride) {
+        uint32_t row = fdiv(t, div);
+        uint32_t cq = t - row * div.d;
+        int64_t c0 = (int64_t)cq * 8;
+        uint32_t w = *reinterpret_cast<const uint32_t*>(codes + (int64_t)row * (cols / 2) + c0 / 2);
+        float e[8];
+        if (kMode == 1) {
+            u32x2 s = *reinterpret_cast<const u32x2*>(scales + (int64_t)(row / 16) * cols + c0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                e[j] = e4m3_decode(s[0] >> (8 * j));
+                e[4 + j] = e4m3_decode(s[1] >> (8 * j));
+            }
+        } else {
+            int64_t si = (kMode == 0) ? (int64_t)row * (cols / 16) + c0 / 16
+                                      : (int64_t)(row / 16) * (cols / 16) + c0 / 16;
+            float ev = e4m3_decode(scales[si]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e[j] = ev;
+        }
+        float v[8];
+        float2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+        float2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+        float2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+        float2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+        v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (v[j] * e[j]) * s_g;
+        if (kOutBF16) {
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t a = __float_as_uint(v[2 * j]), b = __float_as_uint(v[2 * j + 1]);
+                a += 0x7FFFu + ((a >> 16) & 1u);  // round to nearest even (finite inputs)
+                b += 0x7FFFu + ((b >> 16) & 1u);
+                o[j] = (a >> 16) | (b & 0xFFFF0000u);
+            }
+            *reinterpret_cast<u32x4*>(out + ((int64_t)row * ld_out + c0) * 2) = o;
+        } else {
+            u32x4 a, b;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[j] = __float_as_uint(v[j]);
+                b[j] = __float_as_uint(v[4 + j]);
+            }
+            u32x4* dst = reinterpret_cast<u32x4*>(out + ((int64_t)row * ld_out + c0) * 4);
+            dst[0] = a;
+            dst[1] = b;
+        }
+    }
+}
+
+// ------------------------------------------------------------ launchers
+
+static int grid_for(uint64_t work_threads, int cap)
+{
+    uint64_t g = (work_threads + 255) / 256;
+    if (g < 1) g = 1;
+    if (g > (uint64_t)cap) g = cap;
+    return (int)g;
+}
+
+constexpr int kGridCap = 8192;  // >= 32 workgroups per CU on 256 CUs
+
+static QuantParams make_params(const QuantArgs& a)
+{
+    QuantParams p{};
+    p.x = static_cast<const uint8_t*>(a.x);
+    p.rows = a.rows;
+    p.cols = a.cols;
+    p.ld = a.ld;
+    p.codes = a.codes;
+    p.scales = a.scales;
+    p.tensor_scale = a.tensor_scale;
+    p.amax_out = a.amax_out;
+    p.seed = a.seed;
+    p.stream_id = a.stream_id;
+    p.mask = a.mask;
+    return p;
+}
+
+// Which kernel family a quantize call maps to, with its work items.
+enum Family { kRows, kCols, k2D };
+
+static Family family_of(const QuantArgs& a)
+{
+    if (a.block2d) return k2D;
+    return a.axis == 1 ? kRows : kCols;
+}
+
+static void set_items(const QuantArgs& a, Family f, QuantParams& p)
+{
+    if (f == kRows) {
+        p.items = (uint32_t)(a.rows * (a.cols / 16));
+        p.div = make_fastdiv((uint32_t)(a.cols / 16));
+    } else if (f == kCols) {
+        p.items = (uint32_t)((a.rows / 16) * (a.cols / 8));
+        p.div = make_fastdiv((uint32_t)(a.cols / 8));
+    } else {
+        uint32_t strips = (uint32_t)((a.cols + 255) / 256);
+        p.items = (uint32_t)((a.rows / 16) * strips);
+        p.div = make_fastdiv(strips);
+    }
+}
+
+#define NVFP4_DISPATCH_BOOL(cond, NAME, ...) \
+    do {                                     \
+        if (cond) {                          \
+            constexpr bool NAME = true;      \
+            __VA_ARGS__;                     \
+        } else {                             \
+            constexpr bool NAME = false;     \
+            __VA_ARGS__;                     \
+        }                                    \
+    } while (0)
+
+hipError_t launch_amax(const QuantArgs& a, float* partials, float* amax_dst, hipStream_t s)
+{
+    QuantParams p = make_params(a);
+    p.partials = partials;
+    // amax without the transform is layout independent: use the row kernel
+    Family f = (a.rht && !a.block2d && a.axis == 0) ? kCols : kRows;
+    QuantArgs aa = a;
+    set_items(aa, f, p);
+    int grid = grid_for(p.items, kMaxAmaxPartials);
+    bool dense = (a.ld == a.cols);
+    bool rht = a.rht && !a.block2d;
+    if (f == kRows) {
+        NVFP4_DISPATCH_BOOL(a.bf16, BF, NVFP4_DISPATCH_BOOL(rht, RH, NVFP4_DISPATCH_BOOL(dense, DE,
+            hipLaunchKernelGGL((k_quant_rows<BF, false, RH, true, DE>), dim3(grid), dim3(256), 0, s,
+                               p))));
+    } else {
+        NVFP4_DISPATCH_BOOL(a.bf16, BF,
+            hipLaunchKernelGGL((k_quant_cols<BF, false, true, true>), dim3(grid), dim3(256), 0, s,
+                               p));
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(256), 0, s, partials, grid, amax_dst,
+                       a.amax_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantArgs& a, const float* amax_src, bool write_amax_out,
+                           hipStream_t s)
+{
+    QuantParams p = make_params(a);
+    p.amax_src = amax_src;
+    p.write_amax_out = write_amax_out && a.amax_out != nullptr;
+    Family f = family_of(a);
+    set_items(a, f, p);
+    bool dense = (a.ld == a.cols);
+    if (f == kRows) {
+        int grid = grid_for(p.items, kGridCap);
+        NVFP4_DISPATCH_BOOL(a.bf16, BF, NVFP4_DISPATCH_BOOL(a.sr, SR,
+            NVFP4_DISPATCH_BOOL(a.rht, RH, NVFP4_DISPATCH_BOOL(dense, DE,
+                hipLaunchKernelGGL((k_quant_rows<BF, SR, RH, false, DE>), dim3(grid), dim3(256), 0,
+                                   s, p)))));
+    } else if (f == kCols) {
+        int grid = grid_for(p.items, kGridCap);
+        NVFP4_DISPATCH_BOOL(a.bf16, BF, NVFP4_DISPATCH_BOOL(a.sr, SR,
+            NVFP4_DISPATCH_BOOL(a.rht, RH,
+                hipLaunchKernelGGL((k_quant_cols<BF, SR, RH, false>), dim3(grid), dim3(256), 0, s,
+                                   p))));
+    } else {
+        int grid = grid_for((uint64_t)p.items * 64, kGridCap);
+        NVFP4_DISPATCH_BOOL(a.bf16, BF, NVFP4_DISPATCH_BOOL(a.sr, SR,
+            hipLaunchKernelGGL((k_quant_2d<BF, SR>), dim3(grid), dim3(256), 0, s, p)));
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_write_zero_scale(float* tensor_scale, float* amax_out, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_write_zero_scale, dim3(1), dim3(1), 0, s, tensor_scale, amax_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_rht16(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                        int axis, uint32_t mask, float* y, int64_t ld_y, hipStream_t s)
+{
+    const uint8_t* xb = static_cast<const uint8_t*>(x);
+    if (axis == 1) {
+        uint32_t items = (uint32_t)(rows * (cols / 16));
+        FastDiv div = make_fastdiv((uint32_t)(cols / 16));
+        int grid = grid_for(items, kGridCap);
+        NVFP4_DISPATCH_BOOL(bf16, BF,
+            hipLaunchKernelGGL((k_rht16_rows<BF>), dim3(grid), dim3(256), 0, s, xb, ld_x, items,
+                               div, mask, y, ld_y));
+    } else {
+        uint32_t items = (uint32_t)((rows / 16) * (cols / 8));
+        FastDiv div = make_fastdiv((uint32_t)(cols / 8));
+        int grid = grid_for(items, kGridCap);
+        NVFP4_DISPATCH_BOOL(bf16, BF,
+            hipLaunchKernelGGL((k_rht16_cols<BF>), dim3(grid), dim3(256), 0, s, xb, ld_x, items,
+                               div, mask, y, ld_y));
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts,
+                             int64_t rows, int64_t cols, int block2d, int axis, bool out_bf16,
+                             void* out, int64_t ld_out, hipStream_t s)
+{
+    uint32_t items = (uint32_t)(rows * (cols / 8));
+    FastDiv div = make_fastdiv((uint32_t)(cols / 8));
+    int grid = grid_for(items, kGridCap);
+    uint8_t* o = static_cast<uint8_t*>(out);
+    int mode = block2d ? 2 : (axis == 1 ? 0 : 1);
+#define NVFP4_DQ(M)                                                                              \
+    NVFP4_DISPATCH_BOOL(out_bf16, OB,                                                            \
+        hipLaunchKernelGGL((k_dequant<OB, M>), dim3(grid), dim3(256), 0, s, codes, scales, ts,   \
+                           cols, items, div, o, ld_out))
+    if (mode == 0) NVFP4_DQ(0);
+    else if (mode == 1) NVFP4_DQ(1);
+    else NVFP4_DQ(2);
+#undef NVFP4_DQ
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

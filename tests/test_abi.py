@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI (CPU only: no call here reaches the GPU).
+
+The library must load and export every entry point include/nvfp4.h declares;
+argument validation must reject bad calls before anything is enqueued (these
+calls return before touching HIP, so they run without a GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import nvfp4_bit_microscaled_amd as m
+    return m.lib
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert names == sorted(["nvfp4_version", "nvfp4_status_string",
+                            "nvfp4_quantize_workspace_size", "nvfp4_quantize", "nvfp4_rht16",
+                            "nvfp4_dequantize", "nvfp4_gemm"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import nvfp4_bit_microscaled_amd as m
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in m.EXPORTS
+
+
+def test_version_and_status_strings(lib):
+    import nvfp4_bit_microscaled_amd as m
+    assert m.version() >= 100
+    for code, name in m.STATUS_NAMES.items():
+        assert m.status_string(code) == name
+    assert m.status_string(99) == "NVFP4_ERR_UNKNOWN"
+    assert m.nvfp4_quantize_workspace_size(1 << 15, 1 << 12) >= 4
+
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10008)
+ODD = ctypes.c_void_p(0x10001)
+
+
+def q(lib, **kw):
+    args = dict(x=FAKE, dt=0, rows=32, cols=64, ld=64, block=0, axis=1, rnd=0, seed=0, sid=0,
+                rht=0, mask=0, amax_in=FAKE, amax_out=None, codes=FAKE, scales=FAKE, ts=FAKE,
+                ws=None, wsb=0, stream=None)
+    args.update(kw)
+    return lib.nvfp4_quantize(*args.values())
+
+
+def test_quantize_validation(lib):
+    assert q(lib, dt=5) == 1
+    assert q(lib, block=3) == 1
+    assert q(lib, rnd=2) == 1
+    assert q(lib, axis=2) == 1
+    assert q(lib, rht=2) == 1
+    assert q(lib, rows=-1) == 1
+    assert q(lib, ts=None) == 1
+    assert q(lib, cols=40, ld=40) == 2              # cols % 16
+    assert q(lib, rows=24, axis=0) == 2             # rows % 16 for axis 0
+    assert q(lib, rows=24, block=1) == 2            # rows % 16 for 2D
+    assert q(lib, ld=32) == 2                       # ld < cols
+    assert q(lib, block=1, rht=1) == 5              # RHT needs 1D
+    assert q(lib, x=MISALIGNED) == 3
+    assert q(lib, ld=68, dt=0) == 3                 # 136-byte BF16 rows are not 16-byte multiples
+    assert q(lib, codes=MISALIGNED) == 3
+    assert q(lib, amax_in=None, ws=None) == 6       # amax pass needs the workspace
+    assert q(lib, amax_in=None, ws=FAKE, wsb=8) == 6
+    assert q(lib, x=None) == 1
+
+
+def g(lib, **kw):
+    args = dict(layout=0, M=64, N=64, K=64, ac=FAKE, asc=FAKE, ats=FAKE, ab=0, bc=FAKE, bsc=FAKE,
+                bts=FAKE, bb=1, odt=0, c=FAKE, ldc=64, stream=None)
+    args.update(kw)
+    return lib.nvfp4_gemm(*args.values())
+
+
+def test_gemm_validation(lib):
+    assert g(lib, layout=3) == 1
+    assert g(lib, odt=7) == 1
+    assert g(lib, M=-1) == 1
+    assert g(lib, K=40) == 2                        # K % 16
+    assert g(lib, ldc=32) == 2
+    assert g(lib, layout=1, N=40, ldc=40) == 2      # NN: B packed along N
+    assert g(lib, layout=2, M=40) == 2              # TN: A packed along M
+    assert g(lib, bb=1, N=40, ldc=40) == 4          # 2D operand with N % 16
+    assert g(lib, c=ODD) == 3
+    assert g(lib, ac=MISALIGNED) == 3
+    assert g(lib, ac=None) == 1
+    assert g(lib, M=0) == 0                         # empty output: nothing to do
+    assert g(lib, N=0) == 0
+
+
+def test_rht_and_dequant_validation(lib):
+    assert lib.nvfp4_rht16(FAKE, 0, 32, 40, 40, 1, 0, FAKE, 40, None) == 2
+    assert lib.nvfp4_rht16(FAKE, 0, 24, 64, 64, 0, 0, FAKE, 64, None) == 2
+    assert lib.nvfp4_rht16(FAKE, 0, 32, 64, 64, 3, 0, FAKE, 64, None) == 1
+    assert lib.nvfp4_rht16(FAKE, 0, 0, 64, 64, 1, 0, FAKE, 64, None) == 0
+    assert lib.nvfp4_dequantize(FAKE, FAKE, FAKE, 32, 40, 0, 1, 0, FAKE, 40, None) == 2
+    assert lib.nvfp4_dequantize(FAKE, FAKE, FAKE, 24, 64, 1, 1, 0, FAKE, 64, None) == 2
+    assert lib.nvfp4_dequantize(FAKE, FAKE, FAKE, 32, 64, 0, 1, 9, FAKE, 64, None) == 1
+    assert lib.nvfp4_dequantize(MISALIGNED, FAKE, FAKE, 32, 64, 0, 1, 0, FAKE, 64, None) == 3

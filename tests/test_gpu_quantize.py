@@ -1,0 +1,177 @@
+"""GPU parity: nvfp4_quantize / nvfp4_rht16 / nvfp4_dequantize against the CPU oracle.
+
+Codes, scales, the tensor scale and amax must be bit-identical (integer
+results decided in FP32 on both sides under the documented convention).
+Sources: two-level microscaling -- guiahardware.es "NVFP4: cos'e e come supera
+FP8 e BF16", section "Cos'e NVFP4"; 2D weight blocks, RHT on wgrad inputs and
+stochastic rounding of gradients -- readjensen.com NVFP4 recipe paragraph.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import to_oracle_input
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_bit_microscaled_amd as m
+    torch.cuda.set_device(0)
+    return m
+
+
+MODES = {"rows": dict(block2d=False, axis=1), "cols": dict(block2d=False, axis=0),
+         "2d": dict(block2d=True, axis=1)}
+
+
+def gen(kind, rows, cols, seed, dtype=torch.bfloat16):
+    f = {"act": workloads.activations, "w": workloads.weights, "grad": workloads.gradients}[kind]
+    x = f(rows, cols, seed=seed)
+    return x if dtype == torch.bfloat16 else x.to(torch.float32)
+
+
+def compare(nv, x_cpu, mode, sr=False, rht=False, mask=0, seed=0, stream_id=0, ld_pad=0,
+            amax_in=None):
+    rows, cols = x_cpu.shape
+    if ld_pad:
+        wide = torch.zeros(rows, cols + ld_pad, dtype=x_cpu.dtype)
+        wide[:, :cols] = x_cpu
+        xg = wide.cuda()[:, :cols]
+    else:
+        xg = x_cpu.cuda()
+    ain = None if amax_in is None else torch.tensor([amax_in], dtype=torch.float32, device="cuda")
+    q = nv.quantize(xg, sr=sr, rht=rht, mask=mask, seed=seed, stream_id=stream_id, amax_in=ain,
+                    **MODES[mode])
+    torch.cuda.synchronize()
+    oc, osc, ots, oam = oracle.quantize(to_oracle_input(x_cpu), sr=sr, rht=rht, mask=mask,
+                                        seed=seed, stream_id=stream_id, amax_in=amax_in,
+                                        **MODES[mode])
+    assert q.tensor_scale.item() == ots
+    assert q.amax.item() == oam
+    gc, gs = q.codes.cpu().numpy(), q.scales.cpu().numpy()
+    nbad_s = int((gs != osc).sum())
+    nbad_c = int((gc != oc).sum())
+    assert nbad_s == 0 and nbad_c == 0, "%d scale bytes and %d code bytes differ" % (nbad_s, nbad_c)
+    return q
+
+
+SHAPES = [(256, 256), (48, 272), (16, 16), (528, 1040), (96, 4112)]
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("kind", ["act", "w", "grad"])
+def test_rne_matches_oracle(nv, mode, shape, kind):
+    compare(nv, gen(kind, *shape, seed=hash((mode, shape, kind)) & 0xFFFF), mode)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("shape", [(256, 256), (48, 272), (528, 1040)])
+def test_sr_matches_oracle(nv, mode, shape):
+    x = gen("grad", *shape, seed=7)
+    compare(nv, x, mode, sr=True, seed=1, stream_id=0)
+    compare(nv, x, mode, sr=True, seed=0xDEADBEEF12345, stream_id=3)
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("sr", [False, True])
+@pytest.mark.parametrize("shape", [(256, 256), (48, 272), (528, 1040)])
+def test_rht_quantize_matches_oracle(nv, axis, sr, shape):
+    x = gen("grad" if sr else "act", *shape, seed=11)
+    mode = "rows" if axis == 1 else "cols"
+    compare(nv, x, mode, sr=sr, rht=True, mask=workloads.sign_mask(1), seed=1, stream_id=1)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_fp32_input_strided_and_amax_in(nv, mode):
+    x = gen("act", 64, 320, seed=3, dtype=torch.float32)
+    compare(nv, x, mode, ld_pad=16)
+    compare(nv, x.to(torch.bfloat16), mode, ld_pad=48)
+    compare(nv, x, mode, amax_in=123.5)
+    compare(nv, x, mode, sr=True, seed=5, amax_in=float(x.abs().max()) * 4)
+
+
+def test_edge_values(nv):
+    rows, cols = 32, 64
+    x = torch.zeros(rows, cols, dtype=torch.float32)
+    x[0, 0] = 2688.0                      # s_g = 1
+    x[1, 16:32] = 1e-4                    # scale underflows: zero block
+    x[2, 32:48] = -0.0                    # all-zero block
+    x[3, 48] = 6 * 2.0 ** -9 * 1.0001     # smallest subnormal E4M3 scale
+    x[3, 49] = -0.0
+    x[4, :16] = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -0.75, -1.25,
+                              -1.75, -2.5, -3.5, -5.0, -6.0]) * (6.0 / 6.0)  # exact E2M1 midpoints
+    x[5, :16] = torch.tensor([1e-40, -1e-40, 3e-39, 1.17e-38, 1e-30, 7.0, 100.0, -1e-45,
+                              0.0, 2.0 ** -126, 2.0 ** -149, 5.9, 6.1, -6.1, 0.1, 0.3])
+    x[6:8, :] = torch.randn(2, cols) * 1e-38  # subnormal-range values
+    for mode in MODES:
+        compare(nv, x, mode)
+        compare(nv, x, mode, sr=True, seed=2)
+    compare(nv, x, "rows", rht=True, mask=0xBEEF)
+    compare(nv, x, "cols", rht=True, mask=0xBEEF, sr=True, seed=3)
+    # all-zero and tiny tensors
+    for mode in MODES:
+        compare(nv, torch.zeros(16, 32), mode)
+        compare(nv, torch.full((16, 32), 1e-42), mode)
+
+
+def test_empty_tensor_writes_zero_scale(nv):
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    q = nv.quantize(x)
+    torch.cuda.synchronize()
+    assert q.tensor_scale.item() == 0.0 and q.amax.item() == 0.0
+
+
+def test_rht16_standalone_matches_oracle(nv):
+    for axis in (0, 1):
+        for dtype in (torch.bfloat16, torch.float32):
+            x = gen("act", 528, 1040, seed=9, dtype=dtype)
+            y = nv.rht16(x.cuda(), axis, 0x5A3C)
+            torch.cuda.synchronize()
+            ref = oracle.rht16(to_oracle_input(x), axis=axis, mask=0x5A3C)
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_fused_rht_equals_rht_then_quantize(nv):
+    x = gen("grad", 256, 512, seed=12)
+    xg = x.cuda()
+    for axis in (0, 1):
+        y = nv.rht16(xg, axis, 0x1234)
+        q1 = nv.quantize(xg, axis=axis, rht=True, mask=0x1234, sr=True, seed=1, stream_id=1)
+        q2 = nv.quantize(y, axis=axis, sr=True, seed=1, stream_id=1)
+        torch.cuda.synchronize()
+        assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
+        assert q1.tensor_scale.item() == q2.tensor_scale.item()
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_dequantize_matches_oracle(nv, mode):
+    x = gen("act", 528, 1040, seed=4)
+    oc, osc, ots, _ = oracle.quantize(to_oracle_input(x), **MODES[mode])
+    t = nv.NVFP4Tensor(torch.from_numpy(oc).cuda(), torch.from_numpy(osc).cuda(),
+                       torch.tensor([ots], dtype=torch.float32, device="cuda"),
+                       torch.zeros(1, device="cuda"), 528, 1040, MODES[mode]["block2d"],
+                       MODES[mode]["axis"])
+    f = nv.dequantize(t, torch.float32)
+    b = nv.dequantize(t, torch.bfloat16)
+    torch.cuda.synchronize()
+    rf, rb = oracle.dequantize(oc, osc, ots, 528, 1040, **MODES[mode])
+    assert np.array_equal(f.cpu().numpy().view(np.uint32), rf.view(np.uint32))
+    assert np.array_equal(b.cpu().view(torch.int16).numpy().view(np.uint16), rb)
+
+
+def test_deterministic_and_stream_ordered(nv):
+    x = gen("grad", 512, 1024, seed=21).cuda()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q1 = nv.quantize(x, axis=0, rht=True, mask=7, sr=True, seed=9)
+        q2 = nv.quantize(x, axis=0, rht=True, mask=7, sr=True, seed=9)
+    s.synchronize()
+    assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
+    q3 = nv.quantize(x, axis=0, rht=True, mask=7, sr=True, seed=10)
+    torch.cuda.synchronize()
+    assert not torch.equal(q1.codes, q3.codes)
