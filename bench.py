@@ -1,0 +1,263 @@
+"""Benchmark: one NVFP4 training step of a Llama-3-8B-shaped MLP on one MI355X.
+
+A step is one pass of the whole hot path over 32768 tokens (seq 8192 x
+batch 4, the benchmark shape of the readjensen.com NVFP4 training-recipe page,
+benchmark paragraph), with the recipe of that page's recipe paragraph:
+
+  fprop   quantize X (1x16 RNE), W_gu and W_down (16x16 RNE)
+          H = X W_gu^T                        NT  32768 x 28672 x 4096
+          Act = silu(gate) * up  (torch, BF16 glue)
+          quantize Act (1x16 RNE)
+          Y = Act W_down^T                    NT  32768 x 4096 x 14336
+  bwd     dY, dH synthetic (Student-t(3) x 1e-3)
+          down:    dAct = dY W_down           NN  32768 x 14336 x 4096   (dY 1x16 SR)
+                   dW_down = dY^T Act         TN  4096 x 14336 x 32768   (RHT16 + SR / RHT16)
+          gate/up: dX = dH W_gu               NN  32768 x 4096 x 28672   (dH 1x16 SR)
+                   dW_gu = dH^T X             TN  28672 x 4096 x 32768   (RHT16 + SR / RHT16)
+
+Inputs are resident in HBM before timing starts.  The JSON line reports the
+step's NVFP4 GEMM throughput (GEMM FLOPs / step time), per-kernel HIP-event
+timings, the roofline of the dominant GEMM kernel and the CPU oracle's
+throughput on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense FP16/BF16 MFMA
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=64)
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events around each library call on the current stream, grouped by kind."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+        self.enabled = False
+
+    def run(self, kind, fn, *a, **kw):
+        if not self.enabled:
+            return fn(*a, **kw)
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r = fn(*a, **kw)
+        e1.record()
+        self.pending.append((kind, e0, e1))
+        return r
+
+    def totals(self):
+        out = {}
+        for kind, e0, e1 in self.pending:
+            t, n = out.get(kind, (0.0, 0))
+            out[kind] = (t + e0.elapsed_time(e1), n + 1)
+        return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import torch.nn.functional as F
+
+    import nvfp4_bit_microscaled_amd as nv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = workloads.LLAMA8B
+    T, D, Fh = cfg["tokens"], cfg["hidden"], cfg["ffn"]
+    mask = workloads.sign_mask(cfg["mask_seed"])
+    sr_seed = cfg["sr_seed"]
+
+    print("generating inputs on the GPU", file=sys.stderr, flush=True)
+    X = workloads.activations(T, D, cfg["x_seed"], device="cuda")
+    W_gu = workloads.weights(2 * Fh, D, cfg["wgu_seed"], device="cuda")
+    W_down = workloads.weights(D, Fh, cfg["wdown_seed"], device="cuda")
+    dY = workloads.gradients(T, D, cfg["dy_seed"], device="cuda")
+    dH = workloads.gradients(T, 2 * Fh, cfg["dh_seed"], device="cuda")
+    torch.cuda.synchronize()
+
+    timer = Timer(torch)
+    gemm_flops = {}   # (name) -> flops per call
+    qbytes = {}       # (name) -> algorithmic HBM bytes per call
+
+    def qb(rows, cols, in_bytes=2, amax_pass=True):
+        # read input (twice when the amax pass runs) + codes + scales
+        return rows * cols * (in_bytes * (2 if amax_pass else 1) + 0.5 + 1 / 16)
+
+    def Q(name, x, **kw):
+        qbytes[name] = qb(*x.shape)
+        return timer.run("quantize", nv.quantize, x, **kw)
+
+    def G(name, layout, a, b, M, N, K, out=None):
+        gemm_flops[name] = 2.0 * M * N * K
+        return timer.run("gemm_" + layout, nv.gemm, layout, a, b, out_dtype=torch.bfloat16,
+                         out=out)
+
+    bufs = {}
+
+    def buf(name, shape):
+        t = bufs.get(name)
+        if t is None:
+            t = bufs[name] = torch.empty(*shape, dtype=torch.bfloat16, device=dev)
+        return t
+
+    def step():
+        # ---- fprop
+        xq = Q("X_rows", X)
+        wgu = Q("Wgu_2d", W_gu, block2d=True)
+        wdn = Q("Wdown_2d", W_down, block2d=True)
+        H = G("fprop_gu", "NT", xq, wgu, T, 2 * Fh, D, out=buf("H", (T, 2 * Fh)))
+        act = timer.run("swiglu", lambda: F.silu(H[:, :Fh]) * H[:, Fh:])
+        aq = Q("Act_rows", act)
+        G("fprop_down", "NT", aq, wdn, T, D, Fh, out=buf("Y", (T, D)))
+        # ---- backward, down projection
+        dyq = Q("dY_rows_sr", dY, sr=True, seed=sr_seed, stream_id=0)
+        G("dgrad_down", "NN", dyq, wdn, T, Fh, D, out=buf("dAct", (T, Fh)))
+        dyt = Q("dY_cols_rht_sr", dY, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,
+                stream_id=1)
+        at = Q("Act_cols_rht", act, axis=0, rht=True, mask=mask)
+        G("wgrad_down", "TN", dyt, at, D, Fh, T, out=buf("dWdown", (D, Fh)))
+        # ---- backward, gate/up projection
+        dhq = Q("dH_rows_sr", dH, sr=True, seed=sr_seed, stream_id=0)
+        G("dgrad_gu", "NN", dhq, wgu, T, D, 2 * Fh, out=buf("dX", (T, D)))
+        dht = Q("dH_cols_rht_sr", dH, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,
+                stream_id=1)
+        xt = Q("X_cols_rht", X, axis=0, rht=True, mask=mask)
+        G("wgrad_gu", "TN", dht, xt, 2 * Fh, D, T, out=buf("dWgu", (2 * Fh, D)))
+
+    print("warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, bracketed by synchronizations
+    timer.enabled = True
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    totals = timer.totals()
+    print("timed %d steps: %.3f ms/step (host wall %.3f s)" % (args.steps, ms_step, wall),
+          file=sys.stderr, flush=True)
+
+    flops_step = sum(gemm_flops.values())
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    per_kind = {k: {"ms_per_step": t / args.steps, "calls_per_step": n / args.steps}
+                for k, (t, n) in totals.items()}
+    # GEMM kernels per layout: flops per launch and average launch time
+    layout_flops = {"NT": gemm_flops["fprop_gu"] + gemm_flops["fprop_down"],
+                    "NN": gemm_flops["dgrad_down"] + gemm_flops["dgrad_gu"],
+                    "TN": gemm_flops["wgrad_down"] + gemm_flops["wgrad_gu"]}
+    gemm_kinds = {}
+    for lay, fl in layout_flops.items():
+        t, n = totals["gemm_" + lay]
+        gemm_kinds[lay] = {"tflops": fl * args.steps / (t * 1e-3) / 1e12,
+                           "avg_launch_ms": t / n, "launches": n}
+    dom = max(gemm_kinds, key=lambda k: totals["gemm_" + k][0])
+    d = gemm_kinds[dom]
+    achieved = d["tflops"]
+    q_t, q_n = totals["quantize"]
+    q_bytes = sum(qbytes.values()) * args.steps
+    gemm_t = sum(totals["gemm_" + k][0] for k in layout_flops)
+    line = {
+        "metric": "NVFP4 GEMM TFLOPS (8B MLP shapes) + quantize GB/s, % of MI355X roofline",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 operands, f16 mfma, f32 accumulate",
+        "data": "synthetic (seeded activations/weights/Student-t gradients, HBM-resident)",
+        "config": {"workload": "llama3-8b-mlp-fwd+bwd-step", "tokens": T, "hidden": D,
+                   "ffn": Fh, "gemm_tflop_per_step": round(flops_step / 1e12, 4),
+                   "parallelism": "none (1 GPU)"},
+        "gemm_only_tflops": round(flops_step * args.steps / (gemm_t * 1e-3) / 1e12, 2),
+        "gemm_by_layout": {k: {kk: round(vv, 4) for kk, vv in v.items()}
+                           for k, v in gemm_kinds.items()},
+        "quantize_GBps": round(q_bytes / (q_t * 1e-3) / 1e9, 1),
+        "quantize_frac_of_hbm": round(q_bytes / (q_t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "time_breakdown_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in per_kind.items()},
+        "roofline": {"bound": "mfma", "kernel": "k_gemm (%s layout)" % dom,
+                     "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+    del bufs
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args, torch, nv, workloads, X, W_gu)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(args, torch, nv, workloads, X, W_gu):
+    """The oracle, as it stands, on a bounded sample of the step: fprop GEMM 1
+    for the first `rows` tokens (all 28672 outputs, full K = 4096)."""
+    import numpy as np
+
+    import oracle
+    rows = args.cpu_sample_rows
+    cores = len(os.sched_getaffinity(0))
+    oracle.set_num_threads(cores)
+    x = X[:rows].cpu()
+    w = W_gu.cpu()
+    t0 = time.perf_counter()
+    xc, xs, xts, _ = oracle.quantize(workloads.bf16_bits(x),
+                                     amax_in=float(X.abs().max().item()))
+    wc, wsc, wts, _ = oracle.quantize(workloads.bf16_bits(w), block2d=True)
+    tq = time.perf_counter() - t0
+    N, K = w.shape
+    ms, ns = np.meshgrid(np.arange(rows), np.arange(N), indexing="ij")
+    t1 = time.perf_counter()
+    oracle.gemm_pairs("NT", rows, N, K, (xc, xs, xts, False), (wc, wsc, wts, True), ms.ravel(),
+                      ns.ravel())
+    tg = time.perf_counter() - t1
+    flops = 2.0 * rows * N * K
+    qbytes = (x.numel() + w.numel()) * (2 + 0.5 + 1 / 16) + w.numel() * 2
+    return {"value": round(flops / tg / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "fprop GEMM 1 (NT, 2D-quantized W_gu) on the first %d tokens: "
+                      "%d x 28672 x 4096 FP64 dot products (%.2f GFLOP) in %.1f s"
+                      % (rows, rows, flops / 1e9, tg),
+            "quantize_GBps": round(qbytes / tq / 1e9, 4),
+            "quantize_sample": "X rows 0-%d (1x16 RNE) and W_gu (16x16 RNE, amax pass), %.1f s"
+                               % (rows - 1, tq)}
+
+
+if __name__ == "__main__":
+    main()
