@@ -51,72 +51,161 @@ __device__ __forceinline__ void transpose8x8_nibbles(const uint32_t in[8], uint3
     }
 }
 
-// Stage one operand's k-tile into LDS as K-contiguous codes [R][BK/2] and
-// per-row scale codes [R][BK/16].  rows0: first row (M or N index) of the
-// tile; MN: operand extent along rows; k0: first K index.
-template <int R, int BK, bool kKMajor, bool k2D>
-__device__ __forceinline__ void stage_operand(const uint8_t* __restrict__ codes,
-                                              const uint8_t* __restrict__ scales, int64_t MN,
-                                              int64_t K, int64_t rows0, int64_t k0,
-                                              uint8_t* lds_codes, uint8_t* lds_scales)
+// ---------------------------------------------------------------------------
+// Main kernel: 256 x 256 output tile per workgroup of 256 threads, K step 128.
+// Four waves in a 2 x 2 grid, each owning a 128 x 128 sub-tile = 4 x 4 MFMA
+// 32x32 accumulators (256 FP32 per lane, held in AGPRs).
+//
+// LDS (per stage, double buffered): for each operand, codes in a
+// "fragment-major" layout -- plane c (0..3) holds, for every tile row, the
+// 16 bytes of codes k in [32c, 32c + 32) -- plus 8 scale bytes per row.  A
+// plane stride of 16*256 + 32 bytes keeps both the staging writes (8 lanes =
+// 2 rows x 4 planes) and the fragment reads (8 lanes = 8 rows of one plane)
+// free of bank conflicts.
+//
+// K order inside a k-tile: lanes 0-31 take planes {0, 2}, lanes 32-63 planes
+// {1, 3}; MFMA step s = 4h + q uses 32-bit word q of plane (lane/32 + 2h).
+// The MFMA sums over both lane halves, so step s contracts the 16 codes
+// k = 64h + 8q + [0, 8) and 64h + 32 + 8q + [0, 8): a permutation of K that
+// A and B share, so the sum is unchanged.  Each lane scales its own 8 codes
+// by the E4M3 scale of their 16-block, so blocks need not align with MFMA
+// steps.  Scale bytes of a row are stored as blocks (0,1,4,5 | 2,3,6,7) so a
+// lane reads its four with one 32-bit load.
+// ---------------------------------------------------------------------------
+constexpr int kTM = 256, kTN = 256, kTK = 128;
+constexpr int kPlaneStride = 256 * 16 + 32;
+constexpr int kCodeTile = 4 * kPlaneStride;      // 16512 bytes
+constexpr int kScaleTile = 256 * 8;              // 2048 bytes
+constexpr int kOperandTile = kCodeTile + kScaleTile;
+constexpr int kStage = 2 * kOperandTile;         // A and B
+constexpr int kLdsBytes = 2 * kStage;            // double buffered: 74240 bytes
+
+// Per-thread staging registers for one operand's k-tile.
+struct Staged {
+    u32x4 code[4];   // K-major: 4 x 16-byte chunks; MN-major: 8 x 8 bytes in code[0..3]
+    uint32_t sc[8];  // scale bytes (K-major: sc[0..1] hold 8 bytes; MN-major: one per entry)
+};
+
+template <bool kKMajor, bool k2D, bool kFull>
+__device__ __forceinline__ void stage_load(const uint8_t* __restrict__ codes,
+                                           const uint8_t* __restrict__ scales, int64_t MN,
+                                           int64_t K, int64_t row0, int64_t k0, Staged& st)
 {
-    constexpr int kCodeRowBytes = BK / 2;
-    constexpr int kKB = BK / 16;
-    const int tid = threadIdx.x;
+    const int t = threadIdx.x;
     if (kKMajor) {
-        // storage [MN, K]: codes row stride K/2 bytes, u32 = 8 K-consecutive codes
-        constexpr int kChunks = R * BK / 8;
-        for (int c = tid; c < kChunks; c += 256) {
-            int r = c / (BK / 8), q = c % (BK / 8);
-            int64_t row = rows0 + r, k = k0 + q * 8;
-            uint32_t w = 0u;
-            if (row < MN && k < K)
-                w = *reinterpret_cast<const uint32_t*>(codes + row * (K / 2) + k / 2);
-            *reinterpret_cast<uint32_t*>(lds_codes + r * kCodeRowBytes + q * 4) = w;
+        // chunk f = it*256 + t: row f/4, plane f%4 (16 bytes = 32 codes)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            int f = it * 256 + t;
+            int r = f >> 2, c = f & 3;
+            int64_t row = row0 + r, k = k0 + 32 * c;
+            const uint8_t* src = codes + row * (K / 2) + k / 2;
+            if (kFull) {
+                st.code[it] = *reinterpret_cast<const u32x4*>(src);
+            } else {  // rows are only 8-byte aligned when K % 32 != 0: 4-byte loads
+                u32x4 w = {0u, 0u, 0u, 0u};
+                if (row < MN) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (k + 8 * q < K) w[q] = reinterpret_cast<const uint32_t*>(src)[q];
+                }
+                st.code[it] = w;
+            }
         }
-        for (int c = tid; c < R * kKB; c += 256) {
-            int r = c / kKB, j = c % kKB;
-            int64_t row = rows0 + r, kb = k0 / 16 + j;
-            uint8_t e = 0;
-            if (row < MN && kb * 16 < K)
-                e = k2D ? scales[(row / 16) * (K / 16) + kb] : scales[row * (K / 16) + kb];
-            lds_scales[r * kKB + j] = e;
+        // scales: thread t owns row t, 8 bytes (k-blocks k0/16 .. +7)
+        int64_t row = row0 + t, kb = k0 / 16;
+        int64_t ld = K / 16;
+        const uint8_t* src = scales + (k2D ? (row / 16) * ld : row * ld) + kb;
+        if (kFull) {
+            u32x2 w = *reinterpret_cast<const u32x2*>(src);
+            st.sc[0] = w[0];
+            st.sc[1] = w[1];
+        } else {
+            uint32_t w0 = 0u, w1 = 0u;
+            if (row < MN) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    uint32_t b = (kb + j < ld) ? (uint32_t)src[j] : 0u;
+                    if (j < 4) w0 |= b << (8 * j);
+                    else w1 |= b << (8 * (j - 4));
+                }
+            }
+            st.sc[0] = w0;
+            st.sc[1] = w1;
         }
     } else {
-        // storage [K, MN]: codes row stride MN/2 bytes, u32 = 8 MN-consecutive codes
-        constexpr int kBlocks = (BK / 8) * (R / 8);
-        for (int b = tid; b < kBlocks; b += 256) {
-            int kq = b / (R / 8), mq = b % (R / 8);
-            int64_t kk = k0 + kq * 8, m = rows0 + mq * 8;
-            uint32_t in[8], out[8];
+        // storage [K, MN]: thread t reads 8 k-rows x 8 bytes (16 m) at
+        // k-group kg = t % 16, m-group mg = t / 16
+        int kg = t & 15, mg = t >> 4;
+        int64_t m = row0 + 16 * mg;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                in[i] = 0u;
-                if (kk + i < K && m < MN)
-                    in[i] = *reinterpret_cast<const uint32_t*>(codes + (kk + i) * (MN / 2) + m / 2);
-            }
-            transpose8x8_nibbles(in, out);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint32_t*>(lds_codes + (mq * 8 + j) * kCodeRowBytes + kq * 4) =
-                    out[j];
+        for (int i = 0; i < 8; ++i) {
+            int64_t k = k0 + 8 * kg + i;
+            u32x2 w = {0u, 0u};
+            if (kFull || (k < K && m < MN))
+                w = *reinterpret_cast<const u32x2*>(codes + k * (MN / 2) + m / 2);
+            st.code[i >> 1][2 * (i & 1)] = w[0];
+            st.code[i >> 1][2 * (i & 1) + 1] = w[1];
         }
-        for (int c = tid; c < R * kKB; c += 256) {
-            int r = c / kKB, j = c % kKB;
-            int64_t m = rows0 + r, kb = k0 / 16 + j;
-            uint8_t e = 0;
-            if (m < MN && kb * 16 < K)
-                e = k2D ? scales[kb * (MN / 16) + m / 16] : scales[kb * MN + m];
-            lds_scales[r * kKB + j] = e;
+        // scales: thread t owns tile row t, one byte per k-block
+        int64_t row = row0 + t;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int64_t kb = k0 / 16 + j;
+            uint32_t b = 0u;
+            if (kFull || (row < MN && kb * 16 < K))
+                b = k2D ? scales[kb * (MN / 16) + row / 16] : scales[kb * MN + row];
+            st.sc[j] = b;
         }
     }
 }
 
-// Decode the lane's 8 codes (one 32-bit word) times its E4M3 block scale into
-// an FP16 MFMA operand.
-__device__ __forceinline__ half8_t dequant8(uint32_t w, uint32_t scale_code)
+template <bool kKMajor>
+__device__ __forceinline__ void stage_store(const Staged& st, uint8_t* tile)
 {
-    _Float16 e = (_Float16)e4m3_decode(scale_code);
+    const int t = threadIdx.x;
+    uint8_t* sct = tile + kCodeTile;
+    uint32_t s0, s1;  // scale bytes b0..b7 of the row, before reordering
+    int srow;
+    if (kKMajor) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            int f = it * 256 + t;
+            int r = f >> 2, c = f & 3;
+            *reinterpret_cast<u32x4*>(tile + c * kPlaneStride + r * 16) = st.code[it];
+        }
+        s0 = st.sc[0];
+        s1 = st.sc[1];
+        srow = t;
+    } else {
+        int kg = t & 15, mg = t >> 4;
+        uint32_t lo[8], hi[8], tlo[8], thi[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            lo[i] = st.code[i >> 1][2 * (i & 1)];
+            hi[i] = st.code[i >> 1][2 * (i & 1) + 1];
+        }
+        transpose8x8_nibbles(lo, tlo);
+        transpose8x8_nibbles(hi, thi);
+        uint8_t* base = tile + (kg >> 2) * kPlaneStride + 4 * (kg & 3);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            *reinterpret_cast<uint32_t*>(base + (16 * mg + j) * 16) = tlo[j];
+            *reinterpret_cast<uint32_t*>(base + (16 * mg + 8 + j) * 16) = thi[j];
+        }
+        s0 = st.sc[0] | (st.sc[1] << 8) | (st.sc[2] << 16) | (st.sc[3] << 24);
+        s1 = st.sc[4] | (st.sc[5] << 8) | (st.sc[6] << 16) | (st.sc[7] << 24);
+        srow = t;
+    }
+    u32x2 w;
+    w[0] = __builtin_amdgcn_perm(s1, s0, 0x05040100u);  // b0 b1 b4 b5
+    w[1] = __builtin_amdgcn_perm(s1, s0, 0x07060302u);  // b2 b3 b6 b7
+    *reinterpret_cast<u32x2*>(sct + srow * 8) = w;
+}
+
+// 8 FP16 operand values from 8 codes (one 32-bit word) and the block scale.
+__device__ __forceinline__ half8_t dequant_word(uint32_t w, _Float16 e)
+{
     half2_t s2 = {e, e};
     half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
     half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
@@ -128,75 +217,121 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, uint32_t scale_code)
     return r;
 }
 
-// Simple tiled kernel: BM x BN tile per workgroup of 256 threads (2 x 2 waves),
-// each wave (BM/2) x (BN/2) built from 32x32x16 MFMAs.
-template <int BM, int BN, int BK, bool kAK, bool kBK, bool kA2D, bool kB2D, bool kOutBF16>
-__global__ __launch_bounds__(256) void k_gemm_simple(GemmParams p)
+// Output tile index for workgroup `bid`: consecutive ids go round-robin to
+// the 8 XCDs, so ids are first regrouped so each XCD owns a contiguous band
+// of tiles; bands are walked in groups of 8 tile rows, column by column, so
+// the A rows of a group and the B columns just visited stay in that XCD's L2.
+__device__ __forceinline__ void tile_of(uint32_t bid, uint32_t nbm, uint32_t nbn, uint32_t& tm,
+                                        uint32_t& tn)
 {
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int FM = WM / 32, FN = WN / 32;
-    constexpr int kKB = BK / 16;
-    __shared__ __attribute__((aligned(16))) uint8_t sa_codes[BM * BK / 2];
-    __shared__ __attribute__((aligned(16))) uint8_t sb_codes[BN * BK / 2];
-    __shared__ uint8_t sa_scales[BM * kKB];
-    __shared__ uint8_t sb_scales[BN * kKB];
+    const uint32_t total = nbm * nbn;
+    const uint32_t per = total / 8;
+    uint32_t id = bid;
+    if (bid < per * 8) id = (bid % 8) * per + bid / 8;
+    constexpr uint32_t G = 8;
+    uint32_t group = id / (G * nbn);
+    uint32_t first = group * G;
+    uint32_t gsize = (nbm - first) < G ? (nbm - first) : G;
+    uint32_t in = id - group * G * nbn;
+    tm = first + in % gsize;
+    tn = in / gsize;
+}
 
-    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+template <bool kAK, bool kBK, bool kA2D, bool kB2D, bool kOutBF16, bool kFull>
+__global__ __launch_bounds__(256) void k_gemm(GemmParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const uint32_t nbm = (uint32_t)((p.M + kTM - 1) / kTM), nbn = (uint32_t)((p.N + kTN - 1) / kTN);
+    uint32_t tm, tn;
+    tile_of(blockIdx.x, nbm, nbn, tm, tn);
+    const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     const int lr = lane & 31, lk = lane >> 5;
 
-    float16_t acc[FM][FN];
+    float16_t acc[4][4];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    for (int64_t k0 = 0; k0 < p.K; k0 += BK) {
-        stage_operand<BM, BK, kAK, kA2D>(p.a_codes, p.a_scales, p.M, p.K, m0, k0, sa_codes,
-                                         sa_scales);
-        stage_operand<BN, BK, kBK, kB2D>(p.b_codes, p.b_scales, p.N, p.K, n0, k0, sb_codes,
-                                         sb_scales);
-        __syncthreads();
+    const int nk = (int)((p.K + kTK - 1) / kTK);
+    Staged sa, sb;
+    stage_load<kAK, kA2D, kFull>(p.a_codes, p.a_scales, p.M, p.K, m0, 0, sa);
+    stage_load<kBK, kB2D, kFull>(p.b_codes, p.b_scales, p.N, p.K, n0, 0, sb);
+    stage_store<kAK>(sa, lds);
+    stage_store<kBK>(sb, lds + kOperandTile);
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool more = kt + 1 < nk;
+        if (more) {
+            stage_load<kAK, kA2D, kFull>(p.a_codes, p.a_scales, p.M, p.K, m0,
+                                         (int64_t)(kt + 1) * kTK, sa);
+            stage_load<kBK, kB2D, kFull>(p.b_codes, p.b_scales, p.N, p.K, n0,
+                                         (int64_t)(kt + 1) * kTK, sb);
+        }
+        const uint8_t* As = lds + (kt & 1) * kStage;
+        const uint8_t* Bs = As + kOperandTile;
+        // this lane's scales: 4 blocks per row, as FP16 pairs (h = 0: [0], h = 1: [1])
+        half2_t ea[4][2], eb[4][2];
 #pragma unroll
-        for (int s = 0; s < kKB; ++s) {
-            half8_t af[FM], bf[FN];
+        for (int i = 0; i < 4; ++i) {
+            uint32_t w = *reinterpret_cast<const uint32_t*>(As + kCodeTile +
+                                                            (wm * 128 + 32 * i + lr) * 8 + 4 * lk);
+            ea[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+            ea[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+            uint32_t v = *reinterpret_cast<const uint32_t*>(Bs + kCodeTile +
+                                                            (wn * 128 + 32 * i + lr) * 8 + 4 * lk);
+            eb[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+            eb[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
+        }
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                int row = wm * WM + i * 32 + lr;
-                uint32_t w = *reinterpret_cast<const uint32_t*>(sa_codes + row * (BK / 2) +
-                                                                 s * 8 + lk * 4);
-                af[i] = dequant8(w, sa_scales[row * kKB + s]);
+        for (int h = 0; h < 2; ++h) {
+            u32x4 ca[4], cb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ca[i] = *reinterpret_cast<const u32x4*>(As + (lk + 2 * h) * kPlaneStride +
+                                                        (wm * 128 + 32 * i + lr) * 16);
+                cb[i] = *reinterpret_cast<const u32x4*>(Bs + (lk + 2 * h) * kPlaneStride +
+                                                        (wn * 128 + 32 * i + lr) * 16);
             }
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                int row = wn * WN + j * 32 + lr;
-                uint32_t w = *reinterpret_cast<const uint32_t*>(sb_codes + row * (BK / 2) +
-                                                                 s * 8 + lk * 4);
-                bf[j] = dequant8(w, sb_scales[row * kKB + s]);
+            for (int q = 0; q < 4; ++q) {
+                half8_t af[4], bf[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    af[i] = dequant_word(ca[i][q], ea[i][h][q >> 1]);
+                    bf[i] = dequant_word(cb[i][q], eb[i][h][q >> 1]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j],
+                                                                           acc[i][j], 0, 0, 0);
             }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0,
-                                                                        0, 0);
+        }
+        if (more) {
+            uint8_t* nxt = lds + ((kt + 1) & 1) * kStage;
+            stage_store<kAK>(sa, nxt);
+            stage_store<kBK>(sb, nxt + kOperandTile);
         }
         __syncthreads();
     }
 
     const float sab = (*p.a_ts) * (*p.b_ts);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                int64_t row = m0 + wm * WM + i * 32 + 8 * (r / 4) + 4 * lk + (r % 4);
-                int64_t col = n0 + wn * WN + j * 32 + lr;
-                if (row < p.M && col < p.N) {
+                int64_t row = m0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * lk + (r % 4);
+                int64_t col = n0 + wn * 128 + j * 32 + lr;
+                if (kFull || (row < p.M && col < p.N)) {
                     float v = acc[i][j][r] * sab;
                     if (kOutBF16) {
                         uint32_t u = __float_as_uint(v);
@@ -252,12 +387,22 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     p.b_codes = B.codes; p.b_scales = B.scales; p.b_ts = B.ts;
     p.c = static_cast<uint8_t*>(c);
     p.ldc = ldc;
-    constexpr int BM = 128, BN = 128, BK = 64;
-    dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-    NVFP4_BOOL(A.k_major, AK, NVFP4_BOOL(B.k_major, BKM, NVFP4_BOOL(A.block2d != 0, A2,
-        NVFP4_BOOL(B.block2d != 0, B2, NVFP4_BOOL(out_bf16, OB,
-            hipLaunchKernelGGL((k_gemm_simple<BM, BN, BK, AK, BKM, A2, B2, OB>), grid, dim3(256),
-                               0, s, p))))));
+    const bool full = (M % kTM == 0) && (N % kTN == 0) && (K % kTK == 0);
+    const uint64_t tiles = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
+    dim3 grid((unsigned)tiles);
+    // NT: A, B K-major; NN: A K-major, B MN-major; TN: both MN-major
+#define NVFP4_GEMM_LAUNCH(AK, BKM)                                                             \
+    NVFP4_BOOL(A.block2d != 0, A2, NVFP4_BOOL(B.block2d != 0, B2, NVFP4_BOOL(out_bf16, OB,    \
+        NVFP4_BOOL(full, FU, {                                                                 \
+            auto kern = k_gemm<AK, BKM, A2, B2, OB, FU>;                                       \
+            hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                kLdsBytes);                                                    \
+            hipLaunchKernelGGL(kern, grid, dim3(256), kLdsBytes, s, p);                       \
+        }))))
+    if (A.k_major && B.k_major) NVFP4_GEMM_LAUNCH(true, true);
+    else if (A.k_major) NVFP4_GEMM_LAUNCH(true, false);
+    else NVFP4_GEMM_LAUNCH(false, false);
+#undef NVFP4_GEMM_LAUNCH
     return hipGetLastError();
 }
 
