@@ -88,7 +88,7 @@ __device__ __forceinline__ float div_markstein(float ax, float d, float r)
 // Per-block quotient context: d = RN(e * s_g) and r = RN(1/d).
 struct BlockDiv {
     float d, r;
-    bool fast;  // d far from the FP32 range ends: Markstein applies when |x| is not tiny
+    bool fast;  // d far from the FP32 range ends, so Markstein applies to non-tiny |x|
 };
 
 __device__ __forceinline__ BlockDiv make_block_div(float d)
@@ -100,17 +100,43 @@ __device__ __forceinline__ BlockDiv make_block_div(float d)
     return b;
 }
 
-// RN(x / d) with the sign of x (so -0 stays -0).
+// 0 < a < 2^-60 (a >= 0): operands whose Markstein intermediates could underflow.
+__device__ __forceinline__ bool tiny_nonzero(float a)
+{
+    return (__float_as_uint(a) - 1u) < 0x217FFFFFu;
+}
+
+// y[i] = RN(x[i] / d) with the sign of x[i] (so -0 stays -0), for n values of
+// one block.  Markstein everywhere; a wave-uniform branch redoes the rare
+// tiny or extreme operands with IEEE division.
+template <int n>
+__device__ __forceinline__ void quotients(const float* x, const BlockDiv& b, float* y)
+{
+    bool slow = !b.fast;
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+        float ax = __builtin_fabsf(x[i]);
+        y[i] = div_markstein(ax, b.d, b.r);
+        slow |= tiny_nonzero(ax);
+    }
+    if (slow) {
+#pragma unroll
+        for (int i = 0; i < n; ++i) {
+            float ax = __builtin_fabsf(x[i]);
+            if (!b.fast || tiny_nonzero(ax)) y[i] = ax / b.d;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < n; ++i)
+        y[i] = __uint_as_float(__float_as_uint(y[i]) | (__float_as_uint(x[i]) & 0x80000000u));
+}
+
+// Single quotient (block-scale computation).
 __device__ __forceinline__ float quotient(float x, const BlockDiv& b)
 {
-    float ax = __builtin_fabsf(x);
     float y;
-    if (b.fast && ax >= 0x1p-60f) {
-        y = div_markstein(ax, b.d, b.r);
-    } else {
-        y = ax / b.d;  // IEEE division (tiny or extreme operands)
-    }
-    return __uint_as_float(__float_as_uint(y) | (__float_as_uint(x) & 0x80000000u));
+    quotients<1>(&x, b, &y);
+    return y;
 }
 
 // ---------------------------------------------------------------- E2M1
@@ -123,29 +149,24 @@ __device__ __forceinline__ uint32_t fp4_pack2(uint32_t old, float a, float b)
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, sel);
 }
 
-// Magnitude of E2M1 code c (0..7) as FP32.
-__device__ __forceinline__ float e2m1_mag(uint32_t c)
+// Stochastic rounding of a = |y| (y = RN(x/d)) with the uniform word r.
+// Returns the chosen E2M1 magnitude as FP32 (exactly representable, so the
+// hardware RNE conversion encodes it unchanged).  With lo <= a < hi the
+// neighbouring grid values, the result is hi when r < frac * 2^32,
+// frac = (a - lo)/(hi - lo); a >= 6 saturates to 6.  The grid step is 0.5
+// below 2, 1 in [2, 4) and 2 in [4, 6]: t = a / step is exact, lo = floor(t)
+// * step, frac = t - floor(t) (exact), and frac * 2^32 < 2^32 - 255, so its
+// ceiling fits 32 bits and "r < frac * 2^32" is "r < ceil(frac * 2^32)".
+__device__ __forceinline__ float e2m1_sr_value(float a, uint32_t r)
 {
-    // 0, 0.5, 1, 1.5 for c < 4; (1 + (c & 1)/2) * 2^((c >> 1) - 1) above
-    float small = 0.5f * (float)c;
-    float big = __builtin_ldexpf(1.0f + 0.5f * (float)(c & 1u), (int)(c >> 1) - 1);
-    return c < 4 ? small : big;
-}
-
-// Stochastic rounding of |y| (y already RN(x/d), sign carried separately) to an
-// E2M1 magnitude code using the uniform word r: round up from the lower
-// neighbour lo to hi when r < frac * 2^32, frac = (|y| - lo) / (hi - lo).
-// `rne` is the RNE magnitude code of |y| (0..7).
-__device__ __forceinline__ uint32_t e2m1_sr_mag(float ay, uint32_t rne, uint32_t r)
-{
-    if (ay >= 6.0f) return 7u;
-    uint32_t lo = (e2m1_mag(rne) > ay) ? rne - 1u : rne;
-    float vlo = e2m1_mag(lo);
-    float inv_step = lo < 4u ? 2.0f : (lo < 6u ? 1.0f : 0.5f);
-    float frac = (ay - vlo) * inv_step;        // exact (Sterbenz, power-of-two step)
-    float thr = __builtin_ceilf(frac * 4294967296.0f);  // exact; < 2^32
-    uint32_t t = (uint32_t)thr;
-    return (r < t) ? lo + 1u : lo;
+    a = __builtin_fminf(a, 6.0f);
+    int e = a < 2.0f ? 1 : (a < 4.0f ? 0 : -1);
+    float t = __builtin_ldexpf(a, e);
+    float fl = __builtin_floorf(t);
+    float frac = t - fl;
+    uint32_t thr = (uint32_t)__builtin_ceilf(frac * 4294967296.0f);
+    float up = r < thr ? 1.0f : 0.0f;
+    return __builtin_ldexpf(fl + up, -e);
 }
 
 // ---------------------------------------------------------------- Philox

@@ -39,15 +39,30 @@ struct GemmParams {
 };
 
 // 8x8 nibble transpose: in[k] holds element (k, j) in nibble j; out[j] gets
-// element (k, j) in nibble k.
+// element (k, j) in nibble k.  Recursive block transpose: swap the off-
+// diagonal 4x4 blocks (16-bit halves, v_perm), then the 2x2 blocks (bytes,
+// v_perm), then single nibbles (shift + bitfield insert): 32 operations.
 __device__ __forceinline__ void transpose8x8_nibbles(const uint32_t in[8], uint32_t out[8])
 {
+    uint32_t w[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint32_t o = 0u;
+    for (int k = 0; k < 4; ++k) {
+        w[k] = __builtin_amdgcn_perm(in[k + 4], in[k], 0x05040100u);
+        w[k + 4] = __builtin_amdgcn_perm(in[k + 4], in[k], 0x07060302u);
+    }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o |= ((in[k] >> (4 * j)) & 0xFu) << (4 * k);
-        out[j] = o;
+    for (int base = 0; base < 8; base += 4)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            uint32_t a = w[base + k], b = w[base + k + 2];
+            w[base + k] = __builtin_amdgcn_perm(b, a, 0x06020400u);
+            w[base + k + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);
+        }
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+        uint32_t a = w[k], b = w[k + 1];
+        out[k] = ((b << 4) & 0xF0F0F0F0u) | (a & 0x0F0F0F0Fu);
+        out[k + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
     }
 }
 

@@ -96,8 +96,8 @@ __device__ __forceinline__ uint32_t block_scale(float aB, const TensorScale& ts,
     return e;
 }
 
-// Codes for n consecutive elements (n = 8) packed low-nibble-first into
-// n/2 bytes of `out` words.  y[] are RN(x/d) with the sign of x.
+// Codes of 8 quotients y[] = RN(x/d) (sign of x kept), packed low nibble
+// first: element 2j in the low nibble of byte j.
 __device__ __forceinline__ uint32_t pack8_rne(const float y[8])
 {
     uint32_t w = 0u;
@@ -108,21 +108,16 @@ __device__ __forceinline__ uint32_t pack8_rne(const float y[8])
     return w;
 }
 
-// Stochastic rounding of 8 quotients with their 8 uniform words.
-__device__ __forceinline__ uint32_t pack8_sr(const float y[8], const uint32_t r[8])
+// Stochastic rounding: each quotient is replaced by the E2M1 value its word
+// selects (with its sign), which the RNE conversion then encodes exactly.
+template <int n>
+__device__ __forceinline__ void sr_values(float* y, const uint32_t* r)
 {
-    float a[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = __builtin_fabsf(y[i]);
-    uint32_t rne = pack8_rne(a);  // RNE magnitudes of |y|
-    uint32_t w = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t mag = e2m1_sr_mag(a[i], (rne >> (4 * i)) & 7u, r[i]);
-        uint32_t sgn = __float_as_uint(y[i]) >> 31;
-        w |= ((sgn << 3) | mag) << (4 * i);
+    for (int i = 0; i < n; ++i) {
+        float v = e2m1_sr_value(__builtin_fabsf(y[i]), r[i]);
+        y[i] = __uint_as_float(__float_as_uint(v) | (__float_as_uint(y[i]) & 0x80000000u));
     }
-    return w;
 }
 
 // Quantize 8 values sharing one block scale.
@@ -132,9 +127,9 @@ __device__ __forceinline__ uint32_t encode8(const float v[8], const BlockDiv& bd
 {
     if (zero) return 0u;
     float y[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = quotient(v[i], bd);
-    return kSR ? pack8_sr(y, r) : pack8_rne(y);
+    quotients<8>(v, bd, y);
+    if (kSR) sr_values<8>(y, r);
+    return pack8_rne(y);
 }
 
 __device__ __forceinline__ void block_reduce_max_store(float m, float* dst)
@@ -217,9 +212,23 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantParams p)
 
 // ------------------------------------------------------------ 1x16 along columns
 
-// One thread per 16-row x 8-column tile (axis 0): 8 column blocks.  Work item
-// t is column group cg = t % (cols/8) of row block rb = t / (cols/8).  Each
-// row of the tile is one 16-byte (BF16) load; a wave reads 1 KB per row.
+template <bool kBF16>
+__device__ __forceinline__ void load4(const uint8_t* p, float v[4])
+{
+    if (kBF16) {
+        u32x2 w = *reinterpret_cast<const u32x2*>(p);
+        v[0] = bf16_lo(w[0]); v[1] = bf16_hi(w[0]);
+        v[2] = bf16_lo(w[1]); v[3] = bf16_hi(w[1]);
+    } else {
+        u32x4 w = *reinterpret_cast<const u32x4*>(p);
+        v[0] = __uint_as_float(w[0]); v[1] = __uint_as_float(w[1]);
+        v[2] = __uint_as_float(w[2]); v[3] = __uint_as_float(w[3]);
+    }
+}
+
+// One thread per 16-row x 4-column tile (axis 0): four column blocks.  Work
+// item t is column group cg = t % (cols/4) of row block rb = t / (cols/4).
+// A wave reads 512 contiguous bytes of each BF16 row.
 template <bool kBF16, bool kSR, bool kRHT, bool kAmaxOnly>
 __global__ __launch_bounds__(256) void k_quant_cols(QuantParams p)
 {
@@ -234,63 +243,59 @@ __global__ __launch_bounds__(256) void k_quant_cols(QuantParams p)
     for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < p.items; t += stride) {
         uint32_t rb = fdiv(t, p.div);
         uint32_t cg = t - rb * p.div.d;
-        int64_t r0 = (int64_t)rb * 16, c0 = (int64_t)cg * 8;
-        float v[16][8];
+        int64_t r0 = (int64_t)rb * 16, c0 = (int64_t)cg * 4;
+        float v[4][16];  // [column][row]
 #pragma unroll
-        for (int i = 0; i < 16; ++i) load8<kBF16>(p.x + ((r0 + i) * p.ld + c0) * esz, v[i]);
+        for (int i = 0; i < 16; ++i) {
+            float w[4];
+            load4<kBF16>(p.x + ((r0 + i) * p.ld + c0) * esz, w);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j][i] = w[j];
+        }
         if (kRHT) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float col[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) col[i] = v[i][j];
-                rht16_inplace(col, p.mask);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[i][j] = col[i];
-            }
+            for (int j = 0; j < 4; ++j) rht16_inplace(v[j], p.mask);
         }
-        float aB[8];
+        float aB[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             aB[j] = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) aB[j] = __builtin_fmaxf(aB[j], __builtin_fabsf(v[i][j]));
+            for (int i = 0; i < 16; ++i) aB[j] = __builtin_fmaxf(aB[j], __builtin_fabsf(v[j][i]));
         }
         if (kAmaxOnly) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) amax_local = __builtin_fmaxf(amax_local, aB[j]);
+            for (int j = 0; j < 4; ++j) amax_local = __builtin_fmaxf(amax_local, aB[j]);
             continue;
         }
-        BlockDiv bd[8];
-        bool zero[8];
-        uint32_t e[8];
+        uint32_t sc = 0u;
+        float y[4][16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = block_scale(aB[j], ts, bd[j], zero[j]);
-        u32x2 sc;
-        sc[0] = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
-        sc[1] = e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24);
-        *reinterpret_cast<u32x2*>(p.scales + rb * p.cols + c0) = sc;
+        for (int j = 0; j < 4; ++j) {
+            BlockDiv bd;
+            bool zero;
+            uint32_t e = block_scale(aB[j], ts, bd, zero);
+            sc |= e << (8 * j);
+            if (zero) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) y[j][i] = 0.0f;
+            } else {
+                quotients<16>(v[j], bd, y[j]);
+            }
+        }
+        *reinterpret_cast<uint32_t*>(p.scales + rb * p.cols + c0) = sc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float y[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) y[j] = zero[j] ? 0.0f : quotient(v[i][j], bd[j]);
-            uint32_t w;
+            float q[4] = {y[0][i], y[1][i], y[2][i], y[3][i]};
             if (kSR) {
                 uint64_t g = (uint64_t)((r0 + i) * p.cols + c0) >> 2;
-                u32x4 w0 = sr_words(p.seed, p.stream_id, g);
-                u32x4 w1 = sr_words(p.seed, p.stream_id, g + 1);
-                uint32_t r[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-                w = pack8_sr(y, r);
-                // zero blocks give code 0 regardless of the word
-                uint32_t keep = 0u;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) keep |= zero[j] ? 0u : (0xFu << (4 * j));
-                w &= keep;
-            } else {
-                w = pack8_rne(y);
+                u32x4 w = sr_words(p.seed, p.stream_id, g);
+                uint32_t r[4] = {w[0], w[1], w[2], w[3]};
+                sr_values<4>(q, r);
             }
-            *reinterpret_cast<uint32_t*>(p.codes + (r0 + i) * (p.cols / 2) + c0 / 2) = w;
+            uint32_t code = fp4_pack2<1>(fp4_pack2<0>(0u, q[0], q[1]), q[2], q[3]);
+            *reinterpret_cast<uint16_t*>(p.codes + (r0 + i) * (p.cols / 2) + c0 / 2) =
+                (uint16_t)code;
         }
     }
     if (kAmaxOnly) block_reduce_max_store(amax_local, p.partials + blockIdx.x);
@@ -560,8 +565,8 @@ static void set_items(const QuantArgs& a, Family f, QuantParams& p)
         p.items = (uint32_t)(a.rows * (a.cols / 16));
         p.div = make_fastdiv((uint32_t)(a.cols / 16));
     } else if (f == kCols) {
-        p.items = (uint32_t)((a.rows / 16) * (a.cols / 8));
-        p.div = make_fastdiv((uint32_t)(a.cols / 8));
+        p.items = (uint32_t)((a.rows / 16) * (a.cols / 4));
+        p.div = make_fastdiv((uint32_t)(a.cols / 4));
     } else {
         uint32_t strips = (uint32_t)((a.cols + 255) / 256);
         p.items = (uint32_t)((a.rows / 16) * strips);
