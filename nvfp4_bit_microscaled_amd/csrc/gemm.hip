@@ -36,6 +36,7 @@ struct GemmParams {
     const float* b_ts;
     uint8_t* c;
     int64_t ldc;
+    bool a2d, b2d, out_bf16;
 };
 
 // 8x8 nibble transpose: in[k] holds element (k, j) in nibble j; out[j] gets
@@ -101,10 +102,11 @@ struct Staged {
     uint32_t sc[8];  // scale bytes (K-major: sc[0..1] hold 8 bytes; MN-major: one per entry)
 };
 
-template <bool kKMajor, bool k2D, bool kFull>
+template <bool kKMajor, bool kFull>
 __device__ __forceinline__ void stage_load(const uint8_t* __restrict__ codes,
-                                           const uint8_t* __restrict__ scales, int64_t MN,
-                                           int64_t K, int64_t row0, int64_t k0, Staged& st)
+                                           const uint8_t* __restrict__ scales, bool k2D,
+                                           int64_t MN, int64_t K, int64_t row0, int64_t k0,
+                                           Staged& st)
 {
     const int t = threadIdx.x;
     if (kKMajor) {
@@ -252,7 +254,7 @@ __device__ __forceinline__ void tile_of(uint32_t bid, uint32_t nbm, uint32_t nbn
     tn = in / gsize;
 }
 
-template <bool kAK, bool kBK, bool kA2D, bool kB2D, bool kOutBF16, bool kFull>
+template <bool kAK, bool kBK, bool kFull>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -274,8 +276,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
 
     const int nk = (int)((p.K + kTK - 1) / kTK);
     Staged sa, sb;
-    stage_load<kAK, kA2D, kFull>(p.a_codes, p.a_scales, p.M, p.K, m0, 0, sa);
-    stage_load<kBK, kB2D, kFull>(p.b_codes, p.b_scales, p.N, p.K, n0, 0, sb);
+    stage_load<kAK, kFull>(p.a_codes, p.a_scales, p.a2d, p.M, p.K, m0, 0, sa);
+    stage_load<kBK, kFull>(p.b_codes, p.b_scales, p.b2d, p.N, p.K, n0, 0, sb);
     stage_store<kAK>(sa, lds);
     stage_store<kBK>(sb, lds + kOperandTile);
     __syncthreads();
@@ -283,15 +285,25 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
     for (int kt = 0; kt < nk; ++kt) {
         const bool more = kt + 1 < nk;
         if (more) {
-            stage_load<kAK, kA2D, kFull>(p.a_codes, p.a_scales, p.M, p.K, m0,
-                                         (int64_t)(kt + 1) * kTK, sa);
-            stage_load<kBK, kB2D, kFull>(p.b_codes, p.b_scales, p.N, p.K, n0,
-                                         (int64_t)(kt + 1) * kTK, sb);
+            stage_load<kAK, kFull>(p.a_codes, p.a_scales, p.a2d, p.M, p.K, m0,
+                                   (int64_t)(kt + 1) * kTK, sa);
+            stage_load<kBK, kFull>(p.b_codes, p.b_scales, p.b2d, p.N, p.K, n0,
+                                   (int64_t)(kt + 1) * kTK, sb);
         }
         const uint8_t* As = lds + (kt & 1) * kStage;
         const uint8_t* Bs = As + kOperandTile;
-        // this lane's scales: 4 blocks per row, as FP16 pairs (h = 0: [0], h = 1: [1])
+        // this lane's codes (both halves of the k-tile) and scales
+        u32x4 ca[2][4], cb[2][4];
         half2_t ea[4][2], eb[4][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ca[h][i] = *reinterpret_cast<const u32x4*>(As + (lk + 2 * h) * kPlaneStride +
+                                                           (wm * 128 + 32 * i + lr) * 16);
+                cb[h][i] = *reinterpret_cast<const u32x4*>(Bs + (lk + 2 * h) * kPlaneStride +
+                                                           (wn * 128 + 32 * i + lr) * 16);
+            }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             uint32_t w = *reinterpret_cast<const uint32_t*>(As + kCodeTile +
@@ -303,30 +315,39 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
             eb[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
             eb[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
         }
+        // software pipeline over the 8 MFMA steps s = 4h + q: operands of step
+        // s + 1 are dequantized while the 16 MFMAs of step s issue, one MFMA
+        // then four VALU at a time; each step is a scheduling region of its own
+        half8_t af[2][4], bf[2][4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            u32x4 ca[4], cb[4];
+        for (int i = 0; i < 4; ++i) {
+            af[0][i] = dequant_word(ca[0][i][0], ea[i][0][0]);
+            bf[0][i] = dequant_word(cb[0][i][0], eb[i][0][0]);
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ca[i] = *reinterpret_cast<const u32x4*>(As + (lk + 2 * h) * kPlaneStride +
-                                                        (wm * 128 + 32 * i + lr) * 16);
-                cb[i] = *reinterpret_cast<const u32x4*>(Bs + (lk + 2 * h) * kPlaneStride +
-                                                        (wn * 128 + 32 * i + lr) * 16);
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                half8_t af[4], bf[4];
+        for (int st = 0; st < 8; ++st) {
+            const int cur = st & 1, nx = cur ^ 1;
+            if (st < 7) {
+                const int h = (st + 1) >> 2, q = (st + 1) & 3;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    af[i] = dequant_word(ca[i][q], ea[i][h][q >> 1]);
-                    bf[i] = dequant_word(cb[i][q], eb[i][h][q >> 1]);
+                    af[nx][i] = dequant_word(ca[h][i][q], ea[i][h][q >> 1]);
+                    bf[nx][i] = dequant_word(cb[h][i][q], eb[i][h][q >> 1]);
                 }
+            }
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j],
-                                                                           acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][i], bf[cur][j],
+                                                                       acc[i][j], 0, 0, 0);
+            if (st < 7) {
+#pragma unroll
+                for (int g = 0; g < 16; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         if (more) {
@@ -348,7 +369,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
                 int64_t col = n0 + wn * 128 + j * 32 + lr;
                 if (kFull || (row < p.M && col < p.N)) {
                     float v = acc[i][j][r] * sab;
-                    if (kOutBF16) {
+                    if (p.out_bf16) {
                         uint32_t u = __float_as_uint(v);
                         u += 0x7FFFu + ((u >> 16) & 1u);
                         reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + col] = (uint16_t)(u >> 16);
@@ -402,18 +423,20 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     p.b_codes = B.codes; p.b_scales = B.scales; p.b_ts = B.ts;
     p.c = static_cast<uint8_t*>(c);
     p.ldc = ldc;
+    p.a2d = A.block2d != 0;
+    p.b2d = B.block2d != 0;
+    p.out_bf16 = out_bf16;
     const bool full = (M % kTM == 0) && (N % kTN == 0) && (K % kTK == 0);
     const uint64_t tiles = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
     dim3 grid((unsigned)tiles);
     // NT: A, B K-major; NN: A K-major, B MN-major; TN: both MN-major
 #define NVFP4_GEMM_LAUNCH(AK, BKM)                                                             \
-    NVFP4_BOOL(A.block2d != 0, A2, NVFP4_BOOL(B.block2d != 0, B2, NVFP4_BOOL(out_bf16, OB,    \
-        NVFP4_BOOL(full, FU, {                                                                 \
-            auto kern = k_gemm<AK, BKM, A2, B2, OB, FU>;                                       \
-            hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                                kLdsBytes);                                                    \
-            hipLaunchKernelGGL(kern, grid, dim3(256), kLdsBytes, s, p);                       \
-        }))))
+    NVFP4_BOOL(full, FU, {                                                                     \
+        auto kern = k_gemm<AK, BKM, FU>;                                                       \
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,     \
+                            kLdsBytes);                                                        \
+        hipLaunchKernelGGL(kern, grid, dim3(256), kLdsBytes, s, p);                           \
+    })
     if (A.k_major && B.k_major) NVFP4_GEMM_LAUNCH(true, true);
     else if (A.k_major) NVFP4_GEMM_LAUNCH(true, false);
     else NVFP4_GEMM_LAUNCH(false, false);
