@@ -275,88 +275,98 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nk = (int)((p.K + kTK - 1) / kTK);
+
+    // Fragments of the current k-tile: codes of one K half at a time, scales.
+    // (Macros rather than lambdas keep every array index a compile-time
+    // constant, so everything stays in registers.)
+    u32x4 ca0[4], cb0[4], ca1[4], cb1[4];
+    half2_t ea0[4], ea1[4], eb0[4], eb1[4];
+    half8_t af0[4], bf0[4], af1[4], bf1[4];
+#define READ_HALF(As, CA, CB, h)                                                               \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+        CA[i] = *reinterpret_cast<const u32x4*>((As) + (lk + 2 * (h)) * kPlaneStride +         \
+                                                (wm * 128 + 32 * i + lr) * 16);                \
+        CB[i] = *reinterpret_cast<const u32x4*>((As) + kOperandTile +                          \
+                                                (lk + 2 * (h)) * kPlaneStride +                \
+                                                (wn * 128 + 32 * i + lr) * 16);                \
+    }
+#define READ_SCALES(As)                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+        uint32_t w_ = *reinterpret_cast<const uint32_t*>((As) + kCodeTile +                    \
+                                                         (wm * 128 + 32 * i + lr) * 8 + 4 * lk); \
+        ea0[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w_, 1.0f, false);                    \
+        ea1[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w_, 1.0f, true);                     \
+        uint32_t v_ = *reinterpret_cast<const uint32_t*>((As) + kOperandTile + kCodeTile +     \
+                                                         (wn * 128 + 32 * i + lr) * 8 + 4 * lk); \
+        eb0[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v_, 1.0f, false);                    \
+        eb1[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v_, 1.0f, true);                     \
+    }
+    // operands of word q of one K half (codes CA/CB, scales EA/EB) into AF/BF
+#define DEQUANT(AF, BF, CA, CB, EA, EB, q)                                                     \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+        AF[i] = dequant_word(CA[i][q], EA[i][(q) >> 1]);                                       \
+        BF[i] = dequant_word(CB[i][q], EB[i][(q) >> 1]);                                       \
+    }
+#define MFMA(AF, BF)                                                                           \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                              \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(AF[i], BF[j], acc[i][j], 0, 0, 0);
+    // one MFMA then four VALU, sixteen times; each step its own scheduling region
+#define INTERLEAVE()                                                                           \
+    _Pragma("unroll") for (int g = 0; g < 16; ++g) {                                           \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                     \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);
+#define PREFETCH(kt_)                                                                          \
+    stage_load<kAK, kFull>(p.a_codes, p.a_scales, p.a2d, p.M, p.K, m0, (int64_t)(kt_) * kTK, sa); \
+    stage_load<kBK, kFull>(p.b_codes, p.b_scales, p.b2d, p.N, p.K, n0, (int64_t)(kt_) * kTK, sb);
+
+    // Prologue: tile 0 into buffer 0 and its step-0 operands.
     Staged sa, sb;
-    stage_load<kAK, kFull>(p.a_codes, p.a_scales, p.a2d, p.M, p.K, m0, 0, sa);
-    stage_load<kBK, kFull>(p.b_codes, p.b_scales, p.b2d, p.N, p.K, n0, 0, sb);
+    PREFETCH(0);
     stage_store<kAK>(sa, lds);
     stage_store<kBK>(sb, lds + kOperandTile);
     __syncthreads();
+    READ_HALF(lds, ca0, cb0, 0);
+    READ_SCALES(lds);
+    DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 0);
 
+    // Steady state.  Tile kt lives in buffer kt & 1; step s = 4h + q uses
+    // word q of K half h.  Tile kt + 1 is fetched from memory at the start of
+    // tile kt.  Each step's MFMAs run with the next step's operands
+    // dequantized in their shadow; the second K half is read from LDS during
+    // step 1.  After step 6 tile kt + 1 is written to the other buffer (last
+    // read before the previous barrier); past the barrier the step-7 MFMAs of
+    // tile kt cover the LDS reads and step-0 dequantization of tile kt + 1.
+    // The boundary runs on every tile so the loop has one path: on the last
+    // tile the staging registers still hold tile kt and the other buffer is
+    // rewritten with it, never to be read.
     for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        if (more) {
-            stage_load<kAK, kFull>(p.a_codes, p.a_scales, p.a2d, p.M, p.K, m0,
-                                   (int64_t)(kt + 1) * kTK, sa);
-            stage_load<kBK, kFull>(p.b_codes, p.b_scales, p.b2d, p.N, p.K, n0,
-                                   (int64_t)(kt + 1) * kTK, sb);
-        }
-        const uint8_t* As = lds + (kt & 1) * kStage;
-        const uint8_t* Bs = As + kOperandTile;
-        // this lane's codes (both halves of the k-tile) and scales
-        u32x4 ca[2][4], cb[2][4];
-        half2_t ea[4][2], eb[4][2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ca[h][i] = *reinterpret_cast<const u32x4*>(As + (lk + 2 * h) * kPlaneStride +
-                                                           (wm * 128 + 32 * i + lr) * 16);
-                cb[h][i] = *reinterpret_cast<const u32x4*>(Bs + (lk + 2 * h) * kPlaneStride +
-                                                           (wn * 128 + 32 * i + lr) * 16);
-            }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t w = *reinterpret_cast<const uint32_t*>(As + kCodeTile +
-                                                            (wm * 128 + 32 * i + lr) * 8 + 4 * lk);
-            ea[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
-            ea[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
-            uint32_t v = *reinterpret_cast<const uint32_t*>(Bs + kCodeTile +
-                                                            (wn * 128 + 32 * i + lr) * 8 + 4 * lk);
-            eb[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
-            eb[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
-        }
-        // software pipeline over the 8 MFMA steps s = 4h + q: operands of step
-        // s + 1 are dequantized while the 16 MFMAs of step s issue, one MFMA
-        // then four VALU at a time; each step is a scheduling region of its own
-        half8_t af[2][4], bf[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            af[0][i] = dequant_word(ca[0][i][0], ea[i][0][0]);
-            bf[0][i] = dequant_word(cb[0][i][0], eb[i][0][0]);
-        }
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const int cur = st & 1, nx = cur ^ 1;
-            if (st < 7) {
-                const int h = (st + 1) >> 2, q = (st + 1) & 3;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    af[nx][i] = dequant_word(ca[h][i][q], ea[i][h][q >> 1]);
-                    bf[nx][i] = dequant_word(cb[h][i][q], eb[i][h][q >> 1]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][i], bf[cur][j],
-                                                                       acc[i][j], 0, 0, 0);
-            if (st < 7) {
-#pragma unroll
-                for (int g = 0; g < 16; ++g) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        if (more) {
-            uint8_t* nxt = lds + ((kt + 1) & 1) * kStage;
-            stage_store<kAK>(sa, nxt);
-            stage_store<kBK>(sb, nxt + kOperandTile);
-        }
+        const uint8_t* cur = lds + (kt & 1) * kStage;
+        if (kt + 1 < nk) { PREFETCH(kt + 1); }  // never reads past K
+        DEQUANT(af1, bf1, ca0, cb0, ea0, eb0, 1); MFMA(af0, bf0); INTERLEAVE();   // step 0
+        READ_HALF(cur, ca1, cb1, 1);
+        DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 2); MFMA(af1, bf1); INTERLEAVE();   // step 1
+        DEQUANT(af1, bf1, ca0, cb0, ea0, eb0, 3); MFMA(af0, bf0); INTERLEAVE();   // step 2
+        DEQUANT(af0, bf0, ca1, cb1, ea1, eb1, 0); MFMA(af1, bf1); INTERLEAVE();   // step 3
+        DEQUANT(af1, bf1, ca1, cb1, ea1, eb1, 1); MFMA(af0, bf0); INTERLEAVE();   // step 4
+        DEQUANT(af0, bf0, ca1, cb1, ea1, eb1, 2); MFMA(af1, bf1); INTERLEAVE();   // step 5
+        DEQUANT(af1, bf1, ca1, cb1, ea1, eb1, 3); MFMA(af0, bf0); INTERLEAVE();   // step 6
+        uint8_t* nxt = lds + ((kt + 1) & 1) * kStage;
+        stage_store<kAK>(sa, nxt);
+        stage_store<kBK>(sb, nxt + kOperandTile);
         __syncthreads();
+        READ_HALF(nxt, ca0, cb0, 0);
+        READ_SCALES(nxt);
+        DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 0); MFMA(af1, bf1); INTERLEAVE();   // step 7
     }
+#undef READ_HALF
+#undef READ_SCALES
+#undef DEQUANT
+#undef MFMA
+#undef INTERLEAVE
+#undef PREFETCH
 
     const float sab = (*p.a_ts) * (*p.b_ts);
 #pragma unroll
