@@ -250,10 +250,47 @@ def main():
     }
     del bufs
     torch.cuda.empty_cache()
+    line["decode"] = decode_bench(torch, nv, workloads)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, torch, nv, workloads, X, W_gu)
     print(json.dumps(line), flush=True)
+
+
+def decode_bench(torch, nv, workloads):
+    """Decode-style skinny NT GEMM: activations [M, 8192] x weights [28672, 8192],
+    both 1x16 RNE.  HBM-bound on the packed weights (codes + scales); the
+    256 MB Infinity Cache is evicted by reading 1 GiB before each launch (a
+    read leaves no dirty lines to drain during the timed launch)."""
+    cfg = workloads.DECODE
+    K, N = cfg["k"], cfg["n"]
+    w = nv.quantize(workloads.weights(N, K, cfg["w_seed"], device="cuda"))
+    x = workloads.activations(64, K, cfg["act_seed"], device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    wbytes = N * K * (0.5 + 1 / 16)
+    out = {}
+    for M in cfg["ms"]:
+        a = nv.quantize(x[:M].contiguous())
+        y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        times = []
+        for it in range(12):
+            flush.sum()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            nv.gemm("NT", a, w, out=y)
+            e1.record()
+            torch.cuda.synchronize()
+            if it >= 2:
+                times.append(e0.elapsed_time(e1))
+        t = sorted(times)[len(times) // 2] * 1e-3
+        out["M%d" % M] = {"us": round(t * 1e6, 2),
+                          "weights_GBps": round(wbytes / t / 1e9, 1),
+                          "frac_of_hbm": round(wbytes / t / 1e9 / HBM_PEAK_GBPS, 4),
+                          "tflops": round(2.0 * M * N * K / t / 1e12, 2)}
+    del flush
+    return {"shape": "M x 28672 x 8192, weights 1x16 along K", "weight_bytes": int(wbytes),
+            "timing": "median of 10 launches, Infinity Cache evicted before each", **out}
 
 
 def cpu_baseline(args, torch, nv, workloads, X, W_gu):

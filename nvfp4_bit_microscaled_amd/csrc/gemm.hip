@@ -390,6 +390,142 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
             }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny NT kernel for decode-style shapes (M <= 64, K % 128 == 0):
+// C[M, N] = A[M, K] B[N, K]^T.  The packed weights B dominate the traffic
+// (4.5 bits per element) and are streamed once: each wave owns 16 rows of B
+// (16 output columns) over all of K, each lane reading 16 bytes (32 codes)
+// per 128-wide K step; a row's 64 bytes per step come from four adjacent
+// lanes.  The few activation rows are dequantized once per workgroup into LDS
+// as FP16, one K chunk at a time, and read back as MFMA A fragments.  Both
+// operands are prefetched into registers one chunk ahead, issued after
+// everything the current chunk waits for (vector-memory counters drain in
+// order).  The loop is branch-free: rows past M or N are clamped to the last
+// valid row (their outputs are never stored) and K steps past the end are
+// skipped whole.  v_mfma_f32_16x16x32_f16 with the per-lane K permutation of
+// the main kernel: at step s lane (row l % 16, group g = l / 16) supplies
+// k = k0 + 32 g + 8 s + [0, 8) for both operands.
+// ---------------------------------------------------------------------------
+typedef float float4_t __attribute__((ext_vector_type(4)));
+constexpr int kSkN = 64;  // output columns per workgroup
+
+template <int KC, int RMAX>
+__global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
+{
+    constexpr int kSteps = KC / 128;                 // B steps per chunk
+    constexpr int kRow = KC * 2 + 16;                // LDS bytes per activation row
+    constexpr int kAPer = RMAX * 16 * KC / 32 / 256; // 32-code activation pieces per thread
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int R = (int)((p.M + 15) / 16);            // 16-row blocks of A (<= RMAX)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, g = lane >> 4;
+    const int64_t n = (int64_t)blockIdx.x * kSkN + wave * 16 + lr;  // B row of this lane
+    const int64_t nc = n < p.N ? n : p.N - 1;                       // clamped for loads
+    const int64_t K = p.K, lds_b = K / 16;
+    const uint8_t* brow = p.b_codes + nc * (K / 2) + 16 * g;
+    const uint8_t* bsrow = p.b_scales + (p.b2d ? (nc / 16) * lds_b : nc * lds_b) + 2 * g;
+    float4_t acc[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 ac[kAPer], bc[kSteps], bn[kSteps];
+    uint32_t as[kAPer], bs[kSteps], bsn[kSteps];
+    auto load_a = [&](int64_t kc) {
+#pragma unroll
+        for (int i = 0; i < kAPer; ++i) {
+            int idx = threadIdx.x + 256 * i;
+            int m = idx / (KC / 32), c = idx % (KC / 32);
+            int64_t mc = m < p.M ? m : p.M - 1;
+            int64_t k = kc + 32 * c;
+            k = k < K ? k : K - 32;  // pieces past K are never read
+            ac[i] = *reinterpret_cast<const u32x4*>(p.a_codes + mc * (K / 2) + k / 2);
+            const uint8_t* sp =
+                p.a_scales + (p.a2d ? (mc / 16) * lds_b : mc * lds_b) + k / 16;
+            as[i] = *reinterpret_cast<const uint16_t*>(sp);
+        }
+    };
+    auto load_b = [&](int64_t kc, u32x4* c, uint32_t* sc) {
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+            int64_t k = kc + st * 128;
+            k = k < K ? k : K - 128;  // steps past K are skipped
+            c[st] = *reinterpret_cast<const u32x4*>(brow + k / 2);
+            sc[st] = *reinterpret_cast<const uint16_t*>(bsrow + k / 16);
+        }
+    };
+
+    load_a(0);
+    load_b(0, bc, bs);
+    for (int64_t kc = 0; kc < K; kc += KC) {
+        // activations of this chunk -> FP16 in LDS (the previous chunk's readers are done)
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kAPer; ++i) {
+            int idx = threadIdx.x + 256 * i;
+            int m = idx / (KC / 32), c = idx % (KC / 32);
+            if (m < R * 16) {
+                half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as[i], 1.0f, false);
+                uint8_t* dst = lds + m * kRow + 64 * c;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<half8_t*>(dst + 16 * q) = dequant_word(ac[i][q], e2[q >> 1]);
+            }
+        }
+        __syncthreads();
+        // next chunk's operands, issued after everything this chunk still waits for
+        const bool more = kc + KC < K;
+        if (more) {
+            load_a(kc + KC);
+            load_b(kc + KC, bn, bsn);
+        }
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+            if (kc + st * 128 < K) {  // uniform
+                half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[st], 1.0f, false);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    half8_t bf = dequant_word(bc[st][s], e2[s >> 1]);
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r) {
+                        if (r < R) {
+                            half8_t af = *reinterpret_cast<const half8_t*>(
+                                lds + (16 * r + lr) * kRow + (st * 128 + 32 * g + 8 * s) * 2);
+                            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[r], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+        if (more) {
+#pragma unroll
+            for (int st = 0; st < kSteps; ++st) {
+                bc[st] = bn[st];
+                bs[st] = bsn[st];
+            }
+        }
+    }
+    // lane holds C[16 r + 4 g + j][n] in acc[r][j]
+    const float sab = (*p.a_ts) * (*p.b_ts);
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+        if (r >= R) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int64_t row = 16 * r + 4 * g + j;
+            if (row < p.M && n < p.N) {
+                float v = acc[r][j] * sab;
+                if (p.out_bf16) {
+                    uint32_t u = __float_as_uint(v);
+                    u += 0x7FFFu + ((u >> 16) & 1u);
+                    reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + n] = (uint16_t)(u >> 16);
+                } else {
+                    reinterpret_cast<float*>(p.c)[row * p.ldc + n] = v;
+                }
+            }
+        }
+    }
+}
+
 __global__ void k_fill_zero(uint8_t* c, int64_t M, int64_t N, int64_t ldc, int esz)
 {
     int64_t total = M * N;
@@ -436,6 +572,27 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     p.a2d = A.block2d != 0;
     p.b2d = B.block2d != 0;
     p.out_bf16 = out_bf16;
+    if (A.k_major && B.k_major && M <= 64 && K % 128 == 0) {
+        // decode-style shapes: stream the weights with a dedicated kernel
+        dim3 g((unsigned)((N + kSkN - 1) / kSkN));
+        if (M <= 16) {
+            auto kern = k_gemm_skinny<2048, 1>;
+            const int lds = 1 * 16 * (2048 * 2 + 16);
+            hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);
+        } else if (M <= 32) {
+            auto kern = k_gemm_skinny<1024, 2>;
+            const int lds = 2 * 16 * (1024 * 2 + 16);
+            hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);
+        } else {
+            auto kern = k_gemm_skinny<512, 4>;
+            const int lds = 4 * 16 * (512 * 2 + 16);
+            hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);
+        }
+        return hipGetLastError();
+    }
     const bool full = (M % kTM == 0) && (N % kTN == 0) && (K % kTK == 0);
     const uint64_t tiles = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
     dim3 grid((unsigned)tiles);
