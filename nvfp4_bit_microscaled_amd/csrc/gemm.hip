@@ -96,11 +96,28 @@ constexpr int kOperandTile = kCodeTile + kScaleTile;
 constexpr int kStage = 2 * kOperandTile;         // A and B
 constexpr int kLdsBytes = 2 * kStage;            // double buffered: 74240 bytes
 
+// Position of tile row r inside a plane.  Rows are permuted within each
+// group of 8 (r ^ ((r >> 3) & 7)): eight consecutive rows still fill all 32
+// banks (fragment reads), and the transposed staging stores -- eight rows
+// apart -- spread over different banks instead of hitting one.
+// K-major operands are staged row by row without conflicts and keep the
+// identity order.
+template <bool kKMajor>
+__device__ __forceinline__ int swz(int r) { return kKMajor ? r : (r ^ ((r >> 3) & 7)); }
+
 // Per-thread staging registers for one operand's k-tile.
 struct Staged {
-    u32x4 code[4];   // K-major: 4 x 16-byte chunks; MN-major: 8 x 8 bytes in code[0..3]
+    u32x4 code[4];   // K-major: 4 x 16-byte chunks; MN-major: 16 k-rows x 4 bytes
     uint32_t sc[8];  // scale bytes (K-major: sc[0..1] hold 8 bytes; MN-major: one per entry)
 };
+
+// Raw buffer resource over a whole operand plane (full tiles only: every
+// offset is in range, and planes are below 2 GiB).  A per-lane VGPR offset
+// plus a per-load scalar offset keeps one address register per stream.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const uint8_t* base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, 0x00020000);
+}
 
 template <bool kKMajor, bool kFull>
 __device__ __forceinline__ void stage_load(const uint8_t* __restrict__ codes,
@@ -109,70 +126,93 @@ __device__ __forceinline__ void stage_load(const uint8_t* __restrict__ codes,
                                            Staged& st)
 {
     const int t = threadIdx.x;
-    if (kKMajor) {
-        // chunk f = it*256 + t: row f/4, plane f%4 (16 bytes = 32 codes)
+    if (kKMajor && kFull) {
+        // chunk f = it*256 + t: row f/4 = t/4 + 64 it, plane f%4 = t%4
+        const __amdgpu_buffer_rsrc_t rc = plane_rsrc(codes);
+        const int vo = (t >> 2) * (int)(K / 2) + 16 * (t & 3);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            int so = (int)((row0 + 64 * it) * (K / 2) + k0 / 2);
+            st.code[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vo, so, 0));
+        }
+        const __amdgpu_buffer_rsrc_t rs = plane_rsrc(scales);
+        int64_t ld = K / 16;
+        // the lane-dependent part goes in the VGPR offset, the rest is uniform
+        int vs = k2D ? (t >> 4) * (int)ld : t * (int)ld;
+        int ss = (int)((k2D ? (row0 / 16) * ld : row0 * ld) + k0 / 16);
+        u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, vs, ss, 0));
+        st.sc[0] = w[0];
+        st.sc[1] = w[1];
+    } else if (kKMajor) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             int f = it * 256 + t;
             int r = f >> 2, c = f & 3;
             int64_t row = row0 + r, k = k0 + 32 * c;
             const uint8_t* src = codes + row * (K / 2) + k / 2;
-            if (kFull) {
-                st.code[it] = *reinterpret_cast<const u32x4*>(src);
-            } else {  // rows are only 8-byte aligned when K % 32 != 0: 4-byte loads
-                u32x4 w = {0u, 0u, 0u, 0u};
-                if (row < MN) {
+            u32x4 w = {0u, 0u, 0u, 0u};  // rows are only 8-byte aligned when K % 32 != 0
+            if (row < MN) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (k + 8 * q < K) w[q] = reinterpret_cast<const uint32_t*>(src)[q];
-                }
-                st.code[it] = w;
+                for (int q = 0; q < 4; ++q)
+                    if (k + 8 * q < K) w[q] = reinterpret_cast<const uint32_t*>(src)[q];
             }
+            st.code[it] = w;
         }
         // scales: thread t owns row t, 8 bytes (k-blocks k0/16 .. +7)
         int64_t row = row0 + t, kb = k0 / 16;
         int64_t ld = K / 16;
         const uint8_t* src = scales + (k2D ? (row / 16) * ld : row * ld) + kb;
-        if (kFull) {
-            u32x2 w = *reinterpret_cast<const u32x2*>(src);
-            st.sc[0] = w[0];
-            st.sc[1] = w[1];
-        } else {
-            uint32_t w0 = 0u, w1 = 0u;
-            if (row < MN) {
+        uint32_t w0 = 0u, w1 = 0u;
+        if (row < MN) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    uint32_t b = (kb + j < ld) ? (uint32_t)src[j] : 0u;
-                    if (j < 4) w0 |= b << (8 * j);
-                    else w1 |= b << (8 * (j - 4));
-                }
+            for (int j = 0; j < 8; ++j) {
+                uint32_t b = (kb + j < ld) ? (uint32_t)src[j] : 0u;
+                if (j < 4) w0 |= b << (8 * j);
+                else w1 |= b << (8 * (j - 4));
             }
-            st.sc[0] = w0;
-            st.sc[1] = w1;
         }
+        st.sc[0] = w0;
+        st.sc[1] = w1;
     } else {
-        // storage [K, MN]: thread t reads 8 k-rows x 8 bytes (16 m) at
-        // k-group kg = t % 16, m-group mg = t / 16
-        int kg = t & 15, mg = t >> 4;
-        int64_t m = row0 + 16 * mg;
+        // storage [K, MN]: thread t reads 16 k-rows x 4 bytes (8 m codes) at
+        // m-group mg = t % 32 and k-group kq = t / 32 (two k-rows per wave
+        // instruction, 128 contiguous bytes each)
+        int mg = t & 31, kq = t >> 5;
+        int64_t m = row0 + 8 * mg;
+        if (kFull) {
+            const __amdgpu_buffer_rsrc_t rc = plane_rsrc(codes);
+            const int vo = 16 * kq * (int)(MN / 2) + 4 * mg;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int64_t k = k0 + 8 * kg + i;
-            u32x2 w = {0u, 0u};
-            if (kFull || (k < K && m < MN))
-                w = *reinterpret_cast<const u32x2*>(codes + k * (MN / 2) + m / 2);
-            st.code[i >> 1][2 * (i & 1)] = w[0];
-            st.code[i >> 1][2 * (i & 1) + 1] = w[1];
-        }
-        // scales: thread t owns tile row t, one byte per k-block
-        int64_t row = row0 + t;
+            for (int i = 0; i < 16; ++i) {
+                int so = (int)((k0 + i) * (MN / 2) + row0 / 2);
+                st.code[i >> 2][i & 3] = __builtin_amdgcn_raw_buffer_load_b32(rc, vo, so, 0);
+            }
+            const __amdgpu_buffer_rsrc_t rs = plane_rsrc(scales);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            int64_t kb = k0 / 16 + j;
-            uint32_t b = 0u;
-            if (kFull || (row < MN && kb * 16 < K))
-                b = k2D ? scales[kb * (MN / 16) + row / 16] : scales[kb * MN + row];
-            st.sc[j] = b;
+            for (int j = 0; j < 8; ++j) {
+                int64_t kb = k0 / 16 + j;
+                int vs = k2D ? (t >> 4) : t;
+                int ss = (int)(k2D ? kb * (MN / 16) + row0 / 16 : kb * MN + row0);
+                st.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, vs, ss, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                int64_t k = k0 + 16 * kq + i;
+                uint32_t w = 0u;
+                if (k < K && m < MN)
+                    w = *reinterpret_cast<const uint32_t*>(codes + k * (MN / 2) + m / 2);
+                st.code[i >> 2][i & 3] = w;
+            }
+            int64_t row = row0 + t;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                int64_t kb = k0 / 16 + j;
+                uint32_t b = 0u;
+                if (row < MN && kb * 16 < K)
+                    b = k2D ? scales[kb * (MN / 16) + row / 16] : scales[kb * MN + row];
+                st.sc[j] = b;
+            }
         }
     }
 }
@@ -182,42 +222,43 @@ __device__ __forceinline__ void stage_store(const Staged& st, uint8_t* tile)
 {
     const int t = threadIdx.x;
     uint8_t* sct = tile + kCodeTile;
-    uint32_t s0, s1;  // scale bytes b0..b7 of the row, before reordering
-    int srow;
+    uint32_t s0, s1;  // scale bytes b0..b7 of row t, before reordering
     if (kKMajor) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             int f = it * 256 + t;
             int r = f >> 2, c = f & 3;
-            *reinterpret_cast<u32x4*>(tile + c * kPlaneStride + r * 16) = st.code[it];
+            *reinterpret_cast<u32x4*>(tile + c * kPlaneStride + swz<true>(r) * 16) = st.code[it];
         }
         s0 = st.sc[0];
         s1 = st.sc[1];
-        srow = t;
     } else {
-        int kg = t & 15, mg = t >> 4;
+        // 8 m x 16 k codes: two 8x8 nibble transposes give, for each m, the
+        // 16 K-consecutive codes as 8 bytes of its 16-byte chunk
+        int mg = t & 31, kq = t >> 5;
         uint32_t lo[8], hi[8], tlo[8], thi[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            lo[i] = st.code[i >> 1][2 * (i & 1)];
-            hi[i] = st.code[i >> 1][2 * (i & 1) + 1];
+            lo[i] = st.code[i >> 2][i & 3];
+            hi[i] = st.code[(i + 8) >> 2][(i + 8) & 3];
         }
         transpose8x8_nibbles(lo, tlo);
         transpose8x8_nibbles(hi, thi);
-        uint8_t* base = tile + (kg >> 2) * kPlaneStride + 4 * (kg & 3);
+        uint8_t* base = tile + (kq >> 1) * kPlaneStride + 8 * (kq & 1);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            *reinterpret_cast<uint32_t*>(base + (16 * mg + j) * 16) = tlo[j];
-            *reinterpret_cast<uint32_t*>(base + (16 * mg + 8 + j) * 16) = thi[j];
+            u32x2 v;
+            v[0] = tlo[j];
+            v[1] = thi[j];
+            *reinterpret_cast<u32x2*>(base + swz<false>(8 * mg + j) * 16) = v;
         }
         s0 = st.sc[0] | (st.sc[1] << 8) | (st.sc[2] << 16) | (st.sc[3] << 24);
         s1 = st.sc[4] | (st.sc[5] << 8) | (st.sc[6] << 16) | (st.sc[7] << 24);
-        srow = t;
     }
     u32x2 w;
     w[0] = __builtin_amdgcn_perm(s1, s0, 0x05040100u);  // b0 b1 b4 b5
     w[1] = __builtin_amdgcn_perm(s1, s0, 0x07060302u);  // b2 b3 b6 b7
-    *reinterpret_cast<u32x2*>(sct + srow * 8) = w;
+    *reinterpret_cast<u32x2*>(sct + t * 8) = w;
 }
 
 // 8 FP16 operand values from 8 codes (one 32-bit word) and the block scale.
@@ -261,6 +302,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
     const uint32_t nbm = (uint32_t)((p.M + kTM - 1) / kTM), nbn = (uint32_t)((p.N + kTN - 1) / kTN);
     uint32_t tm, tn;
     tile_of(blockIdx.x, nbm, nbn, tm, tn);
+    // the integer divisions above run on the vector ALU; pin the results to
+    // scalar registers so buffer-load scalar offsets derived from them stay
+    // scalar
+    tm = __builtin_amdgcn_readfirstlane(tm);
+    tn = __builtin_amdgcn_readfirstlane(tn);
     const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -285,10 +331,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
 #define READ_HALF(As, CA, CB, h)                                                               \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
         CA[i] = *reinterpret_cast<const u32x4*>((As) + (lk + 2 * (h)) * kPlaneStride +         \
-                                                (wm * 128 + 32 * i + lr) * 16);                \
+                                                swz<kAK>(wm * 128 + 32 * i + lr) * 16);        \
         CB[i] = *reinterpret_cast<const u32x4*>((As) + kOperandTile +                          \
                                                 (lk + 2 * (h)) * kPlaneStride +                \
-                                                (wn * 128 + 32 * i + lr) * 16);                \
+                                                swz<kBK>(wn * 128 + 32 * i + lr) * 16);        \
     }
 #define READ_SCALES(As)                                                                        \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
@@ -593,7 +639,10 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
         }
         return hipGetLastError();
     }
-    const bool full = (M % kTM == 0) && (N % kTN == 0) && (K % kTK == 0);
+    // full tiles: no bounds checks, 32-bit buffer offsets (planes below 2 GiB)
+    const bool small = (uint64_t)M * (uint64_t)K / 2 < (1ull << 31) &&
+                       (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);
+    const bool full = (M % kTM == 0) && (N % kTN == 0) && (K % kTK == 0) && small;
     const uint64_t tiles = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
     dim3 grid((unsigned)tiles);
     // NT: A, B K-major; NN: A K-major, B MN-major; TN: both MN-major
