@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step runs in the library's HIP kernels.
 PyTorch supplies device memory and the current HIP stream.  The library
-must be built (``python -m nvfp4_bit_microscaled_amd.build``); importing
+must be built (``python nvfp4_bit_microscaled_amd/build.py``); importing
 this package without it raises ImportError -- there is no fallback.
 
 NVFP4 (guiahardware.es "NVFP4: cos'e e come supera FP8 e BF16", section
@@ -44,7 +44,7 @@ class NVFP4Error(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libnvfp4.so is not built: run `python -m nvfp4_bit_microscaled_amd.build`"
+        raise ImportError("libnvfp4.so is not built: run `python nvfp4_bit_microscaled_amd/build.py`"
                           " (expected at %s)" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     i64, u64, u32, vp, ci = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int

@@ -1,7 +1,8 @@
 """Build libnvfp4.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Run as ``python -m nvfp4_bit_microscaled_amd.build``; the library lands next to
-this file.  Compiles every time it is called.
+Run as ``python nvfp4_bit_microscaled_amd/build.py`` (a plain script: the
+package itself cannot be imported before the library exists); the library
+lands next to this file.  Compiles every time it is called.
 """
 from __future__ import annotations
 
