@@ -25,6 +25,7 @@ namespace nvfp4 {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 
 struct GemmParams {
     int64_t M, N, K;
@@ -37,6 +38,7 @@ struct GemmParams {
     uint8_t* c;
     int64_t ldc;
     bool a2d, b2d, out_bf16;
+    bool vec_out;  // C rows allow 8-byte (BF16) / 16-byte (FP32) stores
 };
 
 // 8x8 nibble transpose: in[k] holds element (k, j) in nibble j; out[j] gets
@@ -196,22 +198,27 @@ __device__ __forceinline__ void stage_load(const uint8_t* __restrict__ codes,
                 st.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, vs, ss, 0);
             }
         } else {
+            // edge tiles: loads from clamped addresses (MN % 16 == 0, so a group
+            // of 8 columns is wholly inside or outside; K >= 16), zeroed after,
+            // so no load sits under a branch
+            const bool mok = m < MN;
+            const uint8_t* col = codes + (mok ? m / 2 : 0);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 int64_t k = k0 + 16 * kq + i;
-                uint32_t w = 0u;
-                if (k < K && m < MN)
-                    w = *reinterpret_cast<const uint32_t*>(codes + k * (MN / 2) + m / 2);
-                st.code[i >> 2][i & 3] = w;
+                int64_t kc = k < K ? k : K - 1;
+                uint32_t w = *reinterpret_cast<const uint32_t*>(col + kc * (MN / 2));
+                st.code[i >> 2][i & 3] = (mok && k < K) ? w : 0u;
             }
-            int64_t row = row0 + t;
+            const int64_t row = row0 + t;
+            const bool rok = row < MN;
+            const int64_t rc = rok ? row : 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 int64_t kb = k0 / 16 + j;
-                uint32_t b = 0u;
-                if (row < MN && kb * 16 < K)
-                    b = k2D ? scales[kb * (MN / 16) + row / 16] : scales[kb * MN + row];
-                st.sc[j] = b;
+                int64_t kbc = kb * 16 < K ? kb : K / 16 - 1;
+                uint32_t b = k2D ? scales[kbc * (MN / 16) + rc / 16] : scales[kbc * MN + rc];
+                st.sc[j] = (rok && kb * 16 < K) ? b : 0u;
             }
         }
     }
@@ -353,10 +360,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
         AF[i] = dequant_word(CA[i][q], EA[i][(q) >> 1]);                                       \
         BF[i] = dequant_word(CB[i][q], EB[i][(q) >> 1]);                                       \
     }
+    // B as the MFMA's first operand: acc[i][j] holds the transposed 32 x 32
+    // block, so each lane owns four consecutive columns of one C row
 #define MFMA(AF, BF)                                                                           \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                              \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(AF[i], BF[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(BF[j], AF[i], acc[i][j], 0, 0, 0);
     // one MFMA then four VALU, sixteen times; each step its own scheduling region
 #define INTERLEAVE()                                                                           \
     _Pragma("unroll") for (int g = 0; g < 16; ++g) {                                           \
@@ -414,26 +423,97 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
 #undef INTERLEAVE
 #undef PREFETCH
 
+    // Epilogue.  acc[i][j][4g + e] is C[row][col + e] with row = 32 i + lane % 32
+    // and col = 32 j + 8 g + 4 (lane / 32) inside the wave's sub-tile.
     const float sab = (*p.a_ts) * (*p.b_ts);
+    if (kFull && p.vec_out) {
+        if (p.out_bf16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + wm * 128 + i * 32 + lr;
+                uint16_t* crow = reinterpret_cast<uint16_t*>(p.c) + row * p.ldc + n0 + wn * 128 + 4 * lk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        uint32_t h[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            uint32_t u = __float_as_uint(acc[i][j][4 * g + e] * sab);
+                            h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // RNE
+                        }
+                        u32x2 w;
+                        w[0] = h[0] | (h[1] << 16);
+                        w[1] = h[2] | (h[3] << 16);
+                        *reinterpret_cast<u32x2*>(crow + j * 32 + 8 * g) = w;
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + wm * 128 + i * 32 + lr;
+                float* crow = reinterpret_cast<float*>(p.c) + row * p.ldc + n0 + wn * 128 + 4 * lk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float4_t v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * sab;
+                        *reinterpret_cast<float4_t*>(crow + j * 32 + 8 * g) = v;
+                    }
+            }
+        }
+        return;
+    }
+    // edge tiles or rows without vector alignment: four columns at a time
+    // where they all exist and the row allows it, single elements otherwise
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + wm * 128 + i * 32 + lr;
+        if (!kFull && row >= p.M) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                int64_t row = m0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * lk + (r % 4);
-                int64_t col = n0 + wn * 128 + j * 32 + lr;
-                if (kFull || (row < p.M && col < p.N)) {
-                    float v = acc[i][j][r] * sab;
+            for (int g = 0; g < 4; ++g) {
+                const int64_t col = n0 + wn * 128 + j * 32 + 8 * g + 4 * lk;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * sab;
+                const int64_t off = row * p.ldc + col;
+                if (p.vec_out && (kFull || col + 3 < p.N)) {
                     if (p.out_bf16) {
-                        uint32_t u = __float_as_uint(v);
-                        u += 0x7FFFu + ((u >> 16) & 1u);
-                        reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + col] = (uint16_t)(u >> 16);
+                        uint32_t h[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            uint32_t u = __float_as_uint(v[e]);
+                            h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                        }
+                        u32x2 w;
+                        w[0] = h[0] | (h[1] << 16);
+                        w[1] = h[2] | (h[3] << 16);
+                        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.c) + off) = w;
                     } else {
-                        reinterpret_cast<float*>(p.c)[row * p.ldc + col] = v;
+                        float4_t w;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[e] = v[e];
+                        *reinterpret_cast<float4_t*>(reinterpret_cast<float*>(p.c) + off) = w;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (!kFull && col + e >= p.N) break;
+                        if (p.out_bf16) {
+                            uint32_t u = __float_as_uint(v[e]);
+                            u += 0x7FFFu + ((u >> 16) & 1u);
+                            reinterpret_cast<uint16_t*>(p.c)[off + e] = (uint16_t)(u >> 16);
+                        } else {
+                            reinterpret_cast<float*>(p.c)[off + e] = v[e];
+                        }
                     }
                 }
             }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -452,7 +532,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
 // the main kernel: at step s lane (row l % 16, group g = l / 16) supplies
 // k = k0 + 32 g + 8 s + [0, 8) for both operands.
 // ---------------------------------------------------------------------------
-typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kSkN = 64;  // output columns per workgroup
 
 template <int KC, int RMAX>
@@ -618,6 +697,8 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     p.a2d = A.block2d != 0;
     p.b2d = B.block2d != 0;
     p.out_bf16 = out_bf16;
+    const int esz = out_bf16 ? 2 : 4;
+    p.vec_out = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(c) % (4 * esz) == 0;
     if (A.k_major && B.k_major && M <= 64 && K % 128 == 0) {
         // decode-style shapes: stream the weights with a dedicated kernel
         dim3 g((unsigned)((N + kSkN - 1) / kSkN));

@@ -49,6 +49,9 @@ def run_and_check(nv, layout, M, N, K, a_or, a_gpu, b_or, b_gpu, pairs=None):
     yf = nv.gemm(layout, a_gpu, b_gpu, out_dtype=torch.float32)
     yb = nv.gemm(layout, a_gpu, b_gpu, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
+    # same accumulators and scale: the BF16 output is the FP32 one rounded to
+    # nearest even (torch's CPU float -> bfloat16 conversion is RNE)
+    assert torch.equal(yb.cpu(), yf.cpu().to(torch.bfloat16))
     if pairs is None:
         ref, ab = oracle.gemm_full(layout, M, N, K, a_or, b_or)
         check_gemm(yf.cpu().numpy(), yb.float().cpu().numpy(), ref, ab, layout)
@@ -155,3 +158,36 @@ def test_k_zero_and_ones(nv):
     y = nv.gemm("NT", ones(64, K), ones(80, K), out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.all(y == K)
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("pad,offset", [(2, 0), (4, 1), (0, 0)])
+def test_full_tiles_strided_output(nv, layout, out_dtype, pad, offset):
+    """Full 256 x 256 tiles written into a row-padded / offset view of a larger
+    buffer: the results match the oracle and nothing outside the view changes
+    (with a row stride that is not a multiple of 4, or a start that is not
+    4-element aligned, the kernel must fall back to element stores)."""
+    rng = np.random.default_rng(11 + pad + 7 * offset)
+    M, N, K = 256, 512, 384
+    a_shape = (M, K) if layout != "TN" else (K, M)
+    b_shape = (N, K) if layout == "NT" else (K, N)
+    a_axis = 1 if layout != "TN" else 0
+    b_axis = 1 if layout == "NT" else 0
+    a_or, a_g = random_operand(nv, rng, *a_shape, False, a_axis, 0.5, scale_lo=0x30)
+    b_or, b_g = random_operand(nv, rng, *b_shape, layout == "NT", b_axis, 0.25, scale_lo=0x30)
+    buf = torch.full((M, N + pad + offset), -3.0, dtype=out_dtype, device="cuda")
+    view = buf[:, offset:offset + N]
+    nv.gemm(layout, a_g, b_g, out=view)
+    torch.cuda.synchronize()
+    ref, ab = oracle.gemm_full(layout, M, N, K, a_or, b_or)
+    got = view.float().cpu().numpy()
+    if out_dtype == torch.float32:
+        check_gemm(got, None, ref, ab, "strided fp32")
+    else:
+        yf = nv.gemm(layout, a_g, b_g, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        check_gemm(yf.cpu().numpy(), got, ref, ab, "strided bf16")
+        assert torch.equal(view.cpu(), yf.cpu().to(torch.bfloat16))
+    outside = torch.cat([buf[:, :offset], buf[:, offset + N:]], dim=1)
+    assert torch.all(outside == -3.0)
