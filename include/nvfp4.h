@@ -101,6 +101,15 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
  *   block, axis        NVFP4_BLOCK_1D with axis 1 (16 consecutive columns of a
  *                      row) or axis 0 (16 consecutive rows of a column);
  *                      NVFP4_BLOCK_2D: 16x16 tiles, axis ignored
+ *   transpose_out      0: outputs in the storage layout of x (above).
+ *                      1 (1D axis 0 or 2D only): the same quantization written
+ *                      as that of x^T, blocks along its rows: codes
+ *                      [cols, rows/2], scales [cols, rows/16] (1D) or
+ *                      [cols/16, rows/16] (2D).  Values, scales, the RHT and
+ *                      the stochastic-rounding index (row * cols + col of x)
+ *                      are unchanged; only the storage is transposed, so a
+ *                      GEMM contracting over the rows of x reads the result
+ *                      K-major.  NVFP4_ERR_UNSUPPORTED for 1D axis 1.
  *   rounding, seed, stream_id
  *                      NVFP4_ROUND_RNE, or NVFP4_ROUND_SR with the Philox
  *                      stream keyed by seed and stream_id (see above)
@@ -122,7 +131,8 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
  * and for 2D.  ld_x >= cols.  An empty tensor writes s_g = 0 (and amax 0).
  */
 nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
-                            int64_t ld_x, nvfp4_block block, int axis, nvfp4_round rounding,
+                            int64_t ld_x, nvfp4_block block, int axis, int transpose_out,
+                            nvfp4_round rounding,
                             uint64_t seed, uint32_t stream_id, int rht, uint32_t rht_sign_mask,
                             const float* amax_in, float* amax_out, uint8_t* codes,
                             uint8_t* scales, float* tensor_scale, void* workspace,

@@ -55,8 +55,8 @@ def _load():
     L.nvfp4_quantize_workspace_size.restype = ctypes.c_size_t
     L.nvfp4_quantize_workspace_size.argtypes = [i64, i64]
     L.nvfp4_quantize.restype = ci
-    L.nvfp4_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, u64, u32, ci, u32, vp, vp, vp,
-                                 vp, vp, vp, ctypes.c_size_t, vp]
+    L.nvfp4_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, ci, u64, u32, ci, u32, vp, vp,
+                                 vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.nvfp4_rht16.restype = ci
     L.nvfp4_rht16.argtypes = [vp, ci, i64, i64, i64, ci, u32, vp, i64, vp]
     L.nvfp4_dequantize.restype = ci
@@ -100,11 +100,11 @@ def nvfp4_quantize_workspace_size(rows: int, cols: int) -> int:
     return lib.nvfp4_quantize_workspace_size(rows, cols)
 
 
-def nvfp4_quantize(x, x_dtype, rows, cols, ld_x, block, axis, rounding, seed, stream_id, rht,
-                   rht_sign_mask, amax_in, amax_out, codes, scales, tensor_scale, workspace,
-                   workspace_bytes, stream=None) -> int:
-    return lib.nvfp4_quantize(_p(x), x_dtype, rows, cols, ld_x, block, axis, rounding, seed,
-                              stream_id, rht, rht_sign_mask, _p(amax_in), _p(amax_out),
+def nvfp4_quantize(x, x_dtype, rows, cols, ld_x, block, axis, transpose_out, rounding, seed,
+                   stream_id, rht, rht_sign_mask, amax_in, amax_out, codes, scales, tensor_scale,
+                   workspace, workspace_bytes, stream=None) -> int:
+    return lib.nvfp4_quantize(_p(x), x_dtype, rows, cols, ld_x, block, axis, transpose_out,
+                              rounding, seed, stream_id, rht, rht_sign_mask, _p(amax_in), _p(amax_out),
                               _p(codes), _p(scales), _p(tensor_scale), _p(workspace),
                               workspace_bytes, _stream(stream))
 
@@ -171,22 +171,31 @@ def _workspace(device, rows, cols):
 
 def quantize(x: torch.Tensor, block2d: bool = False, axis: int = 1, sr: bool = False,
              seed: int = 0, stream_id: int = 0, rht: bool = False, mask: int = 0,
-             amax_in: torch.Tensor | None = None, out: NVFP4Tensor | None = None) -> NVFP4Tensor:
-    """Quantize a 2-D BF16/FP32 CUDA tensor (row stride may exceed its width)."""
+             amax_in: torch.Tensor | None = None, out: NVFP4Tensor | None = None,
+             transpose: bool = False) -> NVFP4Tensor:
+    """Quantize a 2-D BF16/FP32 CUDA tensor (row stride may exceed its width).
+
+    transpose=True (blocks down the columns: axis 0 or 2D) returns the same
+    quantization stored as that of x^T: an NVFP4Tensor of shape [cols, rows]
+    with blocks along its rows (axis 1), the K-major operand of a GEMM that
+    contracts over the rows of x.
+    """
     assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1
     rows, cols = x.shape
     dev = x.device
+    o_rows, o_cols, o_axis = (cols, rows, 1) if transpose else (rows, cols, axis)
     if out is None:
         out = NVFP4Tensor(
-            codes=torch.empty(rows, cols // 2, dtype=torch.uint8, device=dev),
-            scales=torch.empty(scale_shape(rows, cols, block2d, axis), dtype=torch.uint8,
+            codes=torch.empty(o_rows, o_cols // 2, dtype=torch.uint8, device=dev),
+            scales=torch.empty(scale_shape(o_rows, o_cols, block2d, o_axis), dtype=torch.uint8,
                                device=dev),
             tensor_scale=torch.empty(1, dtype=torch.float32, device=dev),
             amax=torch.empty(1, dtype=torch.float32, device=dev),
-            rows=rows, cols=cols, block2d=block2d, axis=axis)
+            rows=o_rows, cols=o_cols, block2d=block2d, axis=o_axis)
     ws = None if amax_in is not None else _workspace(dev, rows, cols)
     st = nvfp4_quantize(x, _dtype_code(x), rows, cols, x.stride(0),
-                        BLOCK_2D if block2d else BLOCK_1D, axis, ROUND_SR if sr else ROUND_RNE,
+                        BLOCK_2D if block2d else BLOCK_1D, axis, int(transpose),
+                        ROUND_SR if sr else ROUND_RNE,
                         seed, stream_id, int(rht), mask, amax_in, out.amax, out.codes, out.scales,
                         out.tensor_scale, ws, 0 if ws is None else ws.numel())
     _check("nvfp4_quantize", st)

@@ -59,7 +59,8 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols)
 }
 
 nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
-                            int64_t ld_x, nvfp4_block block, int axis, nvfp4_round rounding,
+                            int64_t ld_x, nvfp4_block block, int axis, int transpose_out,
+                            nvfp4_round rounding,
                             uint64_t seed, uint32_t stream_id, int rht, uint32_t rht_sign_mask,
                             const float* amax_in, float* amax_out, uint8_t* codes,
                             uint8_t* scales, float* tensor_scale, void* workspace,
@@ -70,9 +71,11 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, in
     if (rounding != NVFP4_ROUND_RNE && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_INVALID_ARG;
     if (block == NVFP4_BLOCK_1D && axis != 0 && axis != 1) return NVFP4_ERR_INVALID_ARG;
     if (rht != 0 && rht != 1) return NVFP4_ERR_INVALID_ARG;
+    if (transpose_out != 0 && transpose_out != 1) return NVFP4_ERR_INVALID_ARG;
     if (rows < 0 || cols < 0) return NVFP4_ERR_INVALID_ARG;
     if (!tensor_scale) return NVFP4_ERR_INVALID_ARG;
     if (rht && block == NVFP4_BLOCK_2D) return NVFP4_ERR_UNSUPPORTED;
+    if (transpose_out && block == NVFP4_BLOCK_1D && axis == 1) return NVFP4_ERR_UNSUPPORTED;
     if (cols % 16) return NVFP4_ERR_SHAPE;
     bool along_rows = (block == NVFP4_BLOCK_2D) || axis == 0;
     if (along_rows && rows % 16) return NVFP4_ERR_SHAPE;
@@ -123,6 +126,8 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, in
         if (hipStreamSynchronize(s) != hipSuccess) return NVFP4_ERR_HIP;
         if (!std::isfinite(h)) return NVFP4_ERR_NONFINITE;
     }
+    if (transpose_out)
+        return from_hip(launch_quantize_transposed(a, amax_src, amax_in != nullptr, s));
     return from_hip(launch_quantize(a, amax_src, amax_in != nullptr, s));
 }
 

@@ -38,6 +38,11 @@ hipError_t launch_amax(const QuantArgs& a, float* partials, float* amax_dst, hip
 hipError_t launch_quantize(const QuantArgs& a, const float* amax_src, bool write_amax_out,
                            hipStream_t s);
 
+// Pass 2 for blocks down the columns (1D axis 0 or 2D), written transposed:
+// codes [cols, rows/2], scales [cols, rows/16] (1D) / [cols/16, rows/16] (2D).
+hipError_t launch_quantize_transposed(const QuantArgs& a, const float* amax_src,
+                                      bool write_amax_out, hipStream_t s);
+
 // Empty tensor: s_g = 0 and amax = 0.
 hipError_t launch_write_zero_scale(float* tensor_scale, float* amax_out, hipStream_t s);
 

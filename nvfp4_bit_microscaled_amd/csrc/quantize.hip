@@ -301,6 +301,153 @@ __global__ __launch_bounds__(256) void k_quant_cols(QuantParams p)
     if (kAmaxOnly) block_reduce_max_store(amax_local, p.partials + blockIdx.x);
 }
 
+// ------------------------------------------------------------ transposed output
+
+// Blocks down the columns (1x16 along rows, or 16x16), written as the
+// quantization of the transposed tensor: codes [cols, rows/2] and scales
+// [cols, rows/16] (1D) or [cols/16, rows/16] (2D), so a GEMM that contracts
+// over the rows reads both operands K-major.  Element values, scales, the
+// transform and the stochastic-rounding counter are those of the untransposed
+// quantization (idx = row * cols + col of x).
+//
+// One workgroup per 256 x 256 tile.  Thread t quantizes columns 4 (t % 64) ..
+// +3 of row blocks w, w + 4, w + 8, w + 12 (w = t / 64), 16 rows x 4 columns
+// at a time as in the column kernel; the packed codes (8 bytes per column and
+// row block) go to LDS as [column][row block], then leave as 128-byte rows
+// of the transposed tensor.  The row-block slot is XOR-swizzled with the
+// column group so the 64 lanes of a wave write 64 different banks pairs.
+constexpr int kTT = 256;                  // tile rows and columns
+constexpr int kTCodeRow = kTT / 2;        // LDS bytes per transposed row (16 slots x 8)
+constexpr int kTCodeBytes = kTT * kTCodeRow;
+constexpr int kTScaleBytes = kTT * 16;
+
+template <bool kBF16, bool kSR, bool kRHT, bool k2D>
+__global__ __launch_bounds__(256) void k_quant_t(QuantParams p)
+{
+    constexpr int esz = kBF16 ? 2 : 4;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_codes[kTCodeBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scales[kTScaleBytes];
+    const TensorScale ts = make_tensor_scale(*p.amax_src);
+    write_scale_outputs(p, ts);
+    const int t = threadIdx.x, cg = t & 63, w = t >> 6;
+    const int64_t rows = p.rows, cols = p.cols;
+    const int64_t out_ld = rows / 2;     // bytes per transposed code row
+    const int64_t sc_ld = rows / 16;     // bytes per transposed scale row
+    for (uint32_t tile = blockIdx.x; tile < p.items; tile += gridDim.x) {
+        const uint32_t tr = fdiv(tile, p.div);
+        const uint32_t tc = tile - tr * p.div.d;
+        const int64_t R0 = (int64_t)tr * kTT, C0 = (int64_t)tc * kTT;
+        const int64_t c0 = C0 + 4 * cg;
+        const bool col_ok = c0 < cols;   // cols % 16 == 0: a column group is whole
+#pragma unroll 1
+        for (int it = 0; it < 4; ++it) {
+            const int rbl = 4 * it + w;
+            const int64_t r0 = R0 + 16 * rbl;
+            const bool ok = col_ok && r0 < rows;
+            float v[4][16];  // [column][row]
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float x4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (ok) load4<kBF16>(p.x + ((r0 + i) * p.ld + c0) * esz, x4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j][i] = x4[j];
+            }
+            if (kRHT) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) rht16_inplace(v[j], p.mask);
+            }
+            float aB[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                aB[j] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) aB[j] = __builtin_fmaxf(aB[j], __builtin_fabsf(v[j][i]));
+            }
+            if (k2D) {  // the 16x16 block spans the four lanes cg & ~3 .. +3
+                float m = __builtin_fmaxf(__builtin_fmaxf(aB[0], aB[1]), __builtin_fmaxf(aB[2], aB[3]));
+                m = __builtin_fmaxf(m, __shfl_xor(m, 1, 64));
+                m = __builtin_fmaxf(m, __shfl_xor(m, 2, 64));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) aB[j] = m;
+            }
+            uint32_t e[4];
+            u32x2 out[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                BlockDiv bd;
+                bool zero;
+                e[j] = block_scale(aB[j], ts, bd, zero);
+                float y[16];
+                if (zero) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) y[i] = 0.0f;
+                } else {
+                    quotients<16>(v[j], bd, y);
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[j][i] = y[i];
+            }
+            if (kSR) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint64_t g = (uint64_t)((r0 + i) * cols + c0) >> 2;
+                    u32x4 rw = sr_words(p.seed, p.stream_id, g);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float q = v[j][i];
+                        uint32_t r = rw[j];
+                        sr_values<1>(&q, &r);
+                        v[j][i] = q;
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                out[j][0] = pack8_rne(v[j]);
+                out[j][1] = pack8_rne(v[j] + 8);
+            }
+            const int slot = rbl ^ (cg & 15);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x2*>(lds_codes + (4 * cg + j) * kTCodeRow + 8 * slot) = out[j];
+            if (k2D) {
+                if ((cg & 3) == 0) lds_scales[(cg >> 2) * 16 + rbl] = (uint8_t)e[0];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) lds_scales[(4 * cg + j) * 16 + rbl] = (uint8_t)e[j];
+            }
+        }
+        __syncthreads();
+        // codes: transposed row cl gets its 16 slots (row blocks) in order
+        const int nrb = (int)((rows - R0) / 16 < 16 ? (rows - R0) / 16 : 16);
+#pragma unroll 1
+        for (int pass = 0; pass < 8; ++pass) {
+            const int cl = 32 * pass + (t >> 3), ch = t & 7;
+            if (C0 + cl >= cols) continue;
+            const int s = (cl >> 2) & 15;
+            uint8_t* dst = p.codes + (C0 + cl) * out_ld + R0 / 2 + 16 * ch;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rb = 2 * ch + h;
+                if (rb < nrb)
+                    *reinterpret_cast<u32x2*>(dst + 8 * h) =
+                        *reinterpret_cast<const u32x2*>(lds_codes + cl * kTCodeRow + 8 * (rb ^ s));
+            }
+        }
+        // scales: one 16-byte row per transposed scale row
+        const int nsr = k2D ? 16 : 256;
+        if (t < nsr) {
+            const int64_t orow = k2D ? C0 / 16 + t : C0 + t;
+            if (orow < (k2D ? cols / 16 : cols)) {
+                uint8_t* dst = p.scales + orow * sc_ld + R0 / 16;
+                const uint8_t* src = lds_scales + t * 16;
+                for (int b = 0; b < nrb; ++b) dst[b] = src[b];
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // ------------------------------------------------------------ 16x16 blocks
 
 // One wave per 16-row x 256-column strip; lane l covers columns
@@ -637,6 +784,28 @@ hipError_t launch_quantize(const QuantArgs& a, const float* amax_src, bool write
         int grid = grid_for((uint64_t)p.items * 64, kGridCap);
         NVFP4_DISPATCH_BOOL(a.bf16, BF, NVFP4_DISPATCH_BOOL(a.sr, SR,
             hipLaunchKernelGGL((k_quant_2d<BF, SR>), dim3(grid), dim3(256), 0, s, p)));
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_transposed(const QuantArgs& a, const float* amax_src,
+                                      bool write_amax_out, hipStream_t s)
+{
+    QuantParams p = make_params(a);
+    p.amax_src = amax_src;
+    p.write_amax_out = write_amax_out && a.amax_out != nullptr;
+    const uint32_t tiles_c = (uint32_t)((a.cols + kTT - 1) / kTT);
+    p.items = (uint32_t)((a.rows + kTT - 1) / kTT) * tiles_c;
+    p.div = make_fastdiv(tiles_c);
+    int grid = (int)(p.items < (uint32_t)kGridCap ? p.items : (uint32_t)kGridCap);
+    if (a.block2d) {
+        NVFP4_DISPATCH_BOOL(a.bf16, BF, NVFP4_DISPATCH_BOOL(a.sr, SR,
+            hipLaunchKernelGGL((k_quant_t<BF, SR, false, true>), dim3(grid), dim3(256), 0, s, p)));
+    } else {
+        NVFP4_DISPATCH_BOOL(a.bf16, BF, NVFP4_DISPATCH_BOOL(a.sr, SR,
+            NVFP4_DISPATCH_BOOL(a.rht, RH,
+                hipLaunchKernelGGL((k_quant_t<BF, SR, RH, false>), dim3(grid), dim3(256), 0, s,
+                                   p))));
     }
     return hipGetLastError();
 }

@@ -55,7 +55,7 @@ ODD = ctypes.c_void_p(0x10001)
 
 
 def q(lib, **kw):
-    args = dict(x=FAKE, dt=0, rows=32, cols=64, ld=64, block=0, axis=1, rnd=0, seed=0, sid=0,
+    args = dict(x=FAKE, dt=0, rows=32, cols=64, ld=64, block=0, axis=1, tr=0, rnd=0, seed=0, sid=0,
                 rht=0, mask=0, amax_in=FAKE, amax_out=None, codes=FAKE, scales=FAKE, ts=FAKE,
                 ws=None, wsb=0, stream=None)
     args.update(kw)
@@ -75,6 +75,9 @@ def test_quantize_validation(lib):
     assert q(lib, rows=24, block=1) == 2            # rows % 16 for 2D
     assert q(lib, ld=32) == 2                       # ld < cols
     assert q(lib, block=1, rht=1) == 5              # RHT needs 1D
+    assert q(lib, tr=2) == 1
+    assert q(lib, tr=1) == 5                        # transposed output needs blocks down columns
+    assert q(lib, tr=1, axis=0, rows=24) == 2
     assert q(lib, x=MISALIGNED) == 3
     assert q(lib, ld=68, dt=0) == 3                 # 136-byte BF16 rows are not 16-byte multiples
     assert q(lib, codes=MISALIGNED) == 3
