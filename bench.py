@@ -5,15 +5,21 @@ batch 4, the benchmark shape of the readjensen.com NVFP4 training-recipe page,
 benchmark paragraph), with the recipe of that page's recipe paragraph:
 
   fprop   quantize X (1x16 RNE), W_gu and W_down (16x16 RNE)
-          H = X W_gu^T                        NT  32768 x 28672 x 4096
+          H = X W_gu^T                     32768 x 28672 x 4096
           Act = silu(gate) * up  (torch, BF16 glue)
           quantize Act (1x16 RNE)
-          Y = Act W_down^T                    NT  32768 x 4096 x 14336
+          Y = Act W_down^T                 32768 x 4096 x 14336
   bwd     dY, dH synthetic (Student-t(3) x 1e-3)
-          down:    dAct = dY W_down           NN  32768 x 14336 x 4096   (dY 1x16 SR)
-                   dW_down = dY^T Act         TN  4096 x 14336 x 32768   (RHT16 + SR / RHT16)
-          gate/up: dX = dH W_gu               NN  32768 x 4096 x 28672   (dH 1x16 SR)
-                   dW_gu = dH^T X             TN  28672 x 4096 x 32768   (RHT16 + SR / RHT16)
+          down:    dAct = dY W_down        32768 x 14336 x 4096   (dY 1x16 SR)
+                   dW_down = dY^T Act      4096 x 14336 x 32768   (RHT16 + SR / RHT16)
+          gate/up: dX = dH W_gu            32768 x 4096 x 28672   (dH 1x16 SR)
+                   dW_gu = dH^T X          28672 x 4096 x 32768   (RHT16 + SR / RHT16)
+
+Every GEMM runs K-major x K-major (the NT kernel): the operands that are
+contracted over their rows (the weights in dgrad, both wgrad inputs) are
+quantized with transposed output, i.e. stored as the K-major tensors W^T,
+dY^T, Act^T, dH^T, X^T.  The transposed weights reuse the amax of the
+untransposed call.
 
 Inputs are resident in HBM before timing starts.  The JSON line reports the
 step's NVFP4 GEMM throughput (GEMM FLOPs / step time), per-kernel HIP-event
@@ -51,10 +57,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_llama8b.json")
 GEMM_SOURCE = os.path.join(ROOT, "nvfp4_bit_microscaled_amd", "csrc", "gemm.hip")
 
 
-def gemm_traffic(layout):
-    """HBM bytes per launch of the dominant GEMM kernel from the committed
-    rocprofv3 counter summary, or None when it is missing, covers another
-    layout, or was taken on a different GEMM source."""
+def gemm_traffic():
+    """Average HBM bytes per launch of the GEMM kernel over the step's six
+    launches, from the committed rocprofv3 counter summary, or None when it is
+    missing or was taken on a different GEMM source."""
     import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
@@ -63,7 +69,7 @@ def gemm_traffic(layout):
             sha = hashlib.sha256(f.read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if rec.get("gemm_source_sha256") != sha or rec.get("layout") != layout:
+    if rec.get("gemm_source_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -132,12 +138,12 @@ def main():
         return rows * cols * (in_bytes * (2 if amax_pass else 1) + 0.5 + 1 / 16)
 
     def Q(name, x, **kw):
-        qbytes[name] = qb(*x.shape)
+        qbytes[name] = qb(*x.shape, amax_pass=kw.get("amax_in") is None)
         return timer.run("quantize", nv.quantize, x, **kw)
 
-    def G(name, layout, a, b, M, N, K, out=None):
+    def G(name, role, a, b, M, N, K, out=None):
         gemm_flops[name] = 2.0 * M * N * K
-        return timer.run("gemm_" + layout, nv.gemm, layout, a, b, out_dtype=torch.bfloat16,
+        return timer.run("gemm_" + role, nv.gemm, "NT", a, b, out_dtype=torch.bfloat16,
                          out=out)
 
     bufs = {}
@@ -153,24 +159,26 @@ def main():
         xq = Q("X_rows", X)
         wgu = Q("Wgu_2d", W_gu, block2d=True)
         wdn = Q("Wdown_2d", W_down, block2d=True)
-        H = G("fprop_gu", "NT", xq, wgu, T, 2 * Fh, D, out=buf("H", (T, 2 * Fh)))
+        H = G("fprop_gu", "fprop", xq, wgu, T, 2 * Fh, D, out=buf("H", (T, 2 * Fh)))
         act = timer.run("swiglu", lambda: F.silu(H[:, :Fh]) * H[:, Fh:])
         aq = Q("Act_rows", act)
-        G("fprop_down", "NT", aq, wdn, T, D, Fh, out=buf("Y", (T, D)))
+        G("fprop_down", "fprop", aq, wdn, T, D, Fh, out=buf("Y", (T, D)))
         # ---- backward, down projection
         dyq = Q("dY_rows_sr", dY, sr=True, seed=sr_seed, stream_id=0)
-        G("dgrad_down", "NN", dyq, wdn, T, Fh, D, out=buf("dAct", (T, Fh)))
-        dyt = Q("dY_cols_rht_sr", dY, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,
-                stream_id=1)
-        at = Q("Act_cols_rht", act, axis=0, rht=True, mask=mask)
-        G("wgrad_down", "TN", dyt, at, D, Fh, T, out=buf("dWdown", (D, Fh)))
+        wdn_t = Q("Wdown_2d_T", W_down, block2d=True, transpose=True, amax_in=wdn.amax)
+        G("dgrad_down", "dgrad", dyq, wdn_t, T, Fh, D, out=buf("dAct", (T, Fh)))
+        dyt = Q("dY_cols_rht_sr_T", dY, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,
+                stream_id=1, transpose=True)
+        at = Q("Act_cols_rht_T", act, axis=0, rht=True, mask=mask, transpose=True)
+        G("wgrad_down", "wgrad", dyt, at, D, Fh, T, out=buf("dWdown", (D, Fh)))
         # ---- backward, gate/up projection
         dhq = Q("dH_rows_sr", dH, sr=True, seed=sr_seed, stream_id=0)
-        G("dgrad_gu", "NN", dhq, wgu, T, D, 2 * Fh, out=buf("dX", (T, D)))
-        dht = Q("dH_cols_rht_sr", dH, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,
-                stream_id=1)
-        xt = Q("X_cols_rht", X, axis=0, rht=True, mask=mask)
-        G("wgrad_gu", "TN", dht, xt, 2 * Fh, D, T, out=buf("dWgu", (2 * Fh, D)))
+        wgu_t = Q("Wgu_2d_T", W_gu, block2d=True, transpose=True, amax_in=wgu.amax)
+        G("dgrad_gu", "dgrad", dhq, wgu_t, T, D, 2 * Fh, out=buf("dX", (T, D)))
+        dht = Q("dH_cols_rht_sr_T", dH, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,
+                stream_id=1, transpose=True)
+        xt = Q("X_cols_rht_T", X, axis=0, rht=True, mask=mask, transpose=True)
+        G("wgrad_gu", "wgrad", dht, xt, 2 * Fh, D, T, out=buf("dWgu", (2 * Fh, D)))
 
     if args.calibration_copy:
         # a plain elementwise copy of known size: reads 1 GiB, writes 1 GiB
@@ -206,21 +214,20 @@ def main():
     value = flops_step / (ms_step * 1e-3) / 1e12
     per_kind = {k: {"ms_per_step": t / args.steps, "calls_per_step": n / args.steps}
                 for k, (t, n) in totals.items()}
-    # GEMM kernels per layout: flops per launch and average launch time
-    layout_flops = {"NT": gemm_flops["fprop_gu"] + gemm_flops["fprop_down"],
-                    "NN": gemm_flops["dgrad_down"] + gemm_flops["dgrad_gu"],
-                    "TN": gemm_flops["wgrad_down"] + gemm_flops["wgrad_gu"]}
-    gemm_kinds = {}
-    for lay, fl in layout_flops.items():
-        t, n = totals["gemm_" + lay]
-        gemm_kinds[lay] = {"tflops": fl * args.steps / (t * 1e-3) / 1e12,
-                           "avg_launch_ms": t / n, "launches": n}
-    dom = max(gemm_kinds, key=lambda k: totals["gemm_" + k][0])
-    d = gemm_kinds[dom]
-    achieved = d["tflops"]
+    # the six GEMMs by role (all the NT kernel): flops and average launch time
+    role_flops = {"fprop": gemm_flops["fprop_gu"] + gemm_flops["fprop_down"],
+                  "dgrad": gemm_flops["dgrad_down"] + gemm_flops["dgrad_gu"],
+                  "wgrad": gemm_flops["wgrad_down"] + gemm_flops["wgrad_gu"]}
+    gemm_roles = {}
+    for role, fl in role_flops.items():
+        t, n = totals["gemm_" + role]
+        gemm_roles[role] = {"tflops": fl * args.steps / (t * 1e-3) / 1e12,
+                            "avg_launch_ms": t / n, "launches": n}
     q_t, q_n = totals["quantize"]
     q_bytes = sum(qbytes.values()) * args.steps
-    gemm_t = sum(totals["gemm_" + k][0] for k in layout_flops)
+    gemm_t = sum(totals["gemm_" + k][0] for k in role_flops)
+    gemm_n = sum(totals["gemm_" + k][1] for k in role_flops)
+    achieved = flops_step * args.steps / (gemm_t * 1e-3) / 1e12
     line = {
         "metric": "NVFP4 GEMM TFLOPS (8B MLP shapes) + quantize GB/s, % of MI355X roofline",
         "value": round(value, 2),
@@ -237,16 +244,17 @@ def main():
         "config": {"workload": "llama3-8b-mlp-fwd+bwd-step", "tokens": T, "hidden": D,
                    "ffn": Fh, "gemm_tflop_per_step": round(flops_step / 1e12, 4),
                    "parallelism": "none (1 GPU)"},
-        "gemm_only_tflops": round(flops_step * args.steps / (gemm_t * 1e-3) / 1e12, 2),
-        "gemm_by_layout": {k: {kk: round(vv, 4) for kk, vv in v.items()}
-                           for k, v in gemm_kinds.items()},
+        "gemm_only_tflops": round(achieved, 2),
+        "gemm_by_role": {k: {kk: round(vv, 4) for kk, vv in v.items()}
+                         for k, v in gemm_roles.items()},
         "quantize_GBps": round(q_bytes / (q_t * 1e-3) / 1e9, 1),
         "quantize_frac_of_hbm": round(q_bytes / (q_t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "time_breakdown_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in per_kind.items()},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm (%s layout)" % dom,
+        "roofline": {"bound": "mfma", "kernel": "k_gemm NT (all six MLP GEMMs)",
                      "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": gemm_traffic(dom)},
+                     "avg_launch_ms": round(gemm_t / gemm_n, 4),
+                     "traffic": gemm_traffic()},
     }
     del bufs
     torch.cuda.empty_cache()

@@ -316,6 +316,17 @@ __global__ __launch_bounds__(256) void k_quant_cols(QuantParams p)
 // row block) go to LDS as [column][row block], then leave as 128-byte rows
 // of the transposed tensor.  The row-block slot is XOR-swizzled with the
 // column group so the 64 lanes of a wave write 64 different banks pairs.
+// fp4_pack2 into byte `sel` of `old` (sel is a constant once loops unroll)
+__device__ __forceinline__ uint32_t fp4_pack2_at(uint32_t old, float a, float b, int sel)
+{
+    switch (sel) {
+    case 0: return fp4_pack2<0>(old, a, b);
+    case 1: return fp4_pack2<1>(old, a, b);
+    case 2: return fp4_pack2<2>(old, a, b);
+    default: return fp4_pack2<3>(old, a, b);
+    }
+}
+
 constexpr int kTT = 256;                  // tile rows and columns
 constexpr int kTCodeRow = kTT / 2;        // LDS bytes per transposed row (16 slots x 8)
 constexpr int kTCodeBytes = kTT * kTCodeRow;
@@ -343,12 +354,16 @@ __global__ __launch_bounds__(256) void k_quant_t(QuantParams p)
         for (int it = 0; it < 4; ++it) {
             const int rbl = 4 * it + w;
             const int64_t r0 = R0 + 16 * rbl;
-            const bool ok = col_ok && r0 < rows;
+            if (r0 >= rows) break;           // uniform: later row blocks are past the end too
+            // a 16x16 block's four lanes share col_ok, so the shuffles below
+            // only ever read lanes that took the same path
+            if (!col_ok) continue;
+            const uint8_t* src = p.x + (r0 * p.ld + c0) * esz;
             float v[4][16];  // [column][row]
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float x4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                if (ok) load4<kBF16>(p.x + ((r0 + i) * p.ld + c0) * esz, x4);
+                float x4[4];
+                load4<kBF16>(src + (int64_t)i * p.ld * esz, x4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v[j][i] = x4[j];
             }
@@ -371,40 +386,44 @@ __global__ __launch_bounds__(256) void k_quant_t(QuantParams p)
                 for (int j = 0; j < 4; ++j) aB[j] = m;
             }
             uint32_t e[4];
-            u32x2 out[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 4; ++j) {  // quotients in place
                 BlockDiv bd;
                 bool zero;
                 e[j] = block_scale(aB[j], ts, bd, zero);
-                float y[16];
                 if (zero) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) y[i] = 0.0f;
+                    for (int i = 0; i < 16; ++i) v[j][i] = 0.0f;
                 } else {
+                    float y[16];
                     quotients<16>(v[j], bd, y);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) v[j][i] = y[i];
                 }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[j][i] = y[i];
             }
-            if (kSR) {
+            // two rows at a time: SR words of both rows, then one byte
+            // (rows i, i+1) per column into that column's 8-byte code word
+            u32x2 out[4];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
+            for (int j = 0; j < 4; ++j) out[j] = u32x2{0u, 0u};
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                float a[4], b[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { a[j] = v[j][i]; b[j] = v[j][i + 1]; }
+                if (kSR) {
                     const uint64_t g = (uint64_t)((r0 + i) * cols + c0) >> 2;
-                    u32x4 rw = sr_words(p.seed, p.stream_id, g);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float q = v[j][i];
-                        uint32_t r = rw[j];
-                        sr_values<1>(&q, &r);
-                        v[j][i] = q;
-                    }
+                    const uint64_t gstep = (uint64_t)cols >> 2;
+                    u32x4 ra = sr_words(p.seed, p.stream_id, g);
+                    u32x4 rb = sr_words(p.seed, p.stream_id, g + gstep);
+                    uint32_t wa[4] = {ra[0], ra[1], ra[2], ra[3]};
+                    uint32_t wb[4] = {rb[0], rb[1], rb[2], rb[3]};
+                    sr_values<4>(a, wa);
+                    sr_values<4>(b, wb);
                 }
-            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                out[j][0] = pack8_rne(v[j]);
-                out[j][1] = pack8_rne(v[j] + 8);
+                for (int j = 0; j < 4; ++j)
+                    out[j][i >> 3] = fp4_pack2_at(out[j][i >> 3], a[j], b[j], (i >> 1) & 3);
             }
             const int slot = rbl ^ (cg & 15);
 #pragma unroll

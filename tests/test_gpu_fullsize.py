@@ -6,7 +6,9 @@ row slices (first, middle and last rows) quantized by the oracle with the
 same amax and global row offset; GEMMs on the four corner 128 x 128 output
 tiles plus 4096 seeded random outputs, each a full-K FP64 dot product.
 
-Workloads: Llama-3-8B MLP at 32768 tokens (fprop and backward), decode-style
+Workloads: Llama-3-8B MLP at 32768 tokens (fprop and backward, in the NN/TN
+storage layouts and in the all-K-major configuration the training step
+times), decode-style
 skinny GEMMs (M in {1, 16, 64}, K 8192, N 28672) and one GPU's token share of
 a Llama-3.1-405B MLP (8192 tokens, hidden 16384, intermediate 53248).  The
 token count follows the benchmark paragraph of the readjensen.com NVFP4
@@ -42,11 +44,19 @@ def sample_slices(rows, step=16):
     return [(0, 64), (mid, mid + 64), (rows - 64, rows)]
 
 
+def transpose_codes(codes):
+    q = np.empty((codes.shape[0], codes.shape[1] * 2), dtype=np.uint8)
+    q[:, 0::2] = codes & 0xF
+    q[:, 1::2] = codes >> 4
+    qt = np.ascontiguousarray(q.T)
+    return (qt[:, 0::2] | (qt[:, 1::2] << 4)).astype(np.uint8)
+
+
 def check_quantize_sampled(nv, x, block2d=False, axis=1, sr=False, seed=0, stream_id=0,
-                           rht=False, mask=0):
+                           rht=False, mask=0, transpose=False):
     rows, cols = x.shape
     q = nv.quantize(x, block2d=block2d, axis=axis, sr=sr, seed=seed, stream_id=stream_id,
-                    rht=rht, mask=mask)
+                    rht=rht, mask=mask, transpose=transpose)
     torch.cuda.synchronize()
     xc = x.cpu()
     xo = to_oracle_input(xc)
@@ -60,6 +70,11 @@ def check_quantize_sampled(nv, x, block2d=False, axis=1, sr=False, seed=0, strea
                                       sr=sr, seed=seed, stream_id=stream_id, rht=rht, mask=mask,
                                       row0=r0, amax_in=am)
         assert ts == q.tensor_scale.item()
+        if transpose:  # the stored tensor is x^T: rows r0..r1 of x are its columns
+            assert np.array_equal(transpose_codes(c), gc[:, r0 // 2:r1 // 2]), \
+                "transposed codes differ for rows %d..%d" % (r0, r1)
+            assert np.array_equal(np.ascontiguousarray(s.T), gs[:, r0 // 16:r1 // 16])
+            continue
         assert np.array_equal(c, gc[r0:r1]), "codes differ in rows %d..%d" % (r0, r1)
         if block2d or axis == 0:
             assert np.array_equal(s, gs[r0 // 16:r1 // 16])
@@ -90,6 +105,21 @@ def test_llama8b_backward_quantize(nv):
     X = gen("act", T, D, L8["x_seed"])
     check_quantize_sampled(nv, X, axis=0, rht=True, mask=mask)
     del X
+
+
+def test_llama8b_transposed_quantize(nv):
+    """The K-major operands of dgrad (W^T, 16x16) and wgrad (dY^T with RHT + SR,
+    X^T with RHT) as the training step quantizes them."""
+    T, D, F = L8["tokens"], L8["hidden"], L8["ffn"]
+    mask = workloads.sign_mask(L8["mask_seed"])
+    check_quantize_sampled(nv, gen("w", 2 * F, D, L8["wgu_seed"]), block2d=True, transpose=True)
+    check_quantize_sampled(nv, gen("w", D, F, L8["wdown_seed"]), block2d=True, transpose=True)
+    dY = gen("grad", T, D, L8["dy_seed"])
+    check_quantize_sampled(nv, dY, axis=0, rht=True, mask=mask, sr=True, seed=L8["sr_seed"],
+                           stream_id=1, transpose=True)
+    del dY
+    check_quantize_sampled(nv, gen("act", T, D, L8["x_seed"]), axis=0, rht=True, mask=mask,
+                           transpose=True)
 
 
 def test_llama8b_dh_quantize(nv):
@@ -155,6 +185,16 @@ LLAMA8B_GEMMS = [
     ("NN", T8, D8, 2 * F8, False, True),    # dgrad gate+up
     ("TN", D8, F8, T8, False, False),       # wgrad down
     ("TN", 2 * F8, D8, T8, False, False),   # wgrad gate+up
+]
+
+
+# the launch configuration of the training step: every GEMM K-major x K-major,
+# the dgrad weights 16x16 blocks stored transposed
+LLAMA8B_GEMMS += [
+    ("NT", T8, F8, D8, False, True),        # dgrad down, W_down^T
+    ("NT", T8, D8, 2 * F8, False, True),    # dgrad gate+up, W_gu^T
+    ("NT", D8, F8, T8, False, False),       # wgrad down, dY^T x Act^T
+    ("NT", 2 * F8, D8, T8, False, False),   # wgrad gate+up, dH^T x X^T
 ]
 
 
