@@ -302,6 +302,105 @@ __device__ __forceinline__ void tile_of(uint32_t bid, uint32_t nbm, uint32_t nbn
     tn = in / gsize;
 }
 
+// Epilogue of a 256 x 256 tile: acc[i][j][4g + e] (MFMA operands B, A) is
+// C[row][col + e] with row = 32 i + lane % 32 and col = 32 j + 8 g + 4 (lane /
+// 32) inside the wave's 128 x 128 sub-tile.  C = s_A s_B acc, stored as BF16
+// (round to nearest even) or FP32; 8/16-byte stores where the row allows.
+template <bool kFull>
+__device__ __forceinline__ void store_tile(const GemmParams& p, float16_t (&acc)[4][4], int64_t m0,
+                                           int64_t n0, int wm, int wn, int lr, int lk)
+{
+    const float sab = (*p.a_ts) * (*p.b_ts);
+    if (kFull && p.vec_out) {
+        if (p.out_bf16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + wm * 128 + i * 32 + lr;
+                uint16_t* crow = reinterpret_cast<uint16_t*>(p.c) + row * p.ldc + n0 + wn * 128 + 4 * lk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        uint32_t h[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            uint32_t u = __float_as_uint(acc[i][j][4 * g + e] * sab);
+                            h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // RNE
+                        }
+                        u32x2 w;
+                        w[0] = h[0] | (h[1] << 16);
+                        w[1] = h[2] | (h[3] << 16);
+                        *reinterpret_cast<u32x2*>(crow + j * 32 + 8 * g) = w;
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + wm * 128 + i * 32 + lr;
+                float* crow = reinterpret_cast<float*>(p.c) + row * p.ldc + n0 + wn * 128 + 4 * lk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float4_t v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * sab;
+                        *reinterpret_cast<float4_t*>(crow + j * 32 + 8 * g) = v;
+                    }
+            }
+        }
+        return;
+    }
+    // edge tiles or rows without vector alignment: four columns at a time
+    // where they all exist and the row allows it, single elements otherwise
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + wm * 128 + i * 32 + lr;
+        if (!kFull && row >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t col = n0 + wn * 128 + j * 32 + 8 * g + 4 * lk;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * sab;
+                const int64_t off = row * p.ldc + col;
+                if (p.vec_out && (kFull || col + 3 < p.N)) {
+                    if (p.out_bf16) {
+                        uint32_t h[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            uint32_t u = __float_as_uint(v[e]);
+                            h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                        }
+                        u32x2 w;
+                        w[0] = h[0] | (h[1] << 16);
+                        w[1] = h[2] | (h[3] << 16);
+                        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.c) + off) = w;
+                    } else {
+                        float4_t w;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[e] = v[e];
+                        *reinterpret_cast<float4_t*>(reinterpret_cast<float*>(p.c) + off) = w;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (!kFull && col + e >= p.N) break;
+                        if (p.out_bf16) {
+                            uint32_t u = __float_as_uint(v[e]);
+                            u += 0x7FFFu + ((u >> 16) & 1u);
+                            reinterpret_cast<uint16_t*>(p.c)[off + e] = (uint16_t)(u >> 16);
+                        } else {
+                            reinterpret_cast<float*>(p.c)[off + e] = v[e];
+                        }
+                    }
+                }
+            }
+    }
+}
+
 template <bool kAK, bool kBK, bool kFull>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
 {
@@ -423,97 +522,253 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
 #undef INTERLEAVE
 #undef PREFETCH
 
-    // Epilogue.  acc[i][j][4g + e] is C[row][col + e] with row = 32 i + lane % 32
-    // and col = 32 j + 8 g + 4 (lane / 32) inside the wave's sub-tile.
-    const float sab = (*p.a_ts) * (*p.b_ts);
-    if (kFull && p.vec_out) {
-        if (p.out_bf16) {
+    store_tile<kFull>(p, acc, m0, n0, wm, wn, lr, lk);
+}
+
+// ---------------------------------------------------------------------------
+// K-major x K-major kernel (NT, K % 128 == 0): operands go from global memory
+// straight to LDS (buffer loads with the LDS flag; lane l of a wave writes
+// bytes 16 l .. 16 l + 15 of a 1 KB window), three LDS stages, one barrier per
+// k-tile.
+//
+// LDS per stage and operand: 256 rows x 64 code bytes, then 256 rows x 8
+// scale bytes (the row's eight 16-blocks of the k-tile, in order).  The four
+// 16-byte planes of a row (plane p = codes k in [32p, 32p + 32)) sit in slot
+// p ^ ((row >> 1) & 3), so the eight rows a fragment read serves per cycle
+// hit eight different bank groups.  Four consecutive lanes load one row's
+// 64 contiguous bytes.
+//
+// K order inside a k-tile: lanes 0-31 take planes {0, 1}, lanes 32-63 planes
+// {2, 3}; step s = 4h + q contracts word q of plane 2 (lane / 32) + h, so a
+// lane's four scale bytes are one aligned 32-bit word (bytes 2h, 2h + 1 for
+// K half h).
+//
+// Pipeline: tile kt + 2 is requested at the start of tile kt into the stage
+// tile kt - 1 used (every wave finished reading it before the previous
+// barrier).  After step 4 each wave waits for its own copies of tile kt + 1
+// and the workgroup meets at the barrier; the first-half codes and scales of
+// tile kt + 1 are read during step 5 and dequantized during step 7.  Rows
+// past M or N load the last valid row (never stored).
+// ---------------------------------------------------------------------------
+constexpr int kKKRow = 64;
+constexpr int kKKCodes = 256 * kKKRow;           // 16 KB
+constexpr int kKKOperand = kKKCodes + 256 * 8;   // + 2 KB scales
+constexpr int kKKStage = 2 * kKKOperand;
+constexpr int kKKLds = 3 * kKKStage;             // 110592 bytes
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+#define NVFP4_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
+
+struct KKOperand {
+    __amdgpu_buffer_rsrc_t codes, scales;
+    int code_off[4];   // per-lane byte offsets of this wave's four 1 KB code windows
+    int scale_off[2];  // and of its two 256-byte scale windows
+};
+
+__device__ __forceinline__ KKOperand kk_operand(const uint8_t* codes, const uint8_t* scales,
+                                                bool two_d, int64_t MN, int64_t K, int64_t row0)
+{
+    KKOperand o;
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t ldc = K / 2, lds = K / 16;
+    o.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + row0 * ldc), (short)0, 0x7FFFFFFF,
+                                                0x00020000);
+    const int64_t s0 = two_d ? (row0 / 16) * lds : row0 * lds;
+    o.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + s0), (short)0, 0x7FFFFFFF,
+                                                 0x00020000);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + wm * 128 + i * 32 + lr;
-                uint16_t* crow = reinterpret_cast<uint16_t*>(p.c) + row * p.ldc + n0 + wn * 128 + 4 * lk;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        uint32_t h[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            uint32_t u = __float_as_uint(acc[i][j][4 * g + e] * sab);
-                            h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // RNE
-                        }
-                        u32x2 w;
-                        w[0] = h[0] | (h[1] << 16);
-                        w[1] = h[2] | (h[3] << 16);
-                        *reinterpret_cast<u32x2*>(crow + j * 32 + 8 * g) = w;
-                    }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + wm * 128 + i * 32 + lr;
-                float* crow = reinterpret_cast<float*>(p.c) + row * p.ldc + n0 + wn * 128 + 4 * lk;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float4_t v;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * sab;
-                        *reinterpret_cast<float4_t*>(crow + j * 32 + 8 * g) = v;
-                    }
-            }
-        }
-        return;
+    for (int j = 0; j < 4; ++j) {
+        const int r = 16 * (4 * w + j) + (l >> 2), slot = l & 3;
+        const int64_t rg = row0 + r < MN ? row0 + r : MN - 1;
+        const int plane = slot ^ ((r >> 1) & 3);
+        o.code_off[j] = (int)((rg - row0) * ldc) + 16 * plane;
     }
-    // edge tiles or rows without vector alignment: four columns at a time
-    // where they all exist and the row allows it, single elements otherwise
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t row = m0 + wm * 128 + i * 32 + lr;
-        if (!kFull && row >= p.M) continue;
+    for (int j = 0; j < 2; ++j) {
+        const int r = 32 * (2 * w + j) + (l >> 1);
+        const int64_t rg = row0 + r < MN ? row0 + r : MN - 1;
+        const int64_t srow = two_d ? rg / 16 - row0 / 16 : rg - row0;
+        o.scale_off[j] = (int)(srow * lds) + 4 * (l & 1);
+    }
+    return o;
+}
+
+// Copies of k-tile kt of one operand into an LDS stage: four 1 KB code
+// windows and two 256-byte scale windows per wave.
+__device__ __forceinline__ void kk_copy_codes(__amdgpu_buffer_rsrc_t r, const KKOperand& o, int j,
+                                              int kt, uint8_t* dst)
+{
+    const int w = threadIdx.x >> 6;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + (4 * w + j) * 1024), 16,
+                                             o.code_off[j], kt * 64, 0, 0);
+}
+
+__device__ __forceinline__ void kk_copy_scales(__amdgpu_buffer_rsrc_t r, const KKOperand& o, int j,
+                                               int kt, uint8_t* dst)
+{
+    const int w = threadIdx.x >> 6;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + kKKCodes + (2 * w + j) * 256),
+                                             4, o.scale_off[j], kt * 8, 0, 0);
+}
+
+__device__ __forceinline__ void kk_copy(const KKOperand& o, int kt, uint8_t* dst)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kk_copy_codes(o.codes, o, j, kt, dst);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) kk_copy_scales(o.scales, o, j, kt, dst);
+}
+
+__global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const uint32_t nbm = (uint32_t)((p.M + kTM - 1) / kTM), nbn = (uint32_t)((p.N + kTN - 1) / kTN);
+    uint32_t tm, tn;
+    tile_of(blockIdx.x, nbm, nbn, tm, tn);
+    tm = __builtin_amdgcn_readfirstlane(tm);
+    tn = __builtin_amdgcn_readfirstlane(tn);
+    const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lr = lane & 31, lk = lane >> 5;
+    const int nk = (int)(p.K / kTK);
+
+    const KKOperand oa = kk_operand(p.a_codes, p.a_scales, p.a2d, p.M, p.K, m0);
+    const KKOperand ob = kk_operand(p.b_codes, p.b_scales, p.b2d, p.N, p.K, n0);
+
+    float16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t col = n0 + wn * 128 + j * 32 + 8 * g + 4 * lk;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * sab;
-                const int64_t off = row * p.ldc + col;
-                if (p.vec_out && (kFull || col + 3 < p.N)) {
-                    if (p.out_bf16) {
-                        uint32_t h[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            uint32_t u = __float_as_uint(v[e]);
-                            h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-                        }
-                        u32x2 w;
-                        w[0] = h[0] | (h[1] << 16);
-                        w[1] = h[2] | (h[3] << 16);
-                        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.c) + off) = w;
-                    } else {
-                        float4_t w;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) w[e] = v[e];
-                        *reinterpret_cast<float4_t*>(reinterpret_cast<float*>(p.c) + off) = w;
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (!kFull && col + e >= p.N) break;
-                        if (p.out_bf16) {
-                            uint32_t u = __float_as_uint(v[e]);
-                            u += 0x7FFFu + ((u >> 16) & 1u);
-                            reinterpret_cast<uint16_t*>(p.c)[off + e] = (uint16_t)(u >> 16);
-                        } else {
-                            reinterpret_cast<float*>(p.c)[off + e] = v[e];
-                        }
-                    }
-                }
-            }
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // fragment rows: A row wm*128 + 32 i + lr, B row wn*128 + 32 i + lr; the
+    // plane swizzle depends only on lr (row bases are multiples of 32)
+    const int sw = (lr >> 1) & 3;
+    const int a_row = (wm * 128 + lr) * kKKRow, b_row = kKKOperand + (wn * 128 + lr) * kKKRow;
+    const int a_srow = kKKCodes + (wm * 128 + lr) * 8 + 4 * lk;
+    const int b_srow = kKKOperand + kKKCodes + (wn * 128 + lr) * 8 + 4 * lk;
+    const int slot0 = 16 * ((2 * lk) ^ sw), slot1 = 16 * ((2 * lk + 1) ^ sw);
+
+    u32x4 ca0[4], cb0[4], ca1[4], cb1[4];
+    half2_t ea0[4], ea1[4], eb0[4], eb1[4];
+    half8_t af0[4], bf0[4], af1[4], bf1[4];
+    uint32_t sa[4], sb[4];  // raw scale words, converted a step after the read
+#define KK_READ(st, CA, CB, h)                                                                 \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+        CA[i] = *reinterpret_cast<const u32x4*>((st) + a_row + 32 * kKKRow * i + ((h) ? slot1 : slot0)); \
+        CB[i] = *reinterpret_cast<const u32x4*>((st) + b_row + 32 * kKKRow * i + ((h) ? slot1 : slot0)); \
+        sa[i] = *reinterpret_cast<const uint32_t*>((st) + a_srow + 32 * 8 * i);                \
+        sb[i] = *reinterpret_cast<const uint32_t*>((st) + b_srow + 32 * 8 * i);                \
     }
+#define KK_SCALES(EA, EB, h)                                                                   \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+        EA[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[i], 1.0f, (h) != 0);               \
+        EB[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[i], 1.0f, (h) != 0);               \
+    }
+#define KK_DEQUANT(AF, BF, CA, CB, EA, EB, q)                                                  \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+        AF[i] = dequant_word(CA[i][q], EA[i][(q) >> 1]);                                       \
+        BF[i] = dequant_word(CB[i][q], EB[i][(q) >> 1]);                                       \
+    }
+#define KK_MFMA(AF, BF)                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                              \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(BF[j], AF[i], acc[i][j], 0, 0, 0);
+#define KK_INTERLEAVE()                                                                        \
+    _Pragma("unroll") for (int g = 0; g < 16; ++g) {                                           \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                     \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);
+    // the same with this step's share of the next-but-one tile's copies
+    // spread over the MFMAs (one after every fifth MFMA)
+#define KK_INTERLEAVE_COPY()                                                                   \
+    _Pragma("unroll") for (int g = 0; g < 16; ++g) {                                           \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                     \
+        if (g % 5 == 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                     \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);
+
+    // prologue: tiles 0 and 1 requested, tile 0 read
+    kk_copy(oa, 0, lds);
+    kk_copy(ob, 0, lds + kKKOperand);
+    if (nk > 1) {
+        kk_copy(oa, 1, lds + kKKStage);
+        kk_copy(ob, 1, lds + kKKStage + kKKOperand);
+        NVFP4_WAIT_VMCNT(12);
+    } else {
+        NVFP4_WAIT_VMCNT(0);
+    }
+    __builtin_amdgcn_s_barrier();
+    KK_READ(lds, ca0, cb0, 0);
+    KK_SCALES(ea0, eb0, 0);
+    KK_DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 0);
+
+    const __amdgpu_buffer_rsrc_t none =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.a_codes, (short)0, 0, 0x00020000);
+    int s_cur = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
+        const int s_far = s_nxt == 2 ? 0 : s_nxt + 1;
+        const uint8_t* cur = lds + s_cur * kKKStage;
+        const uint8_t* nxt = lds + s_nxt * kKKStage;
+        // tile kt + 2 is copied in twelve loads spread over steps 0-4 (three
+        // in steps 0-1, two in 2-4).  Past the last tile the copies still
+        // issue, through resources with no records: out-of-range buffer loads
+        // return zeros without touching memory, so they only write zeros into
+        // the free stage, and the count of loads per tile stays twelve.
+        const bool far = kt + 2 < nk;
+        const int ktf = far ? kt + 2 : kt;
+        const __amdgpu_buffer_rsrc_t rac = far ? oa.codes : none;
+        const __amdgpu_buffer_rsrc_t ras = far ? oa.scales : none;
+        const __amdgpu_buffer_rsrc_t rbc = far ? ob.codes : none;
+        const __amdgpu_buffer_rsrc_t rbs = far ? ob.scales : none;
+        uint8_t* fa = lds + s_far * kKKStage;
+        uint8_t* fb = fa + kKKOperand;
+        kk_copy_codes(rac, oa, 0, ktf, fa); kk_copy_codes(rac, oa, 1, ktf, fa);
+        kk_copy_codes(rac, oa, 2, ktf, fa);
+        KK_DEQUANT(af1, bf1, ca0, cb0, ea0, eb0, 1); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY();   // 0
+        KK_READ(cur, ca1, cb1, 1);
+        kk_copy_codes(rac, oa, 3, ktf, fa); kk_copy_scales(ras, oa, 0, ktf, fa);
+        kk_copy_scales(ras, oa, 1, ktf, fa);
+        KK_DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 2); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY();   // 1
+        KK_SCALES(ea1, eb1, 1);
+        kk_copy_codes(rbc, ob, 0, ktf, fb); kk_copy_codes(rbc, ob, 1, ktf, fb);
+        KK_DEQUANT(af1, bf1, ca0, cb0, ea0, eb0, 3); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY();   // 2
+        kk_copy_codes(rbc, ob, 2, ktf, fb); kk_copy_codes(rbc, ob, 3, ktf, fb);
+        KK_DEQUANT(af0, bf0, ca1, cb1, ea1, eb1, 0); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY();   // 3
+        kk_copy_scales(rbs, ob, 0, ktf, fb); kk_copy_scales(rbs, ob, 1, ktf, fb);
+        KK_DEQUANT(af1, bf1, ca1, cb1, ea1, eb1, 1); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY();   // 4
+        // this wave's copies of tile kt + 1 have landed (tile kt + 2's may
+        // still be in flight); the plain barrier carries no memory fence, so
+        // those stay outstanding
+        NVFP4_WAIT_VMCNT(12);
+        __builtin_amdgcn_s_barrier();
+        KK_READ(nxt, ca0, cb0, 0);
+        KK_DEQUANT(af0, bf0, ca1, cb1, ea1, eb1, 2); KK_MFMA(af1, bf1); KK_INTERLEAVE();   // 5
+        KK_SCALES(ea0, eb0, 0);
+        KK_DEQUANT(af1, bf1, ca1, cb1, ea1, eb1, 3); KK_MFMA(af0, bf0); KK_INTERLEAVE();   // 6
+        KK_DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 0); KK_MFMA(af1, bf1); KK_INTERLEAVE();   // 7
+        s_cur = s_nxt;
+    }
+#undef KK_READ
+#undef KK_SCALES
+#undef KK_DEQUANT
+#undef KK_MFMA
+#undef KK_INTERLEAVE
+#undef KK_INTERLEAVE_COPY
+    if (m0 + kTM <= p.M && n0 + kTN <= p.N)
+        store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk);
+    else
+        store_tile<false>(p, acc, m0, n0, wm, wn, lr, lk);
 }
 
 // ---------------------------------------------------------------------------
@@ -718,6 +973,13 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
             hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);
         }
+        return hipGetLastError();
+    }
+    if (A.k_major && B.k_major && K % kTK == 0 && K / 2 * kTM < (1ll << 31)) {
+        const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
+        hipFuncSetAttribute((const void*)k_gemm_kk, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kKKLds);
+        hipLaunchKernelGGL(k_gemm_kk, dim3((unsigned)t), dim3(256), kKKLds, s, p);
         return hipGetLastError();
     }
     // full tiles: no bounds checks, 32-bit buffer offsets (planes below 2 GiB)

@@ -191,3 +191,27 @@ def test_full_tiles_strided_output(nv, layout, out_dtype, pad, offset):
         assert torch.equal(view.cpu(), yf.cpu().to(torch.bfloat16))
     outside = torch.cat([buf[:, :offset], buf[:, offset + N:]], dim=1)
     assert torch.all(outside == -3.0)
+
+
+# K-major x K-major with K % 128 == 0: the direct-to-LDS three-stage kernel.
+# One, two, three and many k-tiles (prologue-only, ring start, ring wrap),
+# ragged M and N on both sides of the 256 tile, every block-mode pair.
+KK_SHAPES = [(256, 256, 128), (272, 208, 256), (80, 528, 384), (512, 256, 1152), (784, 96, 640)]
+
+
+@pytest.mark.parametrize("M,N,K", KK_SHAPES)
+@pytest.mark.parametrize("a2d,b2d", [(False, False), (False, True), (True, True), (True, False)])
+def test_nt_kmajor_kernel(nv, M, N, K, a2d, b2d):
+    rng = np.random.default_rng(M * 7 + N * 3 + K + 2 * a2d + b2d)
+    a_or, a_g = random_operand(nv, rng, M, K, a2d, 1, 0.375)
+    b_or, b_g = random_operand(nv, rng, N, K, b2d, 1, 1.25)
+    run_and_check(nv, "NT", M, N, K, a_or, a_g, b_or, b_g)
+
+
+def test_nt_kmajor_odd_rows(nv):
+    """M and N not multiples of 16 (1D blocks only): clamped row loads."""
+    rng = np.random.default_rng(5)
+    M, N, K = 301, 77, 256
+    a_or, a_g = random_operand(nv, rng, M, K, False, 1, 0.5)
+    b_or, b_g = random_operand(nv, rng, N, K, False, 1, 0.5)
+    run_and_check(nv, "NT", M, N, K, a_or, a_g, b_or, b_g)
