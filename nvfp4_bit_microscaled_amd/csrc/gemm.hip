@@ -564,64 +564,70 @@ typedef __attribute__((address_space(3))) void lds_void_t;
     __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
 
 struct KKOperand {
-    __amdgpu_buffer_rsrc_t codes, scales;
-    int code_off[4];   // per-lane byte offsets of this wave's four 1 KB code windows
-    int scale_off[2];  // and of its two 256-byte scale windows
+    __amdgpu_buffer_rsrc_t codes, scales;  // records end at the operand's last row
+    int code_off[4];   // lane offsets in this wave's four 1 KB code windows
+    int scale_off[2];  // and in its two 256-byte scale windows
 };
 
+// Buffer resources start at the tile's first row and end at the operand's
+// last row (at most 256 rows on), so rows past M or N read as zeros.  Code
+// window j of wave w holds rows 16 (4w + j) .. +15, four lanes per row.
 __device__ __forceinline__ KKOperand kk_operand(const uint8_t* codes, const uint8_t* scales,
                                                 bool two_d, int64_t MN, int64_t K, int64_t row0)
 {
     KKOperand o;
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t ldc = K / 2, lds = K / 16;
-    o.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + row0 * ldc), (short)0, 0x7FFFFFFF,
-                                                0x00020000);
+    const int64_t nrow = MN - row0 < 256 ? MN - row0 : 256;
+    o.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + row0 * ldc), (short)0,
+                                                (int)(nrow * ldc), 0x00020000);
     const int64_t s0 = two_d ? (row0 / 16) * lds : row0 * lds;
-    o.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + s0), (short)0, 0x7FFFFFFF,
+    const int64_t srec = two_d ? (nrow + 15) / 16 * lds : nrow * lds;
+    o.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + s0), (short)0, (int)srec,
                                                  0x00020000);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = 16 * (4 * w + j) + (l >> 2), slot = l & 3;
-        const int64_t rg = row0 + r < MN ? row0 + r : MN - 1;
         const int plane = slot ^ ((r >> 1) & 3);
-        o.code_off[j] = (int)((rg - row0) * ldc) + 16 * plane;
+        o.code_off[j] = (int)(r * ldc) + 16 * plane;
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int r = 32 * (2 * w + j) + (l >> 1);
-        const int64_t rg = row0 + r < MN ? row0 + r : MN - 1;
-        const int64_t srow = two_d ? rg / 16 - row0 / 16 : rg - row0;
+        const int srow = two_d ? r / 16 : r;
         o.scale_off[j] = (int)(srow * lds) + 4 * (l & 1);
     }
     return o;
 }
 
-// Copies of k-tile kt of one operand into an LDS stage: four 1 KB code
-// windows and two 256-byte scale windows per wave.
-__device__ __forceinline__ void kk_copy_codes(__amdgpu_buffer_rsrc_t r, const KKOperand& o, int j,
-                                              int kt, uint8_t* dst)
+// Copy number `idx` (0-3: code windows, 4-5: scale windows) of k-tile kt of
+// one operand into its LDS stage area.
+__device__ __forceinline__ void kk_copy_one(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                            const KKOperand& o, int idx, int kt, uint8_t* dst)
 {
-    const int w = threadIdx.x >> 6;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + (4 * w + j) * 1024), 16,
-                                             o.code_off[j], kt * 64, 0, 0);
-}
-
-__device__ __forceinline__ void kk_copy_scales(__amdgpu_buffer_rsrc_t r, const KKOperand& o, int j,
-                                               int kt, uint8_t* dst)
-{
-    const int w = threadIdx.x >> 6;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + kKKCodes + (2 * w + j) * 256),
-                                             4, o.scale_off[j], kt * 8, 0, 0);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (idx < 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void_t*)(dst + (4 * w + idx) * 1024), 16,
+                                                 o.code_off[idx], kt * 64, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void_t*)(dst + kKKCodes + (2 * w + idx - 4) * 256), 4, o.scale_off[idx - 4],
+            kt * 8, 0, 0);
 }
 
 __device__ __forceinline__ void kk_copy(const KKOperand& o, int kt, uint8_t* dst)
 {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kk_copy_codes(o.codes, o, j, kt, dst);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) kk_copy_scales(o.scales, o, j, kt, dst);
+    for (int i = 0; i < 6; ++i) kk_copy_one(o.codes, o.scales, o, i, kt, dst);
 }
+
+// The twelve copies per wave and k-tile (A: 0-5, B: 6-11) and how many of
+// them each step issues: steps 0-4 only, so the barrier after step 4 waits
+// for the previous tile's copies with exactly these twelve in flight.
+struct KKPlan {
+    static constexpr int total = 12;
+    static constexpr int start[9] = {0, 3, 6, 8, 10, 12, 12, 12, 12};
+};
 
 __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 {
@@ -639,6 +645,7 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 
     const KKOperand oa = kk_operand(p.a_codes, p.a_scales, p.a2d, p.M, p.K, m0);
     const KKOperand ob = kk_operand(p.b_codes, p.b_scales, p.b2d, p.N, p.K, n0);
+    using Plan = KKPlan;
 
     float16_t acc[4][4];
 #pragma unroll
@@ -681,21 +688,22 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                              \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(BF[j], AF[i], acc[i][j], 0, 0, 0);
-#define KK_INTERLEAVE()                                                                        \
+    // one MFMA then four VALU, sixteen times, with this step's copies of the
+    // next-but-one tile spread over the MFMAs; each step its own region
+#define KK_INTERLEAVE_COPY(n)                                                                  \
     _Pragma("unroll") for (int g = 0; g < 16; ++g) {                                           \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                     \
+        if (((g + 1) * (n)) / 16 != (g * (n)) / 16)                                            \
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                 \
     }                                                                                          \
     __builtin_amdgcn_sched_barrier(0);
-    // the same with this step's share of the next-but-one tile's copies
-    // spread over the MFMAs (one after every fifth MFMA)
-#define KK_INTERLEAVE_COPY()                                                                   \
-    _Pragma("unroll") for (int g = 0; g < 16; ++g) {                                           \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                     \
-        if (g % 5 == 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                     \
-    }                                                                                          \
-    __builtin_amdgcn_sched_barrier(0);
+#define KK_COPIES(st)                                                                          \
+    _Pragma("unroll") for (int c_ = Plan::start[st]; c_ < Plan::start[(st) + 1]; ++c_) {       \
+        if (c_ < Plan::total / 2) kk_copy_one(rac, ras, oa, c_, ktf, fa);                 \
+        else kk_copy_one(rbc, rbs, ob, c_ - Plan::total / 2, ktf, fb);                    \
+    }
+#define KK_N(st) (Plan::start[(st) + 1] - Plan::start[st])
 
     // prologue: tiles 0 and 1 requested, tile 0 read
     kk_copy(oa, 0, lds);
@@ -703,7 +711,7 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
     if (nk > 1) {
         kk_copy(oa, 1, lds + kKKStage);
         kk_copy(ob, 1, lds + kKKStage + kKKOperand);
-        NVFP4_WAIT_VMCNT(12);
+        NVFP4_WAIT_VMCNT(Plan::total);
     } else {
         NVFP4_WAIT_VMCNT(0);
     }
@@ -720,11 +728,11 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
         const int s_far = s_nxt == 2 ? 0 : s_nxt + 1;
         const uint8_t* cur = lds + s_cur * kKKStage;
         const uint8_t* nxt = lds + s_nxt * kKKStage;
-        // tile kt + 2 is copied in twelve loads spread over steps 0-4 (three
-        // in steps 0-1, two in 2-4).  Past the last tile the copies still
-        // issue, through resources with no records: out-of-range buffer loads
-        // return zeros without touching memory, so they only write zeros into
-        // the free stage, and the count of loads per tile stays twelve.
+        // tile kt + 2 is copied in the plan's loads, spread over the steps.
+        // Past the last tile the copies still issue, through resources with
+        // no records: out-of-range buffer loads return zeros without touching
+        // memory, so they only write zeros into the free stage, and the count
+        // of loads per tile stays fixed.
         const bool far = kt + 2 < nk;
         const int ktf = far ? kt + 2 : kt;
         const __amdgpu_buffer_rsrc_t rac = far ? oa.codes : none;
@@ -733,38 +741,40 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
         const __amdgpu_buffer_rsrc_t rbs = far ? ob.scales : none;
         uint8_t* fa = lds + s_far * kKKStage;
         uint8_t* fb = fa + kKKOperand;
-        kk_copy_codes(rac, oa, 0, ktf, fa); kk_copy_codes(rac, oa, 1, ktf, fa);
-        kk_copy_codes(rac, oa, 2, ktf, fa);
-        KK_DEQUANT(af1, bf1, ca0, cb0, ea0, eb0, 1); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY();   // 0
+        KK_COPIES(0);
+        KK_DEQUANT(af1, bf1, ca0, cb0, ea0, eb0, 1); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY(KK_N(0));  // 0
         KK_READ(cur, ca1, cb1, 1);
-        kk_copy_codes(rac, oa, 3, ktf, fa); kk_copy_scales(ras, oa, 0, ktf, fa);
-        kk_copy_scales(ras, oa, 1, ktf, fa);
-        KK_DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 2); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY();   // 1
+        KK_COPIES(1);
+        KK_DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 2); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY(KK_N(1));  // 1
         KK_SCALES(ea1, eb1, 1);
-        kk_copy_codes(rbc, ob, 0, ktf, fb); kk_copy_codes(rbc, ob, 1, ktf, fb);
-        KK_DEQUANT(af1, bf1, ca0, cb0, ea0, eb0, 3); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY();   // 2
-        kk_copy_codes(rbc, ob, 2, ktf, fb); kk_copy_codes(rbc, ob, 3, ktf, fb);
-        KK_DEQUANT(af0, bf0, ca1, cb1, ea1, eb1, 0); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY();   // 3
-        kk_copy_scales(rbs, ob, 0, ktf, fb); kk_copy_scales(rbs, ob, 1, ktf, fb);
-        KK_DEQUANT(af1, bf1, ca1, cb1, ea1, eb1, 1); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY();   // 4
-        // this wave's copies of tile kt + 1 have landed (tile kt + 2's may
-        // still be in flight); the plain barrier carries no memory fence, so
-        // those stay outstanding
-        NVFP4_WAIT_VMCNT(12);
+        KK_COPIES(2);
+        KK_DEQUANT(af1, bf1, ca0, cb0, ea0, eb0, 3); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY(KK_N(2));  // 2
+        KK_COPIES(3);
+        KK_DEQUANT(af0, bf0, ca1, cb1, ea1, eb1, 0); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY(KK_N(3));  // 3
+        KK_COPIES(4);
+        KK_DEQUANT(af1, bf1, ca1, cb1, ea1, eb1, 1); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY(KK_N(4));  // 4
+        // this wave's copies of tile kt + 1 have landed (tile kt + 2's from
+        // steps 0-4 may still be in flight); the plain barrier carries no
+        // memory fence, so those stay outstanding
+        NVFP4_WAIT_VMCNT(Plan::start[5]);
         __builtin_amdgcn_s_barrier();
         KK_READ(nxt, ca0, cb0, 0);
-        KK_DEQUANT(af0, bf0, ca1, cb1, ea1, eb1, 2); KK_MFMA(af1, bf1); KK_INTERLEAVE();   // 5
+        KK_COPIES(5);
+        KK_DEQUANT(af0, bf0, ca1, cb1, ea1, eb1, 2); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY(KK_N(5));  // 5
         KK_SCALES(ea0, eb0, 0);
-        KK_DEQUANT(af1, bf1, ca1, cb1, ea1, eb1, 3); KK_MFMA(af0, bf0); KK_INTERLEAVE();   // 6
-        KK_DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 0); KK_MFMA(af1, bf1); KK_INTERLEAVE();   // 7
+        KK_COPIES(6);
+        KK_DEQUANT(af1, bf1, ca1, cb1, ea1, eb1, 3); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY(KK_N(6));  // 6
+        KK_COPIES(7);
+        KK_DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 0); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY(KK_N(7));  // 7
         s_cur = s_nxt;
     }
 #undef KK_READ
 #undef KK_SCALES
 #undef KK_DEQUANT
 #undef KK_MFMA
-#undef KK_INTERLEAVE
 #undef KK_INTERLEAVE_COPY
+#undef KK_COPIES
+#undef KK_N
     if (m0 + kTM <= p.M && n0 + kTN <= p.N)
         store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk);
     else
