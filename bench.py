@@ -250,7 +250,7 @@ def main():
         "quantize_GBps": round(q_bytes / (q_t * 1e-3) / 1e9, 1),
         "quantize_frac_of_hbm": round(q_bytes / (q_t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "time_breakdown_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in per_kind.items()},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm NT (all six MLP GEMMs)",
+        "roofline": {"bound": "mfma", "kernel": "k_gemm_kk (K-major x K-major, all six MLP GEMMs)",
                      "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                      "avg_launch_ms": round(gemm_t / gemm_n, 4),
