@@ -565,13 +565,16 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 struct KKOperand {
     __amdgpu_buffer_rsrc_t codes, scales;  // records end at the operand's last row
-    int code_off[4];   // lane offsets in this wave's four 1 KB code windows
-    int scale_off[2];  // and in its two 256-byte scale windows
+    int code_off;      // lane offset in this wave's first 1 KB code window
+    int scale_off;     // and in its first 256-byte scale window
+    int code_step;     // uniform: bytes from one code window to the next (16 rows)
+    int scale_step;    // uniform: bytes from one scale window to the next (32 rows)
 };
 
 // Buffer resources start at the tile's first row and end at the operand's
 // last row (at most 256 rows on), so rows past M or N read as zeros.  Code
-// window j of wave w holds rows 16 (4w + j) .. +15, four lanes per row.
+// window j of wave w holds rows 16 (4w + j) .. +15, four lanes per row; scale
+// window j rows 32 (2w + j) .. +31, two lanes per row.
 __device__ __forceinline__ KKOperand kk_operand(const uint8_t* codes, const uint8_t* scales,
                                                 bool two_d, int64_t MN, int64_t K, int64_t row0)
 {
@@ -585,17 +588,19 @@ __device__ __forceinline__ KKOperand kk_operand(const uint8_t* codes, const uint
     const int64_t srec = two_d ? (nrow + 15) / 16 * lds : nrow * lds;
     o.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + s0), (short)0, (int)srec,
                                                  0x00020000);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 16 * (4 * w + j) + (l >> 2), slot = l & 3;
+    // the plane swizzle depends on row bits 1-2 only, the same in all four
+    // windows, so window j adds a uniform 16 j rows
+    {
+        const int r = 64 * w + (l >> 2), slot = l & 3;
         const int plane = slot ^ ((r >> 1) & 3);
-        o.code_off[j] = (int)(r * ldc) + 16 * plane;
+        o.code_off = (int)(r * ldc) + 16 * plane;
+        o.code_step = (int)(16 * ldc);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int r = 32 * (2 * w + j) + (l >> 1);
+    {
+        const int r = 64 * w + (l >> 1);
         const int srow = two_d ? r / 16 : r;
-        o.scale_off[j] = (int)(srow * lds) + 4 * (l & 1);
+        o.scale_off = (int)(srow * lds) + 4 * (l & 1);
+        o.scale_step = (int)((two_d ? 2 : 32) * lds);
     }
     return o;
 }
@@ -608,11 +613,11 @@ __device__ __forceinline__ void kk_copy_one(__amdgpu_buffer_rsrc_t rc, __amdgpu_
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (idx < 4)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void_t*)(dst + (4 * w + idx) * 1024), 16,
-                                                 o.code_off[idx], kt * 64, 0, 0);
+                                                 o.code_off, kt * 64 + idx * o.code_step, 0, 0);
     else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void_t*)(dst + kKKCodes + (2 * w + idx - 4) * 256), 4, o.scale_off[idx - 4],
-            kt * 8, 0, 0);
+            rs, (lds_void_t*)(dst + kKKCodes + (2 * w + idx - 4) * 256), 4, o.scale_off,
+            kt * 8 + (idx - 4) * o.scale_step, 0, 0);
 }
 
 __device__ __forceinline__ void kk_copy(const KKOperand& o, int kt, uint8_t* dst)
@@ -679,30 +684,63 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
         EA[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[i], 1.0f, (h) != 0);               \
         EB[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[i], 1.0f, (h) != 0);               \
     }
+    // the same for one fragment i (reads spread over a step's sub-steps)
+#define KK_READ_I(st, CA, CB, h, i)                                                            \
+    CA[i] = *reinterpret_cast<const u32x4*>((st) + a_row + 32 * kKKRow * (i) + ((h) ? slot1 : slot0)); \
+    CB[i] = *reinterpret_cast<const u32x4*>((st) + b_row + 32 * kKKRow * (i) + ((h) ? slot1 : slot0)); \
+    sa[i] = *reinterpret_cast<const uint32_t*>((st) + a_srow + 32 * 8 * (i));                  \
+    sb[i] = *reinterpret_cast<const uint32_t*>((st) + b_srow + 32 * 8 * (i));
+#define KK_SCALES_I(EA, EB, h, i)                                                              \
+    EA[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[i], 1.0f, (h) != 0);                   \
+    EB[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[i], 1.0f, (h) != 0);
 #define KK_DEQUANT(AF, BF, CA, CB, EA, EB, q)                                                  \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
         AF[i] = dequant_word(CA[i][q], EA[i][(q) >> 1]);                                       \
         BF[i] = dequant_word(CB[i][q], EB[i][(q) >> 1]);                                       \
     }
-#define KK_MFMA(AF, BF)                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                              \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(BF[j], AF[i], acc[i][j], 0, 0, 0);
     // one MFMA then four VALU, sixteen times, with this step's copies of the
     // next-but-one tile spread over the MFMAs; each step its own region
-#define KK_INTERLEAVE_COPY(n)                                                                  \
-    _Pragma("unroll") for (int g = 0; g < 16; ++g) {                                           \
+    // One MFMA step as four sub-steps, each its own scheduling region: the
+    // four MFMAs of A row block i (one MFMA, four VALU, four times) with the
+    // dequantization of the next step's fragments A[i], B[i] in their shadow,
+    // then, when the copy plan gives this sub-step one, a copy of the
+    // next-but-one tile.  A copy thus always follows an MFMA and copies are
+    // at least four MFMAs apart.
+#define KK_SUB(AFN, BFN, CA, CB, EA, EB, q, AF, BF, i, copy, PRE)                              \
+    PRE(i)                                                                                     \
+    AFN[i] = dequant_word(CA[i][q], EA[i][(q) >> 1]);                                          \
+    BFN[i] = dequant_word(CB[i][q], EB[i][(q) >> 1]);                                          \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(BF[j], AF[i], acc[i][j], 0, 0, 0);   \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                            \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                     \
-        if (((g + 1) * (n)) / 16 != (g * (n)) / 16)                                            \
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                 \
     }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+    if ((copy) >= 0) { KK_COPY(copy); }                                                        \
     __builtin_amdgcn_sched_barrier(0);
-#define KK_COPIES(st)                                                                          \
-    _Pragma("unroll") for (int c_ = Plan::start[st]; c_ < Plan::start[(st) + 1]; ++c_) {       \
-        if (c_ < Plan::total / 2) kk_copy_one(rac, ras, oa, c_, ktf, fa);                 \
-        else kk_copy_one(rbc, rbs, ob, c_ - Plan::total / 2, ktf, fb);                    \
-    }
+#define KK_COPY(c_)                                                                            \
+    if ((c_) < Plan::total / 2) kk_copy_one(rac, ras, oa, (c_), ktf, fa);                      \
+    else kk_copy_one(rbc, rbs, ob, (c_) - Plan::total / 2, ktf, fb);
+    // copy index issued by sub-step i of step st (-1: none): n copies of the
+    // step go to sub-steps 0..n-1 when n >= 3, else to sub-steps 1 and 3
+#define KK_SLOT(st, i)                                                                         \
+    (KK_N(st) >= 3 ? ((i) < KK_N(st) ? Plan::start[st] + (i) : -1)                             \
+                   : (KK_N(st) == 2 ? ((i) == 1 ? Plan::start[st] : ((i) == 3 ? Plan::start[st] + 1 : -1)) \
+                                    : (KK_N(st) == 1 && (i) == 3 ? Plan::start[st] : -1)))
+#define KK_STEP(st, AFN, BFN, CA, CB, EA, EB, q, AF, BF, PRE)                                  \
+    KK_SUB(AFN, BFN, CA, CB, EA, EB, q, AF, BF, 0, KK_SLOT(st, 0), PRE)                        \
+    KK_SUB(AFN, BFN, CA, CB, EA, EB, q, AF, BF, 1, KK_SLOT(st, 1), PRE)                        \
+    KK_SUB(AFN, BFN, CA, CB, EA, EB, q, AF, BF, 2, KK_SLOT(st, 2), PRE)                        \
+    KK_SUB(AFN, BFN, CA, CB, EA, EB, q, AF, BF, 3, KK_SLOT(st, 3), PRE)
+    // per-sub-step extra work: nothing, the second K half of this tile (read
+    // in step 1, scales converted in step 2), the first half of the next tile
+    // (read in step 5, converted in step 6)
+#define KK_PRE_NONE(i)
+#define KK_PRE_READ_H1(i) KK_READ_I(cur, ca1, cb1, 1, i)
+#define KK_PRE_CVT_H1(i) KK_SCALES_I(ea1, eb1, 1, i)
+#define KK_PRE_READ_N0(i) KK_READ_I(nxt, ca0, cb0, 0, i)
+#define KK_PRE_CVT_N0(i) KK_SCALES_I(ea0, eb0, 0, i)
 #define KK_N(st) (Plan::start[(st) + 1] - Plan::start[st])
 
     // prologue: tiles 0 and 1 requested, tile 0 read
@@ -741,39 +779,35 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
         const __amdgpu_buffer_rsrc_t rbs = far ? ob.scales : none;
         uint8_t* fa = lds + s_far * kKKStage;
         uint8_t* fb = fa + kKKOperand;
-        KK_COPIES(0);
-        KK_DEQUANT(af1, bf1, ca0, cb0, ea0, eb0, 1); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY(KK_N(0));  // 0
-        KK_READ(cur, ca1, cb1, 1);
-        KK_COPIES(1);
-        KK_DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 2); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY(KK_N(1));  // 1
-        KK_SCALES(ea1, eb1, 1);
-        KK_COPIES(2);
-        KK_DEQUANT(af1, bf1, ca0, cb0, ea0, eb0, 3); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY(KK_N(2));  // 2
-        KK_COPIES(3);
-        KK_DEQUANT(af0, bf0, ca1, cb1, ea1, eb1, 0); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY(KK_N(3));  // 3
-        KK_COPIES(4);
-        KK_DEQUANT(af1, bf1, ca1, cb1, ea1, eb1, 1); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY(KK_N(4));  // 4
+        KK_STEP(0, af1, bf1, ca0, cb0, ea0, eb0, 1, af0, bf0, KK_PRE_NONE);                     // 0
+        KK_STEP(1, af0, bf0, ca0, cb0, ea0, eb0, 2, af1, bf1, KK_PRE_READ_H1);                  // 1
+        KK_STEP(2, af1, bf1, ca0, cb0, ea0, eb0, 3, af0, bf0, KK_PRE_CVT_H1);                   // 2
+        KK_STEP(3, af0, bf0, ca1, cb1, ea1, eb1, 0, af1, bf1, KK_PRE_NONE);                     // 3
+        KK_STEP(4, af1, bf1, ca1, cb1, ea1, eb1, 1, af0, bf0, KK_PRE_NONE);                     // 4
         // this wave's copies of tile kt + 1 have landed (tile kt + 2's from
         // steps 0-4 may still be in flight); the plain barrier carries no
         // memory fence, so those stay outstanding
         NVFP4_WAIT_VMCNT(Plan::start[5]);
         __builtin_amdgcn_s_barrier();
-        KK_READ(nxt, ca0, cb0, 0);
-        KK_COPIES(5);
-        KK_DEQUANT(af0, bf0, ca1, cb1, ea1, eb1, 2); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY(KK_N(5));  // 5
-        KK_SCALES(ea0, eb0, 0);
-        KK_COPIES(6);
-        KK_DEQUANT(af1, bf1, ca1, cb1, ea1, eb1, 3); KK_MFMA(af0, bf0); KK_INTERLEAVE_COPY(KK_N(6));  // 6
-        KK_COPIES(7);
-        KK_DEQUANT(af0, bf0, ca0, cb0, ea0, eb0, 0); KK_MFMA(af1, bf1); KK_INTERLEAVE_COPY(KK_N(7));  // 7
+        KK_STEP(5, af0, bf0, ca1, cb1, ea1, eb1, 2, af1, bf1, KK_PRE_READ_N0);                  // 5
+        KK_STEP(6, af1, bf1, ca1, cb1, ea1, eb1, 3, af0, bf0, KK_PRE_CVT_N0);                   // 6
+        KK_STEP(7, af0, bf0, ca0, cb0, ea0, eb0, 0, af1, bf1, KK_PRE_NONE);                     // 7
         s_cur = s_nxt;
     }
 #undef KK_READ
 #undef KK_SCALES
 #undef KK_DEQUANT
-#undef KK_MFMA
-#undef KK_INTERLEAVE_COPY
-#undef KK_COPIES
+#undef KK_SUB
+#undef KK_COPY
+#undef KK_SLOT
+#undef KK_STEP
+#undef KK_PRE_NONE
+#undef KK_PRE_READ_H1
+#undef KK_PRE_CVT_H1
+#undef KK_PRE_READ_N0
+#undef KK_PRE_CVT_N0
+#undef KK_READ_I
+#undef KK_SCALES_I
 #undef KK_N
     if (m0 + kTM <= p.M && n0 + kTN <= p.N)
         store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk);
