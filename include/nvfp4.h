@@ -139,6 +139,31 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, in
                             size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace nvfp4_amax needs (per-workgroup partial maxima of
+ * both results; no initialisation needed, reusable on the same stream).
+ */
+size_t nvfp4_amax_workspace_size(int64_t rows, int64_t cols);
+
+/*
+ * Tensor amaxes for the first step of the two-level scaling (s_g = amax /
+ * 2688; guiahardware.es "Cos'e NVFP4", chaitex.ru "FP4" item 2) of a tensor
+ * the recipe quantizes twice (readjensen.com recipe paragraph: row-wise for
+ * fprop/dgrad, column-wise with the RHT for wgrad), in one read of x:
+ *   amax      device float <- max |x|
+ *   amax_rht  NULL, or a device float <- max |y| over y = the 16-point RHT
+ *             down the columns of x (16 consecutive rows, sign mask
+ *             rht_sign_mask, exactly as nvfp4_quantize with axis 0, rht = 1)
+ * Both are exact maxima (order-independent), so passing them as amax_in to
+ * nvfp4_quantize gives the same bits as letting it compute its own.
+ * Shape rules: rows, cols >= 0; cols % 16 == 0; rows % 16 == 0 when amax_rht
+ * is not NULL; ld_x >= cols; x and its rows 16-byte aligned.  An empty
+ * tensor writes 0.  Workspace: nvfp4_amax_workspace_size bytes.
+ */
+nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                        int64_t ld_x, uint32_t rht_sign_mask, float* amax, float* amax_rht,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Standalone 16-point random Hadamard transform (the wgrad-input transform
  * of the recipe paragraph, readjensen.com; "Hadamard transforms" in
  * "Mastering Low-Precision AI", third paragraph).

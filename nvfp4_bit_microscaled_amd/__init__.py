@@ -33,7 +33,8 @@ ROUND_RNE, ROUND_SR = 0, 1
 LAYOUT = {"NT": 0, "NN": 1, "TN": 2}
 
 EXPORTS = ("nvfp4_version", "nvfp4_status_string", "nvfp4_quantize_workspace_size",
-           "nvfp4_quantize", "nvfp4_rht16", "nvfp4_dequantize", "nvfp4_gemm")
+           "nvfp4_quantize", "nvfp4_amax_workspace_size", "nvfp4_amax", "nvfp4_rht16",
+           "nvfp4_dequantize", "nvfp4_gemm")
 
 
 class NVFP4Error(RuntimeError):
@@ -57,6 +58,10 @@ def _load():
     L.nvfp4_quantize.restype = ci
     L.nvfp4_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, ci, u64, u32, ci, u32, vp, vp,
                                  vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.nvfp4_amax_workspace_size.restype = ctypes.c_size_t
+    L.nvfp4_amax_workspace_size.argtypes = [i64, i64]
+    L.nvfp4_amax.restype = ci
+    L.nvfp4_amax.argtypes = [vp, ci, i64, i64, i64, u32, vp, vp, vp, ctypes.c_size_t, vp]
     L.nvfp4_rht16.restype = ci
     L.nvfp4_rht16.argtypes = [vp, ci, i64, i64, i64, ci, u32, vp, i64, vp]
     L.nvfp4_dequantize.restype = ci
@@ -107,6 +112,16 @@ def nvfp4_quantize(x, x_dtype, rows, cols, ld_x, block, axis, transpose_out, rou
                               rounding, seed, stream_id, rht, rht_sign_mask, _p(amax_in), _p(amax_out),
                               _p(codes), _p(scales), _p(tensor_scale), _p(workspace),
                               workspace_bytes, _stream(stream))
+
+
+def nvfp4_amax_workspace_size(rows: int, cols: int) -> int:
+    return lib.nvfp4_amax_workspace_size(rows, cols)
+
+
+def nvfp4_amax(x, x_dtype, rows, cols, ld_x, rht_sign_mask, amax, amax_rht, workspace,
+               workspace_bytes, stream=None) -> int:
+    return lib.nvfp4_amax(_p(x), x_dtype, rows, cols, ld_x, rht_sign_mask, _p(amax),
+                          _p(amax_rht), _p(workspace), workspace_bytes, _stream(stream))
 
 
 def nvfp4_rht16(x, x_dtype, rows, cols, ld_x, axis, sign_mask, y, ld_y, stream=None) -> int:
@@ -160,7 +175,7 @@ _workspaces = {}
 
 
 def _workspace(device, rows, cols):
-    n = nvfp4_quantize_workspace_size(rows, cols)
+    n = max(nvfp4_quantize_workspace_size(rows, cols), nvfp4_amax_workspace_size(rows, cols))
     key = (str(device), torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < n:
@@ -200,6 +215,19 @@ def quantize(x: torch.Tensor, block2d: bool = False, axis: int = 1, sr: bool = F
                         out.tensor_scale, ws, 0 if ws is None else ws.numel())
     _check("nvfp4_quantize", st)
     return out
+
+
+def amax(x: torch.Tensor, rht_mask: int | None = None):
+    """max |x| and, when rht_mask is given, max |RHT16 down the columns of x|,
+    in one read; returns (amax, amax_rht or None) as float32 [1] tensors."""
+    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1
+    rows, cols = x.shape
+    a = torch.empty(1, dtype=torch.float32, device=x.device)
+    ar = None if rht_mask is None else torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = _workspace(x.device, rows, cols)
+    _check("nvfp4_amax", nvfp4_amax(x, _dtype_code(x), rows, cols, x.stride(0),
+                                    0 if rht_mask is None else rht_mask, a, ar, ws, ws.numel()))
+    return a, ar
 
 
 def rht16(x: torch.Tensor, axis: int, mask: int) -> torch.Tensor:

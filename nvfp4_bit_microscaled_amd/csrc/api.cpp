@@ -131,6 +131,47 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, in
     return from_hip(launch_quantize(a, amax_src, amax_in != nullptr, s));
 }
 
+size_t nvfp4_amax_workspace_size(int64_t rows, int64_t cols)
+{
+    (void)rows;
+    (void)cols;
+    return 2 * kMaxAmaxPartials * sizeof(float);
+}
+
+nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                        int64_t ld_x, uint32_t rht_sign_mask, float* amax, float* amax_rht,
+                        void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0 || !amax) return NVFP4_ERR_INVALID_ARG;
+    if (cols % 16) return NVFP4_ERR_SHAPE;
+    if (amax_rht && rows % 16) return NVFP4_ERR_SHAPE;
+    if (ld_x < cols) return NVFP4_ERR_SHAPE;
+    if ((uint64_t)rows * (uint64_t)(cols / 8) > kMaxItems) return NVFP4_ERR_UNSUPPORTED;
+    size_t esz = x_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // an empty tensor: both maxima are 0 (the zero-scale writer stores 0 to
+    // its two outputs)
+    if (rows == 0 || cols == 0) return from_hip(launch_write_zero_scale(amax, amax_rht, s));
+    if (!x) return NVFP4_ERR_INVALID_ARG;
+    if (!aligned16(x) || ((size_t)ld_x * esz) % 16) return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < nvfp4_amax_workspace_size(rows, cols))
+        return NVFP4_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return NVFP4_ERR_ALIGN;
+    QuantArgs a{};
+    a.x = x;
+    a.bf16 = x_dtype == NVFP4_DTYPE_BF16;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld_x;
+    a.axis = 0;
+    a.rht = amax_rht != nullptr;
+    a.mask = rht_sign_mask & 0xFFFFu;
+    float* ws = static_cast<float*>(workspace);
+    if (!amax_rht) return from_hip(launch_amax(a, ws, amax, s));
+    return from_hip(launch_amax_dual(a, ws, amax, amax_rht, s));
+}
+
 nvfp4_status nvfp4_rht16(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
                          int64_t ld_x, int axis, uint32_t sign_mask, float* y, int64_t ld_y,
                          void* stream)

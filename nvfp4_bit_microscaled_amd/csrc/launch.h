@@ -33,6 +33,11 @@ constexpr int kMaxAmaxPartials = 2048;
 // then reduce them into *amax_dst (and *amax_out when non-null).
 hipError_t launch_amax(const QuantArgs& a, float* partials, float* amax_dst, hipStream_t s);
 
+// max |x| and max |RHT16 down the columns of x| in one pass (rows % 16 == 0):
+// partials[] needs 2 * kMaxAmaxPartials floats.
+hipError_t launch_amax_dual(const QuantArgs& a, float* partials, float* amax_dst,
+                            float* amax_rht_dst, hipStream_t s);
+
 // Pass 2: quantize using the amax at *amax_src; writes codes, scales,
 // tensor_scale (and amax_out when amax_src is the caller's amax_in).
 hipError_t launch_quantize(const QuantArgs& a, const float* amax_src, bool write_amax_out,

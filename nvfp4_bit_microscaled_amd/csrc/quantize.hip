@@ -301,6 +301,57 @@ __global__ __launch_bounds__(256) void k_quant_cols(QuantParams p)
     if (kAmaxOnly) block_reduce_max_store(amax_local, p.partials + blockIdx.x);
 }
 
+// ------------------------------------------------------------ both amaxes
+
+// The two tensor amaxes a tensor that feeds both a row-wise quantization and
+// the column-wise RHT quantization of wgrad needs, in one read: max |x| and
+// max |RHT16 down the columns of x| (rows % 16 == 0).  Thread mapping as in
+// the column kernel (16 rows x 4 columns); per-workgroup partial maxima go to
+// partials[0 .. grid) and partials[kMaxAmaxPartials .. + grid).
+template <bool kBF16>
+__global__ __launch_bounds__(256) void k_amax_dual(QuantParams p)
+{
+    constexpr int esz = kBF16 ? 2 : 4;
+    float m_plain = 0.0f, m_rht = 0.0f;
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < p.items; t += stride) {
+        uint32_t rb = fdiv(t, p.div);
+        uint32_t cg = t - rb * p.div.d;
+        int64_t r0 = (int64_t)rb * 16, c0 = (int64_t)cg * 4;
+        float v[4][16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float w[4];
+            load4<kBF16>(p.x + ((r0 + i) * p.ld + c0) * esz, w);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[j][i] = w[j];
+                m_plain = __builtin_fmaxf(m_plain, __builtin_fabsf(w[j]));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            rht16_inplace(v[j], p.mask);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m_rht = __builtin_fmaxf(m_rht, __builtin_fabsf(v[j][i]));
+        }
+    }
+    block_reduce_max_store(m_plain, p.partials + blockIdx.x);
+    __syncthreads();  // the reduction's shared slots are reused
+    block_reduce_max_store(m_rht, p.partials + kMaxAmaxPartials + blockIdx.x);
+}
+
+// fp4_pack2 into byte `sel` of `old` (sel is a constant once loops unroll)
+__device__ __forceinline__ uint32_t fp4_pack2_at(uint32_t old, float a, float b, int sel)
+{
+    switch (sel) {
+    case 0: return fp4_pack2<0>(old, a, b);
+    case 1: return fp4_pack2<1>(old, a, b);
+    case 2: return fp4_pack2<2>(old, a, b);
+    default: return fp4_pack2<3>(old, a, b);
+    }
+}
+
 // ------------------------------------------------------------ transposed output
 
 // Blocks down the columns (1x16 along rows, or 16x16), written as the
@@ -316,17 +367,6 @@ __global__ __launch_bounds__(256) void k_quant_cols(QuantParams p)
 // row block) go to LDS as [column][row block], then leave as 128-byte rows
 // of the transposed tensor.  The row-block slot is XOR-swizzled with the
 // column group so the 64 lanes of a wave write 64 different banks pairs.
-// fp4_pack2 into byte `sel` of `old` (sel is a constant once loops unroll)
-__device__ __forceinline__ uint32_t fp4_pack2_at(uint32_t old, float a, float b, int sel)
-{
-    switch (sel) {
-    case 0: return fp4_pack2<0>(old, a, b);
-    case 1: return fp4_pack2<1>(old, a, b);
-    case 2: return fp4_pack2<2>(old, a, b);
-    default: return fp4_pack2<3>(old, a, b);
-    }
-}
-
 constexpr int kTT = 256;                  // tile rows and columns
 constexpr int kTCodeRow = kTT / 2;        // LDS bytes per transposed row (16 slots x 8)
 constexpr int kTCodeBytes = kTT * kTCodeRow;
@@ -775,6 +815,24 @@ hipError_t launch_amax(const QuantArgs& a, float* partials, float* amax_dst, hip
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(256), 0, s, partials, grid, amax_dst,
                        a.amax_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax_dual(const QuantArgs& a, float* partials, float* amax_dst,
+                            float* amax_rht_dst, hipStream_t s)
+{
+    QuantParams p = make_params(a);
+    p.partials = partials;
+    set_items(a, kCols, p);
+    int grid = grid_for(p.items, kMaxAmaxPartials);
+    NVFP4_DISPATCH_BOOL(a.bf16, BF,
+        hipLaunchKernelGGL((k_amax_dual<BF>), dim3(grid), dim3(256), 0, s, p));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(256), 0, s, partials, grid, amax_dst,
+                       (float*)nullptr);
+    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(256), 0, s, partials + kMaxAmaxPartials,
+                       grid, amax_rht_dst, (float*)nullptr);
     return hipGetLastError();
 }
 

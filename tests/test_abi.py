@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["nvfp4_version", "nvfp4_status_string",
-                            "nvfp4_quantize_workspace_size", "nvfp4_quantize", "nvfp4_rht16",
+                            "nvfp4_quantize_workspace_size", "nvfp4_quantize",
+                            "nvfp4_amax_workspace_size", "nvfp4_amax", "nvfp4_rht16",
                             "nvfp4_dequantize", "nvfp4_gemm"])
 
 
@@ -84,6 +85,27 @@ def test_quantize_validation(lib):
     assert q(lib, amax_in=None, ws=None) == 6       # amax pass needs the workspace
     assert q(lib, amax_in=None, ws=FAKE, wsb=8) == 6
     assert q(lib, x=None) == 1
+
+
+def a(lib, **kw):
+    args = dict(x=FAKE, dt=0, rows=32, cols=64, ld=64, mask=0, amax=FAKE, amax_rht=FAKE, ws=FAKE,
+                wsb=1 << 20, stream=None)
+    args.update(kw)
+    return lib.nvfp4_amax(*args.values())
+
+
+def test_amax_validation(lib):
+    assert a(lib, dt=5) == 1
+    assert a(lib, amax=None) == 1
+    assert a(lib, rows=-1) == 1
+    assert a(lib, cols=40, ld=40) == 2              # cols % 16
+    assert a(lib, rows=24) == 2                     # rows % 16 with the RHT amax
+    assert a(lib, ld=32) == 2
+    assert a(lib, x=MISALIGNED) == 3
+    assert a(lib, ws=None) == 6
+    assert a(lib, wsb=8) == 6
+    assert a(lib, x=None) == 1
+    assert lib.nvfp4_amax_workspace_size(1 << 15, 1 << 12) >= 8
 
 
 def g(lib, **kw):
