@@ -6,7 +6,7 @@ benchmark paragraph), with the recipe of that page's recipe paragraph:
 
   fprop   quantize X (1x16 RNE), W_gu and W_down (16x16 RNE)
           H = X W_gu^T                     32768 x 28672 x 4096
-          Act = silu(gate) * up  (torch, BF16 glue)
+          Act = silu(gate) * up  (BF16), fused with both amaxes of Act
           quantize Act (1x16 RNE)
           Y = Act W_down^T                 32768 x 4096 x 14336
   bwd     dY, dH synthetic (Student-t(3) x 1e-3)
@@ -133,6 +133,7 @@ def main():
     timer = Timer(torch)
     gemm_flops = {}   # (name) -> flops per call
     qbytes = {}       # (name) -> algorithmic HBM bytes per call
+    swbytes = {}      # the fused SwiGLU + amax pass
 
     def qb(rows, cols, in_bytes=2, amax_pass=True):
         # read input (twice when the amax pass runs) + codes + scales
@@ -146,6 +147,11 @@ def main():
         # max |x| and max |RHT16 down the columns of x| in one read
         qbytes[name] = x.shape[0] * x.shape[1] * 2
         return timer.run("quantize", nv.amax, x, rht_mask=mask)
+
+    def SWIGLU(name, h):
+        # act = silu(gate) * up with both amaxes of act: reads H, writes act
+        swbytes[name] = h.shape[0] * h.shape[1] * 2 + h.shape[0] * (h.shape[1] // 2) * 2
+        return timer.run("swiglu", nv.swiglu_amax, h, mask, out=buf("Act", (h.shape[0], h.shape[1] // 2)))
 
     def G(name, role, a, b, M, N, K, out=None):
         gemm_flops[name] = 2.0 * M * N * K
@@ -167,8 +173,7 @@ def main():
         wgu = Q("Wgu_2d", W_gu, block2d=True)
         wdn = Q("Wdown_2d", W_down, block2d=True)
         H = G("fprop_gu", "fprop", xq, wgu, T, 2 * Fh, D, out=buf("H", (T, 2 * Fh)))
-        act = timer.run("swiglu", lambda: F.silu(H[:, :Fh]) * H[:, Fh:])
-        aa, aat = AMX("Act_amax2", act)
+        act, aa, aat = SWIGLU("Act_swiglu_amax2", H)
         aq = Q("Act_rows", act, amax_in=aa)
         G("fprop_down", "fprop", aq, wdn, T, D, Fh, out=buf("Y", (T, D)))
         # ---- backward, down projection
@@ -259,6 +264,7 @@ def main():
                          for k, v in gemm_roles.items()},
         "quantize_GBps": round(q_bytes / (q_t * 1e-3) / 1e9, 1),
         "quantize_frac_of_hbm": round(q_bytes / (q_t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "swiglu_GBps": round(sum(swbytes.values()) * args.steps / (totals["swiglu"][0] * 1e-3) / 1e9, 1),
         "time_breakdown_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in per_kind.items()},
         "roofline": {"bound": "mfma", "kernel": "k_gemm_kk (K-major x K-major, all six MLP GEMMs)",
                      "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,

@@ -164,6 +164,29 @@ nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The activation between the two fprop GEMMs of the MLP, fused with both
+ * tensor amaxes its quantizations need (the MLP GEMMs on NVFP4 inputs with
+ * BF16 outputs: readjensen.com recipe paragraph; the Llama 3 models of its
+ * benchmark paragraph use SwiGLU):
+ *   h         BF16 [rows, 2F], row r at h + r*ld_h elements: gate = columns
+ *             [0, F), up = columns [F, 2F) (the first GEMM's output)
+ *   act       BF16 [rows, F] <- BF16(BF16(silu(gate)) * up), silu(g) =
+ *             g / (1 + exp(-g)) in FP32 (a BF16 framework's rounding points;
+ *             the reciprocal from the hardware unit, within a couple of FP32
+ *             ulp, so act may differ from another library's by one BF16 ulp
+ *             where silu sits on a BF16 rounding boundary)
+ *   amax      device float <- max |act|
+ *   amax_rht  device float <- max |RHT16 down the columns of act| (as
+ *             nvfp4_amax), the amax of act's wgrad quantization
+ * Shape rules: rows % 16 == 0; F % 16 == 0; ld_h >= 2F; ld_act >= F; h, act
+ * and their rows 16-byte aligned.  Workspace: nvfp4_amax_workspace_size.
+ */
+nvfp4_status nvfp4_swiglu_amax(const void* h, int64_t rows, int64_t F, int64_t ld_h, void* act,
+                               int64_t ld_act, uint32_t rht_sign_mask, float* amax,
+                               float* amax_rht, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * Standalone 16-point random Hadamard transform (the wgrad-input transform
  * of the recipe paragraph, readjensen.com; "Hadamard transforms" in
  * "Mastering Low-Precision AI", third paragraph).

@@ -33,7 +33,8 @@ ROUND_RNE, ROUND_SR = 0, 1
 LAYOUT = {"NT": 0, "NN": 1, "TN": 2}
 
 EXPORTS = ("nvfp4_version", "nvfp4_status_string", "nvfp4_quantize_workspace_size",
-           "nvfp4_quantize", "nvfp4_amax_workspace_size", "nvfp4_amax", "nvfp4_rht16",
+           "nvfp4_quantize", "nvfp4_amax_workspace_size", "nvfp4_amax",
+           "nvfp4_swiglu_amax", "nvfp4_rht16",
            "nvfp4_dequantize", "nvfp4_gemm")
 
 
@@ -62,6 +63,9 @@ def _load():
     L.nvfp4_amax_workspace_size.argtypes = [i64, i64]
     L.nvfp4_amax.restype = ci
     L.nvfp4_amax.argtypes = [vp, ci, i64, i64, i64, u32, vp, vp, vp, ctypes.c_size_t, vp]
+    L.nvfp4_swiglu_amax.restype = ci
+    L.nvfp4_swiglu_amax.argtypes = [vp, i64, i64, i64, vp, i64, u32, vp, vp, vp, ctypes.c_size_t,
+                                    vp]
     L.nvfp4_rht16.restype = ci
     L.nvfp4_rht16.argtypes = [vp, ci, i64, i64, i64, ci, u32, vp, i64, vp]
     L.nvfp4_dequantize.restype = ci
@@ -122,6 +126,12 @@ def nvfp4_amax(x, x_dtype, rows, cols, ld_x, rht_sign_mask, amax, amax_rht, work
                workspace_bytes, stream=None) -> int:
     return lib.nvfp4_amax(_p(x), x_dtype, rows, cols, ld_x, rht_sign_mask, _p(amax),
                           _p(amax_rht), _p(workspace), workspace_bytes, _stream(stream))
+
+
+def nvfp4_swiglu_amax(h, rows, F, ld_h, act, ld_act, rht_sign_mask, amax, amax_rht, workspace,
+                      workspace_bytes, stream=None) -> int:
+    return lib.nvfp4_swiglu_amax(_p(h), rows, F, ld_h, _p(act), ld_act, rht_sign_mask, _p(amax),
+                                 _p(amax_rht), _p(workspace), workspace_bytes, _stream(stream))
 
 
 def nvfp4_rht16(x, x_dtype, rows, cols, ld_x, axis, sign_mask, y, ld_y, stream=None) -> int:
@@ -228,6 +238,22 @@ def amax(x: torch.Tensor, rht_mask: int | None = None):
     _check("nvfp4_amax", nvfp4_amax(x, _dtype_code(x), rows, cols, x.stride(0),
                                     0 if rht_mask is None else rht_mask, a, ar, ws, ws.numel()))
     return a, ar
+
+
+def swiglu_amax(h: torch.Tensor, rht_mask: int, out: torch.Tensor | None = None):
+    """act = silu(gate) * up over h = [gate | up] (BF16 [rows, 2F]), with
+    max |act| and max |RHT16 down the columns of act|; returns (act, amax,
+    amax_rht)."""
+    assert h.dim() == 2 and h.is_cuda and h.stride(1) == 1 and h.dtype == torch.bfloat16
+    rows, F = h.shape[0], h.shape[1] // 2
+    if out is None:
+        out = torch.empty(rows, F, dtype=torch.bfloat16, device=h.device)
+    a = torch.empty(1, dtype=torch.float32, device=h.device)
+    ar = torch.empty(1, dtype=torch.float32, device=h.device)
+    ws = _workspace(h.device, rows, F)
+    _check("nvfp4_swiglu_amax", nvfp4_swiglu_amax(h, rows, F, h.stride(0), out, out.stride(0),
+                                                  rht_mask, a, ar, ws, ws.numel()))
+    return out, a, ar
 
 
 def rht16(x: torch.Tensor, axis: int, mask: int) -> torch.Tensor:

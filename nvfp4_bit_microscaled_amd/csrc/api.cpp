@@ -172,6 +172,27 @@ nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_
     return from_hip(launch_amax_dual(a, ws, amax, amax_rht, s));
 }
 
+nvfp4_status nvfp4_swiglu_amax(const void* h, int64_t rows, int64_t F, int64_t ld_h, void* act,
+                               int64_t ld_act, uint32_t rht_sign_mask, float* amax,
+                               float* amax_rht, void* workspace, size_t workspace_bytes,
+                               void* stream)
+{
+    if (rows < 0 || F < 0 || !amax || !amax_rht) return NVFP4_ERR_INVALID_ARG;
+    if (rows % 16 || F % 16) return NVFP4_ERR_SHAPE;
+    if (ld_h < 2 * F || ld_act < F) return NVFP4_ERR_SHAPE;
+    if ((uint64_t)rows * (uint64_t)(F / 4) > kMaxItems) return NVFP4_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (rows == 0 || F == 0) return from_hip(launch_write_zero_scale(amax, amax_rht, s));
+    if (!h || !act) return NVFP4_ERR_INVALID_ARG;
+    if (!aligned16(h) || ((size_t)ld_h * 2) % 16) return NVFP4_ERR_ALIGN;
+    if (!aligned16(act) || ((size_t)ld_act * 2) % 16) return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < nvfp4_amax_workspace_size(rows, F))
+        return NVFP4_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return NVFP4_ERR_ALIGN;
+    return from_hip(launch_swiglu_amax(h, rows, F, ld_h, act, ld_act, rht_sign_mask,
+                                       static_cast<float*>(workspace), amax, amax_rht, s));
+}
+
 nvfp4_status nvfp4_rht16(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
                          int64_t ld_x, int axis, uint32_t sign_mask, float* y, int64_t ld_y,
                          void* stream)

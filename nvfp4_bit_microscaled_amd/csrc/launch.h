@@ -38,6 +38,13 @@ hipError_t launch_amax(const QuantArgs& a, float* partials, float* amax_dst, hip
 hipError_t launch_amax_dual(const QuantArgs& a, float* partials, float* amax_dst,
                             float* amax_rht_dst, hipStream_t s);
 
+// act = BF16(BF16(silu(gate)) * up) over h = [gate | up] (BF16 [rows, 2F]),
+// plus max |act| and max |RHT16 down the columns of act| (rows % 16 == 0,
+// F % 16 == 0); partials[] needs 2 * kMaxAmaxPartials floats.
+hipError_t launch_swiglu_amax(const void* h, int64_t rows, int64_t F, int64_t ld_h, void* act,
+                              int64_t ld_a, uint32_t mask, float* partials, float* amax,
+                              float* amax_rht, hipStream_t s);
+
 // Pass 2: quantize using the amax at *amax_src; writes codes, scales,
 // tensor_scale (and amax_out when amax_src is the caller's amax_in).
 hipError_t launch_quantize(const QuantArgs& a, const float* amax_src, bool write_amax_out,

@@ -341,6 +341,72 @@ __global__ __launch_bounds__(256) void k_amax_dual(QuantParams p)
     block_reduce_max_store(m_rht, p.partials + kMaxAmaxPartials + blockIdx.x);
 }
 
+// ------------------------------------------------------------ SwiGLU + amaxes
+
+// RNE FP32 -> BF16 bits (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The producer of the MLP's second GEMM input, fused with both of its tensor
+// amaxes: act = BF16(BF16(silu(gate)) * up) with silu(g) = g / (1 + exp(-g))
+// in FP32 (the reciprocal from the hardware unit; the BF16 rounding points of
+// a BF16 framework's silu and multiply),
+// written as BF16 [rows, F], plus max |act| and max |RHT16 down the columns of
+// act| (rows % 16 == 0).  gate = h[:, 0:F], up = h[:, F:2F].  Mapping as the
+// column kernel: thread = 16 rows x 4 columns of act.
+__global__ __launch_bounds__(256) void k_swiglu_amax(const uint8_t* h, int64_t ld_h,
+                                                     uint8_t* act, int64_t ld_a, int64_t F,
+                                                     uint32_t items, FastDiv div, uint32_t mask,
+                                                     float* partials)
+{
+    float m_plain = 0.0f, m_rht = 0.0f;
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < items; t += stride) {
+        uint32_t rb = fdiv(t, div);
+        uint32_t cg = t - rb * div.d;
+        int64_t r0 = (int64_t)rb * 16, c0 = (int64_t)cg * 4;
+        float v[4][16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float g[4], u[4];
+            load4<true>(h + ((r0 + i) * ld_h + c0) * 2, g);
+            load4<true>(h + ((r0 + i) * ld_h + F + c0) * 2, u);
+            uint32_t b[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // the reciprocal unit (1 ulp) instead of a correctly rounded
+                // division: the result only feeds a BF16 rounding.  Its
+                // output flushes below 2^-126, so denominators from 2^126 up
+                // (g < -87.3) take the IEEE division.
+                const float den = 1.0f + expf(-g[j]);
+                float sg = g[j] * __builtin_amdgcn_rcpf(den);
+                if (den >= 8.5070592e37f) sg = g[j] / den;  // 2^126
+                float sb = __uint_as_float(f32_to_bf16_bits(sg) << 16);
+                b[j] = f32_to_bf16_bits(sb * u[j]);
+                float a = __uint_as_float(b[j] << 16);
+                v[j][i] = a;
+                m_plain = __builtin_fmaxf(m_plain, __builtin_fabsf(a));
+            }
+            u32x2 w;
+            w[0] = b[0] | (b[1] << 16);
+            w[1] = b[2] | (b[3] << 16);
+            *reinterpret_cast<u32x2*>(act + ((r0 + i) * ld_a + c0) * 2) = w;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            rht16_inplace(v[j], mask);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m_rht = __builtin_fmaxf(m_rht, __builtin_fabsf(v[j][i]));
+        }
+    }
+    block_reduce_max_store(m_plain, partials + blockIdx.x);
+    __syncthreads();  // the reduction's shared slots are reused
+    block_reduce_max_store(m_rht, partials + kMaxAmaxPartials + blockIdx.x);
+}
+
 // fp4_pack2 into byte `sel` of `old` (sel is a constant once loops unroll)
 __device__ __forceinline__ uint32_t fp4_pack2_at(uint32_t old, float a, float b, int sel)
 {
@@ -833,6 +899,25 @@ hipError_t launch_amax_dual(const QuantArgs& a, float* partials, float* amax_dst
                        (float*)nullptr);
     hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(256), 0, s, partials + kMaxAmaxPartials,
                        grid, amax_rht_dst, (float*)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_amax(const void* h, int64_t rows, int64_t F, int64_t ld_h, void* act,
+                              int64_t ld_a, uint32_t mask, float* partials, float* amax,
+                              float* amax_rht, hipStream_t s)
+{
+    const uint32_t items = (uint32_t)((rows / 16) * (F / 4));
+    const FastDiv div = make_fastdiv((uint32_t)(F / 4));
+    int grid = grid_for(items, kMaxAmaxPartials);
+    hipLaunchKernelGGL(k_swiglu_amax, dim3(grid), dim3(256), 0, s, static_cast<const uint8_t*>(h),
+                       ld_h, static_cast<uint8_t*>(act), ld_a, F, items, div, mask & 0xFFFFu,
+                       partials);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(256), 0, s, partials, grid, amax,
+                       (float*)nullptr);
+    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(256), 0, s, partials + kMaxAmaxPartials,
+                       grid, amax_rht, (float*)nullptr);
     return hipGetLastError();
 }
 

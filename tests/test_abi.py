@@ -30,7 +30,8 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["nvfp4_version", "nvfp4_status_string",
                             "nvfp4_quantize_workspace_size", "nvfp4_quantize",
-                            "nvfp4_amax_workspace_size", "nvfp4_amax", "nvfp4_rht16",
+                            "nvfp4_amax_workspace_size", "nvfp4_amax", "nvfp4_swiglu_amax",
+                            "nvfp4_rht16",
                             "nvfp4_dequantize", "nvfp4_gemm"])
 
 
@@ -106,6 +107,27 @@ def test_amax_validation(lib):
     assert a(lib, wsb=8) == 6
     assert a(lib, x=None) == 1
     assert lib.nvfp4_amax_workspace_size(1 << 15, 1 << 12) >= 8
+
+
+def sw(lib, **kw):
+    args = dict(h=FAKE, rows=32, F=64, ldh=128, act=FAKE, lda=64, mask=0, amax=FAKE,
+                amax_rht=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    args.update(kw)
+    return lib.nvfp4_swiglu_amax(*args.values())
+
+
+def test_swiglu_amax_validation(lib):
+    assert sw(lib, amax=None) == 1
+    assert sw(lib, amax_rht=None) == 1
+    assert sw(lib, rows=-16) == 1
+    assert sw(lib, rows=24) == 2                    # rows % 16
+    assert sw(lib, F=40, ldh=80, lda=40) == 2       # F % 16
+    assert sw(lib, ldh=100) == 2                    # ld_h < 2F
+    assert sw(lib, lda=32) == 2                     # ld_act < F
+    assert sw(lib, h=MISALIGNED) == 3
+    assert sw(lib, ldh=132) == 3                    # 264-byte rows are not 16-byte multiples
+    assert sw(lib, ws=None) == 6
+    assert sw(lib, h=None) == 1
 
 
 def g(lib, **kw):

@@ -1,0 +1,102 @@
+"""GPU parity: nvfp4_swiglu_amax, the MLP activation between the two fprop
+GEMMs fused with both tensor amaxes of its output.
+
+act is compared with a plain PyTorch FP32 reference taking the same rounding
+points (silu in FP32 rounded to BF16, product rounded to BF16).  The kernel's
+FP32 silu may differ from the reference's by an ulp or two (exponential and
+reciprocal implementations), which can move silu's BF16 rounding by one step:
+act must equal the rounded product of up with the reference silu's BF16 value
+or one of its two BF16 neighbours, and equal the first in all but a tiny
+fraction of elements.  The two amaxes must equal the
+oracle's on the act the kernel produced, bit for bit.  Source: the MLP GEMMs
+with BF16 outputs (readjensen.com recipe paragraph); Llama 3's SwiGLU MLP
+(benchmark paragraph models).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import to_oracle_input
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_bit_microscaled_amd as m
+    torch.cuda.set_device(0)
+    return m
+
+
+def bf16_neighbours(x):
+    """The BF16 values one step below and above each (finite, BF16) x."""
+    b = x.to(torch.bfloat16).view(torch.int16).to(torch.int32)
+    mag = b & 0x7FFF
+    neg = (b & 0x8000) != 0
+    up_mag, dn_mag = mag + 1, mag - 1
+    # stepping through zero flips the sign
+    above = torch.where(neg, torch.where(mag == 0, 1, -dn_mag), up_mag)
+    below = torch.where(neg, -up_mag, torch.where(mag == 0, -1, dn_mag))
+
+    def to_f(v):
+        bits = torch.where(v < 0, (-v) | 0x8000, v).to(torch.int16)
+        return bits.view(torch.bfloat16).float()
+    return to_f(below), to_f(above)
+
+
+def candidates(h):
+    """act from the reference silu rounded to BF16, and from its two BF16
+    neighbours (a one-ulp difference in the FP32 silu can move its BF16
+    rounding by one step, which the product with up carries to act)."""
+    F = h.shape[1] // 2
+    g, u = h[:, :F].float(), h[:, F:].float()
+    sg = (g / (1.0 + torch.exp(-g))).to(torch.bfloat16).float()
+    lo, hi = bf16_neighbours(sg)
+    return [(v * u).to(torch.bfloat16) for v in (sg, lo, hi)]
+
+
+def make_h(rows, F, seed):
+    h = 3.0 * workloads.activations(rows, 2 * F, seed=seed).float()
+    h[0, :4] = torch.tensor([-100.0, 100.0, -1000.0, 88.0])   # exp overflow / underflow
+    return h.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("rows,F", [(16, 16), (48, 272), (256, 1040), (528, 64)])
+@pytest.mark.parametrize("pad", [0, 16])
+def test_swiglu_and_amaxes(nv, rows, F, pad):
+    h = make_h(rows, F, seed=rows + F)
+    mask = workloads.sign_mask(F)
+    if pad:
+        hw = torch.zeros(rows, 2 * F + pad, dtype=torch.bfloat16)
+        hw[:, :2 * F] = h
+        hg = hw.cuda()[:, :2 * F]
+        out = torch.zeros(rows, F + pad, dtype=torch.bfloat16, device="cuda")[:, :F]
+    else:
+        hg, out = h.cuda(), None
+    act, a, ar = nv.swiglu_amax(hg, mask, out=out)
+    torch.cuda.synchronize()
+    got = act.cpu().view(torch.int16)
+    ref, lo, hi = (c.view(torch.int16) for c in candidates(h))
+    same = got == ref
+    ok = same | (got == lo) | (got == hi)
+    assert bool(ok.all()), "%d outputs match no BF16 silu candidate" % int((~ok).sum())
+    assert float((~same).float().mean()) < 1e-3
+    xo = to_oracle_input(act.cpu())
+    assert a.item() == oracle.amax(xo)
+    assert ar.item() == oracle.amax(xo, rht=True, axis=0, mask=mask)
+
+
+def test_feeds_the_same_quantizations(nv):
+    """Quantizing act with the fused amaxes as amax_in equals quantizing it
+    with self-computed ones (row-wise RNE and transposed column RHT)."""
+    h = make_h(256, 528, seed=3).cuda()
+    mask = workloads.sign_mask(9)
+    act, a, ar = nv.swiglu_amax(h, mask)
+    q1, q2 = nv.quantize(act), nv.quantize(act, amax_in=a)
+    kw = dict(axis=0, rht=True, mask=mask, transpose=True)
+    t1, t2 = nv.quantize(act, **kw), nv.quantize(act, amax_in=ar, **kw)
+    torch.cuda.synchronize()
+    for u, v in ((q1, q2), (t1, t2)):
+        assert torch.equal(u.codes, v.codes) and torch.equal(u.scales, v.scales)
