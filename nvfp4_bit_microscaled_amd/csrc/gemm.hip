@@ -562,6 +562,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 #define NVFP4_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
+// ... and with only the LDS / scalar-memory counter drained (vmcnt left at its
+// maximum 63)
+#define NVFP4_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 struct KKOperand {
     __amdgpu_buffer_rsrc_t codes, scales;  // records end at the operand's last row
@@ -816,20 +819,22 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Skinny NT kernel for decode-style shapes (M <= 64, K % 128 == 0):
-// C[M, N] = A[M, K] B[N, K]^T.  The packed weights B dominate the traffic
-// (4.5 bits per element) and are streamed once: each wave owns 16 rows of B
-// (16 output columns) over all of K, each lane reading 16 bytes (32 codes)
-// per 128-wide K step; a row's 64 bytes per step come from four adjacent
-// lanes.  The few activation rows are dequantized once per workgroup into LDS
-// as FP16, one K chunk at a time, and read back as MFMA A fragments.  Both
-// operands are prefetched into registers one chunk ahead, issued after
-// everything the current chunk waits for (vector-memory counters drain in
-// order).  The loop is branch-free: rows past M or N are clamped to the last
-// valid row (their outputs are never stored) and K steps past the end are
-// skipped whole.  v_mfma_f32_16x16x32_f16 with the per-lane K permutation of
-// the main kernel: at step s lane (row l % 16, group g = l / 16) supplies
-// k = k0 + 32 g + 8 s + [0, 8) for both operands.
+// Skinny NT kernel for decode-style shapes (M <= 64, K a multiple of the K
+// chunk KC = 2048 / 1024 / 512 for M <= 16 / 32 / 64): C[M, N] = A[M, K]
+// B[N, K]^T.  The packed weights B dominate the traffic (4.5 bits per element)
+// and are streamed once: each wave owns 16 rows of B (16 output columns) over
+// all of K.  Inside a chunk, lane group g = lane / 16 owns the contiguous K
+// quarter g KC/4 .. +KC/4 (one 16-byte code load per 128 K, and its scale
+// bytes for the whole chunk in one or two wide loads: the load path is
+// limited by accesses per lane, so 2-byte scale loads per step would cost as
+// much as the codes).  The few activation rows are dequantized once per
+// workgroup into LDS as FP16, one chunk at a time, in the same lane-quarter
+// order (16 bytes of padding per quarter keep the quarters on different
+// banks).  Both operands are prefetched into registers one chunk ahead,
+// issued after everything the current chunk waits for (vector-memory
+// counters drain in order).  Rows past M or N are clamped to the last valid
+// row (never stored).  v_mfma_f32_16x16x32_f16: at step s lane (row l % 16,
+// group g) supplies k = kc + g KC/4 + 32 st + 8 s + [0, 8) for both operands.
 // ---------------------------------------------------------------------------
 constexpr int kSkN = 64;  // output columns per workgroup
 
@@ -837,23 +842,40 @@ template <int KC, int RMAX>
 __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
 {
     constexpr int kSteps = KC / 128;                 // B steps per chunk
-    constexpr int kRow = KC * 2 + 16;                // LDS bytes per activation row
+    constexpr int kQ = KC / 4;                       // K of one lane quarter per chunk
+    constexpr int kQStride = kQ * 2 + 16;            // LDS bytes per activation row quarter
+    constexpr int kRow = 4 * kQStride;               // LDS bytes per activation row
     constexpr int kAPer = RMAX * 16 * KC / 32 / 256; // 32-code activation pieces per thread
+    constexpr int kSB = 2 * kSteps;                  // scale bytes per lane and chunk
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int R = (int)((p.M + 15) / 16);            // 16-row blocks of A (<= RMAX)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, g = lane >> 4;
     const int64_t n = (int64_t)blockIdx.x * kSkN + wave * 16 + lr;  // B row of this lane
     const int64_t nc = n < p.N ? n : p.N - 1;                       // clamped for loads
     const int64_t K = p.K, lds_b = K / 16;
-    const uint8_t* brow = p.b_codes + nc * (K / 2) + 16 * g;
-    const uint8_t* bsrow = p.b_scales + (p.b2d ? (nc / 16) * lds_b : nc * lds_b) + 2 * g;
+    // B through buffer resources over the whole code / scale planes (below
+    // 2 GiB): per-lane offsets in VGPRs, the chunk offset scalar, the step
+    // offset an immediate.  Past the last chunk the prefetch goes through
+    // resources with no records (out-of-range loads return zeros, touching no
+    // memory), so the loop body has no branch around it.
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.b_scales, (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t none =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, (short)0, 0, 0x00020000);
+    const int bo = (int)(nc * (K / 2)) + (kQ / 2) * g;
+    const int bso = (int)(p.b2d ? (nc / 16) * lds_b : nc * lds_b) + (kQ / 16) * g;
     float4_t acc[RMAX];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+    // B: lane g owns the contiguous quarter kc + g KC/4 .. +KC/4 of each chunk,
+    // 32 codes per step, so its scale bytes for the chunk are one contiguous
+    // run of kSB bytes
     u32x4 ac[kAPer], bc[kSteps], bn[kSteps];
-    uint32_t as[kAPer], bs[kSteps], bsn[kSteps];
+    uint32_t as[kAPer];
+    uint32_t bs[kSB / 4], bsn[kSB / 4];
     auto load_a = [&](int64_t kc) {
 #pragma unroll
         for (int i = 0; i < kAPer; ++i) {
@@ -861,78 +883,113 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
             int m = idx / (KC / 32), c = idx % (KC / 32);
             int64_t mc = m < p.M ? m : p.M - 1;
             int64_t k = kc + 32 * c;
-            k = k < K ? k : K - 32;  // pieces past K are never read
+            k = k < K ? k : K - 32;  // the prefetch past the last chunk reads a valid piece
             ac[i] = *reinterpret_cast<const u32x4*>(p.a_codes + mc * (K / 2) + k / 2);
             const uint8_t* sp =
                 p.a_scales + (p.a2d ? (mc / 16) * lds_b : mc * lds_b) + k / 16;
             as[i] = *reinterpret_cast<const uint16_t*>(sp);
         }
     };
-    auto load_b = [&](int64_t kc, u32x4* c, uint32_t* sc) {
+    auto load_b = [&](__amdgpu_buffer_rsrc_t c_rsrc, __amdgpu_buffer_rsrc_t s_rsrc, int kc,
+                      u32x4* c, uint32_t* sc) {
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) {
-            int64_t k = kc + st * 128;
-            k = k < K ? k : K - 128;  // steps past K are skipped
-            c[st] = *reinterpret_cast<const u32x4*>(brow + k / 2);
-            sc[st] = *reinterpret_cast<const uint16_t*>(bsrow + k / 16);
+        for (int st = 0; st < kSteps; ++st)
+            c[st] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, bo + 16 * st, kc / 2, 0));
+#pragma unroll
+        for (int q = 0; q < kSB / 4; q += (kSB >= 16 ? 4 : 2)) {
+            if (kSB >= 16) {
+                u32x4 w = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(s_rsrc, bso + 4 * q, kc / 16, 0));
+                sc[q] = w[0]; sc[q + 1] = w[1]; sc[q + 2] = w[2]; sc[q + 3] = w[3];
+            } else {
+                u32x2 w = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(s_rsrc, bso + 4 * q, kc / 16, 0));
+                sc[q] = w[0]; sc[q + 1] = w[1];
+            }
         }
     };
 
-    load_a(0);
-    load_b(0, bc, bs);
-    for (int64_t kc = 0; kc < K; kc += KC) {
-        // activations of this chunk -> FP16 in LDS (the previous chunk's readers are done)
-        __syncthreads();
+    // one chunk: its activations into LDS, the next chunk's operands issued,
+    // then the products with the B registers loaded one chunk earlier.  The
+    // chunk loop runs in pairs with the two B register sets swapping roles,
+    // so no register copy (and no wait for the prefetch) sits in the loop.
+    auto chunk = [&](int kc, const u32x4 (&cb)[kSteps], const uint32_t (&cs)[kSB / 4],
+                     u32x4 (&nb)[kSteps], uint32_t (&ns)[kSB / 4]) {
+        // activations of this chunk -> FP16 in LDS, row-major by lane quarter
+        // (the previous chunk's readers are done); rows past M hold the last
+        // row again and are never stored.  The barriers only order LDS
+        // accesses: a plain s_barrier after draining this wave's LDS counter
+        // (a __syncthreads fence would also wait for the prefetch in flight).
+        NVFP4_WAIT_LGKMCNT0();
+        __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int i = 0; i < kAPer; ++i) {
             int idx = threadIdx.x + 256 * i;
             int m = idx / (KC / 32), c = idx % (KC / 32);
-            if (m < R * 16) {
-                half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as[i], 1.0f, false);
-                uint8_t* dst = lds + m * kRow + 64 * c;
+            half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as[i], 1.0f, false);
+            const int kl = 32 * c;  // K offset inside the chunk
+            uint8_t* dst = lds + m * kRow + (kl / kQ) * kQStride + (kl % kQ) * 2;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<half8_t*>(dst + 16 * q) = dequant_word(ac[i][q], e2[q >> 1]);
-            }
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<half8_t*>(dst + 16 * q) = dequant_word(ac[i][q], e2[q >> 1]);
         }
-        __syncthreads();
-        // next chunk's operands, issued after everything this chunk still waits for
-        const bool more = kc + KC < K;
-        if (more) {
-            load_a(kc + KC);
-            load_b(kc + KC, bn, bsn);
-        }
+        NVFP4_WAIT_LGKMCNT0();
+        __builtin_amdgcn_s_barrier();
+        // next chunk's operands, A strictly before B (the next chunk's
+        // dequantization then waits for A alone); past the end through the
+        // record-less resources
+        const bool more = kc + KC < (int)K;
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(kc + KC);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(more ? rc : none, more ? rs : none, more ? kc + KC : 0, nb, ns);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) {
-            if (kc + st * 128 < K) {  // uniform
-                half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[st], 1.0f, false);
+            // the step's A fragments first (one LDS latency per step), then
+            // its four B dequantizations and MFMAs
+            half8_t af[4][RMAX];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    half8_t bf = dequant_word(bc[st][s], e2[s >> 1]);
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-                    for (int r = 0; r < RMAX; ++r) {
-                        if (r < R) {
-                            half8_t af = *reinterpret_cast<const half8_t*>(
-                                lds + (16 * r + lr) * kRow + (st * 128 + 32 * g + 8 * s) * 2);
-                            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[r], 0, 0, 0);
-                        }
-                    }
-                }
+                for (int r = 0; r < RMAX; ++r)
+                    af[s][r] = *reinterpret_cast<const half8_t*>(
+                        lds + (16 * r + lr) * kRow + g * kQStride + (32 * st + 8 * s) * 2);
+            // scale bytes 2 st, 2 st + 1 of the lane's run
+            const uint32_t sw = cs[st >> 1] >> (16 * (st & 1));
+            half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                half8_t bf = dequant_word(cb[st][s], e2[s >> 1]);
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r)
+                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s][r], bf, acc[r], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * RMAX, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);         // scale + B dequant
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * RMAX, 0);   // MFMAs
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) {
-#pragma unroll
-            for (int st = 0; st < kSteps; ++st) {
-                bc[st] = bn[st];
-                bs[st] = bsn[st];
-            }
-        }
+    };
+
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(rc, rs, 0, bc, bs);
+    __builtin_amdgcn_sched_barrier(0);
+    // both exits leave the loop, so the loop head is reached only after the
+    // second chunk of a pair (its registers are the live ones there)
+    for (int kc = 0;; kc += 2 * KC) {
+        chunk(kc, bc, bs, bn, bsn);
+        if (kc + KC >= (int)K) break;
+        chunk(kc + KC, bn, bsn, bc, bs);
+        if (kc + 2 * KC >= (int)K) break;
     }
     // lane holds C[16 r + 4 g + j][n] in acc[r][j]
     const float sab = (*p.a_ts) * (*p.b_ts);
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
-        if (r >= R) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             int64_t row = 16 * r + 4 * g + j;
@@ -998,25 +1055,23 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     p.out_bf16 = out_bf16;
     const int esz = out_bf16 ? 2 : 4;
     p.vec_out = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(c) % (4 * esz) == 0;
-    if (A.k_major && B.k_major && M <= 64 && K % 128 == 0) {
-        // decode-style shapes: stream the weights with a dedicated kernel
+    // decode-style shapes (M <= 64): stream the weights with a dedicated
+    // kernel; its K chunk (2048, 1024 or 512 by M) must divide K
+    const int skinny_kc = M <= 16 ? 2048 : (M <= 32 ? 1024 : 512);
+    const bool b_small = (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);  // 32-bit buffer offsets
+    if (A.k_major && B.k_major && M <= 64 && K % skinny_kc == 0 && b_small) {
         dim3 g((unsigned)((N + kSkN - 1) / kSkN));
-        if (M <= 16) {
-            auto kern = k_gemm_skinny<2048, 1>;
-            const int lds = 1 * 16 * (2048 * 2 + 16);
-            hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-            hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);
-        } else if (M <= 32) {
-            auto kern = k_gemm_skinny<1024, 2>;
-            const int lds = 2 * 16 * (1024 * 2 + 16);
-            hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-            hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);
-        } else {
-            auto kern = k_gemm_skinny<512, 4>;
-            const int lds = 4 * 16 * (512 * 2 + 16);
-            hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-            hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);
-        }
+#define NVFP4_SKINNY(KC, RMAX)                                                                 \
+    {                                                                                          \
+        auto kern = k_gemm_skinny<KC, RMAX>;                                                   \
+        const int lds = RMAX * 16 * (KC * 2 + 64);                                             \
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
+        hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
+    }
+        if (M <= 16) NVFP4_SKINNY(2048, 1)
+        else if (M <= 32) NVFP4_SKINNY(1024, 2)
+        else NVFP4_SKINNY(512, 4)
+#undef NVFP4_SKINNY
         return hipGetLastError();
     }
     if (A.k_major && B.k_major && K % kTK == 0 && K / 2 * kTM < (1ll << 31)) {

@@ -215,3 +215,21 @@ def test_nt_kmajor_odd_rows(nv):
     a_or, a_g = random_operand(nv, rng, M, K, False, 1, 0.5)
     b_or, b_g = random_operand(nv, rng, N, K, False, 1, 0.5)
     run_and_check(nv, "NT", M, N, K, a_or, a_g, b_or, b_g)
+
+
+# decode-style NT shapes (M <= 64, K a multiple of the kernel's K chunk: 2048
+# for M <= 16, 1024 for M <= 32, 512 for M <= 64): the skinny kernel, with M
+# and N ragged and one to several chunks
+SKINNY = [(1, 64, 2048, False), (5, 100, 4096, True), (16, 1000, 2048, False),
+          (17, 200, 1024, True), (32, 77, 3072, False), (33, 130, 1536, False),
+          (64, 96, 512, True), (64, 64, 8192, False)]
+
+
+@pytest.mark.parametrize("M,N,K,b2d", SKINNY)
+def test_skinny_decode_kernel(nv, M, N, K, b2d):
+    rng = np.random.default_rng(M * 1000 + N + K)
+    if b2d:
+        N = (N + 15) // 16 * 16
+    a_or, a_g = random_operand(nv, rng, M, K, False, 1, 0.5)
+    b_or, b_g = random_operand(nv, rng, N, K, b2d, 1, 0.75)
+    run_and_check(nv, "NT", M, N, K, a_or, a_g, b_or, b_g)
