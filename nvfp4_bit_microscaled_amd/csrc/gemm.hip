@@ -820,7 +820,7 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 
 // ---------------------------------------------------------------------------
 // Skinny NT kernel for decode-style shapes (M <= 64, K a multiple of the K
-// chunk KC = 2048 / 1024 / 512 for M <= 16 / 32 / 64): C[M, N] = A[M, K]
+// chunk KC = 512): C[M, N] = A[M, K]
 // B[N, K]^T.  The packed weights B dominate the traffic (4.5 bits per element)
 // and are streamed once: each wave owns 16 rows of B (16 output columns) over
 // all of K.  Inside a chunk, lane group g = lane / 16 owns the contiguous K
@@ -832,7 +832,9 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 // order (16 bytes of padding per quarter keep the quarters on different
 // banks).  Both operands are prefetched into registers one chunk ahead,
 // issued after everything the current chunk waits for (vector-memory
-// counters drain in order).  Rows past M or N are clamped to the last valid
+// counters drain in order).  Short chunks stream best: with 2048 or 1024
+// the same weights took 15-25% longer (more bytes in flight per wave, in
+// larger bursts).  Rows past M or N are clamped to the last valid
 // row (never stored).  v_mfma_f32_16x16x32_f16: at step s lane (row l % 16,
 // group g) supplies k = kc + g KC/4 + 32 st + 8 s + [0, 8) for both operands.
 // ---------------------------------------------------------------------------
@@ -866,6 +868,13 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
         __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, (short)0, 0, 0x00020000);
     const int bo = (int)(nc * (K / 2)) + (kQ / 2) * g;
     const int bso = (int)(p.b2d ? (nc / 16) * lds_b : nc * lds_b) + (kQ / 16) * g;
+    // Workgroups walk K starting at different chunks: rows are K/2 bytes
+    // apart, so if every workgroup read the same chunk at once, all reads
+    // would fall in the same few byte ranges of the row pitch (the same
+    // memory channels).  The sum over chunks is the same in any order.
+    const int nchunks = (int)(K / KC);
+    const int rot = (int)(blockIdx.x % (unsigned)nchunks) * KC;
+    auto kpos = [&](int kc) { return kc + rot >= (int)K ? kc + rot - (int)K : kc + rot; };
     float4_t acc[RMAX];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -941,9 +950,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
         // record-less resources
         const bool more = kc + KC < (int)K;
         __builtin_amdgcn_sched_barrier(0);
-        load_a(kc + KC);
+        load_a(kpos(kc + KC));
         __builtin_amdgcn_sched_barrier(0);
-        load_b(more ? rc : none, more ? rs : none, more ? kc + KC : 0, nb, ns);
+        load_b(more ? rc : none, more ? rs : none, more ? kpos(kc + KC) : 0, nb, ns);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) {
@@ -974,9 +983,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
     };
 
     __builtin_amdgcn_sched_barrier(0);
-    load_a(0);
+    load_a(kpos(0));
     __builtin_amdgcn_sched_barrier(0);
-    load_b(rc, rs, 0, bc, bs);
+    load_b(rc, rs, kpos(0), bc, bs);
     __builtin_amdgcn_sched_barrier(0);
     // both exits leave the loop, so the loop head is reached only after the
     // second chunk of a pair (its registers are the live ones there)
@@ -1056,8 +1065,8 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     const int esz = out_bf16 ? 2 : 4;
     p.vec_out = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(c) % (4 * esz) == 0;
     // decode-style shapes (M <= 64): stream the weights with a dedicated
-    // kernel; its K chunk (2048, 1024 or 512 by M) must divide K
-    const int skinny_kc = M <= 16 ? 2048 : (M <= 32 ? 1024 : 512);
+    // kernel; its K chunk must divide K
+    const int skinny_kc = 512;
     const bool b_small = (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);  // 32-bit buffer offsets
     if (A.k_major && B.k_major && M <= 64 && K % skinny_kc == 0 && b_small) {
         dim3 g((unsigned)((N + kSkN - 1) / kSkN));
@@ -1068,8 +1077,8 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
     }
-        if (M <= 16) NVFP4_SKINNY(2048, 1)
-        else if (M <= 32) NVFP4_SKINNY(1024, 2)
+        if (M <= 16) NVFP4_SKINNY(512, 1)
+        else if (M <= 32) NVFP4_SKINNY(512, 2)
         else NVFP4_SKINNY(512, 4)
 #undef NVFP4_SKINNY
         return hipGetLastError();

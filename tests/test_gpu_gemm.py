@@ -217,12 +217,13 @@ def test_nt_kmajor_odd_rows(nv):
     run_and_check(nv, "NT", M, N, K, a_or, a_g, b_or, b_g)
 
 
-# decode-style NT shapes (M <= 64, K a multiple of the kernel's K chunk: 2048
-# for M <= 16, 1024 for M <= 32, 512 for M <= 64): the skinny kernel, with M
-# and N ragged and one to several chunks
+# decode-style NT shapes (M <= 64, K a multiple of the kernel's 512 K chunk):
+# the skinny kernel, with M and N ragged and one, an odd number and an even
+# number of chunks (its chunk loop runs in pairs)
 SKINNY = [(1, 64, 2048, False), (5, 100, 4096, True), (16, 1000, 2048, False),
           (17, 200, 1024, True), (32, 77, 3072, False), (33, 130, 1536, False),
-          (64, 96, 512, True), (64, 64, 8192, False)]
+          (64, 96, 512, True), (64, 64, 8192, False), (1, 300, 2560, False),
+          (7, 48, 512, True), (12, 4200, 1536, False)]
 
 
 @pytest.mark.parametrize("M,N,K,b2d", SKINNY)
