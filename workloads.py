@@ -81,9 +81,9 @@ TINY = dict(act=(256, 256), act_seed=0, w=(128, 256), w_seed=1, gemm=(128, 128, 
 LLAMA8B = dict(tokens=32768, hidden=4096, ffn=14336, x_seed=0, wgu_seed=2, wdown_seed=3,
                dy_seed=4, dh_seed=5, sr_seed=1, mask_seed=1)
 
-# Decode-style skinny GEMM: activations [M, 8192] for M in {1, 16, 64},
+# Decode-style skinny GEMM: activations [M, 8192] for M in {1, 16, 32, 64},
 # weights [28672, 8192] pre-quantized 1x16 along K.
-DECODE = dict(ms=(1, 16, 64), k=8192, n=28672, act_seed=6, w_seed=7)
+DECODE = dict(ms=(1, 16, 32, 64), k=8192, n=28672, act_seed=6, w_seed=7)
 
 # One GPU's token share of a Llama-3.1-405B MLP: 8192 tokens, hidden 16384,
 # intermediate 53248.
