@@ -1,4 +1,5 @@
-"""CPU oracle for NVFP4 quantization, RHT16, dequantization and GEMM.
+"""CPU oracle for NVFP4 quantization, RHT16, dequantization and GEMM, and for
+the MXFP4 format the pages compare NVFP4 with.
 
 TEST INFRASTRUCTURE ONLY.  The product library never imports, links or calls
 this package; only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -83,6 +84,17 @@ def lib():
         L.oracle_gemm_pairs.argtypes = [ctypes.c_int, c_i64, c_i64, c_i64, c_vp, c_vp,
                                         ctypes.c_float, ctypes.c_int, c_vp, c_vp, ctypes.c_float,
                                         ctypes.c_int, c_i64, c_vp, c_vp, c_vp, c_vp]
+        L.oracle_e8m0_value.restype = ctypes.c_double
+        L.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        L.oracle_mx_scale_code.restype = ctypes.c_uint8
+        L.oracle_mx_scale_code.argtypes = [ctypes.c_float]
+        L.oracle_mx_quantize.restype = ctypes.c_int
+        L.oracle_mx_quantize.argtypes = [c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp, c_vp]
+        L.oracle_mx_dequantize.restype = ctypes.c_int
+        L.oracle_mx_dequantize.argtypes = [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]
+        L.oracle_mx_gemm_pairs.restype = ctypes.c_int
+        L.oracle_mx_gemm_pairs.argtypes = [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_i64,
+                                           c_vp, c_vp, c_vp, c_vp]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_set_num_threads.restype = None
@@ -223,6 +235,63 @@ def gemm_full(layout: str, M: int, N: int, K: int, a, b):
     """Full M x N reference (small sizes only)."""
     mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     ref, ab = gemm_pairs(layout, M, N, K, a, b, mm.ravel(), nn.ravel())
+    return ref.reshape(M, N), ab.reshape(M, N)
+
+
+# ---------------------------------------------------------------- MXFP4
+# The power-of-two format the pages compare NVFP4 with ("NVFP4: cos'e e come
+# supera FP8 e BF16", section "Cos'e NVFP4"; "FP4", the section comparing
+# NVFP4 with the open standard), with the block size (32) and scale rule of
+# the OCP Microscaling (MX) v1.0 specification, which the pages do not give.
+
+def e8m0_value(code: int) -> float:
+    return lib().oracle_e8m0_value(code)
+
+
+def mx_scale_code(amax: float) -> int:
+    return lib().oracle_mx_scale_code(amax)
+
+
+def mx_quantize(x: np.ndarray):
+    """Blocks of 32 along the columns.  Returns (codes uint8 [R, C/2], scales uint8 [R, C/32])."""
+    x, dt = _as_input(x)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 32), dtype=np.uint8)
+    if lib().oracle_mx_quantize(_ptr(x), dt, rows, cols, cols, _ptr(codes), _ptr(scales)):
+        raise ValueError("oracle_mx_quantize: bad shape")
+    return codes, scales
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray, rows: int, cols: int):
+    """Returns (fp32 [R, C], bf16 bits uint16 [R, C])."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    f = np.zeros((rows, cols), dtype=np.float32)
+    b = np.zeros((rows, cols), dtype=np.uint16)
+    if lib().oracle_mx_dequantize(_ptr(codes), _ptr(scales), rows, cols, _ptr(f), _ptr(b)):
+        raise ValueError("oracle_mx_dequantize: bad shape")
+    return f, b
+
+
+def mx_gemm_pairs(M: int, N: int, K: int, a, b, ms, ns):
+    """NT: a = (codes [M, K/2], scales [M, K/32]), b likewise [N, ...].
+    Returns (ref fp64, abs fp64) at (ms, ns)."""
+    ac, asc = (np.ascontiguousarray(t, dtype=np.uint8) for t in a)
+    bc, bsc = (np.ascontiguousarray(t, dtype=np.uint8) for t in b)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    ref = np.zeros(len(ms), dtype=np.float64)
+    ab = np.zeros(len(ms), dtype=np.float64)
+    if lib().oracle_mx_gemm_pairs(M, N, K, _ptr(ac), _ptr(asc), _ptr(bc), _ptr(bsc), len(ms),
+                                  _ptr(ms), _ptr(ns), _ptr(ref), _ptr(ab)):
+        raise ValueError("oracle_mx_gemm_pairs: bad shape")
+    return ref, ab
+
+
+def mx_gemm_full(M: int, N: int, K: int, a, b):
+    mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ref, ab = mx_gemm_pairs(M, N, K, a, b, mm.ravel(), nn.ravel())
     return ref.reshape(M, N), ab.reshape(M, N)
 
 

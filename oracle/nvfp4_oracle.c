@@ -34,6 +34,10 @@
  * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
  * easy as 1, 2, 3", SC'11) keyed by (seed, element index).
  *
+ * The MXFP4 functions near the end follow the open MX standard for the
+ * power-of-two format the pages compare NVFP4 with (block size and scale
+ * rule are the standard's; the pages give neither).
+ *
  * Every function is pinned by tests/test_oracle_*.py against something other
  * than itself (torch's float8_e4m3fn and bfloat16 casts, rocRAND's Philox,
  * closed forms, brute force).  No function here is "parity unpinned".
@@ -533,6 +537,114 @@ int oracle_gemm_pairs(int layout, int64_t M, int64_t N, int64_t K, const uint8_t
         }
         ref[p] = sab * s;
         absref[p] = sab * sa;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP4: the power-of-two-scaled format the pages contrast NVFP4 with */
+/* ------------------------------------------------------------------ */
+/*
+ * "NVFP4: cos'e e come supera FP8 e BF16" (section "Cos'e NVFP4") sets the
+ * E4M3-per-16 scheme against simpler power-of-two scaling such as MXFP4, and
+ * "FP4" (chaitex.ru, the section comparing NVFP4 with the open standard)
+ * says MXFP4 uses larger quantization blocks and coarser scale factors.  The
+ * pages give no block size or scale rule; this file takes those of the OCP
+ * Microscaling Formats (MX) v1.0 specification, the open standard named:
+ *   - 32 consecutive elements share one E8M0 scale X = 2^(u - 127), u the
+ *     stored byte (255 is NaN), no tensor-level scale;
+ *   - X = 2^(floor(log2(amax)) - 2): 2 is the exponent of E2M1's largest
+ *     value 6 = 1.5 * 2^2; the exponent is clamped to the E8M0 range, and a
+ *     zero block (or one whose amax is below 2^-125) gets X = 2^-127;
+ *   - each element is x / X rounded to E2M1 to nearest-even, saturating at
+ *     +-6 (a block whose amax/X lies in (6, 8) clips), sign bit kept.
+ */
+
+/* Value of an E8M0 scale byte. */
+double oracle_e8m0_value(uint8_t code)
+{
+    if (code == 255) return NAN;
+    return ldexp(1.0, (int)code - 127);
+}
+
+/* E8M0 byte of the shared scale of a block with maximum magnitude amax. */
+uint8_t oracle_mx_scale_code(float amax)
+{
+    if (!(amax > 0.0f)) return 0;
+    int e;
+    (void)frexp((double)amax, &e); /* amax = f * 2^e, 0.5 <= f < 1 */
+    int x = (e - 1) - 2;           /* floor(log2(amax)) - 2 */
+    if (x < -127) x = -127;
+    if (x > 127) x = 127;
+    return (uint8_t)(x + 127);
+}
+
+/* Quantize rows of x in blocks of 32 consecutive columns (cols % 32 == 0):
+ * codes [rows, cols/2] packed as everywhere else (low nibble = even column),
+ * scales [rows, cols/32] E8M0.  Returns 0, or -1 on a bad shape. */
+int oracle_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                       uint8_t* codes, uint8_t* scales)
+{
+    if (rows < 0 || cols < 0 || cols % 32 != 0 || ld_x < cols) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < cols / 32; ++b) {
+            float v[32], amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                v[i] = load_elem(x, dtype, ld_x, r, 32 * b + i);
+                float a = fabsf(v[i]);
+                if (a > amax) amax = a;
+            }
+            uint8_t u = oracle_mx_scale_code(amax);
+            float X = (float)oracle_e8m0_value(u);
+            scales[r * (cols / 32) + b] = u;
+            for (int i = 0; i < 32; ++i) {
+                float y = v[i] / X;
+                put_code(codes, cols, r, 32 * b + i, oracle_e2m1_encode_rne(y));
+            }
+        }
+    return 0;
+}
+
+/* v = val(code) * X, exact in FP64; FP32 and BF16 (RNE) copies. */
+int oracle_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                         float* out_f32, uint16_t* out_bf16)
+{
+    if (rows < 0 || cols < 0 || cols % 32 != 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            double v = oracle_e2m1_value(code_of(codes, cols, r, c)) *
+                       oracle_e8m0_value(scales[r * (cols / 32) + c / 32]);
+            float f = (float)v;
+            if (out_f32) out_f32[r * cols + c] = f;
+            if (out_bf16) out_bf16[r * cols + c] = oracle_f32_to_bf16(f);
+        }
+    return 0;
+}
+
+/* MXFP4 GEMM reference, NT only: A stored [M, K], B stored [N, K], both in
+ * blocks of 32 along K.  ref[p] = sum_k deq(A)[m,k] deq(B)[n,k] in FP64 (each
+ * product is exact) and absref[p] = sum_k |...| at (ms[p], ns[p]). */
+int oracle_mx_gemm_pairs(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                         const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                         int64_t npairs, const int64_t* ms, const int64_t* ns, double* ref,
+                         double* absref)
+{
+    if (K % 32 != 0 || M < 0 || N < 0) return -1;
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t p = 0; p < npairs; ++p) {
+        double s = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a = oracle_e2m1_value(code_of(a_codes, K, ms[p], k)) *
+                       oracle_e8m0_value(a_scales[ms[p] * (K / 32) + k / 32]);
+            double b = oracle_e2m1_value(code_of(b_codes, K, ns[p], k)) *
+                       oracle_e8m0_value(b_scales[ns[p] * (K / 32) + k / 32]);
+            s += a * b;
+            sa += fabs(a * b);
+        }
+        ref[p] = s;
+        absref[p] = sa;
     }
     return 0;
 }
