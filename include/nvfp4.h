@@ -238,6 +238,43 @@ nvfp4_status nvfp4_gemm(nvfp4_layout layout, int64_t M, int64_t N, int64_t K,
                         const float* b_tensor_scale, nvfp4_block b_block, nvfp4_dtype out_dtype,
                         void* c, int64_t ldc, void* stream);
 
+/*
+ * MXFP4, the power-of-two-scaled format the pages compare NVFP4 with
+ * ("NVFP4: cos'e e come supera FP8 e BF16", guiahardware.es, section "Cos'e
+ * NVFP4": NVFP4's E4M3 scales against power-of-two scaling such as MXFP4;
+ * chaitex.ru "FP4", the comparison with the open standard: MXFP4 has larger
+ * blocks and coarser scales).  The pages give neither the block size nor the
+ * scale rule; these follow the OCP Microscaling Formats (MX) v1.0
+ * specification: 32 consecutive elements of a row share one E8M0 scale byte
+ * u (X = 2^(u - 127)), X = 2^(floor(log2 amax) - 2) with the exponent clamped
+ * to >= -127 (zero blocks get u = 0), and each element is x / X rounded to
+ * E2M1 to nearest-even, saturating at +-6, sign kept.  No tensor scale.
+ *
+ * Storage: codes [rows, cols/2] packed as for NVFP4 (low nibble = even
+ * column), scales [rows, cols/32] row-major, one byte each.
+ *
+ * nvfp4_mx_quantize: x[r*ld_x + c] (BF16 or FP32) -> codes, scales.
+ *   Shape rules: cols % 32 == 0; ld_x >= cols; x, codes 16-byte aligned and
+ *   x's row pitch a multiple of 16 bytes.  rows or cols == 0 writes nothing.
+ * nvfp4_mx_dequantize: out[r*ld_out + c] = val(q) * X (exact in FP32), BF16
+ *   output rounded to nearest-even.  cols % 32 == 0; ld_out >= cols.
+ * nvfp4_mx_gemm: C[M, N] = A[M, K] * B[N, K]^T (NT: both stored K-major)
+ *   with FP32 accumulation on the native scaled FP4 MFMA, BF16 (RNE) or
+ *   FP32 out.  K % 128 == 0; K / 2 * 256 < 2^31; ldc >= N; c element-aligned,
+ *   operand planes 16-byte aligned.  K == 0 writes zeros.
+ * All pointers are caller-owned device memory; launches are asynchronous on
+ * `stream`; argument errors return before anything is enqueued.
+ */
+nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                               int64_t ld_x, uint8_t* codes, uint8_t* scales, void* stream);
+nvfp4_status nvfp4_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                 int64_t cols, nvfp4_dtype out_dtype, void* out, int64_t ld_out,
+                                 void* stream);
+nvfp4_status nvfp4_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                           const uint8_t* a_scales, const uint8_t* b_codes,
+                           const uint8_t* b_scales, nvfp4_dtype out_dtype, void* c, int64_t ldc,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,8 @@ LAYOUT = {"NT": 0, "NN": 1, "TN": 2}
 EXPORTS = ("nvfp4_version", "nvfp4_status_string", "nvfp4_quantize_workspace_size",
            "nvfp4_quantize", "nvfp4_amax_workspace_size", "nvfp4_amax",
            "nvfp4_swiglu_amax", "nvfp4_rht16",
-           "nvfp4_dequantize", "nvfp4_gemm")
+           "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize",
+           "nvfp4_mx_gemm")
 
 
 class NVFP4Error(RuntimeError):
@@ -72,6 +73,12 @@ def _load():
     L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, ci, ci, ci, vp, i64, vp]
     L.nvfp4_gemm.restype = ci
     L.nvfp4_gemm.argtypes = [ci, i64, i64, i64, vp, vp, vp, ci, vp, vp, vp, ci, ci, vp, i64, vp]
+    L.nvfp4_mx_quantize.restype = ci
+    L.nvfp4_mx_quantize.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp]
+    L.nvfp4_mx_dequantize.restype = ci
+    L.nvfp4_mx_dequantize.argtypes = [vp, vp, i64, i64, ci, vp, i64, vp]
+    L.nvfp4_mx_gemm.restype = ci
+    L.nvfp4_mx_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, ci, vp, i64, vp]
     return L
 
 
@@ -150,6 +157,22 @@ def nvfp4_gemm(layout, M, N, K, a_codes, a_scales, a_tensor_scale, a_block, b_co
     return lib.nvfp4_gemm(layout, M, N, K, _p(a_codes), _p(a_scales), _p(a_tensor_scale), a_block,
                           _p(b_codes), _p(b_scales), _p(b_tensor_scale), b_block, out_dtype,
                           _p(c), ldc, _stream(stream))
+
+
+def nvfp4_mx_quantize(x, x_dtype, rows, cols, ld_x, codes, scales, stream=None) -> int:
+    return lib.nvfp4_mx_quantize(_p(x), x_dtype, rows, cols, ld_x, _p(codes), _p(scales),
+                                 _stream(stream))
+
+
+def nvfp4_mx_dequantize(codes, scales, rows, cols, out_dtype, out, ld_out, stream=None) -> int:
+    return lib.nvfp4_mx_dequantize(_p(codes), _p(scales), rows, cols, out_dtype, _p(out), ld_out,
+                                   _stream(stream))
+
+
+def nvfp4_mx_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales, out_dtype, c, ldc,
+                  stream=None) -> int:
+    return lib.nvfp4_mx_gemm(M, N, K, _p(a_codes), _p(a_scales), _p(b_codes), _p(b_scales),
+                             out_dtype, _p(c), ldc, _stream(stream))
 
 
 # ---------------------------------------------------------------- tensor-level helpers
@@ -293,4 +316,49 @@ def gemm(layout: str, a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16,
         LAYOUT[layout], M, N, K, a.codes, a.scales, a.tensor_scale,
         BLOCK_2D if a.block2d else BLOCK_1D, b.codes, b.scales, b.tensor_scale,
         BLOCK_2D if b.block2d else BLOCK_1D, _dtype_code(out), out, out.stride(0)))
+    return out
+
+
+# ---------------------------------------------------------------- MXFP4
+# The power-of-two-scaled format the pages compare NVFP4 with (E2M1 codes,
+# one E8M0 scale per 32 along the row, no tensor scale; block and scale rule
+# of the OCP MX v1.0 standard).
+
+@dataclass
+class MXFP4Tensor:
+    """codes uint8 [R, C/2], scales uint8 [R, C/32] (E8M0)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    cols: int
+
+
+def mx_quantize(x: torch.Tensor, out: MXFP4Tensor | None = None) -> MXFP4Tensor:
+    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1
+    rows, cols = x.shape
+    if out is None:
+        out = MXFP4Tensor(codes=torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device),
+                          scales=torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device),
+                          rows=rows, cols=cols)
+    _check("nvfp4_mx_quantize", nvfp4_mx_quantize(x, _dtype_code(x), rows, cols, x.stride(0),
+                                                  out.codes, out.scales))
+    return out
+
+
+def mx_dequantize(t: MXFP4Tensor, out_dtype=torch.bfloat16) -> torch.Tensor:
+    out = torch.empty(t.rows, t.cols, dtype=out_dtype, device=t.codes.device)
+    _check("nvfp4_mx_dequantize", nvfp4_mx_dequantize(t.codes, t.scales, t.rows, t.cols,
+                                                      _dtype_code(out), out, t.cols))
+    return out
+
+
+def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out_dtype=torch.bfloat16,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """NT: a [M, K], b [N, K] -> C [M, N] = a b^T."""
+    M, K, N = a.rows, a.cols, b.rows
+    assert b.cols == K
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=a.codes.device)
+    _check("nvfp4_mx_gemm", nvfp4_mx_gemm(M, N, K, a.codes, a.scales, b.codes, b.scales,
+                                          _dtype_code(out), out, out.stride(0)))
     return out

@@ -277,4 +277,62 @@ nvfp4_status nvfp4_gemm(nvfp4_layout layout, int64_t M, int64_t N, int64_t K,
     return from_hip(launch_gemm(M, N, K, A, B, out_dtype == NVFP4_DTYPE_BF16, c, ldc, s));
 }
 
+nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                               int64_t ld_x, uint8_t* codes, uint8_t* scales, void* stream)
+{
+    if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0) return NVFP4_ERR_INVALID_ARG;
+    if (cols % 32) return NVFP4_ERR_SHAPE;
+    if (ld_x < cols) return NVFP4_ERR_SHAPE;
+    if ((uint64_t)rows * (uint64_t)(cols / 32) > kMaxItems) return NVFP4_ERR_UNSUPPORTED;
+    if (rows == 0 || cols == 0) return NVFP4_OK;
+    if (!x || !codes || !scales) return NVFP4_ERR_INVALID_ARG;
+    const size_t esz = x_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    if (!aligned16(x) || !aligned16(codes) || ((size_t)ld_x * esz) % 16) return NVFP4_ERR_ALIGN;
+    return from_hip(launch_mx_quantize(x, x_dtype == NVFP4_DTYPE_BF16, rows, cols, ld_x, codes,
+                                       scales, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                 int64_t cols, nvfp4_dtype out_dtype, void* out, int64_t ld_out,
+                                 void* stream)
+{
+    if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0) return NVFP4_ERR_INVALID_ARG;
+    if (cols % 32) return NVFP4_ERR_SHAPE;
+    if (ld_out < cols) return NVFP4_ERR_SHAPE;
+    if ((uint64_t)rows * (uint64_t)(cols / 8) > kMaxItems) return NVFP4_ERR_UNSUPPORTED;
+    if (rows == 0 || cols == 0) return NVFP4_OK;
+    if (!codes || !scales || !out) return NVFP4_ERR_INVALID_ARG;
+    const size_t esz = out_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    if (!aligned16(codes) || !aligned16(out) || ((size_t)ld_out * esz) % 16) return NVFP4_ERR_ALIGN;
+    return from_hip(launch_mx_dequantize(codes, scales, rows, cols,
+                                         out_dtype == NVFP4_DTYPE_BF16, out, ld_out,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                           const uint8_t* a_scales, const uint8_t* b_codes,
+                           const uint8_t* b_scales, nvfp4_dtype out_dtype, void* c, int64_t ldc,
+                           void* stream)
+{
+    if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_INVALID_ARG;
+    if (ldc < N) return NVFP4_ERR_SHAPE;
+    if (K % 128) return NVFP4_ERR_SHAPE;
+    // buffer records of a 256-row tile (and the C offsets) in 32 bits
+    if ((uint64_t)K / 2 * 256 >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return NVFP4_OK;
+    if (!c) return NVFP4_ERR_INVALID_ARG;
+    const size_t esz = out_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    if ((reinterpret_cast<uintptr_t>(c) & (esz - 1)) != 0) return NVFP4_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) return from_hip(launch_fill_zero(c, out_dtype == NVFP4_DTYPE_BF16, M, N, ldc, s));
+    if (!a_codes || !a_scales || !b_codes || !b_scales) return NVFP4_ERR_INVALID_ARG;
+    if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(a_scales) || !aligned16(b_scales))
+        return NVFP4_ERR_ALIGN;
+    return from_hip(launch_mx_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales,
+                                   out_dtype == NVFP4_DTYPE_BF16, c, ldc, s));
+}
+
 }  // extern "C"

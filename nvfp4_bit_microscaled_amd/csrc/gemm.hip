@@ -306,11 +306,11 @@ __device__ __forceinline__ void tile_of(uint32_t bid, uint32_t nbm, uint32_t nbn
 // C[row][col + e] with row = 32 i + lane % 32 and col = 32 j + 8 g + 4 (lane /
 // 32) inside the wave's 128 x 128 sub-tile.  C = s_A s_B acc, stored as BF16
 // (round to nearest even) or FP32; 8/16-byte stores where the row allows.
+// sab is s_A s_B (1 for MXFP4, which has no tensor scale).
 template <bool kFull>
 __device__ __forceinline__ void store_tile(const GemmParams& p, float16_t (&acc)[4][4], int64_t m0,
-                                           int64_t n0, int wm, int wn, int lr, int lk)
+                                           int64_t n0, int wm, int wn, int lr, int lk, float sab)
 {
-    const float sab = (*p.a_ts) * (*p.b_ts);
     if (kFull && p.vec_out) {
         if (p.out_bf16) {
 #pragma unroll
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
 #undef INTERLEAVE
 #undef PREFETCH
 
-    store_tile<kFull>(p, acc, m0, n0, wm, wn, lr, lk);
+    store_tile<kFull>(p, acc, m0, n0, wm, wn, lr, lk, (*p.a_ts) * (*p.b_ts));
 }
 
 // ---------------------------------------------------------------------------
@@ -813,9 +813,9 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 #undef KK_SCALES_I
 #undef KK_N
     if (m0 + kTM <= p.M && n0 + kTN <= p.N)
-        store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk);
+        store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk, (*p.a_ts) * (*p.b_ts));
     else
-        store_tile<false>(p, acc, m0, n0, wm, wn, lr, lk);
+        store_tile<false>(p, acc, m0, n0, wm, wn, lr, lk, (*p.a_ts) * (*p.b_ts));
 }
 
 // ---------------------------------------------------------------------------
@@ -1108,6 +1108,189 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     else if (A.k_major) NVFP4_GEMM_LAUNCH(true, false);
     else NVFP4_GEMM_LAUNCH(false, false);
 #undef NVFP4_GEMM_LAUNCH
+    return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// MXFP4 GEMM on the native scaled FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4,
+// both operands E2M1, E8M0 scales).  The pages set NVFP4 against MXFP4's
+// power-of-two scaling (guiahardware.es "NVFP4: cos'e e come supera FP8 e
+// BF16", section "Cos'e NVFP4"; chaitex.ru "FP4", the comparison with the
+// open standard); the block of 32 and the E8M0 scale are the OCP MX v1.0
+// standard's.  NT only: A [M, K], B [N, K], both K-major, K % 128 == 0.
+//
+// Lane layout of the MFMA with FP4 operands (checked on the hardware against
+// a host reference): lane l supplies row l % 32 and the 32 consecutive K of
+// block l / 32 of its 64-K step as 16 bytes (low nibble first), and the E8M0
+// scale of that (row, block) in the byte of its scale register that op_sel
+// picks.  One lane's 16 bytes are exactly one MX block of one K-major row, so
+// the codes go from LDS to the MFMA untouched: no dequantization at all.
+//
+// Tiles of 256 x 256 (four waves of 128 x 128, 4 x 4 MFMA blocks each), K in
+// tiles of 128 (two MFMA steps), a three-stage LDS ring filled by buffer
+// loads straight to LDS: per wave and k-tile four 1 KB code copies and one
+// 256-byte scale copy per operand.  Code rows are 64 bytes per k-tile with
+// the same 16-byte plane swizzle as the NVFP4 kernel (plane ^ (row >> 1) & 3).
+// ---------------------------------------------------------------------------
+constexpr int kMxCodes = 256 * 64;               // 16 KB
+constexpr int kMxOperand = kMxCodes + 256 * 4;   // + 1 KB of E8M0 scales
+constexpr int kMxStage = 2 * kMxOperand;
+constexpr int kMxLds = 3 * kMxStage;             // 104448 bytes
+
+typedef uint32_t v8i32_t __attribute__((ext_vector_type(8)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+struct MxOperand {
+    __amdgpu_buffer_rsrc_t codes, scales;  // records end at the operand's last row
+    int code_off;   // lane offset in this wave's first 1 KB code window
+    int code_step;  // uniform: bytes from one code window to the next (16 rows)
+    int scale_off;  // lane offset of its row's 4 scale bytes of k-tile 0
+};
+
+// Code window j of wave w holds rows 16 (4w + j) .. +15 (four lanes per row,
+// lane slot ^ swizzle chooses the global 16-byte plane); the scale window of
+// wave w rows 64 w .. +63, one 4-byte word (the k-tile's four blocks) each.
+__device__ __forceinline__ MxOperand mx_operand(const uint8_t* codes, const uint8_t* scales,
+                                                int64_t MN, int64_t K, int64_t row0)
+{
+    MxOperand o;
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t ldc = K / 2, lds = K / 32;
+    const int64_t nrow = MN - row0 < 256 ? MN - row0 : 256;
+    o.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + row0 * ldc), (short)0,
+                                                (int)(nrow * ldc), 0x00020000);
+    o.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + row0 * lds), (short)0,
+                                                 (int)(nrow * lds), 0x00020000);
+    const int r = 64 * w + (l >> 2), slot = l & 3;
+    const int plane = slot ^ ((r >> 1) & 3);
+    o.code_off = (int)(r * ldc) + 16 * plane;
+    o.code_step = (int)(16 * ldc);
+    o.scale_off = (int)((64 * w + l) * lds);
+    return o;
+}
+
+__device__ __forceinline__ void mx_copy(const MxOperand& o, int kt, uint8_t* dst)
+{
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(o.codes, (lds_void_t*)(dst + (4 * w + j) * 1024),
+                                                 16, o.code_off, kt * 64 + j * o.code_step, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.scales, (lds_void_t*)(dst + kMxCodes + w * 256), 4,
+                                             o.scale_off, kt * 4, 0, 0);
+}
+
+__global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const uint32_t nbm = (uint32_t)((p.M + kTM - 1) / kTM), nbn = (uint32_t)((p.N + kTN - 1) / kTN);
+    uint32_t tm, tn;
+    tile_of(blockIdx.x, nbm, nbn, tm, tn);
+    tm = __builtin_amdgcn_readfirstlane(tm);
+    tn = __builtin_amdgcn_readfirstlane(tn);
+    const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lr = lane & 31, lk = lane >> 5;
+    const int nk = (int)(p.K / kTK);
+
+    const MxOperand oa = mx_operand(p.a_codes, p.a_scales, p.M, p.K, m0);
+    const MxOperand ob = mx_operand(p.b_codes, p.b_scales, p.N, p.K, n0);
+
+    float16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // fragment rows A wm*128 + 32 i + lr, B wn*128 + 32 j + lr; step s reads
+    // block 2 s + lk of the k-tile (plane (2 s + lk) ^ swizzle)
+    const int sw = (lr >> 1) & 3;
+    const int a_row = (wm * 128 + lr) * 64, b_row = kMxOperand + (wn * 128 + lr) * 64;
+    const int a_srow = kMxCodes + (wm * 128 + lr) * 4;
+    const int b_srow = kMxOperand + kMxCodes + (wn * 128 + lr) * 4;
+    const int plane0 = 16 * (lk ^ sw), plane1 = 16 * ((2 + lk) ^ sw);
+
+    mx_copy(oa, 0, lds);
+    mx_copy(ob, 0, lds + kMxOperand);
+    if (nk > 1) {
+        mx_copy(oa, 1, lds + kMxStage);
+        mx_copy(ob, 1, lds + kMxStage + kMxOperand);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        // this k-tile's ten copies done (the next tile's ten may still fly);
+        // then every wave's, and every wave is past the reads of k-tile kt-1,
+        // whose stage the copies of kt+2 overwrite
+        if (kt + 1 < nk) NVFP4_WAIT_VMCNT(10);
+        else NVFP4_WAIT_VMCNT(0);
+        NVFP4_WAIT_LGKMCNT0();
+        __builtin_amdgcn_s_barrier();
+        if (kt + 2 < nk) {
+            uint8_t* far = lds + ((kt + 2) % 3) * kMxStage;
+            mx_copy(oa, kt + 2, far);
+            mx_copy(ob, kt + 2, far + kMxOperand);
+        }
+        const uint8_t* st = lds + (kt % 3) * kMxStage;
+        // scale words: byte 0 = block lk (step 0), byte 2 = block 2 + lk (step 1)
+        uint32_t sa[4], sb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sa[i] = *reinterpret_cast<const uint32_t*>(st + a_srow + 32 * 4 * i) >> (8 * lk);
+            sb[i] = *reinterpret_cast<const uint32_t*>(st + b_srow + 32 * 4 * i) >> (8 * lk);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int pl = s ? plane1 : plane0;
+            v8i32_t af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u32x4 a = *reinterpret_cast<const u32x4*>(st + a_row + 32 * 64 * i + pl);
+                u32x4 b = *reinterpret_cast<const u32x4*>(st + b_row + 32 * 64 * i + pl);
+                // FP4 operands occupy the low four registers; the rest is unused
+                af[i] = __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1);
+                bf[i] = __builtin_shufflevector(b, b, 0, 1, 2, 3, -1, -1, -1, -1);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // operands (B, A): lane holds C[32 i + lr][32 j + 8 g + 4 lk + e]
+                    if (s == 0)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            (v8i_t)bf[j], (v8i_t)af[i], acc[i][j], 4, 4, 0, (int)sb[j], 0, (int)sa[i]);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            (v8i_t)bf[j], (v8i_t)af[i], acc[i][j], 4, 4, 2, (int)sb[j], 2, (int)sa[i]);
+                }
+        }
+    }
+    if (m0 + kTM <= p.M && n0 + kTN <= p.N)
+        store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f);
+    else
+        store_tile<false>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f);
+}
+
+hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                          const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                          bool out_bf16, void* c, int64_t ldc, hipStream_t s)
+{
+    GemmParams p;
+    p.M = M; p.N = N; p.K = K;
+    p.a_codes = a_codes; p.a_scales = a_scales;
+    p.b_codes = b_codes; p.b_scales = b_scales;
+    p.a_ts = nullptr; p.b_ts = nullptr;
+    p.c = static_cast<uint8_t*>(c);
+    p.ldc = ldc;
+    p.a2d = p.b2d = false;
+    p.out_bf16 = out_bf16;
+    const int esz = out_bf16 ? 2 : 4;
+    p.vec_out = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(c) % (4 * esz) == 0;
+    const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
+    hipFuncSetAttribute((const void*)k_gemm_mx, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+    hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)t), dim3(256), kMxLds, s, p);
     return hipGetLastError();
 }
 

@@ -76,6 +76,18 @@ struct GemmOperand {
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
                        const GemmOperand& B, bool out_bf16, void* c, int64_t ldc, hipStream_t s);
 
+// MXFP4 (E2M1 elements, E8M0 scale per 32 along the row): codes
+// [rows, cols/2], scales [rows, cols/32]; cols % 32 == 0.
+hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                int64_t cols, bool out_bf16, void* out, int64_t ld_out,
+                                hipStream_t s);
+// MXFP4 GEMM, NT: C[M, N] = A[M, K] B[N, K]^T, both K-major MXFP4, K % 128 == 0.
+hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                          const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                          bool out_bf16, void* c, int64_t ldc, hipStream_t s);
+
 hipError_t launch_fill_zero(void* c, bool bf16, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
 
 }  // namespace nvfp4

@@ -732,13 +732,15 @@ __global__ __launch_bounds__(256) void k_rht16_cols(const uint8_t* x, int64_t ld
 // ------------------------------------------------------------ dequantize
 
 // One thread per 8 consecutive elements of a row (one 32-bit code word).
-// v = RN32((val * e) * s_g); val * e is exact in FP32.
-template <bool kOutBF16, int kMode>  // kMode: 0 = 1D axis 1, 1 = 1D axis 0, 2 = 2D
+// v = RN32((val * e) * s_g); val * e is exact in FP32.  kMode 3 is MXFP4:
+// e = 2^(u - 127) from an E8M0 byte per 32 along the row and no tensor scale
+// (val * e is exact: the smallest product 0.5 * 2^-127 is an FP32 subnormal).
+template <bool kOutBF16, int kMode>  // kMode: 0 = 1D axis 1, 1 = 1D axis 0, 2 = 2D, 3 = MX
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* codes, const uint8_t* scales,
                                                  const float* ts, int64_t cols, uint32_t items,
                                                  FastDiv div, uint8_t* out, int64_t ld_out)
 {
-    const float s_g = *ts;
+    const float s_g = kMode == 3 ? 1.0f : *ts;
     const uint32_t stride = gridDim.x * blockDim.x;
     for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < items; t += stride) {
         uint32_t row = fdiv(t, div);
@@ -746,7 +748,12 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* codes, const uin
         int64_t c0 = (int64_t)cq * 8;
         uint32_t w = *reinterpret_cast<const uint32_t*>(codes + (int64_t)row * (cols / 2) + c0 / 2);
         float e[8];
-        if (kMode == 1) {
+        if (kMode == 3) {
+            const uint32_t u = scales[(int64_t)row * (cols / 32) + c0 / 32];
+            const float ev = __uint_as_float(u == 0 ? 0x00400000u : (u == 255 ? 0x7FC00000u : u << 23));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e[j] = ev;
+        } else if (kMode == 1) {
             u32x2 s = *reinterpret_cast<const u32x2*>(scales + (int64_t)(row / 16) * cols + c0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -794,6 +801,56 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* codes, const uin
 }
 
 // ------------------------------------------------------------ launchers
+
+// ------------------------------------------------------------ MXFP4
+// The power-of-two format the pages set NVFP4 against (guiahardware.es
+// "NVFP4: cos'e e come supera FP8 e BF16", section "Cos'e NVFP4"; chaitex.ru
+// "FP4", the comparison with the open standard), with the OCP MX v1.0 block
+// and scale rule: 32 consecutive elements of a row share the E8M0 scale
+// X = 2^(floor(log2 amax) - 2) (exponent clamped to -127 from below), and
+// each element is E2M1_RNE_sat(x / X) with its sign.  floor(log2 amax) is
+// the biased exponent field of amax minus 127 (0 for zero and subnormal
+// amax, which the clamp sends to X = 2^-127), so the scale byte is
+// max(field - 2, 0), and x / X = x * 2^(127 - u) exactly (a power of two).
+struct MxQuantParams {
+    const uint8_t* x;
+    int64_t ld;       // elements
+    uint32_t items;   // blocks of 32
+    FastDiv div;      // blocks per row
+    uint8_t* codes;   // [rows, cols/2]
+    uint8_t* scales;  // [rows, cols/32]
+};
+
+template <bool kBF16>
+__global__ __launch_bounds__(256) void k_mx_quant(MxQuantParams p)
+{
+    constexpr int esz = kBF16 ? 2 : 4;
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t b = blockIdx.x * blockDim.x + threadIdx.x; b < p.items; b += stride) {
+        const uint32_t row = fdiv(b, p.div);
+        const uint32_t cb = b - row * p.div.d;
+        const uint8_t* src = p.x + ((int64_t)row * p.ld + (int64_t)cb * 32) * esz;
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) load8<kBF16>(src + 8 * q * esz, v + 8 * q);
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+        const uint32_t field = __float_as_uint(amax) >> 23;
+        const uint32_t u = field > 2u ? field - 2u : 0u;
+        const float inv = __uint_as_float((254u - u) << 23);  // 2^(127 - u) = 1 / X
+        float y[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            y[i] = __uint_as_float(__float_as_uint(__builtin_fabsf(v[i]) * inv) |
+                                   (__float_as_uint(v[i]) & 0x80000000u));
+        u32x4 out;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) out[w] = pack8_rne(y + 8 * w);
+        *reinterpret_cast<u32x4*>(p.codes + (int64_t)b * 16) = out;
+        p.scales[b] = (uint8_t)u;
+    }
+}
 
 static int grid_for(uint64_t work_threads, int cap)
 {
@@ -997,6 +1054,35 @@ hipError_t launch_rht16(const void* x, bool bf16, int64_t rows, int64_t cols, in
             hipLaunchKernelGGL((k_rht16_cols<BF>), dim3(grid), dim3(256), 0, s, xb, ld_x, items,
                                div, mask, y, ld_y));
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s)
+{
+    MxQuantParams p;
+    p.x = static_cast<const uint8_t*>(x);
+    p.ld = ld;
+    p.items = (uint32_t)(rows * (cols / 32));
+    p.div = make_fastdiv((uint32_t)(cols / 32));
+    p.codes = codes;
+    p.scales = scales;
+    const int grid = grid_for(p.items, kGridCap);
+    NVFP4_DISPATCH_BOOL(bf16, BF, hipLaunchKernelGGL((k_mx_quant<BF>), dim3(grid), dim3(256), 0, s, p));
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                int64_t cols, bool out_bf16, void* out, int64_t ld_out,
+                                hipStream_t s)
+{
+    uint32_t items = (uint32_t)(rows * (cols / 8));
+    FastDiv div = make_fastdiv((uint32_t)(cols / 8));
+    int grid = grid_for(items, kGridCap);
+    NVFP4_DISPATCH_BOOL(out_bf16, OB,
+        hipLaunchKernelGGL((k_dequant<OB, 3>), dim3(grid), dim3(256), 0, s, codes, scales,
+                           (const float*)nullptr, cols, items, div, static_cast<uint8_t*>(out),
+                           ld_out));
     return hipGetLastError();
 }
 

@@ -32,7 +32,8 @@ def test_header_declares_the_abi():
                             "nvfp4_quantize_workspace_size", "nvfp4_quantize",
                             "nvfp4_amax_workspace_size", "nvfp4_amax", "nvfp4_swiglu_amax",
                             "nvfp4_rht16",
-                            "nvfp4_dequantize", "nvfp4_gemm"])
+                            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize",
+                            "nvfp4_mx_dequantize", "nvfp4_mx_gemm"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -162,3 +163,34 @@ def test_rht_and_dequant_validation(lib):
     assert lib.nvfp4_dequantize(FAKE, FAKE, FAKE, 24, 64, 1, 1, 0, FAKE, 64, None) == 2
     assert lib.nvfp4_dequantize(FAKE, FAKE, FAKE, 32, 64, 0, 1, 9, FAKE, 64, None) == 1
     assert lib.nvfp4_dequantize(MISALIGNED, FAKE, FAKE, 32, 64, 0, 1, 0, FAKE, 64, None) == 3
+
+
+def mxg(lib, **kw):
+    args = dict(M=64, N=64, K=256, ac=FAKE, asc=FAKE, bc=FAKE, bsc=FAKE, odt=0, c=FAKE, ldc=64,
+                stream=None)
+    args.update(kw)
+    return lib.nvfp4_mx_gemm(*args.values())
+
+
+def test_mx_validation(lib):
+    # quantize: x, dtype, rows, cols, ld, codes, scales, stream
+    assert lib.nvfp4_mx_quantize(FAKE, 2, 4, 64, 64, FAKE, FAKE, None) == 1
+    assert lib.nvfp4_mx_quantize(FAKE, 0, 4, 48, 48, FAKE, FAKE, None) == 2   # cols % 32
+    assert lib.nvfp4_mx_quantize(FAKE, 0, 4, 64, 32, FAKE, FAKE, None) == 2   # ld < cols
+    assert lib.nvfp4_mx_quantize(MISALIGNED, 0, 4, 64, 64, FAKE, FAKE, None) == 3
+    assert lib.nvfp4_mx_quantize(FAKE, 0, 4, 64, 68, FAKE, FAKE, None) == 3   # 136-byte rows
+    assert lib.nvfp4_mx_quantize(FAKE, 0, 4, 64, 64, None, FAKE, None) == 1
+    assert lib.nvfp4_mx_quantize(FAKE, 0, 0, 64, 64, None, None, None) == 0
+    assert lib.nvfp4_mx_dequantize(FAKE, FAKE, 4, 48, 0, FAKE, 48, None) == 2
+    assert lib.nvfp4_mx_dequantize(FAKE, FAKE, 4, 64, 5, FAKE, 64, None) == 1
+    assert lib.nvfp4_mx_dequantize(MISALIGNED, FAKE, 4, 64, 0, FAKE, 64, None) == 3
+    assert mxg(lib, K=192) == 2                      # K % 128
+    assert mxg(lib, ldc=32) == 2
+    assert mxg(lib, odt=3) == 1
+    assert mxg(lib, M=-1) == 1
+    assert mxg(lib, c=ODD) == 3
+    assert mxg(lib, ac=MISALIGNED) == 3
+    assert mxg(lib, bsc=None) == 1
+    assert mxg(lib, K=1 << 24) == 5                  # 256 rows of codes past 2^31 bytes
+    assert mxg(lib, M=0) == 0
+
