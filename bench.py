@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense FP16/BF16 MFMA
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 MFMA
 
 
 def parse():
@@ -51,6 +52,8 @@ def parse():
     ap.add_argument("--cpu-sample-rows", type=int, default=64)
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 1 GiB copy kernel (for HBM counter calibration)")
+    ap.add_argument("--mx-only", action="store_true",
+                    help="time only the MXFP4 comparison path and print its JSON object")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode-shape GEMMs and print their JSON object "
                          "(for profiling the skinny kernel; not the bench line)")
@@ -122,6 +125,12 @@ def main():
     torch.cuda.set_device(dev)
     if args.decode_only:
         print(json.dumps({"decode": decode_bench(torch, nv, workloads)}), flush=True)
+        return
+    if args.mx_only:
+        cfg = workloads.LLAMA8B
+        X = workloads.activations(cfg["tokens"], cfg["hidden"], cfg["x_seed"], device="cuda")
+        W_gu = workloads.weights(2 * cfg["ffn"], cfg["hidden"], cfg["wgu_seed"], device="cuda")
+        print(json.dumps({"mxfp4": mxfp4_bench(torch, nv, X, W_gu)}), flush=True)
         return
     cfg = workloads.LLAMA8B
     T, D, Fh = cfg["tokens"], cfg["hidden"], cfg["ffn"]
@@ -281,6 +290,7 @@ def main():
     del bufs
     torch.cuda.empty_cache()
     line["decode"] = decode_bench(torch, nv, workloads)
+    line["mxfp4"] = mxfp4_bench(torch, nv, X, W_gu)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, torch, nv, workloads, X, W_gu)
@@ -341,6 +351,49 @@ def decode_bench(torch, nv, workloads):
             "timing": "mean of 40 back-to-back launches over 4 weight copies (528 MB, "
                       "cache-cold each launch); us_isolated: median of 10 single launches "
                       "after a cache-evicting read", **out}
+
+
+def mxfp4_bench(torch, nv, X, W):
+    """The power-of-two-scaled MXFP4 format the pages compare NVFP4 with, on
+    the step's first GEMM (X [32768, 4096] x W_gu [28672, 4096]^T): GEMM time
+    on the native scaled FP4 MFMA against the same GEMM in NVFP4 (f16 MFMA),
+    quantize bandwidth, and each format's mean squared error on X."""
+    T, D = X.shape
+    N = W.shape[0]
+    reps = 5
+    y = torch.empty(T, N, dtype=torch.bfloat16, device="cuda")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        fn()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    xm, wm = nv.mx_quantize(X), nv.mx_quantize(W)
+    t_q = timed(lambda: nv.mx_quantize(X, out=xm))
+    t_mx = timed(lambda: nv.mx_gemm(xm, wm, out=y))
+    xn, wn = nv.quantize(X), nv.quantize(W, block2d=True)
+    t_nv = timed(lambda: nv.gemm("NT", xn, wn, out=y))
+    del y
+    fl = 2.0 * T * N * D
+    xf = X.float()
+    mse_mx = ((nv.mx_dequantize(xm, torch.float32) - xf) ** 2).mean().item()
+    mse_nv = ((nv.dequantize(xn, torch.float32) - xf) ** 2).mean().item()
+    qb = T * D * (2 + 0.5 + 1 / 32)
+    return {"gemm": "%d x %d x %d NT, BF16 out" % (T, N, D),
+            "kernel": "k_gemm_mx (v_mfma_scale_f32_32x32x64_f8f6f4, FP4 x FP4)",
+            "mx_gemm_ms": round(t_mx, 4), "mx_gemm_tflops": round(fl / t_mx / 1e9, 1),
+            "mx_frac_of_fp4_peak": round(fl / t_mx / 1e9 / MFMA_FP4_PEAK_TFLOPS, 4),
+            "nvfp4_gemm_ms": round(t_nv, 4), "nvfp4_gemm_tflops": round(fl / t_nv / 1e9, 1),
+            "mx_quantize_GBps": round(qb / (t_q * 1e-3) / 1e9, 1),
+            "mse_on_X": {"mxfp4": mse_mx, "nvfp4": mse_nv,
+                         "nvfp4_less_error": round(1 - mse_nv / mse_mx, 4)}}
 
 
 def cpu_baseline(args, torch, nv, workloads, X, W_gu):
