@@ -39,6 +39,7 @@ struct GemmParams {
     int64_t ldc;
     bool a2d, b2d, out_bf16;
     bool vec_out;  // C rows allow 8-byte (BF16) / 16-byte (FP32) stores
+    bool vec16;    // C base and row pitch are 16-byte aligned (whole-line epilogue)
 };
 
 // 8x8 nibble transpose: in[k] holds element (k, j) in nibble j; out[j] gets
@@ -398,6 +399,63 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, float16_t (&acc)
                     }
                 }
             }
+    }
+}
+
+// Epilogue of a full 256 x 256 tile through LDS: each wave writes 32 rows of
+// its 128 x 128 sub-tile (the element mapping of store_tile) into a private
+// LDS buffer, then stores whole rows, 16 bytes per lane, so each store
+// instruction covers whole 128-byte lines of C.  The direct path writes every
+// line in 16-byte pieces from eight different instructions; with one
+// workgroup per CU that path measured 3-4x slower than the same bytes written
+// whole (e.g. 0.70 against 0.24 ms for a 16384 x 16384 x 128 GEMM).  The
+// caller has finished all LDS accesses of the main loop in every wave
+// (barrier) and has no copy into LDS in flight; C rows are 16-byte aligned.
+template <bool kBF16>
+__device__ __forceinline__ void store_tile_lds(const GemmParams& p, float16_t (&acc)[4][4],
+                                               int64_t m0, int64_t n0, int wm, int wn, int lr,
+                                               int lk, float sab, uint8_t* lds)
+{
+    constexpr int esz = kBF16 ? 2 : 4;
+    constexpr int kRowB = 128 * esz;
+    constexpr int kPitch = kRowB + 16;
+    constexpr int kLanesPerRow = kRowB / 16;
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint8_t* wl = lds + wave * 32 * kPitch;
+    const int rr = lane / kLanesPerRow, cc = lane % kLanesPerRow;
+    uint8_t* cbase = p.c + ((m0 + wm * 128) * p.ldc + n0 + wn * 128) * esz + 16 * cc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint8_t* d = wl + lr * kPitch + (32 * j + 8 * g + 4 * lk) * esz;
+                if (kBF16) {
+                    uint32_t h[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint32_t u = __float_as_uint(acc[i][j][4 * g + e] * sab);
+                        h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                    }
+                    u32x2 w;
+                    w[0] = h[0] | (h[1] << 16);
+                    w[1] = h[2] | (h[3] << 16);
+                    *reinterpret_cast<u32x2*>(d) = w;
+                } else {
+                    float4_t w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = acc[i][j][4 * g + e] * sab;
+                    *reinterpret_cast<float4_t*>(d) = w;
+                }
+            }
+#pragma unroll
+        for (int r0 = 0; r0 < 32; r0 += kRowsPerStore) {
+            const int r = r0 + rr;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(wl + r * kPitch + 16 * cc);
+            *reinterpret_cast<u32x4*>(cbase + (int64_t)(32 * i + r) * p.ldc * esz) = v;
+        }
     }
 }
 
@@ -813,7 +871,17 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 #undef KK_SCALES_I
 #undef KK_N
     if (m0 + kTM <= p.M && n0 + kTN <= p.N)
-        store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk, (*p.a_ts) * (*p.b_ts));
+        if (p.vec16) {
+            NVFP4_WAIT_VMCNT(0);
+            NVFP4_WAIT_LGKMCNT0();
+            __builtin_amdgcn_s_barrier();
+            if (p.out_bf16)
+                store_tile_lds<true>(p, acc, m0, n0, wm, wn, lr, lk, (*p.a_ts) * (*p.b_ts), lds);
+            else
+                store_tile_lds<false>(p, acc, m0, n0, wm, wn, lr, lk, (*p.a_ts) * (*p.b_ts), lds);
+        } else {
+            store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk, (*p.a_ts) * (*p.b_ts));
+        }
     else
         store_tile<false>(p, acc, m0, n0, wm, wn, lr, lk, (*p.a_ts) * (*p.b_ts));
 }
@@ -1064,6 +1132,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     p.out_bf16 = out_bf16;
     const int esz = out_bf16 ? 2 : 4;
     p.vec_out = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(c) % (4 * esz) == 0;
+    p.vec16 = (ldc * esz) % 16 == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0;
     // decode-style shapes (M <= 64): stream the weights with a dedicated
     // kernel; its K chunk must divide K
     const int skinny_kc = 512;
@@ -1267,10 +1336,19 @@ __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p)
                 }
         }
     }
-    if (m0 + kTM <= p.M && n0 + kTN <= p.N)
-        store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f);
-    else
+    if (m0 + kTM <= p.M && n0 + kTN <= p.N) {
+        if (p.vec16) {
+            NVFP4_WAIT_VMCNT(0);
+            NVFP4_WAIT_LGKMCNT0();
+            __builtin_amdgcn_s_barrier();
+            if (p.out_bf16) store_tile_lds<true>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f, lds);
+            else store_tile_lds<false>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f, lds);
+        } else {
+            store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f);
+        }
+    } else {
         store_tile<false>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f);
+    }
 }
 
 hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
@@ -1288,6 +1366,7 @@ hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_code
     p.out_bf16 = out_bf16;
     const int esz = out_bf16 ? 2 : 4;
     p.vec_out = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(c) % (4 * esz) == 0;
+    p.vec16 = (ldc * esz) % 16 == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0;
     const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
     hipFuncSetAttribute((const void*)k_gemm_mx, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
     hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)t), dim3(256), kMxLds, s, p);
