@@ -417,46 +417,47 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams& p, float16_t (&
                                                int lk, float sab, uint8_t* lds)
 {
     constexpr int esz = kBF16 ? 2 : 4;
-    constexpr int kRowB = 128 * esz;
-    constexpr int kPitch = kRowB + 16;
-    constexpr int kLanesPerRow = kRowB / 16;
-    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    constexpr int kJ = kBF16 ? 4 : 2;            // 32-column blocks per pass: 256 bytes a row
+    constexpr int kPitch = 256 + 16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint8_t* wl = lds + wave * 32 * kPitch;
-    const int rr = lane / kLanesPerRow, cc = lane % kLanesPerRow;
+    uint8_t* wl = lds + wave * 32 * kPitch;      // 8704 bytes per wave
+    const int rr = lane >> 4, cc = lane & 15;    // 16 lanes a row, 4 rows a store
     uint8_t* cbase = p.c + ((m0 + wm * 128) * p.ldc + n0 + wn * 128) * esz + 16 * cc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int jp = 0; jp < 4 / kJ; ++jp) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint8_t* d = wl + lr * kPitch + (32 * j + 8 * g + 4 * lk) * esz;
-                if (kBF16) {
-                    uint32_t h[4];
+            for (int jj = 0; jj < kJ; ++jj)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        uint32_t u = __float_as_uint(acc[i][j][4 * g + e] * sab);
-                        h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                for (int g = 0; g < 4; ++g) {
+                    const int j = jp * kJ + jj;
+                    uint8_t* d = wl + lr * kPitch + (32 * jj + 8 * g + 4 * lk) * esz;
+                    if (kBF16) {
+                        uint32_t h[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            uint32_t u = __float_as_uint(acc[i][j][4 * g + e] * sab);
+                            h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // RNE
+                        }
+                        u32x2 w;
+                        w[0] = h[0] | (h[1] << 16);
+                        w[1] = h[2] | (h[3] << 16);
+                        *reinterpret_cast<u32x2*>(d) = w;
+                    } else {
+                        float4_t w;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[e] = acc[i][j][4 * g + e] * sab;
+                        *reinterpret_cast<float4_t*>(d) = w;
                     }
-                    u32x2 w;
-                    w[0] = h[0] | (h[1] << 16);
-                    w[1] = h[2] | (h[3] << 16);
-                    *reinterpret_cast<u32x2*>(d) = w;
-                } else {
-                    float4_t w;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = acc[i][j][4 * g + e] * sab;
-                    *reinterpret_cast<float4_t*>(d) = w;
                 }
-            }
 #pragma unroll
-        for (int r0 = 0; r0 < 32; r0 += kRowsPerStore) {
-            const int r = r0 + rr;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(wl + r * kPitch + 16 * cc);
-            *reinterpret_cast<u32x4*>(cbase + (int64_t)(32 * i + r) * p.ldc * esz) = v;
+            for (int r0 = 0; r0 < 32; r0 += 4) {
+                const int r = r0 + rr;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(wl + r * kPitch + 16 * cc);
+                *reinterpret_cast<u32x4*>(cbase + (int64_t)(32 * i + r) * p.ldc * esz + jp * 256) = v;
+            }
         }
-    }
 }
 
 template <bool kAK, bool kBK, bool kFull>
