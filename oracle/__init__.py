@@ -84,6 +84,10 @@ def lib():
         L.oracle_gemm_pairs.argtypes = [ctypes.c_int, c_i64, c_i64, c_i64, c_vp, c_vp,
                                         ctypes.c_float, ctypes.c_int, c_vp, c_vp, ctypes.c_float,
                                         ctypes.c_int, c_i64, c_vp, c_vp, c_vp, c_vp]
+        L.oracle_gemm_w4a16_pairs.restype = ctypes.c_int
+        L.oracle_gemm_w4a16_pairs.argtypes = [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp,
+                                              ctypes.c_float, ctypes.c_int, c_i64, c_vp, c_vp,
+                                              c_vp, c_vp]
         L.oracle_e8m0_value.restype = ctypes.c_double
         L.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
         L.oracle_mx_scale_code.restype = ctypes.c_uint8
@@ -235,6 +239,30 @@ def gemm_full(layout: str, M: int, N: int, K: int, a, b):
     """Full M x N reference (small sizes only)."""
     mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     ref, ab = gemm_pairs(layout, M, N, K, a, b, mm.ravel(), nn.ravel())
+    return ref.reshape(M, N), ab.reshape(M, N)
+
+
+def gemm_w4a16_pairs(M: int, N: int, K: int, a_bf16: np.ndarray, b, ms, ns):
+    """NT with BF16 activations a [M, K] (uint16 bit patterns) and an NVFP4
+    weight b = (codes, scales, s_g, block2d) stored [N, K].  Returns (ref fp64,
+    abs fp64) at (ms, ns)."""
+    bc, bsc, bts, b2d = b
+    a = np.ascontiguousarray(a_bf16, dtype=np.uint16)
+    bc = np.ascontiguousarray(bc, dtype=np.uint8)
+    bsc = np.ascontiguousarray(bsc, dtype=np.uint8)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    ref = np.zeros(len(ms), dtype=np.float64)
+    ab = np.zeros(len(ms), dtype=np.float64)
+    if lib().oracle_gemm_w4a16_pairs(M, N, K, _ptr(a), K, _ptr(bc), _ptr(bsc), bts, int(b2d),
+                                     len(ms), _ptr(ms), _ptr(ns), _ptr(ref), _ptr(ab)):
+        raise ValueError("oracle_gemm_w4a16_pairs: bad shape")
+    return ref, ab
+
+
+def gemm_w4a16_full(M: int, N: int, K: int, a_bf16: np.ndarray, b):
+    mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ref, ab = gemm_w4a16_pairs(M, N, K, a_bf16, b, mm.ravel(), nn.ravel())
     return ref.reshape(M, N), ab.reshape(M, N)
 
 

@@ -541,6 +541,41 @@ int oracle_gemm_pairs(int layout, int64_t M, int64_t N, int64_t K, const uint8_t
     return 0;
 }
 
+/*
+ * Weight-only NVFP4 GEMM reference (BF16 activations, NVFP4 weights), NT:
+ * A stored [M, K] as BF16 bit patterns with row pitch lda, B an NVFP4 tensor
+ * stored [N, K] (1D blocks along K, or 2D).  The juejin.cn page on NVFP4
+ * (item 3, ecosystem support) describes models trained at higher precision
+ * being quantized to NVFP4 for inference, and "FP4" (chaitex.ru, item 1 of
+ * the scaling scheme) quantizes the weight matrix in 16-element blocks; with
+ * the activations left in BF16 the product is
+ *   ref[p] = s_B * sum_k x[m,k] * (val*e)_B[n,k]
+ * in FP64 (each product is exact) and absref[p] = s_B * sum_k |...|.
+ */
+int oracle_gemm_w4a16_pairs(int64_t M, int64_t N, int64_t K, const uint16_t* a, int64_t lda,
+                            const uint8_t* b_codes, const uint8_t* b_scales, float b_ts,
+                            int b_block2d, int64_t npairs, const int64_t* ms, const int64_t* ns,
+                            double* ref, double* absref)
+{
+    if (M < 0 || N < 0 || K < 0 || lda < K) return -1;
+    operand_t B;
+    B.codes = b_codes; B.scales = b_scales; B.block2d = b_block2d;
+    B.rows = N; B.cols = K; B.k_is_row = 0; B.axis = 1;
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t p = 0; p < npairs; ++p) {
+        double s = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double x = (double)load_elem(a, ORACLE_DT_BF16, lda, ms[p], k);
+            double t = x * op_value(&B, ns[p], k);
+            s += t;
+            sa += fabs(t);
+        }
+        ref[p] = (double)b_ts * s;
+        absref[p] = (double)b_ts * sa;
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* MXFP4: the power-of-two-scaled format the pages contrast NVFP4 with */
 /* ------------------------------------------------------------------ */
