@@ -239,6 +239,29 @@ nvfp4_status nvfp4_gemm(nvfp4_layout layout, int64_t M, int64_t N, int64_t K,
                         void* c, int64_t ldc, void* stream);
 
 /*
+ * Weight-only NVFP4 GEMM for decode shapes (BF16 activations, NVFP4 weights):
+ *   C[m, n] = s_B * sum_k a[m, k] (q*e)_B[n, k],  FP32 accumulation.
+ * Source: the juejin.cn page on NVFP4 (item 3: models trained at higher
+ * precision quantized to NVFP4 and served by inference frameworks) and
+ * chaitex.ru "FP4" (item 1 of the scaling scheme: the weight matrix in
+ * 16-element blocks with E4M3 scales, a 32-bit tensor scale).  NT only:
+ *   a, lda            BF16 activations [M, K], a[m*lda + k]
+ *   b_codes/b_scales  NVFP4 weight stored [N, K] (1D blocks along K, or 2D),
+ *   /b_tensor_scale   the layout of nvfp4_quantize
+ *   c, ldc, out_dtype C[m*ldc + n], BF16 (RNE of the FP32 result) or FP32
+ * The weight's block scale times its element is exact in BF16 (at most 6
+ * significant bits), so every product is exact and only the accumulation
+ * order differs from an FP64 reference.
+ * Shape rules: 0 <= M <= 64 (decode; NVFP4_ERR_UNSUPPORTED above), K % 512
+ * == 0, lda >= K with 16-byte aligned rows, N * K / 2 < 2^31, N % 16 == 0 for
+ * a 2D weight.  K == 0 writes zeros.
+ */
+nvfp4_status nvfp4_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
+                              const uint8_t* b_codes, const uint8_t* b_scales,
+                              const float* b_tensor_scale, nvfp4_block b_block,
+                              nvfp4_dtype out_dtype, void* c, int64_t ldc, void* stream);
+
+/*
  * MXFP4, the power-of-two-scaled format the pages compare NVFP4 with
  * ("NVFP4: cos'e e come supera FP8 e BF16", guiahardware.es, section "Cos'e
  * NVFP4": NVFP4's E4M3 scales against power-of-two scaling such as MXFP4;

@@ -36,7 +36,7 @@ EXPORTS = ("nvfp4_version", "nvfp4_status_string", "nvfp4_quantize_workspace_siz
            "nvfp4_quantize", "nvfp4_amax_workspace_size", "nvfp4_amax",
            "nvfp4_swiglu_amax", "nvfp4_rht16",
            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize",
-           "nvfp4_mx_gemm")
+           "nvfp4_mx_gemm", "nvfp4_gemm_w4a16")
 
 
 class NVFP4Error(RuntimeError):
@@ -73,6 +73,8 @@ def _load():
     L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, ci, ci, ci, vp, i64, vp]
     L.nvfp4_gemm.restype = ci
     L.nvfp4_gemm.argtypes = [ci, i64, i64, i64, vp, vp, vp, ci, vp, vp, vp, ci, ci, vp, i64, vp]
+    L.nvfp4_gemm_w4a16.restype = ci
+    L.nvfp4_gemm_w4a16.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, ci, ci, vp, i64, vp]
     L.nvfp4_mx_quantize.restype = ci
     L.nvfp4_mx_quantize.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp]
     L.nvfp4_mx_dequantize.restype = ci
@@ -157,6 +159,13 @@ def nvfp4_gemm(layout, M, N, K, a_codes, a_scales, a_tensor_scale, a_block, b_co
     return lib.nvfp4_gemm(layout, M, N, K, _p(a_codes), _p(a_scales), _p(a_tensor_scale), a_block,
                           _p(b_codes), _p(b_scales), _p(b_tensor_scale), b_block, out_dtype,
                           _p(c), ldc, _stream(stream))
+
+
+def nvfp4_gemm_w4a16(M, N, K, a, lda, b_codes, b_scales, b_tensor_scale, b_block, out_dtype, c,
+                     ldc, stream=None) -> int:
+    return lib.nvfp4_gemm_w4a16(M, N, K, _p(a), lda, _p(b_codes), _p(b_scales),
+                                _p(b_tensor_scale), b_block, out_dtype, _p(c), ldc,
+                                _stream(stream))
 
 
 def nvfp4_mx_quantize(x, x_dtype, rows, cols, ld_x, codes, scales, stream=None) -> int:
@@ -315,6 +324,21 @@ def gemm(layout: str, a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16,
     _check("nvfp4_gemm", nvfp4_gemm(
         LAYOUT[layout], M, N, K, a.codes, a.scales, a.tensor_scale,
         BLOCK_2D if a.block2d else BLOCK_1D, b.codes, b.scales, b.tensor_scale,
+        BLOCK_2D if b.block2d else BLOCK_1D, _dtype_code(out), out, out.stride(0)))
+    return out
+
+
+def gemm_w4a16(a: torch.Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """Weight-only decode GEMM, NT: a BF16 [M, K] (M <= 64), b NVFP4 [N, K]."""
+    assert a.dim() == 2 and a.is_cuda and a.dtype == torch.bfloat16 and a.stride(1) == 1
+    M, K = a.shape
+    N = b.rows
+    assert b.cols == K and b.axis == 1
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=a.device)
+    _check("nvfp4_gemm_w4a16", nvfp4_gemm_w4a16(
+        M, N, K, a, a.stride(0), b.codes, b.scales, b.tensor_scale,
         BLOCK_2D if b.block2d else BLOCK_1D, _dtype_code(out), out, out.stride(0)))
     return out
 

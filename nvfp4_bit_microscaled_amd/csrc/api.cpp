@@ -335,4 +335,31 @@ nvfp4_status nvfp4_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_cod
                                    out_dtype == NVFP4_DTYPE_BF16, c, ldc, s));
 }
 
+nvfp4_status nvfp4_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
+                              const uint8_t* b_codes, const uint8_t* b_scales,
+                              const float* b_tensor_scale, nvfp4_block b_block,
+                              nvfp4_dtype out_dtype, void* c, int64_t ldc, void* stream)
+{
+    if (b_block != NVFP4_BLOCK_1D && b_block != NVFP4_BLOCK_2D) return NVFP4_ERR_INVALID_ARG;
+    if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_INVALID_ARG;
+    if (ldc < N || lda < K) return NVFP4_ERR_SHAPE;
+    if (K % 512) return NVFP4_ERR_SHAPE;
+    if (b_block == NVFP4_BLOCK_2D && N % 16) return NVFP4_ERR_LAYOUT;
+    if (M > 64) return NVFP4_ERR_UNSUPPORTED;
+    if ((uint64_t)N * (uint64_t)K / 2 >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return NVFP4_OK;
+    if (!c) return NVFP4_ERR_INVALID_ARG;
+    const size_t esz = out_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    if ((reinterpret_cast<uintptr_t>(c) & (esz - 1)) != 0) return NVFP4_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) return from_hip(launch_fill_zero(c, out_dtype == NVFP4_DTYPE_BF16, M, N, ldc, s));
+    if (!a || !b_codes || !b_scales || !b_tensor_scale) return NVFP4_ERR_INVALID_ARG;
+    if (!aligned16(a) || ((size_t)lda * 2) % 16 || !aligned16(b_codes) || !aligned16(b_scales))
+        return NVFP4_ERR_ALIGN;
+    GemmOperand B{b_codes, b_scales, b_tensor_scale, b_block == NVFP4_BLOCK_2D, true};
+    return from_hip(launch_gemm_w4a16(M, N, K, static_cast<const uint16_t*>(a), lda, B,
+                                      out_dtype == NVFP4_DTYPE_BF16, c, ldc, s));
+}
+
 }  // extern "C"

@@ -26,6 +26,7 @@ namespace nvfp4 {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 struct GemmParams {
     int64_t M, N, K;
@@ -39,6 +40,8 @@ struct GemmParams {
     int64_t ldc;
     bool a2d, b2d, out_bf16;
     bool vec_out;  // C rows allow 8-byte (BF16) / 16-byte (FP32) stores
+    const uint16_t* a_bf16;  // weight-only GEMM: BF16 activations [M, K], row pitch lda
+    int64_t lda;
     bool vec16;    // C base and row pitch are 16-byte aligned (whole-line epilogue)
 };
 
@@ -287,6 +290,25 @@ __device__ __forceinline__ half8_t dequant_word(uint32_t w, _Float16 e)
 // the 8 XCDs, so ids are first regrouped so each XCD owns a contiguous band
 // of tiles; bands are walked in groups of 8 tile rows, column by column, so
 // the A rows of a group and the B columns just visited stay in that XCD's L2.
+// Eight E2M1 codes times the block scale e as BF16, for the weight-only
+// (BF16-activation) GEMM.  val * e needs at most 6 significant bits, so it
+// is exact in FP32 and its low 16 bits are zero: the BF16 value is the upper
+// half, taken with one v_perm per pair.
+__device__ __forceinline__ bf16x8_t dequant_word_bf16(uint32_t w, float e)
+{
+    u32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float2_t v = q == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
+                   : q == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
+                   : q == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
+                            : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        r[q] = __builtin_amdgcn_perm(__float_as_uint(v[1] * e), __float_as_uint(v[0] * e),
+                                     0x07060302u);
+    }
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
 __device__ __forceinline__ void tile_of(uint32_t bid, uint32_t nbm, uint32_t nbn, uint32_t& tm,
                                         uint32_t& tn)
 {
@@ -909,7 +931,10 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 // ---------------------------------------------------------------------------
 constexpr int kSkN = 64;  // output columns per workgroup
 
-template <int KC, int RMAX>
+// kA16: the weight-only variant, BF16 activations (no activation scales;
+// 32-element pieces copied to LDS as they are), weights dequantized to BF16
+// and v_mfma_f32_16x16x32_bf16.
+template <int KC, int RMAX, bool kA16>
 __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
 {
     constexpr int kSteps = KC / 128;                 // B steps per chunk
@@ -951,8 +976,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
     // B: lane g owns the contiguous quarter kc + g KC/4 .. +KC/4 of each chunk,
     // 32 codes per step, so its scale bytes for the chunk are one contiguous
     // run of kSB bytes
-    u32x4 ac[kAPer], bc[kSteps], bn[kSteps];
-    uint32_t as[kAPer];
+    u32x4 ac[kA16 ? 1 : kAPer], bc[kSteps], bn[kSteps];
+    uint32_t as[kA16 ? 1 : kAPer];
+    u32x4 aw[kA16 ? kAPer : 1][4];  // BF16 pieces (64 bytes each)
     uint32_t bs[kSB / 4], bsn[kSB / 4];
     auto load_a = [&](int64_t kc) {
 #pragma unroll
@@ -962,10 +988,16 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
             int64_t mc = m < p.M ? m : p.M - 1;
             int64_t k = kc + 32 * c;
             k = k < K ? k : K - 32;  // the prefetch past the last chunk reads a valid piece
-            ac[i] = *reinterpret_cast<const u32x4*>(p.a_codes + mc * (K / 2) + k / 2);
-            const uint8_t* sp =
-                p.a_scales + (p.a2d ? (mc / 16) * lds_b : mc * lds_b) + k / 16;
-            as[i] = *reinterpret_cast<const uint16_t*>(sp);
+            if constexpr (kA16) {
+                const u32x4* src = reinterpret_cast<const u32x4*>(p.a_bf16 + mc * p.lda + k);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) aw[i][q] = src[q];
+            } else {
+                ac[i] = *reinterpret_cast<const u32x4*>(p.a_codes + mc * (K / 2) + k / 2);
+                const uint8_t* sp =
+                    p.a_scales + (p.a2d ? (mc / 16) * lds_b : mc * lds_b) + k / 16;
+                as[i] = *reinterpret_cast<const uint16_t*>(sp);
+            }
         }
     };
     auto load_b = [&](__amdgpu_buffer_rsrc_t c_rsrc, __amdgpu_buffer_rsrc_t s_rsrc, int kc,
@@ -1005,12 +1037,17 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
         for (int i = 0; i < kAPer; ++i) {
             int idx = threadIdx.x + 256 * i;
             int m = idx / (KC / 32), c = idx % (KC / 32);
-            half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as[i], 1.0f, false);
             const int kl = 32 * c;  // K offset inside the chunk
             uint8_t* dst = lds + m * kRow + (kl / kQ) * kQStride + (kl % kQ) * 2;
+            if constexpr (kA16) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<half8_t*>(dst + 16 * q) = dequant_word(ac[i][q], e2[q >> 1]);
+                for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(dst + 16 * q) = aw[i][q];
+            } else {
+                half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as[i], 1.0f, false);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<half8_t*>(dst + 16 * q) = dequant_word(ac[i][q], e2[q >> 1]);
+            }
         }
         NVFP4_WAIT_LGKMCNT0();
         __builtin_amdgcn_s_barrier();
@@ -1036,13 +1073,26 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
                         lds + (16 * r + lr) * kRow + g * kQStride + (32 * st + 8 * s) * 2);
             // scale bytes 2 st, 2 st + 1 of the lane's run
             const uint32_t sw = cs[st >> 1] >> (16 * (st & 1));
-            half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+            if constexpr (kA16) {
+                const float e0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
+                const float e1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                half8_t bf = dequant_word(cb[st][s], e2[s >> 1]);
+                for (int s = 0; s < 4; ++s) {
+                    bf16x8_t bf = dequant_word_bf16(cb[st][s], s < 2 ? e0 : e1);
 #pragma unroll
-                for (int r = 0; r < RMAX; ++r)
-                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s][r], bf, acc[r], 0, 0, 0);
+                    for (int r = 0; r < RMAX; ++r)
+                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, af[s][r]), bf, acc[r], 0, 0, 0);
+                }
+            } else {
+                half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    half8_t bf = dequant_word(cb[st][s], e2[s >> 1]);
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r)
+                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s][r], bf, acc[r], 0, 0, 0);
+                }
             }
             __builtin_amdgcn_sched_group_barrier(0x100, 4 * RMAX, 0);   // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);         // scale + B dequant
@@ -1065,7 +1115,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
         if (kc + 2 * KC >= (int)K) break;
     }
     // lane holds C[16 r + 4 g + j][n] in acc[r][j]
-    const float sab = (*p.a_ts) * (*p.b_ts);
+    const float sab = kA16 ? *p.b_ts : (*p.a_ts) * (*p.b_ts);
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
 #pragma unroll
@@ -1124,6 +1174,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
 {
     GemmParams p;
     p.M = M; p.N = N; p.K = K;
+    p.a_bf16 = nullptr; p.lda = 0;
     p.a_codes = A.codes; p.a_scales = A.scales; p.a_ts = A.ts;
     p.b_codes = B.codes; p.b_scales = B.scales; p.b_ts = B.ts;
     p.c = static_cast<uint8_t*>(c);
@@ -1142,7 +1193,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
         dim3 g((unsigned)((N + kSkN - 1) / kSkN));
 #define NVFP4_SKINNY(KC, RMAX)                                                                 \
     {                                                                                          \
-        auto kern = k_gemm_skinny<KC, RMAX>;                                                   \
+        auto kern = k_gemm_skinny<KC, RMAX, false>;                                            \
         const int lds = RMAX * 16 * (KC * 2 + 64);                                             \
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
@@ -1358,6 +1409,7 @@ hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_code
 {
     GemmParams p;
     p.M = M; p.N = N; p.K = K;
+    p.a_bf16 = nullptr; p.lda = 0;
     p.a_codes = a_codes; p.a_scales = a_scales;
     p.b_codes = b_codes; p.b_scales = b_scales;
     p.a_ts = nullptr; p.b_ts = nullptr;
@@ -1371,6 +1423,37 @@ hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_code
     const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
     hipFuncSetAttribute((const void*)k_gemm_mx, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
     hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)t), dim3(256), kMxLds, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a16(int64_t M, int64_t N, int64_t K, const uint16_t* a, int64_t lda,
+                             const GemmOperand& B, bool out_bf16, void* c, int64_t ldc,
+                             hipStream_t s)
+{
+    GemmParams p;
+    p.M = M; p.N = N; p.K = K;
+    p.a_codes = nullptr; p.a_scales = nullptr; p.a_ts = nullptr;
+    p.b_codes = B.codes; p.b_scales = B.scales; p.b_ts = B.ts;
+    p.c = static_cast<uint8_t*>(c);
+    p.ldc = ldc;
+    p.a2d = false;
+    p.b2d = B.block2d != 0;
+    p.out_bf16 = out_bf16;
+    p.vec_out = false;
+    p.a_bf16 = a;
+    p.lda = lda;
+    dim3 g((unsigned)((N + kSkN - 1) / kSkN));
+#define NVFP4_SKINNY16(RMAX)                                                                   \
+    {                                                                                          \
+        auto kern = k_gemm_skinny<512, RMAX, true>;                                            \
+        const int lds = RMAX * 16 * (512 * 2 + 64);                                            \
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
+        hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
+    }
+    if (M <= 16) NVFP4_SKINNY16(1)
+    else if (M <= 32) NVFP4_SKINNY16(2)
+    else NVFP4_SKINNY16(4)
+#undef NVFP4_SKINNY16
     return hipGetLastError();
 }
 

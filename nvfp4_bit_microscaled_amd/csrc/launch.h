@@ -88,6 +88,12 @@ hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_code
                           const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
                           bool out_bf16, void* c, int64_t ldc, hipStream_t s);
 
+// Weight-only GEMM for decode shapes, NT: C[M, N] = A[M, K] B[N, K]^T with
+// BF16 activations (row pitch lda) and an NVFP4 weight; M <= 64, K % 512 == 0.
+hipError_t launch_gemm_w4a16(int64_t M, int64_t N, int64_t K, const uint16_t* a, int64_t lda,
+                             const GemmOperand& B, bool out_bf16, void* c, int64_t ldc,
+                             hipStream_t s);
+
 hipError_t launch_fill_zero(void* c, bool bf16, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
 
 }  // namespace nvfp4

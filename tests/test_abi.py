@@ -33,7 +33,7 @@ def test_header_declares_the_abi():
                             "nvfp4_amax_workspace_size", "nvfp4_amax", "nvfp4_swiglu_amax",
                             "nvfp4_rht16",
                             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize",
-                            "nvfp4_mx_dequantize", "nvfp4_mx_gemm"])
+                            "nvfp4_mx_dequantize", "nvfp4_mx_gemm", "nvfp4_gemm_w4a16"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -193,4 +193,27 @@ def test_mx_validation(lib):
     assert mxg(lib, bsc=None) == 1
     assert mxg(lib, K=1 << 24) == 5                  # 256 rows of codes past 2^31 bytes
     assert mxg(lib, M=0) == 0
+
+
+def w4(lib, **kw):
+    args = dict(M=1, N=64, K=512, a=FAKE, lda=512, bc=FAKE, bsc=FAKE, bts=FAKE, bb=0, odt=0,
+                c=FAKE, ldc=64, stream=None)
+    args.update(kw)
+    return lib.nvfp4_gemm_w4a16(*args.values())
+
+
+def test_w4a16_validation(lib):
+    assert w4(lib, bb=2) == 1
+    assert w4(lib, odt=9) == 1
+    assert w4(lib, M=-1) == 1
+    assert w4(lib, K=256, lda=256) == 2             # K % 512
+    assert w4(lib, lda=100) == 2                    # lda < K
+    assert w4(lib, ldc=32) == 2
+    assert w4(lib, bb=1, N=40, ldc=40) == 4         # 2D weight with N % 16
+    assert w4(lib, M=65) == 5                       # decode shapes only
+    assert w4(lib, a=MISALIGNED) == 3
+    assert w4(lib, lda=516) == 3                    # 1032-byte rows
+    assert w4(lib, c=ODD) == 3
+    assert w4(lib, bts=None) == 1
+    assert w4(lib, M=0) == 0
 
