@@ -341,13 +341,25 @@ def decode_bench(torch, nv, workloads):
             torch.cuda.synchronize()
             if it >= 2:
                 iso.append(f0.elapsed_time(f1))
+        # the same weights with BF16 activations (weight-only GEMM)
+        ab = x[:M].contiguous()
+        for i in range(4):
+            nv.gemm_w4a16(ab, ws[i], out=y)
+        e0.record()
+        for i in range(reps):
+            nv.gemm_w4a16(ab, ws[i % 4], out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        t16 = e0.elapsed_time(e1) * 1e-3 / reps
         out["M%d" % M] = {"us": round(t * 1e6, 2),
+                          "w4a16_us": round(t16 * 1e6, 2),
                           "weights_GBps": round(wbytes / t / 1e9, 1),
                           "frac_of_hbm": round(wbytes / t / 1e9 / HBM_PEAK_GBPS, 4),
                           "tflops": round(2.0 * M * N * K / t / 1e12, 2),
                           "us_isolated": round(sorted(iso)[len(iso) // 2] * 1e3, 2)}
     del flush
-    return {"shape": "M x 28672 x 8192, weights 1x16 along K", "weight_bytes": int(wbytes),
+    return {"shape": "M x 28672 x 8192, weights 1x16 along K (w4a16_us: BF16 activations)",
+            "weight_bytes": int(wbytes),
             "timing": "mean of 40 back-to-back launches over 4 weight copies (528 MB, "
                       "cache-cold each launch); us_isolated: median of 10 single launches "
                       "after a cache-evicting read", **out}
