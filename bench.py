@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--cpu-sample-rows", type=int, default=64)
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 1 GiB copy kernel (for HBM counter calibration)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="the training-step line without the decode and mxfp4 objects "
+                         "(for profiling the step's kernels alone)")
     ap.add_argument("--mx-only", action="store_true",
                     help="time only the MXFP4 comparison path and print its JSON object")
     ap.add_argument("--decode-only", action="store_true",
@@ -289,8 +292,9 @@ def main():
     }
     del bufs
     torch.cuda.empty_cache()
-    line["decode"] = decode_bench(torch, nv, workloads)
-    line["mxfp4"] = mxfp4_bench(torch, nv, X, W_gu)
+    if not args.step_only:
+        line["decode"] = decode_bench(torch, nv, workloads)
+        line["mxfp4"] = mxfp4_bench(torch, nv, X, W_gu)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, torch, nv, workloads, X, W_gu)
