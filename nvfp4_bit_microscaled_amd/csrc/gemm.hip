@@ -960,7 +960,30 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
         __builtin_amdgcn_make_buffer_rsrc((void*)p.b_scales, (short)0, 0x7FFFFFFF, 0x00020000);
     const __amdgpu_buffer_rsrc_t none =
         __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, (short)0, 0, 0x00020000);
-    const int bo = (int)(nc * (K / 2)) + (kQ / 2) * g;
+    // kLines (one activation row block): B codes in whole 128-byte lines.
+    // Load instruction (h, ln) of a chunk reads line ln of rows 8 h .. 8 h + 7
+    // of the wave's 16 (lane l: row 8 h + l / 8, bytes 16 (l % 8) of the
+    // line), and the bytes go through a wave-private LDS buffer into the
+    // fragment layout.  Measured on 28672 x 8192 weights this streams 6-11%
+    // faster for M <= 16 than loading the fragment layout directly (16 bytes
+    // from each of 64 lines per instruction); with more activation rows the
+    // extra LDS costs a workgroup per CU and loses.  Otherwise lane group g
+    // loads its quarter of the chunk directly, 16 bytes per step.
+    constexpr bool kLines = RMAX == 1;
+    static_assert(!kLines || KC == 512, "two 128-byte lines per row and chunk");
+    int bo[2];
+    if constexpr (kLines) {
+        const int64_t brow0 = (int64_t)blockIdx.x * kSkN + wave * 16;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int64_t r = brow0 + 8 * h + (lane >> 3);
+            r = r < p.N ? r : p.N - 1;
+            bo[h] = (int)(r * (K / 2)) + 16 * (lane & 7);
+        }
+    } else {
+        bo[0] = bo[1] = (int)(nc * (K / 2)) + (kQ / 2) * g;
+    }
+    uint8_t* const bl = lds + RMAX * 16 * kRow + wave * 16 * (KC / 2 + 16);  // 16 rows x 272 B
     const int bso = (int)(p.b2d ? (nc / 16) * lds_b : nc * lds_b) + (kQ / 16) * g;
     // Workgroups walk K starting at different chunks: rows are K/2 bytes
     // apart, so if every workgroup read the same chunk at once, all reads
@@ -1003,9 +1026,15 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
     auto load_b = [&](__amdgpu_buffer_rsrc_t c_rsrc, __amdgpu_buffer_rsrc_t s_rsrc, int kc,
                       u32x4* c, uint32_t* sc) {
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st)
-            c[st] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, bo + 16 * st, kc / 2, 0));
+        for (int st = 0; st < kSteps; ++st) {  // kLines: st = 2 h + ln
+            if constexpr (kLines)
+                c[st] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, bo[st >> 1],
+                                                                 kc / 2 + 128 * (st & 1), 0));
+            else
+                c[st] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, bo[0] + 16 * st, kc / 2, 0));
+        }
 #pragma unroll
         for (int q = 0; q < kSB / 4; q += (kSB >= 16 ? 4 : 2)) {
             if (kSB >= 16) {
@@ -1060,6 +1089,23 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
         __builtin_amdgcn_sched_barrier(0);
         load_b(more ? rc : none, more ? rs : none, more ? kpos(kc + KC) : 0, nb, ns);
         __builtin_amdgcn_sched_barrier(0);
+        // this chunk's weight lines into the wave's LDS buffer (row pitch 272
+        // bytes), then each lane takes 16 bytes of its row's quarter g per
+        // step: one wave's LDS accesses complete in order, so no barrier
+        u32x4 cq[kSteps];
+        if constexpr (kLines) {
+#pragma unroll
+            for (int st = 0; st < kSteps; ++st)
+                *reinterpret_cast<u32x4*>(bl + (8 * (st >> 1) + (lane >> 3)) * (KC / 2 + 16) +
+                                          128 * (st & 1) + 16 * (lane & 7)) = cb[st];
+#pragma unroll
+            for (int st = 0; st < kSteps; ++st)
+                cq[st] = *reinterpret_cast<const u32x4*>(bl + lr * (KC / 2 + 16) + (kQ / 2) * g +
+                                                         16 * st);
+        } else {
+#pragma unroll
+            for (int st = 0; st < kSteps; ++st) cq[st] = cb[st];
+        }
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) {
             // the step's A fragments first (one LDS latency per step), then
@@ -1078,7 +1124,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
                 const float e1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    bf16x8_t bf = dequant_word_bf16(cb[st][s], s < 2 ? e0 : e1);
+                    bf16x8_t bf = dequant_word_bf16(cq[st][s], s < 2 ? e0 : e1);
 #pragma unroll
                     for (int r = 0; r < RMAX; ++r)
                         acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -1088,7 +1134,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
                 half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    half8_t bf = dequant_word(cb[st][s], e2[s >> 1]);
+                    half8_t bf = dequant_word(cq[st][s], e2[s >> 1]);
 #pragma unroll
                     for (int r = 0; r < RMAX; ++r)
                         acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s][r], bf, acc[r], 0, 0, 0);
@@ -1194,7 +1240,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
 #define NVFP4_SKINNY(KC, RMAX)                                                                 \
     {                                                                                          \
         auto kern = k_gemm_skinny<KC, RMAX, false>;                                            \
-        const int lds = RMAX * 16 * (KC * 2 + 64);                                             \
+        const int lds = RMAX * 16 * (KC * 2 + 64) + (RMAX == 1 ? 4 * 16 * (KC / 2 + 16) : 0);  \
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
     }
@@ -1446,7 +1492,7 @@ hipError_t launch_gemm_w4a16(int64_t M, int64_t N, int64_t K, const uint16_t* a,
 #define NVFP4_SKINNY16(RMAX)                                                                   \
     {                                                                                          \
         auto kern = k_gemm_skinny<512, RMAX, true>;                                            \
-        const int lds = RMAX * 16 * (512 * 2 + 64);                                            \
+        const int lds = RMAX * 16 * (512 * 2 + 64) + (RMAX == 1 ? 4 * 16 * (512 / 2 + 16) : 0);\
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
     }
