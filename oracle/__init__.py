@@ -99,6 +99,12 @@ def lib():
         L.oracle_mx_gemm_pairs.restype = ctypes.c_int
         L.oracle_mx_gemm_pairs.argtypes = [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_i64,
                                            c_vp, c_vp, c_vp, c_vp]
+        L.oracle_kv_cache_write.restype = ctypes.c_int
+        L.oracle_kv_cache_write.argtypes = [c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp,
+                                            ctypes.c_float, c_i64, c_vp, c_vp]
+        L.oracle_kv_cache_read.restype = ctypes.c_int
+        L.oracle_kv_cache_read.argtypes = [c_vp, c_vp, ctypes.c_float, c_i64, c_i64, c_vp, c_i64,
+                                           c_vp, c_vp]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_set_num_threads.restype = None
@@ -321,6 +327,44 @@ def mx_gemm_full(M: int, N: int, K: int, a, b):
     mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     ref, ab = mx_gemm_pairs(M, N, K, a, b, mm.ravel(), nn.ravel())
     return ref.reshape(M, N), ab.reshape(M, N)
+
+
+def kv_cache_write(x: np.ndarray, slots, amax: float, cache_codes: np.ndarray,
+                   cache_scales: np.ndarray) -> None:
+    """Quantize token rows of x (BF16 bits or FP32, [T, C]) into cache rows
+    slots[t] of (cache_codes [S, C/2], cache_scales [S, C/16]) in place; slots
+    outside [0, S) are skipped.  s_g = RN(amax / 2688)."""
+    x, dt = _as_input(x)
+    tokens, cols = x.shape
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    assert slots.shape == (tokens,)
+    assert cache_codes.dtype == np.uint8 and cache_codes.flags.c_contiguous
+    assert cache_scales.dtype == np.uint8 and cache_scales.flags.c_contiguous
+    num_slots = cache_codes.shape[0]
+    assert cache_codes.shape == (num_slots, cols // 2)
+    assert cache_scales.shape == (num_slots, cols // 16)
+    rc = lib().oracle_kv_cache_write(_ptr(x), dt, tokens, cols, cols, _ptr(slots), amax,
+                                     num_slots, _ptr(cache_codes), _ptr(cache_scales))
+    if rc:
+        raise ValueError("oracle_kv_cache_write: bad shape (%d)" % rc)
+
+
+def kv_cache_read(cache_codes: np.ndarray, cache_scales: np.ndarray, amax: float, slots):
+    """Returns (fp32 [n, C], bf16 bits uint16 [n, C]) of cache rows slots[j],
+    zero rows for slots outside [0, S)."""
+    cache_codes = np.ascontiguousarray(cache_codes, dtype=np.uint8)
+    cache_scales = np.ascontiguousarray(cache_scales, dtype=np.uint8)
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    num_slots, half = cache_codes.shape
+    cols = 2 * half
+    n = slots.shape[0]
+    f = np.zeros((n, cols), dtype=np.float32)
+    b = np.zeros((n, cols), dtype=np.uint16)
+    rc = lib().oracle_kv_cache_read(_ptr(cache_codes), _ptr(cache_scales), amax, num_slots, cols,
+                                    _ptr(slots), n, _ptr(f), _ptr(b))
+    if rc:
+        raise ValueError("oracle_kv_cache_read: bad shape (%d)" % rc)
+    return f, b
 
 
 def num_threads() -> int:

@@ -36,7 +36,8 @@
  *
  * The MXFP4 functions near the end follow the open MX standard for the
  * power-of-two format the pages compare NVFP4 with (block size and scale
- * rule are the standard's; the pages give neither).
+ * rule are the standard's; the pages give neither).  The KV-cache functions
+ * after them store token rows in NVFP4 under a fixed calibration scale.
  *
  * Every function is pinned by tests/test_oracle_*.py against something other
  * than itself (torch's float8_e4m3fn and bfloat16 casts, rocRAND's Philox,
@@ -680,6 +681,84 @@ int oracle_mx_gemm_pairs(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes
         }
         ref[p] = s;
         absref[p] = sa;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* NVFP4 KV cache                                                       */
+/* ------------------------------------------------------------------ */
+/*
+ * The NVIDIA-blog translation on juejin.cn (point 3, the ecosystem) names an
+ * NVFP4 KV cache among the inference uses of the format; "FP4" (chaitex.ru,
+ * mathematical-structure section) gives the inference layout: 16-element
+ * micro-blocks with an E4M3 scale and one FP32 tensor scale.  The pages say
+ * nothing more, so this file takes the plainest reading:
+ *   - a cache holds num_slots rows of `cols` features (heads x head_dim),
+ *     1x16 blocks along the features, round to nearest-even;
+ *   - the tensor scale is fixed for the cache's lifetime, s_g =
+ *     RN(amax / 2688) from a calibration amax the caller supplies (rows
+ *     arrive a few at a time, so no amax over the whole cache exists when a
+ *     row is written); features beyond the calibration amax saturate;
+ *   - writing sends token t to cache row slots[t]; a slot outside
+ *     [0, num_slots) skips the token (padding);
+ *   - reading gathers cache rows slots[j] and dequantizes them exactly as
+ *     the tensor dequantization does; an out-of-range slot gives a zero row.
+ * Each written row gets the same codes and scales as quantizing that token
+ * alone (rounding to nearest, 1x16 blocks, amax_in = the calibration amax).
+ */
+int oracle_kv_cache_write(const void* x, int dtype, int64_t tokens, int64_t cols, int64_t ld_x,
+                          const int64_t* slots, float amax, int64_t num_slots,
+                          uint8_t* cache_codes, uint8_t* cache_scales)
+{
+    if (tokens < 0 || cols < 0 || cols % 16 != 0 || ld_x < cols || num_slots < 0) return -1;
+    float s_g = amax / 2688.0f;   /* FP32 division */
+    float D6 = 6.0f * s_g;        /* FP32 product */
+    int64_t nbc = cols / 16;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < tokens; ++t) {
+        int64_t slot = slots[t];
+        if (slot < 0 || slot >= num_slots) continue;
+        for (int64_t bc = 0; bc < nbc; ++bc) {
+            float buf[16];
+            float* vals[16];
+            int64_t idx[16];
+            uint8_t q[16], e;
+            for (int j = 0; j < 16; ++j) {
+                buf[j] = load_elem(x, dtype, ld_x, t, bc * 16 + j);
+                vals[j] = &buf[j];
+                idx[j] = 0; /* no stochastic rounding: the index is unused */
+            }
+            quantize_block(vals, idx, 16, s_g, D6, 0, 0, 0, &e, q);
+            cache_scales[slot * nbc + bc] = e;
+            for (int j = 0; j < 16; ++j) put_code(cache_codes, cols, slot, bc * 16 + j, q[j]);
+        }
+    }
+    return 0;
+}
+
+/* out row j = dequantized cache row slots[j] (v = RN32(val * e * s_g), and its
+ * BF16 rounding), or zeros when slots[j] is outside [0, num_slots). */
+int oracle_kv_cache_read(const uint8_t* cache_codes, const uint8_t* cache_scales, float amax,
+                         int64_t num_slots, int64_t cols, const int64_t* slots, int64_t n,
+                         float* out_f32, uint16_t* out_bf16)
+{
+    if (n < 0 || cols < 0 || cols % 16 != 0 || num_slots < 0) return -1;
+    float s_g = amax / 2688.0f;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j) {
+        int64_t slot = slots[j];
+        int valid = slot >= 0 && slot < num_slots;
+        for (int64_t c = 0; c < cols; ++c) {
+            float v = 0.0f;
+            if (valid) {
+                double ve = elem_times_scale(cache_codes, cache_scales, num_slots, cols, 0, 1,
+                                             slot, c);
+                v = (float)ve * s_g; /* val*e exact in FP32; one FP32 rounding */
+            }
+            if (out_f32) out_f32[j * cols + c] = v;
+            if (out_bf16) out_bf16[j * cols + c] = oracle_f32_to_bf16(v);
+        }
     }
     return 0;
 }
