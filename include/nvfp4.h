@@ -298,6 +298,47 @@ nvfp4_status nvfp4_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_cod
                            const uint8_t* b_scales, nvfp4_dtype out_dtype, void* c, int64_t ldc,
                            void* stream);
 
+/*
+ * NVFP4 KV cache (NVIDIA-blog translation on juejin.cn, point 3: libraries
+ * keep the KV cache in NVFP4 for long contexts and large batches; "FP4",
+ * chaitex.ru, mathematical-structure section: 16-element micro-blocks with
+ * an E4M3 scale and an FP32 tensor scale).  The pages say nothing more; the
+ * reading taken:
+ *   - a cache holds num_slots rows of `cols` features (e.g. KV heads x head
+ *     dim), in 1x16 blocks along the features, rounded to nearest-even;
+ *   - its tensor scale is fixed while rows arrive: s_g = RN(*amax / 2688)
+ *     from a calibration amax the caller keeps on the device (FP32 scalar);
+ *     features beyond it saturate (block scale 448, element +-6);
+ *   - every row written equals the 1x16 RNE quantization of that token row
+ *     with amax_in = *amax (nvfp4_quantize), and reads equal
+ *     nvfp4_dequantize of the rows gathered.
+ * Storage: cache_codes [num_slots, cols/2] (low nibble = even column),
+ * cache_scales [num_slots, cols/16] row-major E4M3 bytes.
+ *
+ * nvfp4_kv_cache_write: token t (row t of x, pitch ld_x elements, BF16 or
+ *   FP32) goes to cache row slots[t] (int64, device).  A slot outside
+ *   [0, num_slots) skips the token (padding); other cache rows are left
+ *   untouched.  Two tokens with the same valid slot race (either may win).
+ *   cols % 16 == 0; ld_x >= cols; x, cache_codes 16-byte aligned and x's row
+ *   pitch a multiple of 16 bytes; slots 8-byte aligned.  tokens == 0 or
+ *   cols == 0 writes nothing.
+ * nvfp4_kv_cache_read: out row j (pitch ld_out elements, BF16 RNE or FP32)
+ *   = v = RN32(val * e * s_g) of cache row slots[j], or zeros when slots[j]
+ *   is outside [0, num_slots).  Slots may repeat.  cols % 16 == 0;
+ *   ld_out >= cols; out and cache_codes 16-byte aligned, out's row pitch a
+ *   multiple of 16 bytes.
+ * All pointers are caller-owned device memory; launches are asynchronous on
+ * `stream`; argument errors return before anything is enqueued.
+ */
+nvfp4_status nvfp4_kv_cache_write(const void* x, nvfp4_dtype x_dtype, int64_t tokens,
+                                  int64_t cols, int64_t ld_x, const int64_t* slots,
+                                  const float* amax, int64_t num_slots, uint8_t* cache_codes,
+                                  uint8_t* cache_scales, void* stream);
+nvfp4_status nvfp4_kv_cache_read(const uint8_t* cache_codes, const uint8_t* cache_scales,
+                                 const float* amax, int64_t num_slots, int64_t cols,
+                                 const int64_t* slots, int64_t n, nvfp4_dtype out_dtype, void* out,
+                                 int64_t ld_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,8 @@ EXPORTS = ("nvfp4_version", "nvfp4_status_string", "nvfp4_quantize_workspace_siz
            "nvfp4_quantize", "nvfp4_amax_workspace_size", "nvfp4_amax",
            "nvfp4_swiglu_amax", "nvfp4_rht16",
            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize",
-           "nvfp4_mx_gemm", "nvfp4_gemm_w4a16")
+           "nvfp4_mx_gemm", "nvfp4_gemm_w4a16", "nvfp4_kv_cache_write",
+           "nvfp4_kv_cache_read")
 
 
 class NVFP4Error(RuntimeError):
@@ -81,6 +82,10 @@ def _load():
     L.nvfp4_mx_dequantize.argtypes = [vp, vp, i64, i64, ci, vp, i64, vp]
     L.nvfp4_mx_gemm.restype = ci
     L.nvfp4_mx_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, ci, vp, i64, vp]
+    L.nvfp4_kv_cache_write.restype = ci
+    L.nvfp4_kv_cache_write.argtypes = [vp, ci, i64, i64, i64, vp, vp, i64, vp, vp, vp]
+    L.nvfp4_kv_cache_read.restype = ci
+    L.nvfp4_kv_cache_read.argtypes = [vp, vp, vp, i64, i64, vp, i64, ci, vp, i64, vp]
     return L
 
 
@@ -182,6 +187,18 @@ def nvfp4_mx_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales, out_dtype, c, l
                   stream=None) -> int:
     return lib.nvfp4_mx_gemm(M, N, K, _p(a_codes), _p(a_scales), _p(b_codes), _p(b_scales),
                              out_dtype, _p(c), ldc, _stream(stream))
+
+
+def nvfp4_kv_cache_write(x, x_dtype, tokens, cols, ld_x, slots, amax, num_slots, cache_codes,
+                         cache_scales, stream=None) -> int:
+    return lib.nvfp4_kv_cache_write(_p(x), x_dtype, tokens, cols, ld_x, _p(slots), _p(amax),
+                                    num_slots, _p(cache_codes), _p(cache_scales), _stream(stream))
+
+
+def nvfp4_kv_cache_read(cache_codes, cache_scales, amax, num_slots, cols, slots, n, out_dtype, out,
+                        ld_out, stream=None) -> int:
+    return lib.nvfp4_kv_cache_read(_p(cache_codes), _p(cache_scales), _p(amax), num_slots, cols,
+                                   _p(slots), n, out_dtype, _p(out), ld_out, _stream(stream))
 
 
 # ---------------------------------------------------------------- tensor-level helpers
@@ -385,4 +402,53 @@ def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out_dtype=torch.bfloat16,
         out = torch.empty(M, N, dtype=out_dtype, device=a.codes.device)
     _check("nvfp4_mx_gemm", nvfp4_mx_gemm(M, N, K, a.codes, a.scales, b.codes, b.scales,
                                           _dtype_code(out), out, out.stride(0)))
+    return out
+
+
+# ---------------------------------------------------------------- KV cache
+# NVFP4 KV cache: token rows in 1x16 blocks (RNE) under a fixed tensor scale
+# from a calibration amax, written to and gathered from slot-indexed rows.
+
+@dataclass
+class NVFP4KVCache:
+    """codes uint8 [S, C/2], scales uint8 [S, C/16], amax float32 [1] (the
+    calibration amax; s_g = amax / 2688)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    amax: torch.Tensor
+    num_slots: int
+    cols: int
+
+
+def kv_cache_create(num_slots: int, cols: int, amax, device="cuda") -> NVFP4KVCache:
+    """An empty (all-zero) cache; `amax` is a float or a device FP32 tensor [1]."""
+    if not torch.is_tensor(amax):
+        amax = torch.tensor([float(amax)], dtype=torch.float32, device=device)
+    return NVFP4KVCache(codes=torch.zeros(num_slots, cols // 2, dtype=torch.uint8, device=device),
+                        scales=torch.zeros(num_slots, cols // 16, dtype=torch.uint8, device=device),
+                        amax=amax, num_slots=num_slots, cols=cols)
+
+
+def kv_cache_write(cache: NVFP4KVCache, x: torch.Tensor, slots: torch.Tensor) -> None:
+    """Quantize token rows x [T, C] (BF16/FP32) into cache rows slots[t] (int64
+    [T]); slots outside [0, S) are skipped."""
+    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1 and x.shape[1] == cache.cols
+    assert slots.dtype == torch.int64 and slots.is_cuda and slots.is_contiguous()
+    assert slots.numel() == x.shape[0]
+    _check("nvfp4_kv_cache_write", nvfp4_kv_cache_write(
+        x, _dtype_code(x), x.shape[0], x.shape[1], x.stride(0), slots, cache.amax,
+        cache.num_slots, cache.codes, cache.scales))
+
+
+def kv_cache_read(cache: NVFP4KVCache, slots: torch.Tensor, out_dtype=torch.bfloat16,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dequantized cache rows slots[j] -> [n, C]; zero rows for slots outside [0, S)."""
+    assert slots.dtype == torch.int64 and slots.is_cuda and slots.is_contiguous()
+    n = slots.numel()
+    if out is None:
+        out = torch.empty(n, cache.cols, dtype=out_dtype, device=slots.device)
+    assert out.shape == (n, cache.cols) and out.stride(1) == 1
+    _check("nvfp4_kv_cache_read", nvfp4_kv_cache_read(
+        cache.codes, cache.scales, cache.amax, cache.num_slots, cache.cols, slots, n,
+        _dtype_code(out), out, out.stride(0)))
     return out

@@ -362,4 +362,47 @@ nvfp4_status nvfp4_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, in
                                       out_dtype == NVFP4_DTYPE_BF16, c, ldc, s));
 }
 
+nvfp4_status nvfp4_kv_cache_write(const void* x, nvfp4_dtype x_dtype, int64_t tokens,
+                                  int64_t cols, int64_t ld_x, const int64_t* slots,
+                                  const float* amax, int64_t num_slots, uint8_t* cache_codes,
+                                  uint8_t* cache_scales, void* stream)
+{
+    if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (tokens < 0 || cols < 0 || num_slots < 0) return NVFP4_ERR_INVALID_ARG;
+    if (cols % 16) return NVFP4_ERR_SHAPE;
+    if (ld_x < cols) return NVFP4_ERR_SHAPE;
+    if ((uint64_t)tokens * (uint64_t)(cols / 16) > kMaxItems) return NVFP4_ERR_UNSUPPORTED;
+    if (tokens == 0 || cols == 0 || num_slots == 0) return NVFP4_OK;
+    if (!x || !slots || !amax || !cache_codes || !cache_scales) return NVFP4_ERR_INVALID_ARG;
+    const size_t esz = x_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    if (!aligned16(x) || !aligned16(cache_codes) || ((size_t)ld_x * esz) % 16 ||
+        (reinterpret_cast<uintptr_t>(slots) & 7u))
+        return NVFP4_ERR_ALIGN;
+    return from_hip(launch_kv_cache_write(x, x_dtype == NVFP4_DTYPE_BF16, tokens, cols, ld_x,
+                                          slots, num_slots, amax, cache_codes, cache_scales,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_kv_cache_read(const uint8_t* cache_codes, const uint8_t* cache_scales,
+                                 const float* amax, int64_t num_slots, int64_t cols,
+                                 const int64_t* slots, int64_t n, nvfp4_dtype out_dtype, void* out,
+                                 int64_t ld_out, void* stream)
+{
+    if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (n < 0 || cols < 0 || num_slots < 0) return NVFP4_ERR_INVALID_ARG;
+    if (cols % 16) return NVFP4_ERR_SHAPE;
+    if (ld_out < cols) return NVFP4_ERR_SHAPE;
+    if ((uint64_t)n * (uint64_t)(cols / 8) > kMaxItems) return NVFP4_ERR_UNSUPPORTED;
+    if (n == 0 || cols == 0) return NVFP4_OK;
+    if (!out || !slots || !amax) return NVFP4_ERR_INVALID_ARG;
+    if (num_slots > 0 && (!cache_codes || !cache_scales)) return NVFP4_ERR_INVALID_ARG;
+    const size_t esz = out_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    if (!aligned16(out) || ((size_t)ld_out * esz) % 16 || !aligned16(cache_codes) ||
+        (reinterpret_cast<uintptr_t>(slots) & 7u))
+        return NVFP4_ERR_ALIGN;
+    return from_hip(launch_kv_cache_read(cache_codes, cache_scales, amax, num_slots, cols, slots,
+                                         n, out_dtype == NVFP4_DTYPE_BF16, out, ld_out,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -94,6 +94,19 @@ hipError_t launch_gemm_w4a16(int64_t M, int64_t N, int64_t K, const uint16_t* a,
                              const GemmOperand& B, bool out_bf16, void* c, int64_t ldc,
                              hipStream_t s);
 
+// NVFP4 KV cache: token rows of x [tokens, cols] (cols % 16 == 0) quantized
+// (1x16, RNE, s_g = RN(*amax / 2688)) into cache rows slots[t] of codes
+// [num_slots, cols/2] and scales [num_slots, cols/16]; the read gathers cache
+// rows slots[j] into out [n, cols] (pitch ld_out).  Slots outside
+// [0, num_slots) are skipped / read as zeros.
+hipError_t launch_kv_cache_write(const void* x, bool bf16, int64_t tokens, int64_t cols,
+                                 int64_t ld, const int64_t* slots, int64_t num_slots,
+                                 const float* amax, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s);
+hipError_t launch_kv_cache_read(const uint8_t* codes, const uint8_t* scales, const float* amax,
+                                int64_t num_slots, int64_t cols, const int64_t* slots, int64_t n,
+                                bool out_bf16, void* out, int64_t ld_out, hipStream_t s);
+
 hipError_t launch_fill_zero(void* c, bool bf16, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
 
 }  // namespace nvfp4

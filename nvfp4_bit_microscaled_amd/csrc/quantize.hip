@@ -731,6 +731,45 @@ __global__ __launch_bounds__(256) void k_rht16_cols(const uint8_t* x, int64_t ld
 
 // ------------------------------------------------------------ dequantize
 
+// Eight elements of one 32-bit code word (element 2j in the low nibble of
+// byte j) with their scales e[]: v = RN32((val * e) * s_g), val * e exact in
+// FP32; stored as FP32 or BF16 (round to nearest even) at dst, 16-byte
+// aligned.
+template <bool kOutBF16>
+__device__ __forceinline__ void dequant8_store(uint32_t w, const float e[8], float s_g, uint8_t* dst)
+{
+    float v[8];
+    float2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    float2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    float2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    float2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (v[j] * e[j]) * s_g;
+    if (kOutBF16) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t a = __float_as_uint(v[2 * j]), b = __float_as_uint(v[2 * j + 1]);
+            a += 0x7FFFu + ((a >> 16) & 1u);  // round to nearest even (finite inputs)
+            b += 0x7FFFu + ((b >> 16) & 1u);
+            o[j] = (a >> 16) | (b & 0xFFFF0000u);
+        }
+        *reinterpret_cast<u32x4*>(dst) = o;
+    } else {
+        u32x4 a, b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[j] = __float_as_uint(v[j]);
+            b[j] = __float_as_uint(v[4 + j]);
+        }
+        u32x4* d = reinterpret_cast<u32x4*>(dst);
+        d[0] = a;
+        d[1] = b;
+    }
+}
+
 // One thread per 8 consecutive elements of a row (one 32-bit code word).
 // v = RN32((val * e) * s_g); val * e is exact in FP32.  kMode 3 is MXFP4:
 // e = 2^(u - 127) from an E8M0 byte per 32 along the row and no tensor scale
@@ -767,36 +806,86 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* codes, const uin
 #pragma unroll
             for (int j = 0; j < 8; ++j) e[j] = ev;
         }
-        float v[8];
-        float2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-        float2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-        float2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-        float2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-        v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
-        v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+        dequant8_store<kOutBF16>(w, e, s_g, out + ((int64_t)row * ld_out + c0) * (kOutBF16 ? 2 : 4));
+    }
+}
+
+// ------------------------------------------------------------ KV cache
+// NVFP4 KV cache (NVIDIA-blog translation on juejin.cn, point 3: an NVFP4
+// KV cache for long contexts and large batches; "FP4", chaitex.ru,
+// mathematical-structure section: 16-element micro-blocks with an E4M3
+// scale and an FP32 tensor scale).  A cache is num_slots rows of `cols`
+// features in 1x16 blocks, rounded to nearest-even, under one tensor scale
+// s_g = RN(amax / 2688) from a calibration amax that stays fixed while rows
+// arrive.  Writes scatter token rows to cache rows slots[t]; reads gather
+// cache rows slots[j] and dequantize them.  Slots outside [0, num_slots) are
+// skipped on write and read as zero rows.
+struct KvParams {
+    const uint8_t* x;       // write: token rows (BF16 / FP32 bytes)
+    int64_t ld;             // write: row pitch of x in elements; read: of out
+    const int64_t* slots;
+    int64_t num_slots;
+    int64_t cols;
+    const float* amax;      // calibration amax (device scalar)
+    uint8_t* codes;         // [num_slots, cols/2]
+    uint8_t* scales;        // [num_slots, cols/16]
+    uint8_t* out;           // read: [n, cols] rows of pitch ld
+    uint32_t items;
+    FastDiv div;            // work items per token row
+};
+
+// One thread per 16-element block of a token row, the same arithmetic as the
+// 1x16 row quantization with amax_in given.
+template <bool kBF16>
+__global__ __launch_bounds__(256) void k_kv_write(KvParams p)
+{
+    constexpr int esz = kBF16 ? 2 : 4;
+    const TensorScale ts = make_tensor_scale(*p.amax);
+    const int64_t nbc = p.cols / 16;
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t b = blockIdx.x * blockDim.x + threadIdx.x; b < p.items; b += stride) {
+        const uint32_t t = fdiv(b, p.div);
+        const uint32_t cb = b - t * p.div.d;
+        const int64_t slot = p.slots[t];
+        if (slot < 0 || slot >= p.num_slots) continue;
+        const uint8_t* src = p.x + ((int64_t)t * p.ld + (int64_t)cb * 16) * esz;
+        float v[16];
+        load8<kBF16>(src, v);
+        load8<kBF16>(src + 8 * esz, v + 8);
+        float aB = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = (v[j] * e[j]) * s_g;
-        if (kOutBF16) {
-            u32x4 o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t a = __float_as_uint(v[2 * j]), b = __float_as_uint(v[2 * j + 1]);
-                a += 0x7FFFu + ((a >> 16) & 1u);  // round to nearest even (finite inputs)
-                b += 0x7FFFu + ((b >> 16) & 1u);
-                o[j] = (a >> 16) | (b & 0xFFFF0000u);
-            }
-            *reinterpret_cast<u32x4*>(out + ((int64_t)row * ld_out + c0) * 2) = o;
-        } else {
-            u32x4 a, b;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                a[j] = __float_as_uint(v[j]);
-                b[j] = __float_as_uint(v[4 + j]);
-            }
-            u32x4* dst = reinterpret_cast<u32x4*>(out + ((int64_t)row * ld_out + c0) * 4);
-            dst[0] = a;
-            dst[1] = b;
+        for (int i = 0; i < 16; ++i) aB = __builtin_fmaxf(aB, __builtin_fabsf(v[i]));
+        BlockDiv bd;
+        bool zero;
+        const uint32_t e = block_scale(aB, ts, bd, zero);
+        u32x2 out;
+        out[0] = encode8<false>(v, bd, zero, nullptr);
+        out[1] = encode8<false>(v + 8, bd, zero, nullptr);
+        *reinterpret_cast<u32x2*>(p.codes + slot * (p.cols / 2) + (int64_t)cb * 8) = out;
+        p.scales[slot * nbc + cb] = (uint8_t)e;
+    }
+}
+
+// One thread per 8 outputs (one code word) of a gathered row.
+template <bool kOutBF16>
+__global__ __launch_bounds__(256) void k_kv_read(KvParams p)
+{
+    const float s_g = *p.amax / kGlobalDivisor;
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < p.items; t += stride) {
+        const uint32_t row = fdiv(t, p.div);
+        const int64_t c0 = (int64_t)(t - row * p.div.d) * 8;
+        const int64_t slot = p.slots[row];
+        uint32_t w = 0u;
+        float ev = 0.0f;
+        if (slot >= 0 && slot < p.num_slots) {
+            w = *reinterpret_cast<const uint32_t*>(p.codes + slot * (p.cols / 2) + c0 / 2);
+            ev = e4m3_decode(p.scales[slot * (p.cols / 16) + c0 / 16]);
         }
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = ev;
+        dequant8_store<kOutBF16>(w, e, s_g, p.out + ((int64_t)row * p.ld + c0) * (kOutBF16 ? 2 : 4));
     }
 }
 
@@ -1083,6 +1172,47 @@ hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int
         hipLaunchKernelGGL((k_dequant<OB, 3>), dim3(grid), dim3(256), 0, s, codes, scales,
                            (const float*)nullptr, cols, items, div, static_cast<uint8_t*>(out),
                            ld_out));
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_cache_write(const void* x, bool bf16, int64_t tokens, int64_t cols,
+                                 int64_t ld, const int64_t* slots, int64_t num_slots,
+                                 const float* amax, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s)
+{
+    KvParams p{};
+    p.x = static_cast<const uint8_t*>(x);
+    p.ld = ld;
+    p.slots = slots;
+    p.num_slots = num_slots;
+    p.cols = cols;
+    p.amax = amax;
+    p.codes = codes;
+    p.scales = scales;
+    p.items = (uint32_t)(tokens * (cols / 16));
+    p.div = make_fastdiv((uint32_t)(cols / 16));
+    const int grid = grid_for(p.items, kGridCap);
+    NVFP4_DISPATCH_BOOL(bf16, BF, hipLaunchKernelGGL((k_kv_write<BF>), dim3(grid), dim3(256), 0, s, p));
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_cache_read(const uint8_t* codes, const uint8_t* scales, const float* amax,
+                                int64_t num_slots, int64_t cols, const int64_t* slots, int64_t n,
+                                bool out_bf16, void* out, int64_t ld_out, hipStream_t s)
+{
+    KvParams p{};
+    p.ld = ld_out;
+    p.slots = slots;
+    p.num_slots = num_slots;
+    p.cols = cols;
+    p.amax = amax;
+    p.codes = const_cast<uint8_t*>(codes);
+    p.scales = const_cast<uint8_t*>(scales);
+    p.out = static_cast<uint8_t*>(out);
+    p.items = (uint32_t)(n * (cols / 8));
+    p.div = make_fastdiv((uint32_t)(cols / 8));
+    const int grid = grid_for(p.items, kGridCap);
+    NVFP4_DISPATCH_BOOL(out_bf16, OB, hipLaunchKernelGGL((k_kv_read<OB>), dim3(grid), dim3(256), 0, s, p));
     return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ def test_header_declares_the_abi():
                             "nvfp4_amax_workspace_size", "nvfp4_amax", "nvfp4_swiglu_amax",
                             "nvfp4_rht16",
                             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize",
-                            "nvfp4_mx_dequantize", "nvfp4_mx_gemm", "nvfp4_gemm_w4a16"])
+                            "nvfp4_mx_dequantize", "nvfp4_mx_gemm", "nvfp4_gemm_w4a16",
+                            "nvfp4_kv_cache_write", "nvfp4_kv_cache_read"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -217,3 +218,43 @@ def test_w4a16_validation(lib):
     assert w4(lib, bts=None) == 1
     assert w4(lib, M=0) == 0
 
+
+def kvw(lib, **kw):
+    args = dict(x=FAKE, dt=0, tokens=4, cols=128, ld=128, slots=FAKE, amax=FAKE, S=16, cc=FAKE,
+                cs=FAKE, stream=None)
+    args.update(kw)
+    return lib.nvfp4_kv_cache_write(*args.values())
+
+
+def kvr(lib, **kw):
+    args = dict(cc=FAKE, cs=FAKE, amax=FAKE, S=16, cols=128, slots=FAKE, n=4, odt=0, out=FAKE,
+                ld=128, stream=None)
+    args.update(kw)
+    return lib.nvfp4_kv_cache_read(*args.values())
+
+
+def test_kv_cache_validation(lib):
+    assert kvw(lib, dt=2) == 1
+    assert kvw(lib, tokens=-1) == 1
+    assert kvw(lib, S=-1) == 1
+    assert kvw(lib, cols=40, ld=40) == 2          # cols % 16
+    assert kvw(lib, ld=64) == 2                   # ld < cols
+    assert kvw(lib, tokens=1 << 30, cols=1 << 10, ld=1 << 10) == 5   # > 2^32 blocks
+    assert kvw(lib, x=MISALIGNED) == 3
+    assert kvw(lib, ld=132) == 3                  # 264-byte rows
+    assert kvw(lib, slots=ctypes.c_void_p(0x10004)) == 3
+    assert kvw(lib, cc=MISALIGNED) == 3
+    assert kvw(lib, amax=None) == 1
+    assert kvw(lib, slots=None) == 1
+    assert kvw(lib, tokens=0, x=None, slots=None) == 0
+    assert kvw(lib, S=0, cc=None, cs=None) == 0
+    assert kvr(lib, odt=7) == 1
+    assert kvr(lib, n=-2) == 1
+    assert kvr(lib, cols=24, ld=24) == 2
+    assert kvr(lib, ld=100) == 2
+    assert kvr(lib, out=MISALIGNED) == 3
+    assert kvr(lib, ld=132) == 3                  # 264-byte BF16 rows
+    assert kvr(lib, slots=ctypes.c_void_p(0x10002)) == 3
+    assert kvr(lib, out=None) == 1
+    assert kvr(lib, cc=None) == 1
+    assert kvr(lib, n=0, out=None) == 0

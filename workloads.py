@@ -64,6 +64,18 @@ def sign_mask(seed: int) -> int:
     return int(torch.randint(0, 1 << 16, (1,), generator=g).item())
 
 
+def paged_slots(tokens: int, num_slots: int, seed: int, page: int = 16) -> torch.Tensor:
+    """Cache slot of each token for a paged cache: tokens fill pages of `page`
+    consecutive slots in order, and the pages are a seeded random choice of
+    the cache's num_slots / page pages (int64 [tokens])."""
+    g = _gen(seed, "cpu")
+    npages = (tokens + page - 1) // page
+    assert npages * page <= num_slots
+    pages = torch.randperm(num_slots // page, generator=g)[:npages]
+    t = torch.arange(tokens)
+    return pages[t // page] * page + t % page
+
+
 def bf16_bits(x: torch.Tensor):
     """BF16 CPU tensor -> numpy uint16 bit patterns (for the oracle)."""
     assert x.dtype == torch.bfloat16
@@ -89,3 +101,8 @@ DECODE = dict(ms=(1, 16, 32, 64), k=8192, n=28672, act_seed=6, w_seed=7)
 # intermediate 53248.
 LLAMA405B = dict(tokens=8192, hidden=16384, ffn=53248, x_seed=8, wgu_seed=9, wdown_seed=10,
                  dy_seed=11, dh_seed=12, sr_seed=1, mask_seed=1)
+
+# NVFP4 KV cache of a Llama-3-8B-shaped model: 8 KV heads x head dim 128 =
+# 1024 features per token for K (and again for V); 262144 tokens (8 sequences
+# of 32768) scattered over a cache of as many slots in pages of 16.
+KVCACHE = dict(tokens=262144, cols=1024, num_slots=262144, x_seed=13, slot_seed=14, read_seed=15)
