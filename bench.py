@@ -57,6 +57,8 @@ def parse():
                          "(for profiling the step's kernels alone)")
     ap.add_argument("--mx-only", action="store_true",
                     help="time only the MXFP4 comparison path and print its JSON object")
+    ap.add_argument("--kv-only", action="store_true",
+                    help="print only the NVFP4 KV-cache write/read object")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode-shape GEMMs and print their JSON object "
                          "(for profiling the skinny kernel; not the bench line)")
@@ -128,6 +130,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.decode_only:
         print(json.dumps({"decode": decode_bench(torch, nv, workloads)}), flush=True)
+        return
+    if args.kv_only:
+        print(json.dumps({"kv_cache": kv_bench(torch, nv, workloads)}), flush=True)
         return
     if args.mx_only:
         cfg = workloads.LLAMA8B
@@ -295,6 +300,7 @@ def main():
     if not args.step_only:
         line["decode"] = decode_bench(torch, nv, workloads)
         line["mxfp4"] = mxfp4_bench(torch, nv, X, W_gu)
+        line["kv_cache"] = kv_bench(torch, nv, workloads)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, torch, nv, workloads, X, W_gu)
@@ -410,6 +416,50 @@ def mxfp4_bench(torch, nv, X, W):
             "mx_quantize_GBps": round(qb / (t_q * 1e-3) / 1e9, 1),
             "mse_on_X": {"mxfp4": mse_mx, "nvfp4": mse_nv,
                          "nvfp4_less_error": round(1 - mse_nv / mse_mx, 4)}}
+
+
+def kv_bench(torch, nv, workloads):
+    """NVFP4 KV cache of a Llama-3-8B-shaped model (8 KV heads x 128 = 1024
+    features): 262144 BF16 token rows written in pages of 16 over a cache of
+    262144 slots, and every slot gathered back (another page order) to BF16.
+    Both are HBM streams; bytes per call are the algorithmic ones: the write
+    reads 2 B per feature and the slot index and writes 0.5 + 1/16 B per
+    feature, the read the reverse.  Mean of 10 back-to-back calls (537 MB of
+    BF16 per call, twice the Infinity Cache)."""
+    cfg = workloads.KVCACHE
+    T, C, S = cfg["tokens"], cfg["cols"], cfg["num_slots"]
+    x = workloads.activations(T, C, cfg["x_seed"], device="cuda")
+    amax = x.float().abs().max().reshape(1)
+    slots = workloads.paged_slots(T, S, cfg["slot_seed"]).cuda()
+    rslots = workloads.paged_slots(S, S, cfg["read_seed"]).cuda()
+    cache = nv.kv_cache_create(S, C, amax)
+    out = torch.empty(S, C, dtype=torch.bfloat16, device="cuda")
+    reps = 10
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        fn()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_w = timed(lambda: nv.kv_cache_write(cache, x, slots))
+    t_r = timed(lambda: nv.kv_cache_read(cache, rslots, torch.bfloat16, out=out))
+    wb = T * C * (2 + 0.5 + 1 / 16) + 8 * T
+    rb = S * C * (0.5 + 1 / 16 + 2) + 8 * S
+    del x, out, cache
+    return {"shape": "%d tokens x %d features, cache of %d slots, pages of 16" % (T, C, S),
+            "kernels": "k_kv_write<bf16>, k_kv_read<bf16 out>",
+            "write_us": round(t_w * 1e6, 2), "write_GBps": round(wb / t_w / 1e9, 1),
+            "write_frac_of_hbm": round(wb / t_w / 1e9 / HBM_PEAK_GBPS, 4),
+            "read_us": round(t_r * 1e6, 2), "read_GBps": round(rb / t_r / 1e9, 1),
+            "read_frac_of_hbm": round(rb / t_r / 1e9 / HBM_PEAK_GBPS, 4),
+            "bytes_per_call": {"write": int(wb), "read": int(rb)}}
 
 
 def cpu_baseline(args, torch, nv, workloads, X, W_gu):

@@ -830,62 +830,180 @@ struct KvParams {
     uint8_t* codes;         // [num_slots, cols/2]
     uint8_t* scales;        // [num_slots, cols/16]
     uint8_t* out;           // read: [n, cols] rows of pitch ld
-    uint32_t items;
-    FastDiv div;            // work items per token row
+    uint32_t units;         // (row, chunk) pairs, one per wave iteration
+    FastDiv div;            // chunks per row
 };
 
-// One thread per 16-element block of a token row, the same arithmetic as the
-// 1x16 row quantization with amax_in given.
+// Work is split into units of one row chunk; each wave takes units
+// wave, wave + waves, ...  The unit's slot is wave-uniform (a scalar load),
+// and the next unit's slot is loaded one iteration ahead so that its latency
+// overlaps the current unit's memory traffic.
+// (64-bit counters: u + step must not wrap below the unit count.)
+struct KvWalk {
+    uint64_t u, step;
+};
+
+__device__ __forceinline__ KvWalk kv_walk()
+{
+    KvWalk w;
+    w.u = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+    w.step = gridDim.x * (blockDim.x >> 6);
+    return w;
+}
+
+__device__ __forceinline__ int64_t kv_slot_of(const KvParams& p, uint64_t u)
+{
+    if (u >= p.units) return -1;
+    const uint32_t row = __builtin_amdgcn_readfirstlane(fdiv((uint32_t)u, p.div));
+    // the slot table is read-only here: the constant address space lets the
+    // uniform load go through the scalar unit
+    typedef const __attribute__((address_space(4))) int64_t* slot_ptr;
+    return ((slot_ptr)p.slots)[row];
+}
+
+// Write: a chunk is 64 blocks of 16 features of one token row, one block per
+// lane, with the arithmetic of the 1x16 row quantization under amax_in.  Each
+// iteration takes two units (u and u + step) and issues both rows' loads
+// before either is encoded, doubling the bytes in flight per wave.
+template <bool kBF16>
+__device__ __forceinline__ void kv_write_block(const KvParams& p, const TensorScale& ts,
+                                               int64_t slot, uint32_t cb, const float v[16])
+{
+    float aB = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) aB = __builtin_fmaxf(aB, __builtin_fabsf(v[i]));
+    BlockDiv bd;
+    bool zero;
+    const uint32_t e = block_scale(aB, ts, bd, zero);
+    u32x2 out;
+    out[0] = encode8<false>(v, bd, zero, nullptr);
+    out[1] = encode8<false>(v + 8, bd, zero, nullptr);
+    *reinterpret_cast<u32x2*>(p.codes + slot * (p.cols / 2) + (int64_t)cb * 8) = out;
+    p.scales[slot * (p.cols / 16) + cb] = (uint8_t)e;
+}
+
+// 16 consecutive inputs as raw words (BF16: two 16-byte loads, FP32: four),
+// kept unconverted so that several rows' loads can be in flight at once.
+template <bool kBF16>
+struct Raw16 {
+    u32x4 q[kBF16 ? 2 : 4];
+};
+
+template <bool kBF16>
+__device__ __forceinline__ Raw16<kBF16> load_raw16(const uint8_t* src)
+{
+    Raw16<kBF16> r;
+#pragma unroll
+    for (int i = 0; i < (kBF16 ? 2 : 4); ++i) r.q[i] = reinterpret_cast<const u32x4*>(src)[i];
+    return r;
+}
+
+template <bool kBF16>
+__device__ __forceinline__ void unpack16(const Raw16<kBF16>& r, float v[16])
+{
+    if (kBF16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t w = r.q[i / 4][i % 4];
+            v[2 * i] = bf16_lo(w);
+            v[2 * i + 1] = bf16_hi(w);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(r.q[i / 4][i % 4]);
+    }
+}
+
 template <bool kBF16>
 __global__ __launch_bounds__(256) void k_kv_write(KvParams p)
 {
     constexpr int esz = kBF16 ? 2 : 4;
     const TensorScale ts = make_tensor_scale(*p.amax);
-    const int64_t nbc = p.cols / 16;
-    const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t b = blockIdx.x * blockDim.x + threadIdx.x; b < p.items; b += stride) {
-        const uint32_t t = fdiv(b, p.div);
-        const uint32_t cb = b - t * p.div.d;
-        const int64_t slot = p.slots[t];
-        if (slot < 0 || slot >= p.num_slots) continue;
-        const uint8_t* src = p.x + ((int64_t)t * p.ld + (int64_t)cb * 16) * esz;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t nbc = (uint32_t)(p.cols / 16);
+    KvWalk w = kv_walk();
+    int64_t next0 = kv_slot_of(p, w.u);
+    int64_t next1 = kv_slot_of(p, w.u + w.step);
+    for (; w.u < p.units; w.u += 2 * w.step) {
+        const int64_t slot0 = next0, slot1 = next1;
+        next0 = kv_slot_of(p, w.u + 2 * w.step);
+        next1 = kv_slot_of(p, w.u + 3 * w.step);
+        // the second unit exists only while u + step < units; otherwise it
+        // repeats the first unit's addresses (loads in bounds, no stores)
+        const bool has1 = w.u + w.step < p.units;
+        const uint32_t u0 = (uint32_t)w.u;
+        const uint32_t u1 = has1 ? (uint32_t)(w.u + w.step) : u0;
+        const uint32_t t0 = __builtin_amdgcn_readfirstlane(fdiv(u0, p.div));
+        const uint32_t t1 = __builtin_amdgcn_readfirstlane(fdiv(u1, p.div));
+        const uint32_t cb0 = (u0 - t0 * p.div.d) * 64u + lane;
+        const uint32_t cb1 = (u1 - t1 * p.div.d) * 64u + lane;
+        // lanes past the row's last block load that block and store nothing
+        const uint32_t lb0 = cb0 < nbc ? cb0 : nbc - 1u;
+        const uint32_t lb1 = cb1 < nbc ? cb1 : nbc - 1u;
+        const Raw16<kBF16> r0 = load_raw16<kBF16>(p.x + ((int64_t)t0 * p.ld + (int64_t)lb0 * 16) * esz);
+        const Raw16<kBF16> r1 = load_raw16<kBF16>(p.x + ((int64_t)t1 * p.ld + (int64_t)lb1 * 16) * esz);
         float v[16];
-        load8<kBF16>(src, v);
-        load8<kBF16>(src + 8 * esz, v + 8);
-        float aB = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) aB = __builtin_fmaxf(aB, __builtin_fabsf(v[i]));
-        BlockDiv bd;
-        bool zero;
-        const uint32_t e = block_scale(aB, ts, bd, zero);
-        u32x2 out;
-        out[0] = encode8<false>(v, bd, zero, nullptr);
-        out[1] = encode8<false>(v + 8, bd, zero, nullptr);
-        *reinterpret_cast<u32x2*>(p.codes + slot * (p.cols / 2) + (int64_t)cb * 8) = out;
-        p.scales[slot * nbc + cb] = (uint8_t)e;
+        if (slot0 >= 0 && slot0 < p.num_slots && cb0 < nbc) {
+            unpack16<kBF16>(r0, v);
+            kv_write_block<kBF16>(p, ts, slot0, cb0, v);
+        }
+        if (has1 && slot1 >= 0 && slot1 < p.num_slots && cb1 < nbc) {
+            unpack16<kBF16>(r1, v);
+            kv_write_block<kBF16>(p, ts, slot1, cb1, v);
+        }
     }
 }
 
-// One thread per 8 outputs (one code word) of a gathered row.
+// Read: a chunk is 512 features of one gathered row, 8 per lane (one code
+// word), so each lane's 16-byte BF16 store (or two FP32 stores) sits next to
+// its neighbours'.  Out-of-range slots give zero rows.  Two units per
+// iteration, loads first, as in the write.
 template <bool kOutBF16>
 __global__ __launch_bounds__(256) void k_kv_read(KvParams p)
 {
     const float s_g = *p.amax / kGlobalDivisor;
-    const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < p.items; t += stride) {
-        const uint32_t row = fdiv(t, p.div);
-        const int64_t c0 = (int64_t)(t - row * p.div.d) * 8;
-        const int64_t slot = p.slots[row];
-        uint32_t w = 0u;
-        float ev = 0.0f;
-        if (slot >= 0 && slot < p.num_slots) {
-            w = *reinterpret_cast<const uint32_t*>(p.codes + slot * (p.cols / 2) + c0 / 2);
-            ev = e4m3_decode(p.scales[slot * (p.cols / 16) + c0 / 16]);
-        }
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t nq = (uint32_t)(p.cols / 8);
+    KvWalk w = kv_walk();
+    int64_t next0 = kv_slot_of(p, w.u);
+    int64_t next1 = kv_slot_of(p, w.u + w.step);
+    for (; w.u < p.units; w.u += 2 * w.step) {
+        const int64_t slot0 = next0, slot1 = next1;
+        next0 = kv_slot_of(p, w.u + 2 * w.step);
+        next1 = kv_slot_of(p, w.u + 3 * w.step);
+        const bool has1 = w.u + w.step < p.units;
+        const uint32_t u0 = (uint32_t)w.u;
+        const uint32_t u1 = has1 ? (uint32_t)(w.u + w.step) : u0;
+        const uint32_t r0 = __builtin_amdgcn_readfirstlane(fdiv(u0, p.div));
+        const uint32_t r1 = __builtin_amdgcn_readfirstlane(fdiv(u1, p.div));
+        const uint32_t cq0 = (u0 - r0 * p.div.d) * 64u + lane;
+        const uint32_t cq1 = (u1 - r1 * p.div.d) * 64u + lane;
+        const bool v0 = slot0 >= 0 && slot0 < p.num_slots;
+        const bool v1 = slot1 >= 0 && slot1 < p.num_slots;
+        // loads from clamped addresses (slot 0, the row's last word) so that
+        // both units' loads issue unconditionally; invalid ones are discarded
+        const int64_t s0 = v0 ? slot0 : 0, s1 = v1 ? slot1 : 0;
+        const int64_t l0 = (int64_t)(cq0 < nq ? cq0 : nq - 1u) * 8;
+        const int64_t l1 = (int64_t)(cq1 < nq ? cq1 : nq - 1u) * 8;
+        uint32_t w0 = *reinterpret_cast<const uint32_t*>(p.codes + s0 * (p.cols / 2) + l0 / 2);
+        uint32_t w1 = *reinterpret_cast<const uint32_t*>(p.codes + s1 * (p.cols / 2) + l1 / 2);
+        const uint32_t b0 = p.scales[s0 * (p.cols / 16) + l0 / 16];
+        const uint32_t b1 = p.scales[s1 * (p.cols / 16) + l1 / 16];
         float e[8];
+        if (cq0 < nq) {
+            const float ev = v0 ? e4m3_decode(b0) : 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = ev;
-        dequant8_store<kOutBF16>(w, e, s_g, p.out + ((int64_t)row * p.ld + c0) * (kOutBF16 ? 2 : 4));
+            for (int j = 0; j < 8; ++j) e[j] = ev;
+            dequant8_store<kOutBF16>(v0 ? w0 : 0u, e, s_g,
+                                     p.out + ((int64_t)r0 * p.ld + l0) * (kOutBF16 ? 2 : 4));
+        }
+        if (has1 && cq1 < nq) {
+            const float ev = v1 ? e4m3_decode(b1) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e[j] = ev;
+            dequant8_store<kOutBF16>(v1 ? w1 : 0u, e, s_g,
+                                     p.out + ((int64_t)r1 * p.ld + l1) * (kOutBF16 ? 2 : 4));
+        }
     }
 }
 
@@ -1189,9 +1307,10 @@ hipError_t launch_kv_cache_write(const void* x, bool bf16, int64_t tokens, int64
     p.amax = amax;
     p.codes = codes;
     p.scales = scales;
-    p.items = (uint32_t)(tokens * (cols / 16));
-    p.div = make_fastdiv((uint32_t)(cols / 16));
-    const int grid = grid_for(p.items, kGridCap);
+    const uint32_t chunks = (uint32_t)((cols / 16 + 63) / 64);  // 64 blocks per chunk
+    p.units = (uint32_t)(tokens * chunks);
+    p.div = make_fastdiv(chunks);
+    const int grid = grid_for((uint64_t)p.units * 64, kGridCap);
     NVFP4_DISPATCH_BOOL(bf16, BF, hipLaunchKernelGGL((k_kv_write<BF>), dim3(grid), dim3(256), 0, s, p));
     return hipGetLastError();
 }
@@ -1209,9 +1328,10 @@ hipError_t launch_kv_cache_read(const uint8_t* codes, const uint8_t* scales, con
     p.codes = const_cast<uint8_t*>(codes);
     p.scales = const_cast<uint8_t*>(scales);
     p.out = static_cast<uint8_t*>(out);
-    p.items = (uint32_t)(n * (cols / 8));
-    p.div = make_fastdiv((uint32_t)(cols / 8));
-    const int grid = grid_for(p.items, kGridCap);
+    const uint32_t chunks = (uint32_t)((cols / 8 + 63) / 64);   // 512 features per chunk
+    p.units = (uint32_t)(n * chunks);
+    p.div = make_fastdiv(chunks);
+    const int grid = grid_for((uint64_t)p.units * 64, kGridCap);
     NVFP4_DISPATCH_BOOL(out_bf16, OB, hipLaunchKernelGGL((k_kv_read<OB>), dim3(grid), dim3(256), 0, s, p));
     return hipGetLastError();
 }
