@@ -106,11 +106,11 @@ __device__ __forceinline__ bool tiny_nonzero(float a)
     return (__float_as_uint(a) - 1u) < 0x217FFFFFu;
 }
 
-// y[i] = RN(x[i] / d) with the sign of x[i] (so -0 stays -0), for n values of
-// one block.  Markstein everywhere; a wave-uniform branch redoes the rare
-// tiny or extreme operands with IEEE division.
+// y[i] = RN(|x[i]| / d) for n values of one block.  Markstein everywhere; a
+// wave-uniform branch redoes the rare tiny or extreme operands with IEEE
+// division.
 template <int n>
-__device__ __forceinline__ void quotients(const float* x, const BlockDiv& b, float* y)
+__device__ __forceinline__ void quotient_mags(const float* x, const BlockDiv& b, float* y)
 {
     bool slow = !b.fast;
 #pragma unroll
@@ -126,6 +126,13 @@ __device__ __forceinline__ void quotients(const float* x, const BlockDiv& b, flo
             if (!b.fast || tiny_nonzero(ax)) y[i] = ax / b.d;
         }
     }
+}
+
+// y[i] = RN(x[i] / d) with the sign of x[i] (so -0 stays -0).
+template <int n>
+__device__ __forceinline__ void quotients(const float* x, const BlockDiv& b, float* y)
+{
+    quotient_mags<n>(x, b, y);
 #pragma unroll
     for (int i = 0; i < n; ++i)
         y[i] = __uint_as_float(__float_as_uint(y[i]) | (__float_as_uint(x[i]) & 0x80000000u));
@@ -160,7 +167,10 @@ __device__ __forceinline__ uint32_t fp4_pack2(uint32_t old, float a, float b)
 __device__ __forceinline__ float e2m1_sr_value(float a, uint32_t r)
 {
     a = __builtin_fminf(a, 6.0f);
-    int e = a < 2.0f ? 1 : (a < 4.0f ? 0 : -1);
+    // step = 2^(k-2) with k = clamp(exponent of a as m * 2^k, m in [0.5, 1), 1, 3):
+    // 0.5 below 2, 1 in [2, 4), 2 in [4, 6]
+    const int k = __builtin_amdgcn_frexp_expf(a);
+    const int e = 2 - (k < 1 ? 1 : (k > 3 ? 3 : k));
     float t = __builtin_ldexpf(a, e);
     float fl = __builtin_floorf(t);
     float frac = t - fl;
@@ -171,8 +181,15 @@ __device__ __forceinline__ float e2m1_sr_value(float a, uint32_t r)
 
 // ---------------------------------------------------------------- Philox
 
+// a ^ b ^ c in one gfx950 three-input bitwise op (truth table 0x96).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c)
+{
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): multipliers
 // 0xD2511F53 / 0xCD9E8D57, Weyl key increments 0x9E3779B9 / 0xBB67AE85.
+// Per round: two 32x32->64 products and two three-way XORs.
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1)
 {
 #pragma unroll
@@ -180,9 +197,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
         uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
         uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
         u32x4 n;
-        n[0] = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+        n[0] = xor3((uint32_t)(p1 >> 32), c[1], k0);
         n[1] = (uint32_t)p1;
-        n[2] = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        n[2] = xor3((uint32_t)(p0 >> 32), c[3], k1);
         n[3] = (uint32_t)p0;
         c = n;
         k0 += 0x9E3779B9u;

@@ -108,8 +108,9 @@ __device__ __forceinline__ uint32_t pack8_rne(const float y[8])
     return w;
 }
 
-// Stochastic rounding: each quotient is replaced by the E2M1 value its word
-// selects (with its sign), which the RNE conversion then encodes exactly.
+// Stochastic rounding: each signed quotient y[i] = RN(x[i]/d) is replaced by
+// the E2M1 value its word selects (with its sign), which the RNE conversion
+// then encodes exactly.
 template <int n>
 __device__ __forceinline__ void sr_values(float* y, const uint32_t* r)
 {
@@ -120,6 +121,17 @@ __device__ __forceinline__ void sr_values(float* y, const uint32_t* r)
     }
 }
 
+// The same from magnitudes y[i] = RN(|x[i]|/d), with the signs taken from x.
+template <int n>
+__device__ __forceinline__ void sr_values_mag(float* y, const float* x, const uint32_t* r)
+{
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+        float v = e2m1_sr_value(y[i], r[i]);
+        y[i] = __uint_as_float(__float_as_uint(v) | (__float_as_uint(x[i]) & 0x80000000u));
+    }
+}
+
 // Quantize 8 values sharing one block scale.
 template <bool kSR>
 __device__ __forceinline__ uint32_t encode8(const float v[8], const BlockDiv& bd, bool zero,
@@ -127,8 +139,12 @@ __device__ __forceinline__ uint32_t encode8(const float v[8], const BlockDiv& bd
 {
     if (zero) return 0u;
     float y[8];
-    quotients<8>(v, bd, y);
-    if (kSR) sr_values<8>(y, r);
+    if (kSR) {
+        quotient_mags<8>(v, bd, y);
+        sr_values_mag<8>(y, v, r);
+    } else {
+        quotients<8>(v, bd, y);
+    }
     return pack8_rne(y);
 }
 
