@@ -384,12 +384,21 @@ __global__ __launch_bounds__(256) void k_swiglu_amax(const uint8_t* h, int64_t l
         uint32_t rb = fdiv(t, div);
         uint32_t cg = t - rb * div.d;
         int64_t r0 = (int64_t)rb * 16, c0 = (int64_t)cg * 4;
+        // all 32 loads of the tile first: the stores below could alias h as
+        // far as the compiler knows, so loads issued between them would wait
+        u32x2 graw[16], uraw[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            graw[i] = *reinterpret_cast<const u32x2*>(h + ((r0 + i) * ld_h + c0) * 2);
+            uraw[i] = *reinterpret_cast<const u32x2*>(h + ((r0 + i) * ld_h + F + c0) * 2);
+        }
         float v[4][16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float g[4], u[4];
-            load4<true>(h + ((r0 + i) * ld_h + c0) * 2, g);
-            load4<true>(h + ((r0 + i) * ld_h + F + c0) * 2, u);
+            const float g[4] = {bf16_lo(graw[i][0]), bf16_hi(graw[i][0]), bf16_lo(graw[i][1]),
+                                bf16_hi(graw[i][1])};
+            const float u[4] = {bf16_lo(uraw[i][0]), bf16_hi(uraw[i][0]), bf16_lo(uraw[i][1]),
+                                bf16_hi(uraw[i][1])};
             uint32_t b[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
