@@ -286,10 +286,6 @@ __device__ __forceinline__ half8_t dequant_word(uint32_t w, _Float16 e)
     return r;
 }
 
-// Output tile index for workgroup `bid`: consecutive ids go round-robin to
-// the 8 XCDs, so ids are first regrouped so each XCD owns a contiguous band
-// of tiles; bands are walked in groups of 8 tile rows, column by column, so
-// the A rows of a group and the B columns just visited stay in that XCD's L2.
 // Eight E2M1 codes times the block scale e as BF16, for the weight-only
 // (BF16-activation) GEMM.  val * e needs at most 6 significant bits, so it
 // is exact in FP32 and its low 16 bits are zero: the BF16 value is the upper
@@ -309,6 +305,15 @@ __device__ __forceinline__ bf16x8_t dequant_word_bf16(uint32_t w, float e)
     return __builtin_bit_cast(bf16x8_t, r);
 }
 
+// Output tile index for workgroup `bid`: consecutive ids go round-robin to
+// the 8 XCDs, so ids are first regrouped so each XCD owns a contiguous band
+// of tiles; bands are walked in groups of 8 tile rows, column by column.  The
+// 32 tiles an XCD runs at once (one workgroup per CU) are then 8 rows x 4
+// columns that sweep K together, so each k-slice of an A panel is fetched
+// into that XCD's L2 once for 4 tiles and each B k-slice once for 8.  (A
+// panel is reused again one column step later only if it survives a whole K
+// sweep in the 4 MB L2; at these K it does not, and the re-read comes from the
+// Infinity Cache or HBM.)
 __device__ __forceinline__ void tile_of(uint32_t bid, uint32_t nbm, uint32_t nbn, uint32_t& tm,
                                         uint32_t& tn)
 {
