@@ -598,6 +598,38 @@ __global__ __launch_bounds__(256) void k_quant_t(QuantParams p)
     }
 }
 
+// 16 consecutive inputs as raw words (BF16: two 16-byte loads, FP32: four),
+// kept unconverted so that several rows' loads can be in flight at once.
+template <bool kBF16>
+struct Raw16 {
+    u32x4 q[kBF16 ? 2 : 4];
+};
+
+template <bool kBF16>
+__device__ __forceinline__ Raw16<kBF16> load_raw16(const uint8_t* src)
+{
+    Raw16<kBF16> r;
+#pragma unroll
+    for (int i = 0; i < (kBF16 ? 2 : 4); ++i) r.q[i] = reinterpret_cast<const u32x4*>(src)[i];
+    return r;
+}
+
+template <bool kBF16>
+__device__ __forceinline__ void unpack16(const Raw16<kBF16>& r, float v[16])
+{
+    if (kBF16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t w = r.q[i / 4][i % 4];
+            v[2 * i] = bf16_lo(w);
+            v[2 * i + 1] = bf16_hi(w);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(r.q[i / 4][i % 4]);
+    }
+}
+
 // ------------------------------------------------------------ 16x16 blocks
 
 // One wave per 16-row x 256-column strip; lane l covers columns
@@ -620,15 +652,19 @@ __global__ __launch_bounds__(256) void k_quant_2d(QuantParams p)
         int64_t c0 = (int64_t)strip * 256 + cg * 16;
         bool valid = c0 < p.cols;
         int64_t rbase = (int64_t)rb * 16 + rq;
+        // all four rows' loads issue before any use: lanes past the last
+        // column load column 0 of their rows instead and drop the values
+        const int64_t cl = valid ? c0 : 0;
+        Raw16<kBF16> raw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            raw[k] = load_raw16<kBF16>(p.x + ((rbase + 4 * k) * p.ld + cl) * esz);
         float v[4][16];
         float aB = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            if (valid) {
-                const uint8_t* src = p.x + ((rbase + 4 * k) * p.ld + c0) * esz;
-                load8<kBF16>(src, v[k]);
-                load8<kBF16>(src + 8 * esz, v[k] + 8);
-            } else {
+            unpack16<kBF16>(raw[k], v[k]);
+            if (!valid) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[k][i] = 0.0f;
             }
@@ -905,38 +941,6 @@ __device__ __forceinline__ void kv_write_block(const KvParams& p, const TensorSc
     out[1] = encode8<false>(v + 8, bd, zero, nullptr);
     *reinterpret_cast<u32x2*>(p.codes + slot * (p.cols / 2) + (int64_t)cb * 8) = out;
     p.scales[slot * (p.cols / 16) + cb] = (uint8_t)e;
-}
-
-// 16 consecutive inputs as raw words (BF16: two 16-byte loads, FP32: four),
-// kept unconverted so that several rows' loads can be in flight at once.
-template <bool kBF16>
-struct Raw16 {
-    u32x4 q[kBF16 ? 2 : 4];
-};
-
-template <bool kBF16>
-__device__ __forceinline__ Raw16<kBF16> load_raw16(const uint8_t* src)
-{
-    Raw16<kBF16> r;
-#pragma unroll
-    for (int i = 0; i < (kBF16 ? 2 : 4); ++i) r.q[i] = reinterpret_cast<const u32x4*>(src)[i];
-    return r;
-}
-
-template <bool kBF16>
-__device__ __forceinline__ void unpack16(const Raw16<kBF16>& r, float v[16])
-{
-    if (kBF16) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t w = r.q[i / 4][i % 4];
-            v[2 * i] = bf16_lo(w);
-            v[2 * i + 1] = bf16_hi(w);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(r.q[i / 4][i % 4]);
-    }
 }
 
 template <bool kBF16>

@@ -175,3 +175,27 @@ def test_deterministic_and_stream_ordered(nv):
     q3 = nv.quantize(x, axis=0, rht=True, mask=7, sr=True, seed=10)
     torch.cuda.synchronize()
     assert not torch.equal(q1.codes, q3.codes)
+
+
+def test_debug_mode_reports_nonfinite_amax(nv, monkeypatch):
+    """With NVFP4_DEBUG=1 the quantizer synchronizes once and refuses a tensor
+    whose amax is not finite (NVFP4_ERR_NONFINITE), writing no codes; finite
+    tensors quantize as without the flag."""
+    monkeypatch.setenv("NVFP4_DEBUG", "1")
+    x = workloads.activations(32, 64, 3).cuda()
+    ok = nv.quantize(x)
+    monkeypatch.delenv("NVFP4_DEBUG")
+    ref = nv.quantize(x)
+    assert torch.equal(ok.codes, ref.codes) and torch.equal(ok.scales, ref.scales)
+    monkeypatch.setenv("NVFP4_DEBUG", "1")
+    bad = x.clone()
+    bad[3, 5] = float("inf")
+    codes = torch.full((32, 32), 0x5A, dtype=torch.uint8, device="cuda")
+    scales = torch.full((32, 4), 0x5A, dtype=torch.uint8, device="cuda")
+    ts = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(nv.nvfp4_quantize_workspace_size(32, 64), dtype=torch.uint8, device="cuda")
+    st = nv.nvfp4_quantize(bad, nv.DTYPE_BF16, 32, 64, 64, nv.BLOCK_1D, 1, 0, nv.ROUND_RNE, 0, 0,
+                           0, 0, None, None, codes, scales, ts, ws, ws.numel())
+    torch.cuda.synchronize()
+    assert st == 8, nv.status_string(st)
+    assert torch.all(codes == 0x5A) and torch.all(scales == 0x5A)
