@@ -463,8 +463,13 @@ constexpr int kTCodeRow = kTT / 2;        // LDS bytes per transposed row (16 sl
 constexpr int kTCodeBytes = kTT * kTCodeRow;
 constexpr int kTScaleBytes = kTT * 16;
 
+// Occupancy: the 1D variants fit three waves per SIMD (at most 168 VGPRs)
+// without spilling; left alone the compiler took 203 for the SR variant,
+// two waves per SIMD, and ran 7% slower.  The 2D variants keep their
+// registers (they would spill).
 template <bool kBF16, bool kSR, bool kRHT, bool k2D>
-__global__ __launch_bounds__(256) void k_quant_t(QuantParams p)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(k2D ? 1 : 3)))
+void k_quant_t(QuantParams p)
 {
     constexpr int esz = kBF16 ? 2 : 4;
     __shared__ __attribute__((aligned(16))) uint8_t lds_codes[kTCodeBytes];
