@@ -262,6 +262,41 @@ nvfp4_status nvfp4_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, in
                               nvfp4_dtype out_dtype, void* c, int64_t ldc, void* stream);
 
 /*
+ * The first fprop GEMM of the MLP with the activation after it fused into its
+ * epilogue (the MLP GEMMs on NVFP4 inputs with BF16 outputs: readjensen.com
+ * recipe paragraph; the Llama 3 models of its benchmark paragraph use
+ * SwiGLU).  It computes, in one launch (plus two one-workgroup reductions):
+ *   H         = s_A s_B A B^T rounded to BF16, exactly as nvfp4_gemm NT with
+ *               BF16 output (A [M, K], B [N, K], both blocked along K);
+ *               stored to h [M, N] (row pitch ldh) only when h is non-NULL
+ *   act       BF16 [M, N/2] (row pitch ld_act) <- the nvfp4_swiglu_amax
+ *               arithmetic on H, bit for bit
+ *   amax      device float <- max |act|
+ *   amax_rht  device float <- max |RHT16 down the columns of act|
+ * B's rows are W_gu's gate and up rows interleaved in blocks of 64: rows
+ * 128q .. 128q+63 are gate rows 64q .. 64q+63 and rows 128q+64 .. 128q+127
+ * the up rows 64q .. 64q+63, so H's column 128q + c (c < 64) is gate column
+ * 64q + c and 128q + 64 + c its up column.  act's column 64q + c pairs them.
+ * (A weight stored in this row order is an ordinary NVFP4 tensor: quantize,
+ * dequantize and the dgrad/wgrad GEMMs treat it like any other.)
+ * Shape rules: N % 128 == 0; M % 16 == 0; K % 128 == 0, K > 0; K/2 * 256 <
+ * 2^31; ld_act >= N/2; ldh >= N when h is given.  Code and scale planes
+ * 16-byte aligned; act 8-byte aligned with ld_act % 4 == 0.  M == 0 or
+ * N == 0 writes only amax = amax_rht = 0.  Workspace:
+ * nvfp4_gemm_swiglu_workspace_size(M, N) bytes (two floats per 256 x 256
+ * output tile).
+ */
+size_t nvfp4_gemm_swiglu_workspace_size(int64_t M, int64_t N);
+nvfp4_status nvfp4_gemm_swiglu(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                               const uint8_t* a_scales, const float* a_tensor_scale,
+                               nvfp4_block a_block, const uint8_t* b_codes,
+                               const uint8_t* b_scales, const float* b_tensor_scale,
+                               nvfp4_block b_block, void* h, int64_t ldh, void* act,
+                               int64_t ld_act, uint32_t rht_sign_mask, float* amax,
+                               float* amax_rht, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * MXFP4, the power-of-two-scaled format the pages compare NVFP4 with
  * ("NVFP4: cos'e e come supera FP8 e BF16", guiahardware.es, section "Cos'e
  * NVFP4": NVFP4's E4M3 scales against power-of-two scaling such as MXFP4;

@@ -37,7 +37,7 @@ EXPORTS = ("nvfp4_version", "nvfp4_status_string", "nvfp4_quantize_workspace_siz
            "nvfp4_swiglu_amax", "nvfp4_rht16",
            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize",
            "nvfp4_mx_gemm", "nvfp4_gemm_w4a16", "nvfp4_kv_cache_write",
-           "nvfp4_kv_cache_read")
+           "nvfp4_kv_cache_read", "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu")
 
 
 class NVFP4Error(RuntimeError):
@@ -86,6 +86,11 @@ def _load():
     L.nvfp4_kv_cache_write.argtypes = [vp, ci, i64, i64, i64, vp, vp, i64, vp, vp, vp]
     L.nvfp4_kv_cache_read.restype = ci
     L.nvfp4_kv_cache_read.argtypes = [vp, vp, vp, i64, i64, vp, i64, ci, vp, i64, vp]
+    L.nvfp4_gemm_swiglu_workspace_size.restype = ctypes.c_size_t
+    L.nvfp4_gemm_swiglu_workspace_size.argtypes = [i64, i64]
+    L.nvfp4_gemm_swiglu.restype = ci
+    L.nvfp4_gemm_swiglu.argtypes = [i64, i64, i64, vp, vp, vp, ci, vp, vp, vp, ci, vp, i64, vp, i64,
+                                    u32, vp, vp, vp, ctypes.c_size_t, vp]
     return L
 
 
@@ -199,6 +204,19 @@ def nvfp4_kv_cache_read(cache_codes, cache_scales, amax, num_slots, cols, slots,
                         ld_out, stream=None) -> int:
     return lib.nvfp4_kv_cache_read(_p(cache_codes), _p(cache_scales), _p(amax), num_slots, cols,
                                    _p(slots), n, out_dtype, _p(out), ld_out, _stream(stream))
+
+
+def nvfp4_gemm_swiglu_workspace_size(M: int, N: int) -> int:
+    return lib.nvfp4_gemm_swiglu_workspace_size(M, N)
+
+
+def nvfp4_gemm_swiglu(M, N, K, a_codes, a_scales, a_tensor_scale, a_block, b_codes, b_scales,
+                      b_tensor_scale, b_block, h, ldh, act, ld_act, rht_sign_mask, amax, amax_rht,
+                      workspace, workspace_bytes, stream=None) -> int:
+    return lib.nvfp4_gemm_swiglu(M, N, K, _p(a_codes), _p(a_scales), _p(a_tensor_scale), a_block,
+                                 _p(b_codes), _p(b_scales), _p(b_tensor_scale), b_block, _p(h),
+                                 ldh, _p(act), ld_act, rht_sign_mask, _p(amax), _p(amax_rht),
+                                 _p(workspace), workspace_bytes, _stream(stream))
 
 
 # ---------------------------------------------------------------- tensor-level helpers
@@ -343,6 +361,52 @@ def gemm(layout: str, a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16,
         BLOCK_2D if a.block2d else BLOCK_1D, b.codes, b.scales, b.tensor_scale,
         BLOCK_2D if b.block2d else BLOCK_1D, _dtype_code(out), out, out.stride(0)))
     return out
+
+
+def interleave_gate_up(w: torch.Tensor) -> torch.Tensor:
+    """W_gu [2F, K] as [gate | up] rows -> the row order nvfp4_gemm_swiglu takes:
+    gate and up rows interleaved in blocks of 64 (F % 64 == 0).  A plain row
+    permutation (a storage-order choice for the weight)."""
+    F2, K = w.shape
+    F = F2 // 2
+    assert F2 % 128 == 0
+    return w.reshape(2, F // 64, 64, K).transpose(0, 1).reshape(F2, K).contiguous()
+
+
+def deinterleave_gate_up_columns(h: torch.Tensor) -> torch.Tensor:
+    """The inverse permutation on the columns of H = A W^T: [gate | up]."""
+    rows, F2 = h.shape
+    F = F2 // 2
+    return h.reshape(rows, F // 64, 2, 64).transpose(1, 2).reshape(rows, F2)
+
+
+def gemm_swiglu(a: NVFP4Tensor, b: NVFP4Tensor, rht_mask: int, store_h: bool = False,
+                act_out: torch.Tensor | None = None, h_out: torch.Tensor | None = None):
+    """GEMM 1 of the MLP with SwiGLU and both amaxes of its output in the
+    epilogue: a [M, K], b [N, K] with gate/up rows interleaved in blocks of 64
+    (interleave_gate_up).  Returns (act [M, N/2], amax, amax_rht, H or None)."""
+    M, K, N = a.rows, a.cols, b.rows
+    assert b.cols == K and not a.axis == 0 and not b.axis == 0
+    dev = a.codes.device
+    act = act_out if act_out is not None else torch.empty(M, N // 2, dtype=torch.bfloat16,
+                                                          device=dev)
+    h = h_out
+    if h is None and store_h:
+        h = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    am = torch.empty(1, dtype=torch.float32, device=dev)
+    amr = torch.empty(1, dtype=torch.float32, device=dev)
+    nws = nvfp4_gemm_swiglu_workspace_size(M, N)
+    key = ("swiglu", str(dev), torch.cuda.current_stream(dev).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nws:
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    _check("nvfp4_gemm_swiglu", nvfp4_gemm_swiglu(
+        M, N, K, a.codes, a.scales, a.tensor_scale, BLOCK_2D if a.block2d else BLOCK_1D,
+        b.codes, b.scales, b.tensor_scale, BLOCK_2D if b.block2d else BLOCK_1D,
+        h, h.stride(0) if h is not None else 0, act, act.stride(0), rht_mask, am, amr, ws,
+        ws.numel()))
+    return act, am, amr, h
 
 
 def gemm_w4a16(a: torch.Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16,

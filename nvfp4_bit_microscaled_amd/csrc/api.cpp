@@ -405,4 +405,48 @@ nvfp4_status nvfp4_kv_cache_read(const uint8_t* cache_codes, const uint8_t* cach
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t nvfp4_gemm_swiglu_workspace_size(int64_t M, int64_t N)
+{
+    if (M <= 0 || N <= 0) return 2 * sizeof(float);
+    const uint64_t t = (uint64_t)((M + 255) / 256) * (uint64_t)((N + 255) / 256);
+    return (size_t)(2 * t * sizeof(float));
+}
+
+nvfp4_status nvfp4_gemm_swiglu(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                               const uint8_t* a_scales, const float* a_tensor_scale,
+                               nvfp4_block a_block, const uint8_t* b_codes,
+                               const uint8_t* b_scales, const float* b_tensor_scale,
+                               nvfp4_block b_block, void* h, int64_t ldh, void* act,
+                               int64_t ld_act, uint32_t rht_sign_mask, float* amax,
+                               float* amax_rht, void* workspace, size_t workspace_bytes,
+                               void* stream)
+{
+    if (a_block != NVFP4_BLOCK_1D && a_block != NVFP4_BLOCK_2D) return NVFP4_ERR_INVALID_ARG;
+    if (b_block != NVFP4_BLOCK_1D && b_block != NVFP4_BLOCK_2D) return NVFP4_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || !amax || !amax_rht) return NVFP4_ERR_INVALID_ARG;
+    if (N % 128 || M % 16) return NVFP4_ERR_SHAPE;
+    if (K == 0 || K % 128) return NVFP4_ERR_SHAPE;
+    if (ld_act < N / 2 || (h && ldh < N)) return NVFP4_ERR_SHAPE;
+    // buffer records of a 256-row tile in 32 bits; tile ids in 31 bits
+    if ((uint64_t)K / 2 * 256 >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
+    const uint64_t tiles = (uint64_t)((M + 255) / 256) * (uint64_t)((N + 255) / 256);
+    if (tiles >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M == 0 || N == 0) return from_hip(launch_write_zero_scale(amax, amax_rht, s));
+    if (!act || !a_codes || !a_scales || !a_tensor_scale || !b_codes || !b_scales ||
+        !b_tensor_scale)
+        return NVFP4_ERR_INVALID_ARG;
+    if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) || !aligned16(b_scales))
+        return NVFP4_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(act) & 7u) != 0 || ld_act % 4) return NVFP4_ERR_ALIGN;
+    if (h && (reinterpret_cast<uintptr_t>(h) & 1u) != 0) return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < nvfp4_gemm_swiglu_workspace_size(M, N))
+        return NVFP4_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return NVFP4_ERR_ALIGN;
+    GemmOperand A{a_codes, a_scales, a_tensor_scale, a_block == NVFP4_BLOCK_2D, true};
+    GemmOperand B{b_codes, b_scales, b_tensor_scale, b_block == NVFP4_BLOCK_2D, true};
+    return from_hip(launch_gemm_swiglu(M, N, K, A, B, h, ldh, act, ld_act, rht_sign_mask,
+                                       static_cast<float*>(workspace), amax, amax_rht, s));
+}
+
 }  // extern "C"

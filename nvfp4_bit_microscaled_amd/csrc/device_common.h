@@ -244,6 +244,31 @@ __device__ __forceinline__ void rht16_inplace(float v[16], uint32_t mask)
     for (int i = 0; i < 16; ++i) v[i] = 0.25f * v[i];
 }
 
+// ---------------------------------------------------------------- SwiGLU
+
+// RNE FP32 -> BF16 bits (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// act = BF16(BF16(silu(g)) * u) for BF16-valued g (gate) and u (up), with
+// silu(g) = g / (1 + exp(-g)) in FP32: the rounding points of a BF16
+// framework's silu and multiply.  The reciprocal unit (1 ulp) stands in for a
+// correctly rounded division, as the result only feeds a BF16 rounding; its
+// output flushes below 2^-126, so denominators from 2^126 up (g < -87.3) take
+// the IEEE division.  The standalone SwiGLU pass and the GEMM epilogue that
+// fuses it both use this, so their outputs agree bit for bit.
+__device__ __forceinline__ uint32_t swiglu_bf16_bits(float g, float u)
+{
+    const float den = 1.0f + expf(-g);
+    float sg = g * __builtin_amdgcn_rcpf(den);
+    if (den >= 8.5070592e37f) sg = g / den;  // 2^126
+    const float sb = __uint_as_float(f32_to_bf16_bits(sg) << 16);
+    return f32_to_bf16_bits(sb * u);
+}
+
 // ---------------------------------------------------------------- reductions
 
 __device__ __forceinline__ float wave_max(float v)

@@ -43,6 +43,13 @@ struct GemmParams {
     const uint16_t* a_bf16;  // weight-only GEMM: BF16 activations [M, K], row pitch lda
     int64_t lda;
     bool vec16;    // C base and row pitch are 16-byte aligned (whole-line epilogue)
+    // SwiGLU epilogue (k_gemm_kk<true>): act [M, N/2] BF16, row pitch ld_act;
+    // H itself (through c) only when store_h; two amax partials per workgroup
+    uint8_t* act;
+    int64_t ld_act;
+    uint32_t rht_mask;
+    float* partials;   // [grid] max|act|, then [grid] max|RHT16 of act down columns|
+    bool store_h, act_vec16;
 };
 
 // 8x8 nibble transpose: in[k] holds element (k, j) in nibble j; out[j] gets
@@ -641,6 +648,10 @@ constexpr int kKKCodes = 256 * kKKRow;           // 16 KB
 constexpr int kKKOperand = kKKCodes + 256 * 8;   // + 2 KB scales
 constexpr int kKKStage = 2 * kKKOperand;
 constexpr int kKKLds = 3 * kKKStage;             // 110592 bytes
+// the SwiGLU epilogue's workgroup reduction slots (8 floats), past the H and
+// act staging areas (4 x 8704 + 4 x 4608 bytes)
+constexpr int kKKLdsReserve = 4 * 32 * (256 + 16) + 4 * 32 * (128 + 16);
+static_assert(kKKLdsReserve + 32 <= kKKLds, "epilogue LDS fits the operand ring");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -651,6 +662,128 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // ... and with only the LDS / scalar-memory counter drained (vmcnt left at its
 // maximum 63)
 #define NVFP4_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+// SwiGLU epilogue of a 256 x 256 tile of H = s_A s_B A B^T whose B rows are
+// interleaved in blocks of 64: rows 128 q .. 128 q + 63 are gate rows
+// 64 q .. 64 q + 63 and rows 128 q + 64 .. 128 q + 127 the matching up rows.
+// A wave's 128 x 128 sub-tile then holds gate columns 0-63 in acc[.][0..1]
+// and their up columns in acc[.][2..3] of the same lanes (column
+// 32 j + 8 g + 4 lk + e), so act = BF16(BF16(silu(g)) u) of the BF16-rounded
+// H values needs no data exchange.  act column c' of the wave's 128 x 64 block
+// is column n0 / 2 + 64 wn + c' of act.  Both amaxes of act are reduced here:
+// max|act|, and max|RHT16 of act down its columns| over 16-row groups (rows
+// 32 i + lr, lr = lane % 32: a group is lanes 16 h .. 16 h + 15 of one lane
+// half, so the butterflies are lane swaps at distances 1, 2, 4, 8).  Rows past
+// M hold zeros (A's rows past M read as zeros) and are not stored; M % 16 == 0
+// keeps them out of every group with stored rows.  N % 128 == 0: a wave's
+// columns are all valid or all past N.
+__device__ __forceinline__ void swiglu_epilogue(const GemmParams& p, float16_t (&acc)[4][4],
+                                                int64_t m0, int64_t n0, int wm, int wn, int lr,
+                                                int lk, float sab, uint8_t* lds)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool wave_ok = n0 + 128 * wn < p.N;  // wave-uniform
+    float m_plain = 0.0f, m_rht = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float gv = __uint_as_float(f32_to_bf16_bits(acc[i][j][r] * sab) << 16);
+                const float uv = __uint_as_float(f32_to_bf16_bits(acc[i][j + 2][r] * sab) << 16);
+                const float a = __uint_as_float(swiglu_bf16_bits(gv, uv) << 16);
+                acc[i][j][r] = a;
+                m_plain = __builtin_fmaxf(m_plain, __builtin_fabsf(a));
+            }
+    if (wave_ok) {
+        // d_i x_i, butterflies (x_j + x_{j+h}, x_j - x_{j+h}) for j & h == 0,
+        // then 1/4: the lane at group row i & h == 0 keeps the sum, its
+        // partner the difference, in the transform's FP32 operation order
+        const uint32_t sgn = ((p.rht_mask >> (lr & 15)) & 1u) << 31;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float v = __uint_as_float(__float_as_uint(acc[i][j][r]) ^ sgn);
+#pragma unroll
+                    for (int h = 1; h < 16; h <<= 1) {
+                        const float pv = __shfl_xor(v, h, 64);
+                        v = (lr & h) ? pv - v : v + pv;
+                    }
+                    m_rht = __builtin_fmaxf(m_rht, __builtin_fabsf(0.25f * v));
+                }
+    } else {
+        m_plain = 0.0f;
+    }
+    // act: 32 rows at a time through a wave-private LDS area (full tiles with
+    // 16-byte aligned act rows: 8 lanes per 128-byte row), else 8-byte stores
+    const int64_t row0 = m0 + wm * 128;
+    const int64_t col0 = n0 / 2 + 64 * wn;
+    if (wave_ok) {
+        if (p.act_vec16 && m0 + kTM <= p.M) {
+            constexpr int kP = 128 + 16;
+            uint8_t* wl = lds + 4 * 32 * (256 + 16) + wave * 32 * kP;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        u32x2 w;
+                        w[0] = (__float_as_uint(acc[i][j][4 * g]) >> 16) |
+                               (__float_as_uint(acc[i][j][4 * g + 1]) & 0xFFFF0000u);
+                        w[1] = (__float_as_uint(acc[i][j][4 * g + 2]) >> 16) |
+                               (__float_as_uint(acc[i][j][4 * g + 3]) & 0xFFFF0000u);
+                        *reinterpret_cast<u32x2*>(wl + lr * kP + (32 * j + 8 * g + 4 * lk) * 2) = w;
+                    }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = 8 * q + (lane >> 3);
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(wl + r * kP + 16 * (lane & 7));
+                    *reinterpret_cast<u32x4*>(p.act + ((row0 + 32 * i + r) * p.ld_act + col0) * 2 +
+                                              16 * (lane & 7)) = v;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = row0 + 32 * i + lr;
+                if (row >= p.M) continue;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        u32x2 w;
+                        w[0] = (__float_as_uint(acc[i][j][4 * g]) >> 16) |
+                               (__float_as_uint(acc[i][j][4 * g + 1]) & 0xFFFF0000u);
+                        w[1] = (__float_as_uint(acc[i][j][4 * g + 2]) >> 16) |
+                               (__float_as_uint(acc[i][j][4 * g + 3]) & 0xFFFF0000u);
+                        *reinterpret_cast<u32x2*>(p.act + (row * p.ld_act + col0 + 32 * j + 8 * g +
+                                                           4 * lk) * 2) = w;
+                    }
+            }
+        }
+    }
+    // both maxima of the workgroup: wave maxima, then four waves through LDS
+    m_plain = wave_max(m_plain);
+    m_rht = wave_max(m_rht);
+    float* red = reinterpret_cast<float*>(lds + kKKLdsReserve);
+    if (lane == 0) {
+        red[wave] = m_plain;
+        red[4 + wave] = m_rht;
+    }
+    NVFP4_WAIT_LGKMCNT0();
+    __builtin_amdgcn_s_barrier();
+    if (threadIdx.x == 0) {
+        p.partials[blockIdx.x] =
+            __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+        p.partials[gridDim.x + blockIdx.x] =
+            __builtin_fmaxf(__builtin_fmaxf(red[4], red[5]), __builtin_fmaxf(red[6], red[7]));
+    }
+}
 
 struct KKOperand {
     __amdgpu_buffer_rsrc_t codes, scales;  // records end at the operand's last row
@@ -723,6 +856,8 @@ struct KKPlan {
     static constexpr int start[9] = {0, 3, 6, 8, 10, 12, 12, 12, 12};
 };
 
+// kSwiGLU: GEMM 1 of the MLP with the SwiGLU epilogue (swiglu_epilogue).
+template <bool kSwiGLU>
 __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -898,6 +1033,22 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 #undef KK_READ_I
 #undef KK_SCALES_I
 #undef KK_N
+    if constexpr (kSwiGLU) {
+        NVFP4_WAIT_VMCNT(0);
+        NVFP4_WAIT_LGKMCNT0();
+        __builtin_amdgcn_s_barrier();  // every wave is done with the operand ring
+        const float sab = (*p.a_ts) * (*p.b_ts);
+        if (p.store_h) {
+            if (m0 + kTM <= p.M && n0 + kTN <= p.N) {
+                if (p.vec16) store_tile_lds<true>(p, acc, m0, n0, wm, wn, lr, lk, sab, lds);
+                else store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk, sab);
+            } else {
+                store_tile<false>(p, acc, m0, n0, wm, wn, lr, lk, sab);
+            }
+        }
+        swiglu_epilogue(p, acc, m0, n0, wm, wn, lr, lk, sab, lds);
+        return;
+    }
     if (m0 + kTM <= p.M && n0 + kTN <= p.N)
         if (p.vec16) {
             NVFP4_WAIT_VMCNT(0);
@@ -1257,9 +1408,9 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     }
     if (A.k_major && B.k_major && K % kTK == 0 && K / 2 * kTM < (1ll << 31)) {
         const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
-        hipFuncSetAttribute((const void*)k_gemm_kk, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kKKLds);
-        hipLaunchKernelGGL(k_gemm_kk, dim3((unsigned)t), dim3(256), kKKLds, s, p);
+        hipFuncSetAttribute((const void*)k_gemm_kk<false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kKKLds);
+        hipLaunchKernelGGL(k_gemm_kk<false>, dim3((unsigned)t), dim3(256), kKKLds, s, p);
         return hipGetLastError();
     }
     // full tiles: no bounds checks, 32-bit buffer offsets (planes below 2 GiB)
@@ -1283,6 +1434,43 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     return hipGetLastError();
 }
 
+
+// GEMM 1 of the MLP with the SwiGLU epilogue: H = s_A s_B A B^T (A [M, K],
+// B [N, K] with gate/up rows interleaved in blocks of 64, N % 128 == 0,
+// M % 16 == 0, K % 128 == 0), act [M, N/2], optionally H itself, and both
+// amaxes of act (partials: 2 floats per 256 x 256 tile).
+hipError_t launch_gemm_swiglu(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
+                              const GemmOperand& B, void* h, int64_t ldh, void* act,
+                              int64_t ld_act, uint32_t mask, float* partials, float* amax,
+                              float* amax_rht, hipStream_t s)
+{
+    GemmParams p{};
+    p.M = M; p.N = N; p.K = K;
+    p.a_codes = A.codes; p.a_scales = A.scales; p.a_ts = A.ts;
+    p.b_codes = B.codes; p.b_scales = B.scales; p.b_ts = B.ts;
+    p.a2d = A.block2d != 0;
+    p.b2d = B.block2d != 0;
+    p.out_bf16 = true;
+    p.store_h = h != nullptr;
+    p.c = static_cast<uint8_t*>(h);
+    p.ldc = h ? ldh : 0;
+    p.vec_out = h && ldh % 4 == 0 && reinterpret_cast<uintptr_t>(h) % 8 == 0;
+    p.vec16 = h && (ldh * 2) % 16 == 0 && reinterpret_cast<uintptr_t>(h) % 16 == 0;
+    p.act = static_cast<uint8_t*>(act);
+    p.ld_act = ld_act;
+    p.act_vec16 = (ld_act * 2) % 16 == 0 && reinterpret_cast<uintptr_t>(act) % 16 == 0;
+    p.rht_mask = mask & 0xFFFFu;
+    p.partials = partials;
+    const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
+    hipFuncSetAttribute((const void*)k_gemm_kk<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        kKKLds);
+    hipLaunchKernelGGL(k_gemm_kk<true>, dim3((unsigned)t), dim3(256), kKKLds, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_amax_finalize(partials, (int)t, amax, s);
+    if (e != hipSuccess) return e;
+    return launch_amax_finalize(partials + t, (int)t, amax_rht, s);
+}
 
 // ---------------------------------------------------------------------------
 // MXFP4 GEMM on the native scaled FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4,

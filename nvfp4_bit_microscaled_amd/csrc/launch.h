@@ -107,6 +107,18 @@ hipError_t launch_kv_cache_read(const uint8_t* codes, const uint8_t* scales, con
                                 int64_t num_slots, int64_t cols, const int64_t* slots, int64_t n,
                                 bool out_bf16, void* out, int64_t ld_out, hipStream_t s);
 
+// max over partials[0 .. n) into *amax (one workgroup).
+hipError_t launch_amax_finalize(const float* partials, int n, float* amax, hipStream_t s);
+
+// GEMM 1 of the MLP with the SwiGLU epilogue (NT, both K-major): B's rows are
+// gate/up interleaved in blocks of 64; N % 128 == 0, M % 16 == 0, K % 128 == 0.
+// act [M, N/2] BF16 (pitch ld_act), H [M, N] BF16 only when h is non-null;
+// partials needs 2 floats per 256 x 256 output tile.
+hipError_t launch_gemm_swiglu(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
+                              const GemmOperand& B, void* h, int64_t ldh, void* act,
+                              int64_t ld_act, uint32_t mask, float* partials, float* amax,
+                              float* amax_rht, hipStream_t s);
+
 hipError_t launch_fill_zero(void* c, bool bf16, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
 
 }  // namespace nvfp4

@@ -359,13 +359,6 @@ __global__ __launch_bounds__(256) void k_amax_dual(QuantParams p)
 
 // ------------------------------------------------------------ SwiGLU + amaxes
 
-// RNE FP32 -> BF16 bits (finite inputs)
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // The producer of the MLP's second GEMM input, fused with both of its tensor
 // amaxes: act = BF16(BF16(silu(gate)) * up) with silu(g) = g / (1 + exp(-g))
 // in FP32 (the reciprocal from the hardware unit; the BF16 rounding points of
@@ -402,15 +395,7 @@ __global__ __launch_bounds__(256) void k_swiglu_amax(const uint8_t* h, int64_t l
             uint32_t b[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                // the reciprocal unit (1 ulp) instead of a correctly rounded
-                // division: the result only feeds a BF16 rounding.  Its
-                // output flushes below 2^-126, so denominators from 2^126 up
-                // (g < -87.3) take the IEEE division.
-                const float den = 1.0f + expf(-g[j]);
-                float sg = g[j] * __builtin_amdgcn_rcpf(den);
-                if (den >= 8.5070592e37f) sg = g[j] / den;  // 2^126
-                float sb = __uint_as_float(f32_to_bf16_bits(sg) << 16);
-                b[j] = f32_to_bf16_bits(sb * u[j]);
+                b[j] = swiglu_bf16_bits(g[j], u[j]);
                 float a = __uint_as_float(b[j] << 16);
                 v[j][i] = a;
                 m_plain = __builtin_fmaxf(m_plain, __builtin_fabsf(a));
@@ -1197,6 +1182,13 @@ hipError_t launch_amax_dual(const QuantArgs& a, float* partials, float* amax_dst
                        (float*)nullptr);
     hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(256), 0, s, partials + kMaxAmaxPartials,
                        grid, amax_rht_dst, (float*)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax_finalize(const float* partials, int n, float* amax, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(256), 0, s, partials, n, amax,
+                       (float*)nullptr);
     return hipGetLastError();
 }
 

@@ -34,7 +34,8 @@ def test_header_declares_the_abi():
                             "nvfp4_rht16",
                             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize",
                             "nvfp4_mx_dequantize", "nvfp4_mx_gemm", "nvfp4_gemm_w4a16",
-                            "nvfp4_kv_cache_write", "nvfp4_kv_cache_read"])
+                            "nvfp4_kv_cache_write", "nvfp4_kv_cache_read",
+                            "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -258,3 +259,34 @@ def test_kv_cache_validation(lib):
     assert kvr(lib, out=None) == 1
     assert kvr(lib, cc=None) == 1
     assert kvr(lib, n=0, out=None) == 0
+
+
+def gsw(lib, **kw):
+    args = dict(M=256, N=256, K=256, ac=FAKE, asc=FAKE, ats=FAKE, ab=0, bc=FAKE, bsc=FAKE, bts=FAKE,
+                bb=1, h=None, ldh=0, act=FAKE, ld_act=128, mask=0, amax=FAKE, amax_rht=FAKE,
+                ws=FAKE, wsb=1 << 20, stream=None)
+    args.update(kw)
+    return lib.nvfp4_gemm_swiglu(*args.values())
+
+
+def test_gemm_swiglu_validation(lib):
+    import nvfp4_bit_microscaled_amd as m
+    assert m.nvfp4_gemm_swiglu_workspace_size(256, 256) == 8
+    assert m.nvfp4_gemm_swiglu_workspace_size(32768, 28672) == 2 * 128 * 112 * 4
+    assert gsw(lib, ab=3) == 1
+    assert gsw(lib, M=-16) == 1
+    assert gsw(lib, amax=None) == 1
+    assert gsw(lib, N=192) == 2                 # N % 128
+    assert gsw(lib, M=40) == 2                  # M % 16
+    assert gsw(lib, K=0) == 2
+    assert gsw(lib, K=96) == 2                  # K % 128
+    assert gsw(lib, ld_act=120) == 2            # ld_act < N / 2
+    assert gsw(lib, h=FAKE, ldh=200) == 2       # ldh < N
+    assert gsw(lib, K=1 << 24) == 5             # 256-row records past 2^31 bytes
+    assert gsw(lib, act=None) == 1
+    assert gsw(lib, bc=MISALIGNED) == 3
+    assert gsw(lib, act=ctypes.c_void_p(0x10004)) == 3
+    assert gsw(lib, ld_act=130) == 3            # rows not a multiple of 8 bytes
+    assert gsw(lib, h=ODD, ldh=256) == 3
+    assert gsw(lib, wsb=4) == 6
+    assert gsw(lib, ws=None) == 6
