@@ -260,14 +260,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
 // output flushes below 2^-126, so denominators from 2^126 up (g < -87.3) take
 // the IEEE division.  The standalone SwiGLU pass and the GEMM epilogue that
 // fuses it both use this, so their outputs agree bit for bit.
+// kMayDivide = false leaves the division out: valid when g >= -87 (then
+// 1 + exp(-g) <= 1 + exp(87) < 2^126), which callers check for a whole wave
+// with swiglu_low (a per-lane select would compute the division always).
+template <bool kMayDivide>
 __device__ __forceinline__ uint32_t swiglu_bf16_bits(float g, float u)
 {
     const float den = 1.0f + expf(-g);
     float sg = g * __builtin_amdgcn_rcpf(den);
-    if (den >= 8.5070592e37f) sg = g / den;  // 2^126
+    if (kMayDivide && den >= 8.5070592e37f) sg = g / den;  // 2^126
     const float sb = __uint_as_float(f32_to_bf16_bits(sg) << 16);
     return f32_to_bf16_bits(sb * u);
 }
+
+// True where swiglu_bf16_bits may need its division.
+__device__ __forceinline__ bool swiglu_low(float g) { return g < -87.0f; }
 
 // ---------------------------------------------------------------- reductions
 

@@ -18,6 +18,8 @@
 // FP16 is used rather than BF16 because the VALU has a packed FP16 multiply
 // (two scale products per instruction) and the FP16 and BF16 MFMA rates are
 // equal; both hold the scaled products exactly.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -684,18 +686,36 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmParams& p, float16_t (
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool wave_ok = n0 + 128 * wn < p.N;  // wave-uniform
     float m_plain = 0.0f, m_rht = 0.0f;
+    // H rounded to BF16 in place, then act into the gate slots, with the rare
+    // division only if some gate value of the wave needs it
+    bool low = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float gv = __uint_as_float(f32_to_bf16_bits(acc[i][j][r] * sab) << 16);
-                const float uv = __uint_as_float(f32_to_bf16_bits(acc[i][j + 2][r] * sab) << 16);
-                const float a = __uint_as_float(swiglu_bf16_bits(gv, uv) << 16);
-                acc[i][j][r] = a;
-                m_plain = __builtin_fmaxf(m_plain, __builtin_fabsf(a));
+                acc[i][j][r] = __uint_as_float(f32_to_bf16_bits(acc[i][j][r] * sab) << 16);
+                if (j < 2) low |= swiglu_low(acc[i][j][r]);
             }
+    auto act_of = [&](auto may_divide) {
+        constexpr bool kDiv = decltype(may_divide)::value;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float a = __uint_as_float(
+                        swiglu_bf16_bits<kDiv>(acc[i][j][r], acc[i][j + 2][r]) << 16);
+                    acc[i][j][r] = a;
+                    m_plain = __builtin_fmaxf(m_plain, __builtin_fabsf(a));
+                }
+    };
+    if (__builtin_amdgcn_ballot_w64(low) != 0)
+        act_of(std::integral_constant<bool, true>{});
+    else
+        act_of(std::integral_constant<bool, false>{});
     if (wave_ok) {
         // d_i x_i, butterflies (x_j + x_{j+h}, x_j - x_{j+h}) for j & h == 0,
         // then 1/4: the lane at group row i & h == 0 keeps the sum, its

@@ -395,7 +395,10 @@ __global__ __launch_bounds__(256) void k_swiglu_amax(const uint8_t* h, int64_t l
             uint32_t b[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                b[j] = swiglu_bf16_bits(g[j], u[j]);
+                // per-lane select of the division: a wave-wide check of the
+                // gate values would need the tile's code twice, and the
+                // registers it costs lose more than the division here
+                b[j] = swiglu_bf16_bits<true>(g[j], u[j]);
                 float a = __uint_as_float(b[j] << 16);
                 v[j][i] = a;
                 m_plain = __builtin_fmaxf(m_plain, __builtin_fabsf(a));
