@@ -153,3 +153,23 @@ def test_full_size_llama8b_gemm1(nv):
     check_against_unfused(nv, act, am, amr, h, mask)
     del h
     check_amaxes_oracle(act, am, amr, mask)
+
+
+def test_gate_values_below_minus_87_take_the_division(nv):
+    """Weights scaled so that many gate values fall below -87, where silu's
+    denominator passes 2^126 and the epilogue takes its division path (waves
+    without such values take the path without it): still bit-equal to the
+    separate pass, which selects per element."""
+    M, F, K = 512, 256, 256
+    mask = workloads.sign_mask(9)
+    x = workloads.activations(M, K, 21)
+    w = nv.interleave_gate_up(workloads.weights(2 * F, K, 22).float() * 150.0)
+    a = nv.quantize(x.cuda())
+    b = nv.quantize(w.to(torch.bfloat16).cuda(), block2d=True)
+    act, am, amr, h = nv.gemm_swiglu(a, b, mask, store_h=True)
+    torch.cuda.synchronize()
+    gate = nv.deinterleave_gate_up_columns(h)[:, :F].float()
+    frac = (gate < -87.0).float().mean().item()
+    assert 0.001 < frac < 0.5, frac     # some waves take the division path, others not
+    check_against_unfused(nv, act, am, amr, h, mask)
+    check_amaxes_oracle(act, am, amr, mask)
