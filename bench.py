@@ -94,7 +94,7 @@ class Timer:
         self.pending = []
         self.enabled = False
 
-    def run(self, kind, fn, *a, **kw):
+    def run(self, kind, fn, *a, name=None, **kw):
         if not self.enabled:
             return fn(*a, **kw)
         e0 = self.torch.cuda.Event(enable_timing=True)
@@ -102,14 +102,17 @@ class Timer:
         e0.record()
         r = fn(*a, **kw)
         e1.record()
-        self.pending.append((kind, e0, e1))
+        self.pending.append((kind, name, e0, e1))
         return r
 
-    def totals(self):
+    def totals(self, by_name=False):
         out = {}
-        for kind, e0, e1 in self.pending:
-            t, n = out.get(kind, (0.0, 0))
-            out[kind] = (t + e0.elapsed_time(e1), n + 1)
+        for kind, name, e0, e1 in self.pending:
+            key = name if by_name else kind
+            if key is None:
+                continue
+            t, n = out.get(key, (0.0, 0))
+            out[key] = (t + e0.elapsed_time(e1), n + 1)
         return out
 
 
@@ -164,12 +167,12 @@ def main():
 
     def Q(name, x, **kw):
         qbytes[name] = qb(*x.shape, amax_pass=kw.get("amax_in") is None)
-        return timer.run("quantize", nv.quantize, x, **kw)
+        return timer.run("quantize", nv.quantize, x, name=name, **kw)
 
     def AMX(name, x):
         # max |x| and max |RHT16 down the columns of x| in one read
         qbytes[name] = x.shape[0] * x.shape[1] * 2
-        return timer.run("quantize", nv.amax, x, rht_mask=mask)
+        return timer.run("quantize", nv.amax, x, rht_mask=mask, name=name)
 
     def SWIGLU(name, h):
         # act = silu(gate) * up with both amaxes of act: reads H, writes act
@@ -262,6 +265,16 @@ def main():
         gemm_roles[role] = {"tflops": fl * args.steps / (t * 1e-3) / 1e12,
                             "avg_launch_ms": t / n, "launches": n}
     q_t, q_n = totals["quantize"]
+    # each quantize / amax call: time, algorithmic GB/s, and what bounds it
+    # (the stochastic-rounding calls are bound by VALU work: Philox and the
+    # exact SR selection; the others stream HBM)
+    q_calls = {}
+    for name, (t, n) in timer.totals(by_name=True).items():
+        if name not in qbytes:
+            continue
+        q_calls[name] = {"us": round(t / n * 1e3, 1),
+                         "GBps": round(qbytes[name] / (t / n * 1e-3) / 1e9, 1),
+                         "bound": "valu" if "_sr" in name else "hbm"}
     q_bytes = sum(qbytes.values()) * args.steps
     gemm_t = sum(totals["gemm_" + k][0] for k in role_flops)
     gemm_n = sum(totals["gemm_" + k][1] for k in role_flops)
@@ -287,6 +300,7 @@ def main():
                          for k, v in gemm_roles.items()},
         "quantize_GBps": round(q_bytes / (q_t * 1e-3) / 1e9, 1),
         "quantize_frac_of_hbm": round(q_bytes / (q_t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "quantize_by_call": q_calls,
         "swiglu_GBps": round(sum(swbytes.values()) * args.steps / (totals["swiglu"][0] * 1e-3) / 1e9, 1),
         "time_breakdown_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in per_kind.items()},
         "roofline": {"bound": "mfma", "kernel": "k_gemm_kk (K-major x K-major, all six MLP GEMMs)",
