@@ -105,6 +105,12 @@ def lib():
         L.oracle_kv_cache_read.restype = ctypes.c_int
         L.oracle_kv_cache_read.argtypes = [c_vp, c_vp, ctypes.c_float, c_i64, c_i64, c_vp, c_i64,
                                            c_vp, c_vp]
+        L.oracle_silu_f32.restype = ctypes.c_float
+        L.oracle_silu_f32.argtypes = [ctypes.c_float]
+        L.oracle_swiglu_one.restype = ctypes.c_uint16
+        L.oracle_swiglu_one.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+        L.oracle_swiglu.restype = ctypes.c_int
+        L.oracle_swiglu.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_set_num_threads.restype = None
@@ -327,6 +333,23 @@ def mx_gemm_full(M: int, N: int, K: int, a, b):
     mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     ref, ab = mx_gemm_pairs(M, N, K, a, b, mm.ravel(), nn.ravel())
     return ref.reshape(M, N), ab.reshape(M, N)
+
+
+def silu_f32(g: float) -> float:
+    return lib().oracle_silu_f32(g)
+
+
+def swiglu(h_bf16: np.ndarray):
+    """act = BF16(BF16(silu(gate)) * up) for h = [gate | up] (uint16 BF16 bits,
+    [rows, 2F]); returns (act, BF16(silu(gate))) as uint16 BF16 bits [rows, F]."""
+    h = np.ascontiguousarray(h_bf16, dtype=np.uint16)
+    rows, F2 = h.shape
+    act = np.zeros((rows, F2 // 2), dtype=np.uint16)
+    sb = np.zeros((rows, F2 // 2), dtype=np.uint16)
+    rc = lib().oracle_swiglu(_ptr(h), rows, F2 // 2, F2, _ptr(act), _ptr(sb))
+    if rc:
+        raise ValueError("oracle_swiglu: bad shape")
+    return act, sb
 
 
 def kv_cache_write(x: np.ndarray, slots, amax: float, cache_codes: np.ndarray,

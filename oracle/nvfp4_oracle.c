@@ -686,6 +686,59 @@ int oracle_mx_gemm_pairs(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes
 }
 
 /* ------------------------------------------------------------------ */
+/* SwiGLU                                                               */
+/* ------------------------------------------------------------------ */
+/*
+ * The activation between the MLP's two fprop GEMMs (the MLP GEMMs with BF16
+ * outputs: readjensen.com recipe paragraph; the Llama 3 models of its
+ * benchmark paragraph use SwiGLU), at a BF16 framework's rounding points:
+ *   act = BF16( BF16(silu(g)) * u ),  silu(g) = g / (1 + exp(-g)) in FP32
+ * for h = [gate | up] in BF16 [rows, 2F] (row pitch ld_h elements); act is
+ * written as BF16 bit patterns [rows, F], dense.  exp is the C library's
+ * single-precision expf, the division IEEE.
+ */
+static uint16_t bf16_bits_of(float f)
+{
+    return oracle_f32_to_bf16(f);
+}
+
+static float f32_of_bf16(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* silu(g) in FP32 for one value, and act for one (g, u) pair. */
+float oracle_silu_f32(float g)
+{
+    float den = 1.0f + expf(-g);
+    return g / den;
+}
+
+uint16_t oracle_swiglu_one(uint16_t g_bf16, uint16_t u_bf16)
+{
+    float sg = oracle_silu_f32(f32_of_bf16(g_bf16));
+    float sb = f32_of_bf16(bf16_bits_of(sg));
+    return bf16_bits_of(sb * f32_of_bf16(u_bf16));
+}
+
+/* act (and, if sb is not NULL, the BF16 silu values BF16(silu(gate))). */
+int oracle_swiglu(const uint16_t* h, int64_t rows, int64_t F, int64_t ld_h, uint16_t* act,
+                  uint16_t* sb)
+{
+    if (rows < 0 || F < 0 || ld_h < 2 * F) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < F; ++c) {
+            act[r * F + c] = oracle_swiglu_one(h[r * ld_h + c], h[r * ld_h + F + c]);
+            if (sb) sb[r * F + c] = bf16_bits_of(oracle_silu_f32(f32_of_bf16(h[r * ld_h + c])));
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* NVFP4 KV cache                                                       */
 /* ------------------------------------------------------------------ */
 /*

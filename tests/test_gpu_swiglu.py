@@ -100,3 +100,34 @@ def test_feeds_the_same_quantizations(nv):
     torch.cuda.synchronize()
     for u, v in ((q1, q2), (t1, t2)):
         assert torch.equal(u.codes, v.codes) and torch.equal(u.scales, v.scales)
+
+
+@pytest.mark.parametrize("rows,F", [(48, 272), (528, 64), (4096, 1024)])
+def test_act_against_the_oracle(nv, rows, F):
+    """act against the oracle's SwiGLU (FP32 silu with the C library's expf and
+    an IEEE division, BF16 rounding points): equal, or the product of up with
+    one of the two BF16 neighbours of the oracle's BF16 silu, and the latter
+    only where the oracle's FP32 silu lies within 4 FP32 ulps of the BF16
+    rounding boundary between the two (the kernel's exp and reciprocal are
+    within an ulp or two, so they may round silu to the other side)."""
+    h = make_h(rows, F, seed=rows * 3 + F)
+    mask = workloads.sign_mask(F + 1)
+    act, a, ar = nv.swiglu_amax(h.cuda(), mask)
+    torch.cuda.synchronize()
+    hb = to_oracle_input(h)
+    ref, sb = oracle.swiglu(hb)
+    sbf = torch.from_numpy(sb.view(np.int16)).view(torch.bfloat16).float()
+    lo, hi = bf16_neighbours(sbf)
+    u = h[:, F:].float()
+    got = act.cpu().view(torch.int16).numpy().view(np.uint16)
+    cand_lo = (lo * u).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    cand_hi = (hi * u).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    same = got == ref
+    ok = same | (got == cand_lo) | (got == cand_hi)
+    assert ok.all(), "%d outputs off by more than one BF16 step of silu" % int((~ok).sum())
+    g = h[:, :F].float().numpy()
+    for r, c in np.argwhere(~same):
+        sg = np.float32(oracle.silu_f32(float(g[r, c])))
+        other = (lo if got[r, c] == cand_lo[r, c] else hi)[r, c].item()
+        mid = (float(sbf[r, c]) + other) / 2.0
+        assert abs(float(sg) - mid) <= 4 * float(np.spacing(np.abs(sg))), (g[r, c], sg, mid)
