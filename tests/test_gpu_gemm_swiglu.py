@@ -6,7 +6,7 @@ SwiGLU activation and both amaxes of its output in the GEMM's epilogue.
   the same operands (same kernel main loop).
 - act and both amaxes equal, bit for bit, nvfp4_swiglu_amax run on that H
   (after undoing the gate/up column interleave); the standalone pass is
-  itself checked against a PyTorch FP32 reference in test_gpu_swiglu.
+  itself checked against the oracle's SwiGLU in test_gpu_swiglu.
 - Both amaxes equal the oracle's on the act the kernel produced.
 
 Source: the MLP GEMMs on NVFP4 inputs with BF16 outputs (readjensen.com

@@ -1,16 +1,16 @@
 """GPU parity: nvfp4_swiglu_amax, the MLP activation between the two fprop
 GEMMs fused with both tensor amaxes of its output.
 
-act is compared with a plain PyTorch FP32 reference taking the same rounding
-points (silu in FP32 rounded to BF16, product rounded to BF16).  The kernel's
-FP32 silu may differ from the reference's by an ulp or two (exponential and
-reciprocal implementations), which can move silu's BF16 rounding by one step:
-act must equal the rounded product of up with the reference silu's BF16 value
-or one of its two BF16 neighbours, and equal the first in all but a tiny
-fraction of elements.  The two amaxes must equal the
-oracle's on the act the kernel produced, bit for bit.  Source: the MLP GEMMs
-with BF16 outputs (readjensen.com recipe paragraph); Llama 3's SwiGLU MLP
-(benchmark paragraph models).
+act is compared with the oracle's SwiGLU and with a plain PyTorch FP32
+computation, both taking the same rounding points (silu in FP32 rounded to
+BF16, product rounded to BF16).  The kernel's FP32 silu may differ from a
+reference's by an ulp or two (exponential and reciprocal implementations),
+which can move silu's BF16 rounding by one step: act must equal the rounded
+product of up with the reference silu's BF16 value or one of its two BF16
+neighbours, the latter only near a BF16 rounding boundary.  The two amaxes
+must equal the oracle's on the act the kernel produced, bit for bit.
+Source: the MLP GEMMs with BF16 outputs (readjensen.com recipe paragraph);
+Llama 3's SwiGLU MLP (benchmark paragraph models).
 """
 import numpy as np
 import pytest
