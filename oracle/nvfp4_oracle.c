@@ -37,7 +37,9 @@
  * The MXFP4 functions near the end follow the open MX standard for the
  * power-of-two format the pages compare NVFP4 with (block size and scale
  * rule are the standard's; the pages give neither).  The KV-cache functions
- * after them store token rows in NVFP4 under a fixed calibration scale.
+ * after them store token rows in NVFP4 under a fixed calibration scale, and
+ * the SwiGLU function computes the MLP activation between its two GEMMs at
+ * BF16 rounding points.
  *
  * Every function is pinned by tests/test_oracle_*.py against something other
  * than itself (torch's float8_e4m3fn and bfloat16 casts, rocRAND's Philox,
