@@ -508,6 +508,18 @@ def kv_bench(torch, nv, workloads):
             "bytes_per_call": {"write": int(wb), "read": int(rb)}}
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, torch, nv, workloads, X, W_gu):
     """The oracle, as it stands, on a bounded sample of the step: fprop GEMM 1
     for the first `rows` tokens (all 28672 outputs, full K = 4096)."""
@@ -530,13 +542,26 @@ def cpu_baseline(args, torch, nv, workloads, X, W_gu):
     oracle.gemm_pairs("NT", rows, N, K, (xc, xs, xts, False), (wc, wsc, wts, True), ms.ravel(),
                       ns.ravel())
     tg = time.perf_counter() - t1
+    # the same on one thread, over rows / cores tokens (about the same wall time)
+    rows1 = max(1, rows // cores)
+    ms1, ns1 = np.meshgrid(np.arange(rows1), np.arange(N), indexing="ij")
+    oracle.set_num_threads(1)
+    t2 = time.perf_counter()
+    oracle.gemm_pairs("NT", rows1, N, K, (xc, xs, xts, False), (wc, wsc, wts, True), ms1.ravel(),
+                      ns1.ravel())
+    t1s = time.perf_counter() - t2
+    oracle.set_num_threads(cores)
     flops = 2.0 * rows * N * K
+    flops1 = 2.0 * rows1 * N * K
     qbytes = (x.numel() + w.numel()) * (2 + 0.5 + 1 / 16) + w.numel() * 2
     return {"value": round(flops / tg / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "fprop GEMM 1 (NT, 2D-quantized W_gu) on the first %d tokens: "
-                      "%d x 28672 x 4096 FP64 dot products (%.2f GFLOP) in %.1f s"
-                      % (rows, rows, flops / 1e9, tg),
+                      "%d x %d x %d FP64 dot products (%.2f GFLOP) in %.1f s"
+                      % (rows, rows, N, K, flops / 1e9, tg),
+            "single_thread_value": round(flops1 / t1s / 1e12, 6),
+            "single_thread_sample": "the same GEMM on the first %d tokens, one thread, %.1f s"
+                                    % (rows1, t1s),
             "quantize_GBps": round(qbytes / tq / 1e9, 4),
             "quantize_sample": "X rows 0-%d (1x16 RNE) and W_gu (16x16 RNE, amax pass), %.1f s"
                                % (rows - 1, tq)}
