@@ -29,6 +29,16 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// BF16 bits of two FP32 values rounded to nearest even, a in the low half:
+// one v_cvt_pk_bf16_f32 (these kernels keep FP32 denormals, so those round
+// like any other value).
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b)
+{
+    const float2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 struct GemmParams {
     int64_t M, N, K;
@@ -358,15 +368,9 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, float16_t (&acc)
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        uint32_t h[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            uint32_t u = __float_as_uint(acc[i][j][4 * g + e] * sab);
-                            h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // RNE
-                        }
                         u32x2 w;
-                        w[0] = h[0] | (h[1] << 16);
-                        w[1] = h[2] | (h[3] << 16);
+                        w[0] = bf16_pair(acc[i][j][4 * g] * sab, acc[i][j][4 * g + 1] * sab);
+                        w[1] = bf16_pair(acc[i][j][4 * g + 2] * sab, acc[i][j][4 * g + 3] * sab);
                         *reinterpret_cast<u32x2*>(crow + j * 32 + 8 * g) = w;
                     }
             }
@@ -405,15 +409,9 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, float16_t (&acc)
                 const int64_t off = row * p.ldc + col;
                 if (p.vec_out && (kFull || col + 3 < p.N)) {
                     if (p.out_bf16) {
-                        uint32_t h[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            uint32_t u = __float_as_uint(v[e]);
-                            h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-                        }
                         u32x2 w;
-                        w[0] = h[0] | (h[1] << 16);
-                        w[1] = h[2] | (h[3] << 16);
+                        w[0] = bf16_pair(v[0], v[1]);
+                        w[1] = bf16_pair(v[2], v[3]);
                         *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.c) + off) = w;
                     } else {
                         float4_t w;
@@ -426,9 +424,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, float16_t (&acc)
                     for (int e = 0; e < 4; ++e) {
                         if (!kFull && col + e >= p.N) break;
                         if (p.out_bf16) {
-                            uint32_t u = __float_as_uint(v[e]);
-                            u += 0x7FFFu + ((u >> 16) & 1u);
-                            reinterpret_cast<uint16_t*>(p.c)[off + e] = (uint16_t)(u >> 16);
+                            reinterpret_cast<uint16_t*>(p.c)[off + e] = (uint16_t)bf16_pair(v[e], 0.0f);
                         } else {
                             reinterpret_cast<float*>(p.c)[off + e] = v[e];
                         }
@@ -470,15 +466,9 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams& p, float16_t (&
                     const int j = jp * kJ + jj;
                     uint8_t* d = wl + lr * kPitch + (32 * jj + 8 * g + 4 * lk) * esz;
                     if (kBF16) {
-                        uint32_t h[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            uint32_t u = __float_as_uint(acc[i][j][4 * g + e] * sab);
-                            h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // RNE
-                        }
                         u32x2 w;
-                        w[0] = h[0] | (h[1] << 16);
-                        w[1] = h[2] | (h[3] << 16);
+                        w[0] = bf16_pair(acc[i][j][4 * g] * sab, acc[i][j][4 * g + 1] * sab);
+                        w[1] = bf16_pair(acc[i][j][4 * g + 2] * sab, acc[i][j][4 * g + 3] * sab);
                         *reinterpret_cast<u32x2*>(d) = w;
                     } else {
                         float4_t w;
