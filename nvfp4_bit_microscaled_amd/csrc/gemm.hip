@@ -866,8 +866,16 @@ struct KKPlan {
     static constexpr int start[9] = {0, 3, 6, 8, 10, 12, 12, 12, 12};
 };
 
+// Epilogue variants of k_gemm_kk.  kKKEpiAny handles every tile (edge tiles,
+// unaligned C rows, either output type).  The other two serve grids whose
+// tiles are all full with 16-byte aligned C rows, with only the LDS-staged
+// store of one output type: without the edge-tile code the accumulators leave
+// their AGPRs right where they are stored, instead of all at once with a part
+// spilled to scratch, whose reloads waited behind the tile's global stores.
+constexpr int kKKEpiAny = 0, kKKEpiBF16 = 1, kKKEpiF32 = 2;
+
 // kSwiGLU: GEMM 1 of the MLP with the SwiGLU epilogue (swiglu_epilogue).
-template <bool kSwiGLU>
+template <bool kSwiGLU, int kEpi = kKKEpiAny>
 __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -1059,7 +1067,12 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
         swiglu_epilogue(p, acc, m0, n0, wm, wn, lr, lk, sab, lds);
         return;
     }
-    if (m0 + kTM <= p.M && n0 + kTN <= p.N)
+    if constexpr (kEpi != kKKEpiAny) {
+        NVFP4_WAIT_VMCNT(0);
+        NVFP4_WAIT_LGKMCNT0();
+        __builtin_amdgcn_s_barrier();
+        store_tile_lds<kEpi == kKKEpiBF16>(p, acc, m0, n0, wm, wn, lr, lk, (*p.a_ts) * (*p.b_ts), lds);
+    } else if (m0 + kTM <= p.M && n0 + kTN <= p.N) {
         if (p.vec16) {
             NVFP4_WAIT_VMCNT(0);
             NVFP4_WAIT_LGKMCNT0();
@@ -1071,8 +1084,9 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
         } else {
             store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk, (*p.a_ts) * (*p.b_ts));
         }
-    else
+    } else {
         store_tile<false>(p, acc, m0, n0, wm, wn, lr, lk, (*p.a_ts) * (*p.b_ts));
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1418,9 +1432,11 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     }
     if (A.k_major && B.k_major && K % kTK == 0 && K / 2 * kTM < (1ll << 31)) {
         const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
-        hipFuncSetAttribute((const void*)k_gemm_kk<false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kKKLds);
-        hipLaunchKernelGGL(k_gemm_kk<false>, dim3((unsigned)t), dim3(256), kKKLds, s, p);
+        const bool all_full = M % kTM == 0 && N % kTN == 0 && p.vec16;
+        auto kern = !all_full ? k_gemm_kk<false, kKKEpiAny>
+                              : (out_bf16 ? k_gemm_kk<false, kKKEpiBF16> : k_gemm_kk<false, kKKEpiF32>);
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kKKLds);
+        hipLaunchKernelGGL(kern, dim3((unsigned)t), dim3(256), kKKLds, s, p);
         return hipGetLastError();
     }
     // full tiles: no bounds checks, 32-bit buffer offsets (planes below 2 GiB)
