@@ -1567,6 +1567,9 @@ __device__ __forceinline__ void mx_copy(const MxOperand& o, int kt, uint8_t* dst
                                              o.scale_off, kt * 4, 0, 0);
 }
 
+// kEpi as for k_gemm_kk: kKKEpiAny for any grid, the other two for grids of
+// full tiles with 16-byte aligned C rows (no spilled accumulators).
+template <int kEpi>
 __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -1653,7 +1656,12 @@ __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p)
                 }
         }
     }
-    if (m0 + kTM <= p.M && n0 + kTN <= p.N) {
+    if constexpr (kEpi != kKKEpiAny) {
+        NVFP4_WAIT_VMCNT(0);
+        NVFP4_WAIT_LGKMCNT0();
+        __builtin_amdgcn_s_barrier();
+        store_tile_lds<kEpi == kKKEpiBF16>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f, lds);
+    } else if (m0 + kTM <= p.M && n0 + kTN <= p.N) {
         if (p.vec16) {
             NVFP4_WAIT_VMCNT(0);
             NVFP4_WAIT_LGKMCNT0();
@@ -1686,8 +1694,11 @@ hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_code
     p.vec_out = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(c) % (4 * esz) == 0;
     p.vec16 = (ldc * esz) % 16 == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0;
     const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
-    hipFuncSetAttribute((const void*)k_gemm_mx, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
-    hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)t), dim3(256), kMxLds, s, p);
+    const bool all_full = M % kTM == 0 && N % kTN == 0 && p.vec16;
+    auto kern = !all_full ? k_gemm_mx<kKKEpiAny>
+                          : (out_bf16 ? k_gemm_mx<kKKEpiBF16> : k_gemm_mx<kKKEpiF32>);
+    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+    hipLaunchKernelGGL(kern, dim3((unsigned)t), dim3(256), kMxLds, s, p);
     return hipGetLastError();
 }
 
