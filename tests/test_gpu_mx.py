@@ -115,8 +115,12 @@ def test_mx_gemm_random_operands(nv, M, N, K):
     b = random_mx(rng, N, K)
     print("mx gemm", M, N, K, flush=True)
     ag, bg = to_gpu(nv, *a, M, K), to_gpu(nv, *b, N, K)
-    yf = nv.mx_gemm(ag, bg, torch.float32).cpu().numpy()
-    yb = nv.mx_gemm(ag, bg, torch.bfloat16).float().cpu().numpy()
+    yf_t = nv.mx_gemm(ag, bg, torch.float32).cpu()
+    yb_t = nv.mx_gemm(ag, bg, torch.bfloat16).cpu()
+    # same accumulators: the BF16 output is the FP32 one rounded to nearest
+    # even (torch's CPU float -> bfloat16 conversion is RNE)
+    assert torch.equal(yb_t, yf_t.to(torch.bfloat16))
+    yf, yb = yf_t.numpy(), yb_t.float().numpy()
     if M * N <= 300 * 300:
         ref, ab = oracle.mx_gemm_full(M, N, K, a, b)
         check_gemm(yf, yb, ref, ab, "mx %dx%dx%d" % (M, N, K))
