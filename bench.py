@@ -347,10 +347,43 @@ def main():
         line["decode"] = decode_bench(torch, nv, workloads)
         line["mxfp4"] = mxfp4_bench(torch, nv, X, W_gu)
         line["kv_cache"] = kv_bench(torch, nv, workloads)
+        line["dequantize_rht16"] = dequant_rht_bench(torch, nv, X, mask)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, torch, nv, workloads, X, W_gu)
     print(json.dumps(line), flush=True)
+
+
+def dequant_rht_bench(torch, nv, X, mask, reps=20):
+    """The two HBM streams outside the step: dequantize X's NVFP4 copy
+    (32768 x 4096, 1x16) to BF16 and FP32, and the standalone RHT16 down X's
+    columns (BF16 in, FP32 out). Mean of back-to-back calls, HIP events."""
+    xq = nv.quantize(X)
+    n = X.numel()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    out = {"shape": "%d x %d" % tuple(X.shape), "timing": "mean of %d back-to-back calls" % reps}
+    for name, dt, ob in (("dequant_bf16", torch.bfloat16, 2), ("dequant_f32", torch.float32, 4)):
+        us = timed(lambda: nv.dequantize(xq, dt))
+        b = n * (0.5 + 1 / 16 + ob)
+        out[name] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1),
+                     "frac_of_hbm": round(b / us / 1e3 / HBM_PEAK_GBPS, 4), "bytes": int(b)}
+    us = timed(lambda: nv.rht16(X, axis=0, mask=mask))
+    b = n * (2 + 4)
+    out["rht16_cols"] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1),
+                         "frac_of_hbm": round(b / us / 1e3 / HBM_PEAK_GBPS, 4), "bytes": int(b)}
+    return out
 
 
 def decode_bench(torch, nv, workloads):
