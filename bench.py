@@ -16,11 +16,12 @@ benchmark paragraph), with the recipe of that page's recipe paragraph:
                    dW_gu = dH^T X          28672 x 4096 x 32768   (RHT16 + SR / RHT16)
 
 Every GEMM runs K-major x K-major (the NT kernel): the operands that are
-contracted over their rows (the weights in dgrad, both wgrad inputs) are
-quantized with transposed output, i.e. stored as the K-major tensors W^T,
-dY^T, Act^T, dH^T, X^T.  The transposed weights reuse the amax of the
-untransposed call; X, Act, dY and dH get both of their tensor amaxes (plain,
-and of the column RHT) from one read (nvfp4_amax).
+contracted over their rows are stored as the K-major tensors W^T, dY^T,
+Act^T, dH^T, X^T.  The wgrad inputs are quantized with transposed output; the
+16x16-block weights are transpose-consistent, so W^T is W's own quantization
+with its codes and scales transposed (nvfp4_transpose), not a second
+quantization.  X, Act, dY and dH get both of their tensor amaxes (plain, and
+of the column RHT) from one read (nvfp4_amax).
 
 Inputs are resident in HBM before timing starts.  The JSON line reports the
 step's NVFP4 GEMM throughput (GEMM FLOPs / step time), per-kernel HIP-event
@@ -161,13 +162,22 @@ def main():
     qbytes = {}       # (name) -> algorithmic HBM bytes per call
     swbytes = {}      # the fused SwiGLU + amax pass
 
-    def qb(rows, cols, in_bytes=2, amax_pass=True):
-        # read input (twice when the amax pass runs) + codes + scales
-        return rows * cols * (in_bytes * (2 if amax_pass else 1) + 0.5 + 1 / 16)
+    def qb(rows, cols, in_bytes=2, amax_pass=True, block2d=False):
+        # read input (twice when the amax pass runs) + codes + scales (one
+        # byte per 16 elements in 1x16 blocks, per 256 in 16x16 blocks)
+        return rows * cols * (in_bytes * (2 if amax_pass else 1) + 0.5
+                              + (1 / 256 if block2d else 1 / 16))
 
     def Q(name, x, **kw):
-        qbytes[name] = qb(*x.shape, amax_pass=kw.get("amax_in") is None)
+        qbytes[name] = qb(*x.shape, amax_pass=kw.get("amax_in") is None,
+                          block2d=kw.get("block2d", False))
         return timer.run("quantize", nv.quantize, x, name=name, **kw)
+
+    def TR(name, q):
+        # storage transpose of a 16x16-block operand: codes and scales read
+        # and written once
+        qbytes[name] = q.rows * q.cols * 2 * (0.5 + 1 / 256)
+        return timer.run("quantize", nv.transpose, q, name=name)
 
     def AMX(name, x):
         # max |x| and max |RHT16 down the columns of x| in one read
@@ -227,7 +237,7 @@ def main():
         ady, adyt = AMX("dY_amax2", dY)
         fork()
         with torch.cuda.stream(side):
-            wdn_t = Q("Wdown_2d_T", W_down, block2d=True, transpose=True, amax_in=wdn.amax)
+            wdn_t = TR("Wdown_2d_T", wdn)
             at = Q("Act_cols_rht_T", act, axis=0, rht=True, mask=mask, transpose=True, amax_in=aat)
         dyq = Q("dY_rows_sr", dY, sr=True, seed=sr_seed, stream_id=0, amax_in=ady)
         dyt = Q("dY_cols_rht_sr_T", dY, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,
@@ -239,7 +249,7 @@ def main():
         adh, adht = AMX("dH_amax2", dH)
         fork()
         with torch.cuda.stream(side):
-            wgu_t = Q("Wgu_2d_T", W_gu, block2d=True, transpose=True, amax_in=wgu.amax)
+            wgu_t = TR("Wgu_2d_T", wgu)
             xt = Q("X_cols_rht_T", X, axis=0, rht=True, mask=mask, transpose=True, amax_in=axt)
         dhq = Q("dH_rows_sr", dH, sr=True, seed=sr_seed, stream_id=0, amax_in=adh)
         dht = Q("dH_cols_rht_sr_T", dH, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,

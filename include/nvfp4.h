@@ -139,6 +139,34 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, in
                             size_t workspace_bytes, void* stream);
 
 /*
+ * The same NVFP4 tensor stored as its transpose.  The recipe quantizes
+ * weights in 16x16 blocks so that fprop (which reads W) and dgrad (which
+ * reads W^T) see the same values (readjensen.com NVFP4 training-recipe page,
+ * recipe paragraph): a 16x16 block of W is a 16x16 block of W^T with the same
+ * scale, and W^T's element (c, r) is W's (r, c) with the same code.  This call
+ * writes that W^T from W's codes and scales without reading W again:
+ *   codes, scales     the rows x cols input in the storage layout above
+ *                     (block, axis)
+ *   codes_t           [cols, rows/2] <- codes of the transposed tensor
+ *   scales_t          the input's scale plane transposed byte for byte:
+ *                     2D [rows/16, cols/16] -> [cols/16, rows/16];
+ *                     1D axis 1 [rows, cols/16] -> [cols/16, rows] (the
+ *                     output's blocks run down its columns: axis 0);
+ *                     1D axis 0 [rows/16, cols] -> [cols, rows/16] (axis 1)
+ * The tensor scale is unchanged: the transposed tensor uses the input's
+ * tensor_scale.  For 2D blocks, and for 1D round-to-nearest quantizations
+ * read with the block axis swapped, the result is bit for bit the
+ * quantization of x^T (same amax); stochastically rounded tensors keep the
+ * rounding of x's element indices.
+ * Shape rules: rows % 16 == 0, cols % 16 == 0.  codes and codes_t 16-byte
+ * aligned; the output must not overlap the input.  rows or cols == 0 writes
+ * nothing.
+ */
+nvfp4_status nvfp4_transpose(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                             int64_t cols, nvfp4_block block, int axis, uint8_t* codes_t,
+                             uint8_t* scales_t, void* stream);
+
+/*
  * Bytes of device workspace nvfp4_amax needs (per-workgroup partial maxima of
  * both results; no initialisation needed, reusable on the same stream).
  */
@@ -359,9 +387,10 @@ nvfp4_status nvfp4_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_cod
  *   cols == 0 writes nothing.
  * nvfp4_kv_cache_read: out row j (pitch ld_out elements, BF16 RNE or FP32)
  *   = v = RN32(val * e * s_g) of cache row slots[j], or zeros when slots[j]
- *   is outside [0, num_slots).  Slots may repeat.  cols % 16 == 0;
- *   ld_out >= cols; out and cache_codes 16-byte aligned, out's row pitch a
- *   multiple of 16 bytes.
+ *   is outside [0, num_slots).  Slots may repeat.  An empty cache
+ *   (num_slots == 0; cache_codes and cache_scales may then be NULL) reads
+ *   zeros for every row.  cols % 16 == 0; ld_out >= cols; out and
+ *   cache_codes 16-byte aligned, out's row pitch a multiple of 16 bytes.
  * All pointers are caller-owned device memory; launches are asynchronous on
  * `stream`; argument errors return before anything is enqueued.
  */

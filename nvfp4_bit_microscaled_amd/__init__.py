@@ -37,7 +37,8 @@ EXPORTS = ("nvfp4_version", "nvfp4_status_string", "nvfp4_quantize_workspace_siz
            "nvfp4_swiglu_amax", "nvfp4_rht16",
            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize",
            "nvfp4_mx_gemm", "nvfp4_gemm_w4a16", "nvfp4_kv_cache_write",
-           "nvfp4_kv_cache_read", "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu")
+           "nvfp4_kv_cache_read", "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu",
+           "nvfp4_transpose")
 
 
 class NVFP4Error(RuntimeError):
@@ -61,6 +62,8 @@ def _load():
     L.nvfp4_quantize.restype = ci
     L.nvfp4_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, ci, u64, u32, ci, u32, vp, vp,
                                  vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.nvfp4_transpose.restype = ci
+    L.nvfp4_transpose.argtypes = [vp, vp, i64, i64, ci, ci, vp, vp, vp]
     L.nvfp4_amax_workspace_size.restype = ctypes.c_size_t
     L.nvfp4_amax_workspace_size.argtypes = [i64, i64]
     L.nvfp4_amax.restype = ci
@@ -135,6 +138,11 @@ def nvfp4_quantize(x, x_dtype, rows, cols, ld_x, block, axis, transpose_out, rou
                               rounding, seed, stream_id, rht, rht_sign_mask, _p(amax_in), _p(amax_out),
                               _p(codes), _p(scales), _p(tensor_scale), _p(workspace),
                               workspace_bytes, _stream(stream))
+
+
+def nvfp4_transpose(codes, scales, rows, cols, block, axis, codes_t, scales_t, stream=None) -> int:
+    return lib.nvfp4_transpose(_p(codes), _p(scales), rows, cols, block, axis, _p(codes_t),
+                               _p(scales_t), _stream(stream))
 
 
 def nvfp4_amax_workspace_size(rows: int, cols: int) -> int:
@@ -294,6 +302,30 @@ def quantize(x: torch.Tensor, block2d: bool = False, axis: int = 1, sr: bool = F
     return out
 
 
+def transpose(t: NVFP4Tensor, out: NVFP4Tensor | None = None) -> NVFP4Tensor:
+    """The same NVFP4 tensor stored as its transpose [cols, rows]: codes and
+    scales transposed, the tensor scale (and amax) shared with `t`.  A 2D
+    tensor stays 2D; 1D blocks along rows become blocks down the columns and
+    vice versa."""
+    o_axis = t.axis if t.block2d else 1 - t.axis
+    if out is None:
+        dev = t.codes.device
+        out = NVFP4Tensor(
+            codes=torch.empty(t.cols, t.rows // 2, dtype=torch.uint8, device=dev),
+            scales=torch.empty(scale_shape(t.cols, t.rows, t.block2d, o_axis), dtype=torch.uint8,
+                               device=dev),
+            tensor_scale=t.tensor_scale, amax=t.amax, rows=t.cols, cols=t.rows,
+            block2d=t.block2d, axis=o_axis)
+    assert out.rows == t.cols and out.cols == t.rows and out.block2d == t.block2d
+    assert tuple(out.codes.shape) == (t.cols, t.rows // 2) and out.codes.is_contiguous()
+    assert tuple(out.scales.shape) == scale_shape(t.cols, t.rows, t.block2d, o_axis)
+    assert out.scales.is_contiguous() and t.codes.is_contiguous() and t.scales.is_contiguous()
+    _check("nvfp4_transpose", nvfp4_transpose(
+        t.codes, t.scales, t.rows, t.cols, BLOCK_2D if t.block2d else BLOCK_1D, t.axis,
+        out.codes, out.scales))
+    return out
+
+
 def amax(x: torch.Tensor, rht_mask: int | None = None):
     """max |x| and, when rht_mask is given, max |RHT16 down the columns of x|,
     in one read; returns (amax, amax_rht or None) as float32 [1] tensors."""
@@ -342,20 +374,41 @@ def dequantize(t: NVFP4Tensor, out_dtype=torch.bfloat16) -> torch.Tensor:
 
 def gemm(layout: str, a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16,
          out: torch.Tensor | None = None) -> torch.Tensor:
-    """NT: a [M,K], b [N,K]; NN: a [M,K], b [K,N]; TN: a [K,M], b [K,N]."""
+    """NT: a [M,K], b [N,K]; NN: a [M,K], b [K,N]; TN: a [K,M], b [K,N].
+
+    Each operand's blocks must run along K: a 1D operand stored with K along
+    its columns has axis 1, one stored with K along its rows axis 0."""
     if layout == "NT":
         M, K = a.rows, a.cols
-        N = b.rows
+        N, Kb = b.rows, b.cols
+        a_axis, b_axis = 1, 1
     elif layout == "NN":
         M, K = a.rows, a.cols
-        N = b.cols
+        Kb, N = b.rows, b.cols
+        a_axis, b_axis = 1, 0
     elif layout == "TN":
         K, M = a.rows, a.cols
-        N = b.cols
+        Kb, N = b.rows, b.cols
+        a_axis, b_axis = 0, 0
     else:
         raise ValueError(layout)
+    if Kb != K:
+        raise ValueError("gemm %s: A has K = %d but B has K = %d" % (layout, K, Kb))
+    for name, op, ax in (("A", a, a_axis), ("B", b, b_axis)):
+        if not op.block2d and op.axis != ax:
+            raise ValueError("gemm %s: operand %s has 1D blocks along axis %d, not along K "
+                             "(axis %d)" % (layout, name, op.axis, ax))
+        if tuple(op.codes.shape) != (op.rows, op.cols // 2) or not op.codes.is_contiguous():
+            raise ValueError("gemm %s: operand %s codes are not a dense [%d, %d] plane"
+                             % (layout, name, op.rows, op.cols // 2))
+        if tuple(op.scales.shape) != scale_shape(op.rows, op.cols, op.block2d, op.axis) \
+                or not op.scales.is_contiguous():
+            raise ValueError("gemm %s: operand %s scales do not match its block layout"
+                             % (layout, name))
     if out is None:
         out = torch.empty(M, N, dtype=out_dtype, device=a.codes.device)
+    if tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise ValueError("gemm %s: out must be [%d, %d] with unit column stride" % (layout, M, N))
     _check("nvfp4_gemm", nvfp4_gemm(
         LAYOUT[layout], M, N, K, a.codes, a.scales, a.tensor_scale,
         BLOCK_2D if a.block2d else BLOCK_1D, b.codes, b.scales, b.tensor_scale,

@@ -131,6 +131,22 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, in
     return from_hip(launch_quantize(a, amax_src, amax_in != nullptr, s));
 }
 
+nvfp4_status nvfp4_transpose(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                             int64_t cols, nvfp4_block block, int axis, uint8_t* codes_t,
+                             uint8_t* scales_t, void* stream)
+{
+    if (block != NVFP4_BLOCK_1D && block != NVFP4_BLOCK_2D) return NVFP4_ERR_INVALID_ARG;
+    if (block == NVFP4_BLOCK_1D && axis != 0 && axis != 1) return NVFP4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0) return NVFP4_ERR_INVALID_ARG;
+    if (rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+    if ((uint64_t)rows * (uint64_t)(cols / 8) > kMaxItems) return NVFP4_ERR_UNSUPPORTED;
+    if (rows == 0 || cols == 0) return NVFP4_OK;
+    if (!codes || !scales || !codes_t || !scales_t) return NVFP4_ERR_INVALID_ARG;
+    if (!aligned16(codes) || !aligned16(codes_t)) return NVFP4_ERR_ALIGN;
+    return from_hip(launch_transpose(codes, scales, rows, cols, block == NVFP4_BLOCK_2D, axis,
+                                     codes_t, scales_t, static_cast<hipStream_t>(stream)));
+}
+
 size_t nvfp4_amax_workspace_size(int64_t rows, int64_t cols)
 {
     (void)rows;
@@ -397,12 +413,17 @@ nvfp4_status nvfp4_kv_cache_read(const uint8_t* cache_codes, const uint8_t* cach
     if (!out || !slots || !amax) return NVFP4_ERR_INVALID_ARG;
     if (num_slots > 0 && (!cache_codes || !cache_scales)) return NVFP4_ERR_INVALID_ARG;
     const size_t esz = out_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
-    if (!aligned16(out) || ((size_t)ld_out * esz) % 16 || !aligned16(cache_codes) ||
+    if (!aligned16(out) || ((size_t)ld_out * esz) % 16 ||
         (reinterpret_cast<uintptr_t>(slots) & 7u))
         return NVFP4_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // an empty cache has no valid slot: every row reads as zeros, and the
+    // gather kernel (which reads slot 0 for out-of-range slots) never runs
+    if (num_slots == 0)
+        return from_hip(launch_fill_zero(out, out_dtype == NVFP4_DTYPE_BF16, n, cols, ld_out, s));
+    if (!aligned16(cache_codes)) return NVFP4_ERR_ALIGN;
     return from_hip(launch_kv_cache_read(cache_codes, cache_scales, amax, num_slots, cols, slots,
-                                         n, out_dtype == NVFP4_DTYPE_BF16, out, ld_out,
-                                         static_cast<hipStream_t>(stream)));
+                                         n, out_dtype == NVFP4_DTYPE_BF16, out, ld_out, s));
 }
 
 size_t nvfp4_gemm_swiglu_workspace_size(int64_t M, int64_t N)

@@ -55,6 +55,13 @@ hipError_t launch_quantize(const QuantArgs& a, const float* amax_src, bool write
 hipError_t launch_quantize_transposed(const QuantArgs& a, const float* amax_src,
                                       bool write_amax_out, hipStream_t s);
 
+// The NVFP4 tensor [rows, cols] stored as its transpose: codes_t
+// [cols, rows/2], scales_t = the input scale plane transposed byte for byte
+// (rows % 16 == 0, cols % 16 == 0).
+hipError_t launch_transpose(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                            int64_t cols, int block2d, int axis, uint8_t* codes_t,
+                            uint8_t* scales_t, hipStream_t s);
+
 // Empty tensor: s_g = 0 and amax = 0.
 hipError_t launch_write_zero_scale(float* tensor_scale, float* amax_out, hipStream_t s);
 

@@ -591,6 +591,123 @@ void k_quant_t(QuantParams p)
     }
 }
 
+// ------------------------------------------------------------ storage transpose
+
+// The same NVFP4 tensor stored as its transpose: element (r, c) of the
+// rows x cols input becomes element (c, r) of the cols x rows output with
+// the same code and block scale.  For 16x16 blocks this is the recipe's
+// transpose consistency (readjensen.com recipe paragraph: fprop and dgrad
+// see the same weight values), so dgrad's K-major weight needs no second
+// quantization.  The scale plane is transposed byte for byte: 2D
+// [R/16, C/16] -> [C/16, R/16]; blocks along rows [R, C/16] -> blocks down
+// the columns of the output [C/16, R]; and the reverse.
+struct TransposeParams {
+    const uint8_t* codes;
+    const uint8_t* scales;
+    uint8_t* codes_t;
+    uint8_t* scales_t;
+    int64_t rows, cols;
+    int64_t s_rows, s_cols;  // input scale plane [s_rows, s_cols]
+    int s_tr_log, s_tc_log;  // log2 of its sub-block per 256 x 256 tile
+    int s_r_div, s_c_div;    // tile origin -> sub-block origin (divide by 1 or 16)
+    uint32_t tiles;
+    FastDiv div;             // tiles per tile row
+};
+
+// Transpose a 16 x 16 matrix of nibbles held as 16 rows of 64 bits (row i
+// = lo[i] | hi[i] << 32, element j at bits 4j .. 4j+3).  Block-recursive:
+// at each level the top-right and bottom-left sub-blocks of every block
+// trade places, which swaps one bit of the row and column indices; the four
+// levels together map (i, j) to (j, i).  The 8x8 level swaps whole words;
+// the others work within each 32-bit word.
+__device__ __forceinline__ void nibble_transpose16(uint32_t lo[16], uint32_t hi[16])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t t = hi[i];
+        hi[i] = lo[i + 8];
+        lo[i + 8] = t;
+    }
+#pragma unroll
+    for (int lvl = 0; lvl < 3; ++lvl) {
+        const int dist = 4 >> lvl, sh = 16 >> lvl;
+        const uint32_t m = lvl == 0 ? 0x0000FFFFu : (lvl == 1 ? 0x00FF00FFu : 0x0F0F0F0Fu);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i & dist) continue;
+            uint32_t t = ((lo[i] >> sh) ^ lo[i + dist]) & m;
+            lo[i + dist] ^= t;
+            lo[i] ^= t << sh;
+            t = ((hi[i] >> sh) ^ hi[i + dist]) & m;
+            hi[i + dist] ^= t;
+            hi[i] ^= t << sh;
+        }
+    }
+}
+
+// LDS chunk swizzle of the transposed tile: 8-byte chunk c of row R sits at
+// c ^ swz(R) (even, so 16-byte pairs stay adjacent).
+__device__ __forceinline__ int transpose_swz(int R) { return (R >> 3) & 14; }
+
+// One workgroup per 256 x 256 tile of the input.  Thread (br, bc) = (t / 16,
+// t % 16) loads block (br, bc) of the tile as 16 rows of 8 bytes (16 lanes
+// cover one 128-byte row segment), transposes it in registers and writes its
+// 16 output rows to LDS; the tile then leaves as 128-byte segments of the
+// output rows (8 bytes per lane).
+__global__ __launch_bounds__(256) void k_transpose(TransposeParams p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds_c[kTT * kTCodeRow];
+    __shared__ uint8_t lds_s[kTT * 16];
+    const int t = threadIdx.x, br = t >> 4, bc = t & 15;
+    const int64_t rows = p.rows, cols = p.cols;
+    const int64_t in_ld = cols / 2, out_ld = rows / 2;
+    const int s_tr = 1 << p.s_tr_log, s_n = s_tr << p.s_tc_log;
+    for (uint32_t tile = blockIdx.x; tile < p.tiles; tile += gridDim.x) {
+        const uint32_t tr = fdiv(tile, p.div);
+        const uint32_t tc = tile - tr * p.div.d;
+        const int64_t R0 = (int64_t)tr * kTT, C0 = (int64_t)tc * kTT;
+        if (R0 + 16 * br < rows && C0 + 16 * bc < cols) {
+            const uint8_t* src = p.codes + (R0 + 16 * br) * in_ld + (C0 + 16 * bc) / 2;
+            uint32_t lo[16], hi[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const u32x2 w = *reinterpret_cast<const u32x2*>(src + i * in_ld);
+                lo[i] = w[0];
+                hi[i] = w[1];
+            }
+            nibble_transpose16(lo, hi);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int R = 16 * bc + j;
+                *reinterpret_cast<u32x2*>(lds_c + R * kTCodeRow + 8 * (br ^ transpose_swz(R))) =
+                    u32x2{lo[j], hi[j]};
+            }
+        }
+        // scale sub-block [sr0, +s_tr) x [sc0, +s_tc), stored transposed in LDS
+        const int64_t sr0 = R0 / p.s_r_div, sc0 = C0 / p.s_c_div;
+        for (int i = t; i < s_n; i += 256) {
+            const int r = i >> p.s_tc_log, c = i & ((1 << p.s_tc_log) - 1);
+            if (sr0 + r < p.s_rows && sc0 + c < p.s_cols)
+                lds_s[c * s_tr + r] = p.scales[(sr0 + r) * p.s_cols + sc0 + c];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int k = 0; k < 16; ++k) {
+            const int idx = t + 256 * k, R = idx >> 4, c8 = idx & 15;
+            if (C0 + R < cols && R0 + 16 * c8 < rows)
+                *reinterpret_cast<u32x2*>(p.codes_t + (C0 + R) * out_ld + R0 / 2 + 8 * c8) =
+                    *reinterpret_cast<const u32x2*>(lds_c + R * kTCodeRow +
+                                                    8 * (c8 ^ transpose_swz(R)));
+        }
+        for (int i = t; i < s_n; i += 256) {
+            const int c = i >> p.s_tr_log, r = i & (s_tr - 1);
+            if (sr0 + r < p.s_rows && sc0 + c < p.s_cols)
+                p.scales_t[(sc0 + c) * p.s_rows + sr0 + r] = lds_s[c * s_tr + r];
+        }
+        __syncthreads();
+    }
+}
+
 // 16 consecutive inputs as raw words (BF16: two 16-byte loads, FP32: four),
 // kept unconverted so that several rows' loads can be in flight at once.
 template <bool kBF16>
@@ -1262,6 +1379,35 @@ hipError_t launch_quantize_transposed(const QuantArgs& a, const float* amax_src,
                 hipLaunchKernelGGL((k_quant_t<BF, SR, RH, false>), dim3(grid), dim3(256), 0, s,
                                    p))));
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                            int64_t cols, int block2d, int axis, uint8_t* codes_t,
+                            uint8_t* scales_t, hipStream_t s)
+{
+    TransposeParams p{};
+    p.codes = codes;
+    p.scales = scales;
+    p.codes_t = codes_t;
+    p.scales_t = scales_t;
+    p.rows = rows;
+    p.cols = cols;
+    if (block2d) {
+        p.s_rows = rows / 16; p.s_cols = cols / 16;
+        p.s_tr_log = 4; p.s_tc_log = 4; p.s_r_div = 16; p.s_c_div = 16;
+    } else if (axis == 1) {
+        p.s_rows = rows; p.s_cols = cols / 16;
+        p.s_tr_log = 8; p.s_tc_log = 4; p.s_r_div = 1; p.s_c_div = 16;
+    } else {
+        p.s_rows = rows / 16; p.s_cols = cols;
+        p.s_tr_log = 4; p.s_tc_log = 8; p.s_r_div = 16; p.s_c_div = 1;
+    }
+    const uint32_t tiles_c = (uint32_t)((cols + kTT - 1) / kTT);
+    p.tiles = (uint32_t)((rows + kTT - 1) / kTT) * tiles_c;
+    p.div = make_fastdiv(tiles_c);
+    const int grid = (int)(p.tiles < (uint32_t)kGridCap ? p.tiles : (uint32_t)kGridCap);
+    hipLaunchKernelGGL(k_transpose, dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

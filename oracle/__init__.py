@@ -80,6 +80,9 @@ def lib():
         L.oracle_dequantize.restype = ctypes.c_int
         L.oracle_dequantize.argtypes = [c_vp, c_vp, ctypes.c_float, c_i64, c_i64, ctypes.c_int,
                                         ctypes.c_int, c_vp, c_vp]
+        L.oracle_transpose.restype = ctypes.c_int
+        L.oracle_transpose.argtypes = [c_vp, c_vp, c_i64, c_i64, ctypes.c_int, ctypes.c_int, c_vp,
+                                       c_vp]
         L.oracle_gemm_pairs.restype = ctypes.c_int
         L.oracle_gemm_pairs.argtypes = [ctypes.c_int, c_i64, c_i64, c_i64, c_vp, c_vp,
                                         ctypes.c_float, ctypes.c_int, c_vp, c_vp, ctypes.c_float,
@@ -225,6 +228,27 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, s_g: float, rows: int, col
     lib().oracle_dequantize(_ptr(codes), _ptr(scales), s_g, rows, cols, int(block2d), axis,
                             _ptr(f), _ptr(b))
     return f, b
+
+
+def transpose(codes: np.ndarray, scales: np.ndarray, rows: int, cols: int,
+              block2d: bool = False, axis: int = 1):
+    """The NVFP4 tensor [rows, cols] stored as its transpose [cols, rows]:
+    returns (codes uint8 [cols, rows/2], scales uint8 in the transposed
+    tensor's layout: 2D [cols/16, rows/16]; from axis 1 -> axis 0
+    [cols/16, rows]; from axis 0 -> axis 1 [cols, rows/16])."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    ct = np.zeros((cols, rows // 2), dtype=np.uint8)
+    if block2d:
+        st = np.zeros((cols // 16, rows // 16), dtype=np.uint8)
+    elif axis == 1:
+        st = np.zeros((cols // 16, rows), dtype=np.uint8)
+    else:
+        st = np.zeros((cols, rows // 16), dtype=np.uint8)
+    if lib().oracle_transpose(_ptr(codes), _ptr(scales), rows, cols, int(block2d), axis, _ptr(ct),
+                              _ptr(st)):
+        raise ValueError("oracle_transpose: bad shape")
+    return ct, st
 
 
 def gemm_pairs(layout: str, M: int, N: int, K: int, a, b, ms, ns):

@@ -489,6 +489,36 @@ int oracle_dequantize(const uint8_t* codes, const uint8_t* scales, float s_g, in
     return 0;
 }
 
+/*
+ * The same NVFP4 tensor stored as its transpose.  Element (r, c) of the
+ * rows x cols input is element (c, r) of the cols x rows output, with the
+ * same code and the same block scale; the tensor scale is unchanged.  The
+ * block of (r, c) becomes the block of (c, r): a 16x16 block stays 16x16,
+ * blocks along rows (axis 1) become blocks down the columns (axis 0) and
+ * vice versa.  This is what the recipe's 2D weight blocks are for (the
+ * readjensen.com recipe paragraph: fprop and dgrad see transpose-consistent
+ * values); the function is plain storage work, element by element.
+ * Shape rule: rows % 16 == 0 and cols % 16 == 0.  Returns 0, or -1.
+ */
+int oracle_transpose(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                     int block2d, int axis, uint8_t* codes_t, uint8_t* scales_t)
+{
+    if (rows % 16 || cols % 16 || (!block2d && axis != 0 && axis != 1)) return -1;
+    const int axis_t = block2d ? axis : 1 - axis;
+    /* one output row (input column c) per iteration: threads write disjoint rows */
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; ++c)
+        for (int64_t r = 0; r < rows; ++r) {
+            put_code(codes_t, rows, c, r, code_of(codes, cols, r, c));
+            const uint8_t e = scale_of(scales, rows, cols, block2d, axis, r, c);
+            /* the output tensor is cols x rows; (c, r) is its element */
+            if (block2d) scales_t[(c / 16) * (rows / 16) + r / 16] = e;
+            else if (axis_t == 1) scales_t[c * (rows / 16) + r / 16] = e;
+            else scales_t[(c / 16) * rows + r] = e;
+        }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* GEMM                                                                 */
 /* ------------------------------------------------------------------ */

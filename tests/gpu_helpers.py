@@ -4,6 +4,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import oracle
+
 
 def to_oracle_input(x: torch.Tensor) -> np.ndarray:
     """CPU numpy view of a BF16 (as uint16 bits) or FP32 tensor, dense."""
@@ -38,3 +40,48 @@ def check_gemm(out_f32: np.ndarray | None, out_bf16: np.ndarray | None, ref: np.
         err = np.abs(out_bf16.astype(np.float64) - ref_b)
         bad = err > allowed
         assert not bad.any(), "%s: %d BF16 outputs off by more than the bound" % (what, bad.sum())
+
+
+def bf16_neighbours(x: torch.Tensor):
+    """The BF16 values one step below and above each (finite, BF16) x."""
+    b = x.to(torch.bfloat16).view(torch.int16).to(torch.int32)
+    mag = b & 0x7FFF
+    neg = (b & 0x8000) != 0
+    up_mag, dn_mag = mag + 1, mag - 1
+    # stepping through zero flips the sign
+    above = torch.where(neg, torch.where(mag == 0, 1, -dn_mag), up_mag)
+    below = torch.where(neg, -up_mag, torch.where(mag == 0, -1, dn_mag))
+
+    def to_f(v):
+        bits = torch.where(v < 0, (-v) | 0x8000, v).to(torch.int16)
+        return bits.view(torch.bfloat16).float()
+    return to_f(below), to_f(above)
+
+
+def check_act_against_oracle(h: torch.Tensor, act: torch.Tensor, what: str = ""):
+    """act (CPU BF16 [rows, F]) against the oracle's SwiGLU of h = [gate | up]
+    (CPU BF16 [rows, 2F]): equal, or the product of up with one of the two BF16
+    neighbours of the oracle's BF16 silu, the latter only where the oracle's
+    FP32 silu lies within 4 FP32 ulps of the BF16 rounding boundary between
+    the two (the kernel's exp and reciprocal are within an ulp or two, so they
+    may round silu to the other side).  Returns the number of such flips."""
+    F = h.shape[1] // 2
+    hb = to_oracle_input(h)
+    ref, sb = oracle.swiglu(hb)
+    sbf = torch.from_numpy(sb.view(np.int16)).view(torch.bfloat16).float()
+    lo, hi = bf16_neighbours(sbf)
+    u = h[:, F:].float()
+    got = act.view(torch.int16).numpy().view(np.uint16)
+    cand_lo = (lo * u).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    cand_hi = (hi * u).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    same = got == ref
+    ok = same | (got == cand_lo) | (got == cand_hi)
+    assert ok.all(), "%s: %d outputs off by more than one BF16 step of silu" % (
+        what, int((~ok).sum()))
+    g = h[:, :F].float().numpy()
+    for r, c in np.argwhere(~same):
+        sg = np.float32(oracle.silu_f32(float(g[r, c])))
+        other = (lo if got[r, c] == cand_lo[r, c] else hi)[r, c].item()
+        mid = (float(sbf[r, c]) + other) / 2.0
+        assert abs(float(sg) - mid) <= 4 * float(np.spacing(np.abs(sg))), (what, g[r, c], sg, mid)
+    return int((~same).sum())

@@ -35,7 +35,8 @@ def test_header_declares_the_abi():
                             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize",
                             "nvfp4_mx_dequantize", "nvfp4_mx_gemm", "nvfp4_gemm_w4a16",
                             "nvfp4_kv_cache_write", "nvfp4_kv_cache_read",
-                            "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu"])
+                            "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu",
+                            "nvfp4_transpose"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -259,6 +260,59 @@ def test_kv_cache_validation(lib):
     assert kvr(lib, out=None) == 1
     assert kvr(lib, cc=None) == 1
     assert kvr(lib, n=0, out=None) == 0
+    assert kvr(lib, S=0, cc=None, cs=None, out=MISALIGNED) == 3   # checked before the zero fill
+
+
+def test_transpose_validation(lib):
+    def tr(**kw):
+        args = dict(codes=FAKE, scales=FAKE, rows=32, cols=64, block=1, axis=1, codes_t=FAKE,
+                    scales_t=FAKE, stream=None)
+        args.update(kw)
+        return lib.nvfp4_transpose(*args.values())
+    assert tr(block=2) == 1
+    assert tr(block=0, axis=3) == 1
+    assert tr(rows=-16) == 1
+    assert tr(rows=24) == 2                       # rows % 16
+    assert tr(cols=40) == 2                       # cols % 16
+    assert tr(rows=1 << 31, cols=1 << 7) == 5     # more than 2^32 code words
+    assert tr(codes_t=None) == 1
+    assert tr(scales=None) == 1
+    assert tr(codes=MISALIGNED) == 3
+    assert tr(codes_t=MISALIGNED) == 3
+    assert tr(rows=0, codes=None, scales=None, codes_t=None, scales_t=None) == 0
+
+
+def test_gemm_binding_checks_operands():
+    """The Python gemm() rejects operands whose K, block axis or planes do not
+    fit the layout, and a wrong out tensor, before any library call."""
+    import torch
+
+    import nvfp4_bit_microscaled_amd as m
+
+    def op(rows, cols, block2d=False, axis=1):
+        return m.NVFP4Tensor(torch.zeros(rows, cols // 2, dtype=torch.uint8),
+                             torch.zeros(m.scale_shape(rows, cols, block2d, axis), dtype=torch.uint8),
+                             torch.ones(1), torch.zeros(1), rows, cols, block2d, axis)
+    with pytest.raises(ValueError, match="K"):
+        m.gemm("NT", op(32, 64), op(48, 128))                # K 64 vs 128
+    with pytest.raises(ValueError, match="K"):
+        m.gemm("NN", op(32, 64), op(32, 48, axis=0))         # B has 32 rows, K = 64
+    with pytest.raises(ValueError, match="K"):
+        m.gemm("TN", op(64, 32, axis=0), op(48, 16, axis=0))
+    with pytest.raises(ValueError, match="axis"):
+        m.gemm("NT", op(32, 64), op(48, 64, axis=0))         # NT needs axis 1 on B
+    with pytest.raises(ValueError, match="axis"):
+        m.gemm("NN", op(32, 64), op(64, 48, axis=1))         # NN needs axis 0 on B
+    with pytest.raises(ValueError, match="axis"):
+        m.gemm("TN", op(64, 32, axis=1), op(64, 48, axis=0))
+    bad = op(32, 64)
+    bad.scales = torch.zeros(32, 2, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="scales"):
+        m.gemm("NT", bad, op(48, 64))
+    with pytest.raises(ValueError, match="out"):
+        m.gemm("NT", op(32, 64), op(48, 64), out=torch.empty(32, 40))
+    with pytest.raises(ValueError, match="out"):
+        m.gemm("NT", op(32, 64), op(48, 64), out=torch.empty(48, 32).t())
 
 
 def gsw(lib, **kw):

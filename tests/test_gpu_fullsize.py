@@ -53,10 +53,18 @@ def transpose_codes(codes):
 
 
 def check_quantize_sampled(nv, x, block2d=False, axis=1, sr=False, seed=0, stream_id=0,
-                           rht=False, mask=0, transpose=False):
+                           rht=False, mask=0, transpose=False, via_transpose=False):
+    """via_transpose: quantize in x's own storage, then nvfp4_transpose (the
+    training step's path for the 16x16 dgrad weight); the result is checked
+    as the transposed-storage quantization."""
     rows, cols = x.shape
+    print("quantize %dx%d 2d=%d axis=%d sr=%d rht=%d transpose=%d via=%d" % (
+        rows, cols, block2d, axis, sr, rht, transpose, via_transpose), flush=True)
     q = nv.quantize(x, block2d=block2d, axis=axis, sr=sr, seed=seed, stream_id=stream_id,
-                    rht=rht, mask=mask, transpose=transpose)
+                    rht=rht, mask=mask, transpose=transpose and not via_transpose)
+    if via_transpose:
+        q = nv.transpose(q)
+        transpose = True
     torch.cuda.synchronize()
     xc = x.cpu()
     xo = to_oracle_input(xc)
@@ -215,6 +223,16 @@ LLAMA405B_GEMMS = [
 ]
 
 
+# the K-major launches of the 405B-share step: dgrad against the transposed
+# 16x16 weights, wgrad on the transposed 1D (RHT) gradient and input
+LLAMA405B_GEMMS += [
+    ("NT", T4, F4, D4, False, True),        # dgrad down, W_down^T  (K = 16384)
+    ("NT", T4, D4, 2 * F4, False, True),    # dgrad gate+up, W_gu^T (K = 106496)
+    ("NT", D4, F4, T4, False, False),       # wgrad down, dY^T x Act^T (K = 8192)
+    ("NT", 2 * F4, D4, T4, False, False),   # wgrad gate+up, dH^T x X^T (K = 8192)
+]
+
+
 @pytest.mark.parametrize("layout,M,N,K,a2d,b2d", LLAMA405B_GEMMS)
 def test_llama405b_gemms_sampled(nv, layout, M, N, K, a2d, b2d):
     run_gemm_sampled(nv, layout, M, N, K, seed=(M ^ N ^ K) + 1, a2d=a2d, b2d=b2d)
@@ -223,12 +241,77 @@ def test_llama405b_gemms_sampled(nv, layout, M, N, K, a2d, b2d):
 def test_llama405b_quantize(nv):
     T, D, F = T4, D4, F4
     mask = workloads.sign_mask(L405["mask_seed"])
-    check_quantize_sampled(nv, gen("act", T, D, L405["x_seed"]))
-    check_quantize_sampled(nv, gen("w", D, F, L405["wdown_seed"]), block2d=True)
+    X = gen("act", T, D, L405["x_seed"])
+    check_quantize_sampled(nv, X)
+    check_quantize_sampled(nv, X, axis=0, rht=True, mask=mask, transpose=True)        # X^T
+    del X
     dY = gen("grad", T, D, L405["dy_seed"])
     check_quantize_sampled(nv, dY, sr=True, seed=L405["sr_seed"])
     check_quantize_sampled(nv, dY, axis=0, rht=True, mask=mask, sr=True, seed=L405["sr_seed"],
                            stream_id=1)
+    check_quantize_sampled(nv, dY, axis=0, rht=True, mask=mask, sr=True, seed=L405["sr_seed"],
+                           stream_id=1, transpose=True)                              # dY^T
+
+
+def test_llama405b_weights(nv):
+    """W_down and W_gu (106496 x 16384, the largest tensor of any workload) in
+    16x16 blocks, and their K-major dgrad copies W^T from nvfp4_transpose."""
+    D, F = D4, F4
+    W = gen("w", D, F, L405["wdown_seed"])
+    check_quantize_sampled(nv, W, block2d=True)
+    check_quantize_sampled(nv, W, block2d=True, via_transpose=True)
+    del W
+    W = gen("w", 2 * F, D, L405["wgu_seed"])
+    check_quantize_sampled(nv, W, block2d=True)
+    check_quantize_sampled(nv, W, block2d=True, via_transpose=True)
+    del W
+
+
+def test_llama405b_dh_and_act(nv):
+    """dH [8192, 106496]: rows with SR (dgrad) and RHT + SR down the columns in
+    transposed storage (wgrad); Act [8192, 53248] (activation-distributed
+    stand-in): rows RNE (fprop) and RHT down the columns, transposed (wgrad)."""
+    T, F = T4, F4
+    mask = workloads.sign_mask(L405["mask_seed"])
+    dH = gen("grad", T, 2 * F, L405["dh_seed"])
+    check_quantize_sampled(nv, dH, sr=True, seed=L405["sr_seed"], stream_id=0)
+    check_quantize_sampled(nv, dH, axis=0, rht=True, mask=mask, sr=True, seed=L405["sr_seed"],
+                           stream_id=1, transpose=True)
+    del dH
+    Act = gen("act", T, F, 14)
+    check_quantize_sampled(nv, Act)
+    check_quantize_sampled(nv, Act, axis=0, rht=True, mask=mask, transpose=True)
+    del Act
+
+
+def positive_nvfp4(nv, rng, rows, cols, ts, scale_lo, scale_hi):
+    """Operand whose every element is positive (codes 1..7: 0.5 .. 6) with
+    scales drawn from [scale_lo, scale_hi]: a constant-sign dot product, where
+    FP32 accumulation errors do not cancel."""
+    c = (rng.integers(1, 8, size=(rows, cols // 2), dtype=np.uint8)
+         | (rng.integers(1, 8, size=(rows, cols // 2), dtype=np.uint8) << 4)).astype(np.uint8)
+    s = rng.integers(scale_lo, scale_hi + 1, size=(rows, cols // 16), dtype=np.uint8)
+    g = nv.NVFP4Tensor(torch.from_numpy(c).cuda(), torch.from_numpy(s).cuda(),
+                       torch.tensor([ts], dtype=torch.float32, device="cuda"),
+                       torch.zeros(1, device="cuda"), rows, cols, False, 1)
+    return (c, s, ts, False), g
+
+
+# the step's longest K (405B dgrad gate+up) and the 8B wgrad K; a narrow scale
+# band (E4M3 1.0 .. 2.0: similar-sized terms) and the full normal range
+@pytest.mark.parametrize("M,N,K", [(160, 96, 106496), (256, 256, 32768)])
+@pytest.mark.parametrize("band", [(0x38, 0x40), (0x08, 0x7E)])
+def test_constant_sign_long_k(nv, M, N, K, band):
+    rng = np.random.default_rng(K + band[0])
+    a_or, a_g = positive_nvfp4(nv, rng, M, K, 2.0 ** -6, *band)
+    b_or, b_g = positive_nvfp4(nv, rng, N, K, 2.0 ** -5, *band)
+    print("constant sign %dx%dx%d band %s" % (M, N, K, band), flush=True)
+    yf = nv.gemm("NT", a_g, b_g, out_dtype=torch.float32)
+    yb = nv.gemm("NT", a_g, b_g, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, ab = oracle.gemm_full("NT", M, N, K, a_or, b_or)
+    assert np.all(ref > 0) and np.array_equal(ref, ab)
+    check_gemm(yf.cpu().numpy(), yb.float().cpu().numpy(), ref, ab, "constant sign K=%d" % K)
 
 
 DEC = workloads.DECODE

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import to_oracle_input
+from gpu_helpers import bf16_neighbours, check_act_against_oracle, to_oracle_input
 
 pytestmark = pytest.mark.gpu
 
@@ -28,22 +28,6 @@ def nv():
     import nvfp4_bit_microscaled_amd as m
     torch.cuda.set_device(0)
     return m
-
-
-def bf16_neighbours(x):
-    """The BF16 values one step below and above each (finite, BF16) x."""
-    b = x.to(torch.bfloat16).view(torch.int16).to(torch.int32)
-    mag = b & 0x7FFF
-    neg = (b & 0x8000) != 0
-    up_mag, dn_mag = mag + 1, mag - 1
-    # stepping through zero flips the sign
-    above = torch.where(neg, torch.where(mag == 0, 1, -dn_mag), up_mag)
-    below = torch.where(neg, -up_mag, torch.where(mag == 0, -1, dn_mag))
-
-    def to_f(v):
-        bits = torch.where(v < 0, (-v) | 0x8000, v).to(torch.int16)
-        return bits.view(torch.bfloat16).float()
-    return to_f(below), to_f(above)
 
 
 def candidates(h):
@@ -114,20 +98,4 @@ def test_act_against_the_oracle(nv, rows, F):
     mask = workloads.sign_mask(F + 1)
     act, a, ar = nv.swiglu_amax(h.cuda(), mask)
     torch.cuda.synchronize()
-    hb = to_oracle_input(h)
-    ref, sb = oracle.swiglu(hb)
-    sbf = torch.from_numpy(sb.view(np.int16)).view(torch.bfloat16).float()
-    lo, hi = bf16_neighbours(sbf)
-    u = h[:, F:].float()
-    got = act.cpu().view(torch.int16).numpy().view(np.uint16)
-    cand_lo = (lo * u).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    cand_hi = (hi * u).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    same = got == ref
-    ok = same | (got == cand_lo) | (got == cand_hi)
-    assert ok.all(), "%d outputs off by more than one BF16 step of silu" % int((~ok).sum())
-    g = h[:, :F].float().numpy()
-    for r, c in np.argwhere(~same):
-        sg = np.float32(oracle.silu_f32(float(g[r, c])))
-        other = (lo if got[r, c] == cand_lo[r, c] else hi)[r, c].item()
-        mid = (float(sbf[r, c]) + other) / 2.0
-        assert abs(float(sg) - mid) <= 4 * float(np.spacing(np.abs(sg))), (g[r, c], sg, mid)
+    check_act_against_oracle(h, act.cpu(), "swiglu %dx%d" % (rows, F))
