@@ -147,6 +147,21 @@ def test_kv_empty_calls(nv):
     assert torch.all(cache.codes == 0) and torch.all(cache.scales == 0)
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_kv_read_from_an_empty_cache(nv, out_dtype):
+    """A cache of zero slots: every slot is out of range, so every row reads
+    as zeros (the library fills the output; no cache memory is touched)."""
+    cache = nv.kv_cache_create(0, 64, 1.0)
+    slots = torch.tensor([0, 3, -1, 7], dtype=torch.int64, device="cuda")
+    out = torch.full((4, 64), 9.0, dtype=out_dtype, device="cuda")
+    nv.kv_cache_read(cache, slots, out_dtype, out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+    ref_f, ref_b = oracle.kv_cache_read(np.zeros((0, 32), np.uint8), np.zeros((0, 4), np.uint8),
+                                        1.0, slots.cpu().numpy())
+    assert not ref_f.any() and not ref_b.any()
+
+
 def test_kv_cache_full_size_llama8b_layer(nv):
     """The bench's workload at one tensor's full size: 262144 tokens x 1024
     features written in pages over 262144 slots, then all read back in a
