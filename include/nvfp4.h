@@ -139,6 +139,28 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, in
                             size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_quantize for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, outputs and errors are those of
+ * nvfp4_quantize without the workspace.  When amax_in is NULL the amax pass
+ * uses a scratch array inside the library instead: 8448 bytes per GPU
+ * (nvfp4_quantize_workspace_size, which does not depend on the tensor size;
+ * a larger need would return NVFP4_ERR_WORKSPACE), held by each GPU the
+ * library runs on until the process ends.  The call allocates nothing.  It
+ * uses the scratch of the current device, so `stream` must belong to the
+ * current device.  All calls on one GPU share that scratch: two calls with
+ * amax_in == NULL whose work overlaps on one GPU (different streams, no
+ * ordering between them) race and may compute a wrong amax; calls ordered
+ * on one stream do not.  Nothing in the scratch needs to start at zero.
+ */
+nvfp4_status nvfp4_quantize_noalloc(const void* x, nvfp4_dtype x_dtype, int64_t rows,
+                                    int64_t cols, int64_t ld_x, nvfp4_block block, int axis,
+                                    int transpose_out, nvfp4_round rounding, uint64_t seed,
+                                    uint32_t stream_id, int rht, uint32_t rht_sign_mask,
+                                    const float* amax_in, float* amax_out, uint8_t* codes,
+                                    uint8_t* scales, float* tensor_scale, void* stream);
+
+/*
  * The same NVFP4 tensor stored as its transpose.  The recipe quantizes
  * weights in 16x16 blocks so that fprop (which reads W) and dgrad (which
  * reads W^T) see the same values (readjensen.com NVFP4 training-recipe page,

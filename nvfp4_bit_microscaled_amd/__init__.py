@@ -38,7 +38,7 @@ EXPORTS = ("nvfp4_version", "nvfp4_status_string", "nvfp4_quantize_workspace_siz
            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize",
            "nvfp4_mx_gemm", "nvfp4_gemm_w4a16", "nvfp4_kv_cache_write",
            "nvfp4_kv_cache_read", "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu",
-           "nvfp4_transpose")
+           "nvfp4_transpose", "nvfp4_quantize_noalloc")
 
 
 class NVFP4Error(RuntimeError):
@@ -62,6 +62,9 @@ def _load():
     L.nvfp4_quantize.restype = ci
     L.nvfp4_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, ci, u64, u32, ci, u32, vp, vp,
                                  vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.nvfp4_quantize_noalloc.restype = ci
+    L.nvfp4_quantize_noalloc.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, ci, u64, u32, ci, u32,
+                                         vp, vp, vp, vp, vp, vp]
     L.nvfp4_transpose.restype = ci
     L.nvfp4_transpose.argtypes = [vp, vp, i64, i64, ci, ci, vp, vp, vp]
     L.nvfp4_amax_workspace_size.restype = ctypes.c_size_t
@@ -138,6 +141,15 @@ def nvfp4_quantize(x, x_dtype, rows, cols, ld_x, block, axis, transpose_out, rou
                               rounding, seed, stream_id, rht, rht_sign_mask, _p(amax_in), _p(amax_out),
                               _p(codes), _p(scales), _p(tensor_scale), _p(workspace),
                               workspace_bytes, _stream(stream))
+
+
+def nvfp4_quantize_noalloc(x, x_dtype, rows, cols, ld_x, block, axis, transpose_out, rounding,
+                           seed, stream_id, rht, rht_sign_mask, amax_in, amax_out, codes, scales,
+                           tensor_scale, stream=None) -> int:
+    return lib.nvfp4_quantize_noalloc(_p(x), x_dtype, rows, cols, ld_x, block, axis,
+                                      transpose_out, rounding, seed, stream_id, rht,
+                                      rht_sign_mask, _p(amax_in), _p(amax_out), _p(codes),
+                                      _p(scales), _p(tensor_scale), _stream(stream))
 
 
 def nvfp4_transpose(codes, scales, rows, cols, block, axis, codes_t, scales_t, stream=None) -> int:

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 #include "nvfp4.h"
@@ -28,6 +29,38 @@ constexpr uint64_t kMaxItems = 0xFFFFFFFFull;  // kernels index work items in 32
 
 // Workspace layout: [0, kMaxAmaxPartials) partial maxima, then the amax slot.
 constexpr size_t kWorkspaceFloats = kMaxAmaxPartials + 64;
+
+}  // namespace
+
+// Scratch of nvfp4_quantize_noalloc: the amax pass's per-workgroup partial
+// maxima and the reduced amax, laid out as nvfp4_quantize's workspace
+// (8448 bytes).  Each GPU the library runs on holds its own copy until the
+// process ends.  Host code never uses this name as an address: the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[kWorkspaceFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call made with that device current, then kept).
+nvfp4_status scratch_of_current_device(float** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return NVFP4_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NVFP4_ERR_HIP;
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return NVFP4_OK;
+}
 
 }  // namespace
 
@@ -129,6 +162,29 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, in
     if (transpose_out)
         return from_hip(launch_quantize_transposed(a, amax_src, amax_in != nullptr, s));
     return from_hip(launch_quantize(a, amax_src, amax_in != nullptr, s));
+}
+
+nvfp4_status nvfp4_quantize_noalloc(const void* x, nvfp4_dtype x_dtype, int64_t rows,
+                                    int64_t cols, int64_t ld_x, nvfp4_block block, int axis,
+                                    int transpose_out, nvfp4_round rounding, uint64_t seed,
+                                    uint32_t stream_id, int rht, uint32_t rht_sign_mask,
+                                    const float* amax_in, float* amax_out, uint8_t* codes,
+                                    uint8_t* scales, float* tensor_scale, void* stream)
+{
+    float* ws = nullptr;
+    size_t ws_bytes = 0;
+    // the scratch is needed only for the amax pass of a non-empty tensor;
+    // nvfp4_quantize validates everything else before anything is enqueued
+    if (!amax_in && rows > 0 && cols > 0) {
+        if (nvfp4_quantize_workspace_size(rows, cols) > sizeof(scratch))
+            return NVFP4_ERR_WORKSPACE;
+        const nvfp4_status st = scratch_of_current_device(&ws);
+        if (st != NVFP4_OK) return st;
+        ws_bytes = sizeof(scratch);
+    }
+    return nvfp4_quantize(x, x_dtype, rows, cols, ld_x, block, axis, transpose_out, rounding,
+                          seed, stream_id, rht, rht_sign_mask, amax_in, amax_out, codes, scales,
+                          tensor_scale, ws, ws_bytes, stream);
 }
 
 nvfp4_status nvfp4_transpose(const uint8_t* codes, const uint8_t* scales, int64_t rows,

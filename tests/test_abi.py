@@ -36,7 +36,7 @@ def test_header_declares_the_abi():
                             "nvfp4_mx_dequantize", "nvfp4_mx_gemm", "nvfp4_gemm_w4a16",
                             "nvfp4_kv_cache_write", "nvfp4_kv_cache_read",
                             "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu",
-                            "nvfp4_transpose"])
+                            "nvfp4_transpose", "nvfp4_quantize_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
