@@ -60,6 +60,10 @@ def parse():
                     help="time only the MXFP4 comparison path and print its JSON object")
     ap.add_argument("--kv-only", action="store_true",
                     help="print only the NVFP4 KV-cache write/read object")
+    ap.add_argument("--quant-only", action="store_true",
+                    help="one untimed step, then only the isolated replay of its quantize, "
+                         "amax, transpose and SwiGLU calls (for per-kernel counters); prints "
+                         "the calls in replay order with their times")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode-shape GEMMs and print their JSON object "
                          "(for profiling the skinny kernel; not the bench line)")
@@ -94,8 +98,11 @@ class Timer:
         self.torch = torch
         self.pending = []
         self.enabled = False
+        self.recorded = None   # list: named calls of one step, kept for the isolated replay
 
     def run(self, kind, fn, *a, name=None, **kw):
+        if self.recorded is not None and name is not None:
+            self.recorded.append((kind, name, fn, a, kw))
         if not self.enabled:
             return fn(*a, **kw)
         e0 = self.torch.cuda.Event(enable_timing=True)
@@ -187,7 +194,8 @@ def main():
     def SWIGLU(name, h):
         # act = silu(gate) * up with both amaxes of act: reads H, writes act
         swbytes[name] = h.shape[0] * h.shape[1] * 2 + h.shape[0] * (h.shape[1] // 2) * 2
-        return timer.run("swiglu", nv.swiglu_amax, h, mask, out=buf("Act", (h.shape[0], h.shape[1] // 2)))
+        return timer.run("swiglu", nv.swiglu_amax, h, mask, name=name,
+                         out=buf("Act", (h.shape[0], h.shape[1] // 2)))
 
     def G(name, role, a, b, M, N, K, out=None):
         gemm_flops[name] = 2.0 * M * N * K
@@ -266,6 +274,23 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.quant_only:
+        step()
+        torch.cuda.synchronize()
+        timer.recorded = []
+        step()
+        torch.cuda.synchronize()
+        calls = timer.recorded
+        timer.recorded = None
+        iso = isolated_times(torch, calls, dev, reps=3)
+        print(json.dumps({"quant_only": {
+            "replay": "each call once untimed, then a 1 GiB cache-evicting read, then 3 "
+                      "times back to back (timed), in this order",
+            "order": [name for _, name, _, _, _ in calls],
+            "isolated_us": {k: round(v, 2) for k, v in iso.items()},
+            "bytes": {k: int(v) for k, v in qbytes.items()}}}), flush=True)
+        return
+
     print("warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -288,6 +313,16 @@ def main():
     print("timed %d steps: %.3f ms/step (host wall %.3f s)" % (args.steps, ms_step, wall),
           file=sys.stderr, flush=True)
 
+    # every quantize, amax, transpose and SwiGLU call of one more step, replayed
+    # one at a time on one stream (nothing beside it), each after a cache-evicting
+    # write: the per-kernel times the two-stream step cannot give
+    timer.enabled = False
+    timer.recorded = []
+    step()
+    torch.cuda.synchronize()
+    iso = isolated_times(torch, timer.recorded, dev)
+    timer.recorded = None
+
     flops_step = sum(gemm_flops.values())
     value = flops_step / (ms_step * 1e-3) / 1e12
     per_kind = {k: {"ms_per_step": t / args.steps, "calls_per_step": n / args.steps}
@@ -305,13 +340,22 @@ def main():
     # (the stochastic-rounding calls are bound by VALU work: Philox and the
     # exact SR selection; the others stream HBM)
     q_calls = {}
+    counters = quantize_counters()
     for name, (t, n) in timer.totals(by_name=True).items():
         if name not in qbytes:
             continue
-        q_calls[name] = {"us": round(t / n * 1e3, 1),
-                         "GBps": round(qbytes[name] / (t / n * 1e-3) / 1e9, 1),
-                         "bound": "valu" if "_sr" in name else "hbm"}
+        it = iso[name]
+        q_calls[name] = {"us_in_step": round(t / n * 1e3, 1),
+                         "isolated_us": round(it, 1),
+                         "isolated_GBps": round(qbytes[name] / (it * 1e-6) / 1e9, 1),
+                         "isolated_frac_of_hbm": round(qbytes[name] / (it * 1e-6) / 1e9
+                                                       / HBM_PEAK_GBPS, 4),
+                         "bytes": int(qbytes[name])}
+        if counters is not None and name in counters:
+            q_calls[name]["bound"] = counters[name]["bound"]
+            q_calls[name]["counters"] = counters[name]
     q_bytes = sum(qbytes.values()) * args.steps
+    q_iso = sum(iso[k] for k in qbytes)
     gemm_t = sum(totals["gemm_" + k][0] for k in role_flops)
     # the quantize phases' wall time: the step outside the GEMMs and the
     # SwiGLU pass, which run alone on the main stream (the per-call times
@@ -341,7 +385,12 @@ def main():
         "quantize_GBps": round(q_bytes / (q_wall * 1e-3) / 1e9, 1),
         "quantize_frac_of_hbm": round(q_bytes / (q_wall * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "quantize_wall_ms_per_step": round(q_wall / args.steps, 4),
+        "quantize_isolated_GBps": round(sum(qbytes.values()) / (q_iso * 1e-6) / 1e9, 1),
+        "quantize_isolated_frac_of_hbm": round(sum(qbytes.values()) / (q_iso * 1e-6) / 1e9
+                                               / HBM_PEAK_GBPS, 4),
+        "quantize_isolated_ms_per_step": round(q_iso / 1e3, 4),
         "quantize_by_call": q_calls,
+        "swiglu_isolated_us": round(iso["Act_swiglu_amax2"], 1),
         "swiglu_GBps": round(sum(swbytes.values()) * args.steps / (totals["swiglu"][0] * 1e-3) / 1e9, 1),
         "time_breakdown_ms_per_step": {("quantize_calls_sum" if k == "quantize" else k):
                                        round(v["ms_per_step"], 4) for k, v in per_kind.items()},
@@ -362,6 +411,51 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, torch, nv, workloads, X, W_gu)
     print(json.dumps(line), flush=True)
+
+
+def isolated_times(torch, calls, dev, reps=10):
+    """Kernel time (us) of each recorded call run alone on one stream: the
+    mean of `reps` back-to-back repetitions between two events, after one
+    untimed call and a 1 GiB read that evicts the L2 and the 256 MB Infinity
+    Cache.  Back-to-back calls re-read their input; every input here but the
+    two 16x16 weights' codes is at least as large as the Infinity Cache, so
+    little of it is still cached when the next call starts."""
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    out = {}
+    for kind, name, fn, a, kw in calls:
+        fn(*a, **kw)
+        flush.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            fn(*a, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1e3 / reps
+    del flush
+    return out
+
+
+QCOUNTER_FILE = os.path.join(ROOT, "profiles", "quantize_counters_llama8b.json")
+QUANT_SOURCE = os.path.join(ROOT, "nvfp4_bit_microscaled_amd", "csrc", "quantize.hip")
+
+
+def quantize_counters():
+    """Per-call counter summary of the step's quantize kernels (HBM bytes, VALU
+    busy, the bound they imply) from the committed rocprofv3 run, or None when
+    it is missing or was taken on a different quantize source."""
+    import hashlib
+    try:
+        with open(QCOUNTER_FILE) as f:
+            rec = json.load(f)
+        with open(QUANT_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("quantize_source_sha256") != sha:
+        return None
+    return rec.get("calls")
 
 
 def dequant_rht_bench(torch, nv, X, mask, reps=20):
