@@ -277,16 +277,36 @@ nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
  * whose dims are not multiples of 16).
  *   c, ldc, out_dtype  C[m*ldc + n], BF16 (recipe output) or FP32; c needs only
  *                      element alignment and ldc >= N is free
+ *   workspace, workspace_bytes
+ *                      nvfp4_gemm_workspace_size(layout, M, N, K) bytes of
+ *                      device memory, 16-byte aligned, no initialisation
+ *                      needed.  Required when K > 32768 (NVFP4_ERR_WORKSPACE
+ *                      otherwise).  For K <= 32768 it is optional: with it, a
+ *                      last round of 256 x 256 output tiles that would leave
+ *                      at least half of the device's compute units idle runs
+ *                      as two K halves per tile (two FP32 planes of M x N,
+ *                      summed before the output rounding); NULL/0 runs
+ *                      every tile whole.  The size depends on the current
+ *                      device's compute-unit count.
+ * Accumulation: the matrix unit's FP32 accumulation does not round to
+ * nearest (a small bias per instruction, measured on the MI355X), so one
+ * accumulation chain keeps the error within 1e-5 * sum |a*b| only up to
+ * K = 32768 for all-positive products.  Above that, K is cut into slices of
+ * at most 32768 (multiples of 512), each slice's s_A s_B * sum goes to its
+ * own FP32 plane of the workspace, and the planes are summed in order with
+ * IEEE FP32 additions before the BF16 rounding.
  * Shape rules: M, N, K >= 0; K % 16 == 0; a dimension along which codes are
  * packed but which is not K (N for NN, M and N for TN) must be a multiple of
  * 16.  K == 0 writes zeros.
  */
+size_t nvfp4_gemm_workspace_size(nvfp4_layout layout, int64_t M, int64_t N, int64_t K);
 nvfp4_status nvfp4_gemm(nvfp4_layout layout, int64_t M, int64_t N, int64_t K,
                         const uint8_t* a_codes, const uint8_t* a_scales,
                         const float* a_tensor_scale, nvfp4_block a_block,
                         const uint8_t* b_codes, const uint8_t* b_scales,
                         const float* b_tensor_scale, nvfp4_block b_block, nvfp4_dtype out_dtype,
-                        void* c, int64_t ldc, void* stream);
+                        void* c, int64_t ldc, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * Weight-only NVFP4 GEMM for decode shapes (BF16 activations, NVFP4 weights):
@@ -303,8 +323,9 @@ nvfp4_status nvfp4_gemm(nvfp4_layout layout, int64_t M, int64_t N, int64_t K,
  * significant bits), so every product is exact and only the accumulation
  * order differs from an FP64 reference.
  * Shape rules: 0 <= M <= 64 (decode; NVFP4_ERR_UNSUPPORTED above), K % 512
- * == 0, lda >= K with 16-byte aligned rows, N * K / 2 < 2^31, N % 16 == 0 for
- * a 2D weight.  K == 0 writes zeros.
+ * == 0, K <= 32768 (one FP32 accumulation chain; see nvfp4_gemm), lda >= K
+ * with 16-byte aligned rows, N * K / 2 < 2^31, N % 16 == 0 for a 2D weight.
+ * K == 0 writes zeros.
  */
 nvfp4_status nvfp4_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
                               const uint8_t* b_codes, const uint8_t* b_scales,
@@ -329,8 +350,9 @@ nvfp4_status nvfp4_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, in
  * 64q + c and 128q + 64 + c its up column.  act's column 64q + c pairs them.
  * (A weight stored in this row order is an ordinary NVFP4 tensor: quantize,
  * dequantize and the dgrad/wgrad GEMMs treat it like any other.)
- * Shape rules: N % 128 == 0; M % 16 == 0; K % 128 == 0, K > 0; K/2 * 256 <
- * 2^31; ld_act >= N/2; ldh >= N when h is given.  Code and scale planes
+ * Shape rules: N % 128 == 0; M % 16 == 0; K % 128 == 0, 0 < K <= 32768 (one
+ * FP32 accumulation chain; see nvfp4_gemm); ld_act >= N/2; ldh >= N when h
+ * is given.  Code and scale planes
  * 16-byte aligned; act 8-byte aligned with ld_act % 4 == 0.  M == 0 or
  * N == 0 writes only amax = amax_rht = 0.  Workspace:
  * nvfp4_gemm_swiglu_workspace_size(M, N) bytes (two floats per 256 x 256

@@ -38,7 +38,7 @@ EXPORTS = ("nvfp4_version", "nvfp4_status_string", "nvfp4_quantize_workspace_siz
            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize",
            "nvfp4_mx_gemm", "nvfp4_gemm_w4a16", "nvfp4_kv_cache_write",
            "nvfp4_kv_cache_read", "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu",
-           "nvfp4_transpose", "nvfp4_quantize_noalloc")
+           "nvfp4_transpose", "nvfp4_quantize_noalloc", "nvfp4_gemm_workspace_size")
 
 
 class NVFP4Error(RuntimeError):
@@ -79,7 +79,10 @@ def _load():
     L.nvfp4_dequantize.restype = ci
     L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, ci, ci, ci, vp, i64, vp]
     L.nvfp4_gemm.restype = ci
-    L.nvfp4_gemm.argtypes = [ci, i64, i64, i64, vp, vp, vp, ci, vp, vp, vp, ci, ci, vp, i64, vp]
+    L.nvfp4_gemm.argtypes = [ci, i64, i64, i64, vp, vp, vp, ci, vp, vp, vp, ci, ci, vp, i64, vp,
+                             ctypes.c_size_t, vp]
+    L.nvfp4_gemm_workspace_size.restype = ctypes.c_size_t
+    L.nvfp4_gemm_workspace_size.argtypes = [ci, i64, i64, i64]
     L.nvfp4_gemm_w4a16.restype = ci
     L.nvfp4_gemm_w4a16.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, ci, ci, vp, i64, vp]
     L.nvfp4_mx_quantize.restype = ci
@@ -184,11 +187,16 @@ def nvfp4_dequantize(codes, scales, tensor_scale, rows, cols, block, axis, out_d
                                 out_dtype, _p(out), ld_out, _stream(stream))
 
 
+def nvfp4_gemm_workspace_size(layout: int, M: int, N: int, K: int) -> int:
+    return lib.nvfp4_gemm_workspace_size(layout, M, N, K)
+
+
 def nvfp4_gemm(layout, M, N, K, a_codes, a_scales, a_tensor_scale, a_block, b_codes, b_scales,
-               b_tensor_scale, b_block, out_dtype, c, ldc, stream=None) -> int:
+               b_tensor_scale, b_block, out_dtype, c, ldc, workspace=None, workspace_bytes=0,
+               stream=None) -> int:
     return lib.nvfp4_gemm(layout, M, N, K, _p(a_codes), _p(a_scales), _p(a_tensor_scale), a_block,
                           _p(b_codes), _p(b_scales), _p(b_tensor_scale), b_block, out_dtype,
-                          _p(c), ldc, _stream(stream))
+                          _p(c), ldc, _p(workspace), workspace_bytes, _stream(stream))
 
 
 def nvfp4_gemm_w4a16(M, N, K, a, lda, b_codes, b_scales, b_tensor_scale, b_block, out_dtype, c,
@@ -421,10 +429,20 @@ def gemm(layout: str, a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16,
         out = torch.empty(M, N, dtype=out_dtype, device=a.codes.device)
     if tuple(out.shape) != (M, N) or out.stride(1) != 1:
         raise ValueError("gemm %s: out must be [%d, %d] with unit column stride" % (layout, M, N))
+    nws = nvfp4_gemm_workspace_size(LAYOUT[layout], M, N, K)
+    ws = None
+    if nws > 0:
+        # K longer than one accumulation chain: FP32 planes of the K slices
+        key = ("gemm", str(out.device), torch.cuda.current_stream(out.device).cuda_stream)
+        ws = _workspaces.get(key)
+        if ws is None or ws.numel() < nws:
+            ws = torch.empty(nws, dtype=torch.uint8, device=out.device)
+            _workspaces[key] = ws
     _check("nvfp4_gemm", nvfp4_gemm(
         LAYOUT[layout], M, N, K, a.codes, a.scales, a.tensor_scale,
         BLOCK_2D if a.block2d else BLOCK_1D, b.codes, b.scales, b.tensor_scale,
-        BLOCK_2D if b.block2d else BLOCK_1D, _dtype_code(out), out, out.stride(0)))
+        BLOCK_2D if b.block2d else BLOCK_1D, _dtype_code(out), out, out.stride(0), ws,
+        0 if ws is None else ws.numel()))
     return out
 
 

@@ -66,7 +66,7 @@ nvfp4_status scratch_of_current_device(float** out)
 
 extern "C" {
 
-int nvfp4_version(void) { return 100; }
+int nvfp4_version(void) { return 200; }
 
 const char* nvfp4_status_string(nvfp4_status s)
 {
@@ -311,12 +311,22 @@ nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t nvfp4_gemm_workspace_size(nvfp4_layout layout, int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    int64_t ks;
+    const int nsl = gemm_k_slices(K, &ks);
+    if (nsl > 1) return (size_t)nsl * (size_t)M * (size_t)N * sizeof(float);
+    return gemm_split_bytes(layout == NVFP4_LAYOUT_NT, M, N, K);
+}
+
 nvfp4_status nvfp4_gemm(nvfp4_layout layout, int64_t M, int64_t N, int64_t K,
                         const uint8_t* a_codes, const uint8_t* a_scales,
                         const float* a_tensor_scale, nvfp4_block a_block,
                         const uint8_t* b_codes, const uint8_t* b_scales,
                         const float* b_tensor_scale, nvfp4_block b_block, nvfp4_dtype out_dtype,
-                        void* c, int64_t ldc, void* stream)
+                        void* c, int64_t ldc, void* workspace, size_t workspace_bytes,
+                        void* stream)
 {
     if (layout != NVFP4_LAYOUT_NT && layout != NVFP4_LAYOUT_NN && layout != NVFP4_LAYOUT_TN)
         return NVFP4_ERR_INVALID_ARG;
@@ -344,9 +354,21 @@ nvfp4_status nvfp4_gemm(nvfp4_layout layout, int64_t M, int64_t N, int64_t K,
         return NVFP4_ERR_INVALID_ARG;
     if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) || !aligned16(b_scales))
         return NVFP4_ERR_ALIGN;
+    // K slices (K > 32768) need the workspace; the last-round K split only
+    // runs when the caller supplied enough of it
+    int64_t ks;
+    const bool sliced = gemm_k_slices(K, &ks) > 1;
+    const size_t need = nvfp4_gemm_workspace_size(layout, M, N, K);
+    float* ws = nullptr;
+    if (need > 0 && workspace && workspace_bytes >= need) {
+        if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+        ws = static_cast<float*>(workspace);
+    } else if (sliced) {
+        return NVFP4_ERR_WORKSPACE;
+    }
     GemmOperand A{a_codes, a_scales, a_tensor_scale, a_block == NVFP4_BLOCK_2D, a_kmajor};
     GemmOperand B{b_codes, b_scales, b_tensor_scale, b_block == NVFP4_BLOCK_2D, b_kmajor};
-    return from_hip(launch_gemm(M, N, K, A, B, out_dtype == NVFP4_DTYPE_BF16, c, ldc, s));
+    return from_hip(launch_gemm(M, N, K, A, B, out_dtype == NVFP4_DTYPE_BF16, c, ldc, ws, s));
 }
 
 nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
@@ -419,6 +441,7 @@ nvfp4_status nvfp4_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, in
     if (K % 512) return NVFP4_ERR_SHAPE;
     if (b_block == NVFP4_BLOCK_2D && N % 16) return NVFP4_ERR_LAYOUT;
     if (M > 64) return NVFP4_ERR_UNSUPPORTED;
+    if (K > kMaxChainK) return NVFP4_ERR_UNSUPPORTED;
     if ((uint64_t)N * (uint64_t)K / 2 >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return NVFP4_OK;
     if (!c) return NVFP4_ERR_INVALID_ARG;
@@ -504,8 +527,10 @@ nvfp4_status nvfp4_gemm_swiglu(int64_t M, int64_t N, int64_t K, const uint8_t* a
     if (N % 128 || M % 16) return NVFP4_ERR_SHAPE;
     if (K == 0 || K % 128) return NVFP4_ERR_SHAPE;
     if (ld_act < N / 2 || (h && ldh < N)) return NVFP4_ERR_SHAPE;
-    // buffer records of a 256-row tile in 32 bits; tile ids in 31 bits
+    // buffer records of a 256-row tile in 32 bits; tile ids in 31 bits; one
+    // FP32 accumulation chain over K
     if ((uint64_t)K / 2 * 256 >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
+    if (K > kMaxChainK) return NVFP4_ERR_UNSUPPORTED;
     const uint64_t tiles = (uint64_t)((M + 255) / 256) * (uint64_t)((N + 255) / 256);
     if (tiles >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -42,6 +42,7 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b)
 
 struct GemmParams {
     int64_t M, N, K;
+    int64_t kp;   // K-major operands: K extent of a row of the planes (>= K; > K for a K slice)
     const uint8_t* a_codes;
     const uint8_t* a_scales;
     const uint8_t* b_codes;
@@ -62,6 +63,11 @@ struct GemmParams {
     uint32_t rht_mask;
     float* partials;   // [grid] max|act|, then [grid] max|RHT16 of act down columns|
     bool store_h, act_vec16;
+    // K-split of the last round of tiles (k_gemm_kk<.., true>): workgroup b
+    // takes K half b % 2 of tile tile_base + b / 2 (K = the half's length,
+    // kp the whole K) and writes the FP32 partial to c (half 0) or c2 (half 1)
+    uint32_t tile_base;
+    uint8_t* c2;
 };
 
 // 8x8 nibble transpose: in[k] holds element (k, j) in nibble j; out[j] gets
@@ -144,24 +150,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const uint8_t* base
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, 0x00020000);
 }
 
+// K-major planes have rows of kp elements (kp / 2 code bytes, kp / 16 scale
+// bytes); the GEMM covers K <= kp of them (a K slice starts at the planes'
+// base pointers).
 template <bool kKMajor, bool kFull>
 __device__ __forceinline__ void stage_load(const uint8_t* __restrict__ codes,
                                            const uint8_t* __restrict__ scales, bool k2D,
-                                           int64_t MN, int64_t K, int64_t row0, int64_t k0,
-                                           Staged& st)
+                                           int64_t MN, int64_t K, int64_t kp, int64_t row0,
+                                           int64_t k0, Staged& st)
 {
     const int t = threadIdx.x;
     if (kKMajor && kFull) {
         // chunk f = it*256 + t: row f/4 = t/4 + 64 it, plane f%4 = t%4
         const __amdgpu_buffer_rsrc_t rc = plane_rsrc(codes);
-        const int vo = (t >> 2) * (int)(K / 2) + 16 * (t & 3);
+        const int vo = (t >> 2) * (int)(kp / 2) + 16 * (t & 3);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            int so = (int)((row0 + 64 * it) * (K / 2) + k0 / 2);
+            int so = (int)((row0 + 64 * it) * (kp / 2) + k0 / 2);
             st.code[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vo, so, 0));
         }
         const __amdgpu_buffer_rsrc_t rs = plane_rsrc(scales);
-        int64_t ld = K / 16;
+        int64_t ld = kp / 16;
         // the lane-dependent part goes in the VGPR offset, the rest is uniform
         int vs = k2D ? (t >> 4) * (int)ld : t * (int)ld;
         int ss = (int)((k2D ? (row0 / 16) * ld : row0 * ld) + k0 / 16);
@@ -174,7 +183,7 @@ __device__ __forceinline__ void stage_load(const uint8_t* __restrict__ codes,
             int f = it * 256 + t;
             int r = f >> 2, c = f & 3;
             int64_t row = row0 + r, k = k0 + 32 * c;
-            const uint8_t* src = codes + row * (K / 2) + k / 2;
+            const uint8_t* src = codes + row * (kp / 2) + k / 2;
             u32x4 w = {0u, 0u, 0u, 0u};  // rows are only 8-byte aligned when K % 32 != 0
             if (row < MN) {
 #pragma unroll
@@ -185,13 +194,13 @@ __device__ __forceinline__ void stage_load(const uint8_t* __restrict__ codes,
         }
         // scales: thread t owns row t, 8 bytes (k-blocks k0/16 .. +7)
         int64_t row = row0 + t, kb = k0 / 16;
-        int64_t ld = K / 16;
+        int64_t ld = kp / 16;
         const uint8_t* src = scales + (k2D ? (row / 16) * ld : row * ld) + kb;
         uint32_t w0 = 0u, w1 = 0u;
         if (row < MN) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                uint32_t b = (kb + j < ld) ? (uint32_t)src[j] : 0u;
+                uint32_t b = (kb + j < K / 16) ? (uint32_t)src[j] : 0u;
                 if (j < 4) w0 |= b << (8 * j);
                 else w1 |= b << (8 * (j - 4));
             }
@@ -558,8 +567,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p)
     }                                                                                          \
     __builtin_amdgcn_sched_barrier(0);
 #define PREFETCH(kt_)                                                                          \
-    stage_load<kAK, kFull>(p.a_codes, p.a_scales, p.a2d, p.M, p.K, m0, (int64_t)(kt_) * kTK, sa); \
-    stage_load<kBK, kFull>(p.b_codes, p.b_scales, p.b2d, p.N, p.K, n0, (int64_t)(kt_) * kTK, sb);
+    stage_load<kAK, kFull>(p.a_codes, p.a_scales, p.a2d, p.M, p.K, p.kp, m0, (int64_t)(kt_) * kTK, sa); \
+    stage_load<kBK, kFull>(p.b_codes, p.b_scales, p.b2d, p.N, p.K, p.kp, n0, (int64_t)(kt_) * kTK, sb);
 
     // Prologue: tile 0 into buffer 0 and its step-0 operands.
     Staged sa, sb;
@@ -807,17 +816,20 @@ struct KKOperand {
 // last row (at most 256 rows on), so rows past M or N read as zeros.  Code
 // window j of wave w holds rows 16 (4w + j) .. +15, four lanes per row; scale
 // window j rows 32 (2w + j) .. +31, two lanes per row.
+// Rows are kp elements long (kp / 2 code bytes, kp / 16 scale bytes); the
+// records end right after the last K code / scale byte of the last row.
 __device__ __forceinline__ KKOperand kk_operand(const uint8_t* codes, const uint8_t* scales,
-                                                bool two_d, int64_t MN, int64_t K, int64_t row0)
+                                                bool two_d, int64_t MN, int64_t K, int64_t kp,
+                                                int64_t row0)
 {
     KKOperand o;
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int64_t ldc = K / 2, lds = K / 16;
+    const int64_t ldc = kp / 2, lds = kp / 16;
     const int64_t nrow = MN - row0 < 256 ? MN - row0 : 256;
     o.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + row0 * ldc), (short)0,
-                                                (int)(nrow * ldc), 0x00020000);
+                                                (int)((nrow - 1) * ldc + K / 2), 0x00020000);
     const int64_t s0 = two_d ? (row0 / 16) * lds : row0 * lds;
-    const int64_t srec = two_d ? (nrow + 15) / 16 * lds : nrow * lds;
+    const int64_t srec = (two_d ? (nrow + 15) / 16 - 1 : nrow - 1) * lds + K / 16;
     o.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + s0), (short)0, (int)srec,
                                                  0x00020000);
     // the plane swizzle depends on row bits 1-2 only, the same in all four
@@ -875,13 +887,25 @@ struct KKPlan {
 constexpr int kKKEpiAny = 0, kKKEpiBF16 = 1, kKKEpiF32 = 2;
 
 // kSwiGLU: GEMM 1 of the MLP with the SwiGLU epilogue (swiglu_epilogue).
-template <bool kSwiGLU, int kEpi = kKKEpiAny>
+// kSplit: the K halves of the last round's tiles (GemmParams::tile_base).
+template <bool kSwiGLU, int kEpi = kKKEpiAny, bool kSplit = false>
 __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const uint32_t nbm = (uint32_t)((p.M + kTM - 1) / kTM), nbn = (uint32_t)((p.N + kTN - 1) / kTN);
     uint32_t tm, tn;
-    tile_of(blockIdx.x, nbm, nbn, tm, tn);
+    if constexpr (kSplit) {
+        tile_of(p.tile_base + (blockIdx.x >> 1), nbm, nbn, tm, tn);
+        if (blockIdx.x & 1) {  // second half: K p.K .. 2 p.K of each row
+            p.a_codes += p.K / 2;
+            p.a_scales += p.K / 16;
+            p.b_codes += p.K / 2;
+            p.b_scales += p.K / 16;
+            p.c = p.c2;
+        }
+    } else {
+        tile_of(blockIdx.x, nbm, nbn, tm, tn);
+    }
     tm = __builtin_amdgcn_readfirstlane(tm);
     tn = __builtin_amdgcn_readfirstlane(tn);
     const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
@@ -890,8 +914,8 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
     const int lr = lane & 31, lk = lane >> 5;
     const int nk = (int)(p.K / kTK);
 
-    const KKOperand oa = kk_operand(p.a_codes, p.a_scales, p.a2d, p.M, p.K, m0);
-    const KKOperand ob = kk_operand(p.b_codes, p.b_scales, p.b2d, p.N, p.K, n0);
+    const KKOperand oa = kk_operand(p.a_codes, p.a_scales, p.a2d, p.M, p.K, p.kp, m0);
+    const KKOperand ob = kk_operand(p.b_codes, p.b_scales, p.b2d, p.N, p.K, p.kp, n0);
     using Plan = KKPlan;
 
     float16_t acc[4][4];
@@ -1395,11 +1419,81 @@ hipError_t launch_fill_zero(void* c, bool bf16, int64_t M, int64_t N, int64_t ld
         }                           \
     } while (0)
 
-hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
-                       const GemmOperand& B, bool out_bf16, void* c, int64_t ldc, hipStream_t s)
+// Compute units of the current device (looked up once per device).
+static int device_cu_count()
 {
-    GemmParams p;
-    p.M = M; p.N = N; p.K = K;
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Tiles of the K-major kernel's last round that run as two K halves: when
+// the tile count leaves a last round at most half full (one workgroup per
+// CU), its tiles are split along K so the round fills the CUs and takes half
+// as long.  0 when no split applies (short K, K sliced, full last round).
+uint64_t gemm_tail_tiles(int64_t M, int64_t N, int64_t K, int64_t kp)
+{
+    if (kp != K || K % (2 * kTK) != 0 || K < 4096) return 0;
+    const uint64_t ncu = (uint64_t)device_cu_count();
+    const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
+    if (ncu == 0 || t <= ncu) return 0;
+    const uint64_t tail = t % ncu;
+    return 2 * tail <= ncu ? tail : 0;
+}
+
+// Workspace bytes of the last-round K split for a GEMM of these operands
+// (both K-major: the NT layout), 0 when launch_gemm_one does not split:
+// decode shapes take the skinny kernel, other shapes the 256 x 256 one.
+size_t gemm_split_bytes(bool both_kmajor, int64_t M, int64_t N, int64_t K)
+{
+    if (!both_kmajor || K % kTK != 0 || K > kMaxChainK) return 0;
+    if (M <= 64 && K % 512 == 0 && (uint64_t)N * (uint64_t)K / 2 < (1ull << 31)) return 0;
+    if (K / 2 * kTM >= (1ll << 31)) return 0;
+    return gemm_tail_tiles(M, N, K, K) ? (size_t)2 * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+// C over the split tiles: the two FP32 halves (planes [M, N]) summed, then
+// rounded to BF16 or stored as FP32.  One workgroup per tile (tile ids as
+// the K-major kernel maps them); thread t covers 4 columns of rows t / 64,
+// t / 64 + 4, ...
+__global__ __launch_bounds__(256) void k_sum_tail_tiles(const float* h0, const float* h1,
+                                                        int64_t M, int64_t N, uint32_t tile_base,
+                                                        bool out_bf16, uint8_t* c, int64_t ldc)
+{
+    const uint32_t nbm = (uint32_t)((M + kTM - 1) / kTM), nbn = (uint32_t)((N + kTN - 1) / kTN);
+    uint32_t tm, tn;
+    tile_of(tile_base + blockIdx.x, nbm, nbn, tm, tn);
+    const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
+    const int t = threadIdx.x;
+    const int64_t col = n0 + 4 * (t & 63);
+    for (int r = t >> 6; r < kTM; r += 4) {
+        const int64_t row = m0 + r;
+        if (row >= M) break;
+        for (int q = 0; q < 4; ++q) {
+            if (col + q >= N) break;
+            const float v = h0[row * N + col + q] + h1[row * N + col + q];
+            if (out_bf16)
+                reinterpret_cast<uint16_t*>(c)[row * ldc + col + q] = (uint16_t)f32_to_bf16_bits(v);
+            else
+                reinterpret_cast<float*>(c)[row * ldc + col + q] = v;
+        }
+    }
+}
+
+// One GEMM launch over K (<= kp: a K slice when kp > K).
+static hipError_t launch_gemm_one(int64_t M, int64_t N, int64_t K, int64_t kp,
+                                  const GemmOperand& A, const GemmOperand& B, bool out_bf16,
+                                  void* c, int64_t ldc, hipStream_t s, float* split_ws = nullptr)
+{
+    GemmParams p{};
+    p.M = M; p.N = N; p.K = K; p.kp = kp;
     p.a_bf16 = nullptr; p.lda = 0;
     p.a_codes = A.codes; p.a_scales = A.scales; p.a_ts = A.ts;
     p.b_codes = B.codes; p.b_scales = B.scales; p.b_ts = B.ts;
@@ -1415,7 +1509,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     // kernel; its K chunk must divide K
     const int skinny_kc = 512;
     const bool b_small = (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);  // 32-bit buffer offsets
-    if (A.k_major && B.k_major && M <= 64 && K % skinny_kc == 0 && b_small) {
+    if (A.k_major && B.k_major && M <= 64 && K % skinny_kc == 0 && b_small && kp == K) {
         dim3 g((unsigned)((N + kSkN - 1) / kSkN));
 #define NVFP4_SKINNY(KC, RMAX)                                                                 \
     {                                                                                          \
@@ -1430,18 +1524,38 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
 #undef NVFP4_SKINNY
         return hipGetLastError();
     }
-    if (A.k_major && B.k_major && K % kTK == 0 && K / 2 * kTM < (1ll << 31)) {
+    if (A.k_major && B.k_major && K % kTK == 0 && kp / 2 * kTM < (1ll << 31)) {
         const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
         const bool all_full = M % kTM == 0 && N % kTN == 0 && p.vec16;
         auto kern = !all_full ? k_gemm_kk<false, kKKEpiAny>
                               : (out_bf16 ? k_gemm_kk<false, kKKEpiBF16> : k_gemm_kk<false, kKKEpiF32>);
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kKKLds);
-        hipLaunchKernelGGL(kern, dim3((unsigned)t), dim3(256), kKKLds, s, p);
+        const uint64_t tail = split_ws ? gemm_tail_tiles(M, N, K, kp) : 0;
+        hipLaunchKernelGGL(kern, dim3((unsigned)(t - tail)), dim3(256), kKKLds, s, p);
+        if (tail == 0) return hipGetLastError();
+        // the last round: each of its tiles as two K halves on two CUs, FP32
+        // partials into the two workspace planes, then summed into C
+        GemmParams q = p;
+        q.K = K / 2;
+        q.kp = kp;
+        q.out_bf16 = false;
+        q.c = reinterpret_cast<uint8_t*>(split_ws);
+        q.c2 = reinterpret_cast<uint8_t*>(split_ws + M * N);
+        q.ldc = N;
+        q.vec_out = N % 4 == 0;
+        q.vec16 = N % 4 == 0;
+        q.tile_base = (uint32_t)(t - tail);
+        const bool full_q = M % kTM == 0 && N % kTN == 0 && q.vec16;
+        auto ks = full_q ? k_gemm_kk<false, kKKEpiF32, true> : k_gemm_kk<false, kKKEpiAny, true>;
+        hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, kKKLds);
+        hipLaunchKernelGGL(ks, dim3((unsigned)(2 * tail)), dim3(256), kKKLds, s, q);
+        hipLaunchKernelGGL(k_sum_tail_tiles, dim3((unsigned)tail), dim3(256), 0, s, split_ws,
+                           split_ws + M * N, M, N, (uint32_t)(t - tail), out_bf16, p.c, ldc);
         return hipGetLastError();
     }
     // full tiles: no bounds checks, 32-bit buffer offsets (planes below 2 GiB)
-    const bool small = (uint64_t)M * (uint64_t)K / 2 < (1ull << 31) &&
-                       (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);
+    const bool small = (uint64_t)M * (uint64_t)kp / 2 < (1ull << 31) &&
+                       (uint64_t)N * (uint64_t)kp / 2 < (1ull << 31);
     const bool full = (M % kTM == 0) && (N % kTN == 0) && (K % kTK == 0) && small;
     const uint64_t tiles = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
     dim3 grid((unsigned)tiles);
@@ -1460,6 +1574,90 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
     return hipGetLastError();
 }
 
+// Sum of the K-slice partial products: c[m, n] = sum over j of
+// ws[j][m][n] (FP32, j in order), rounded to BF16 or stored as FP32.
+// Four consecutive outputs per thread when the rows allow it.
+__global__ __launch_bounds__(256) void k_sum_slices(const float* ws, int nsl, int64_t M,
+                                                    int64_t N, bool out_bf16, uint8_t* c,
+                                                    int64_t ldc)
+{
+    const int64_t plane = M * N, quads = (N + 3) / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < M * quads;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / quads, c0 = (i - r * quads) * 4;
+        const int cnt = N - c0 < 4 ? (int)(N - c0) : 4;
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < nsl; ++j) {
+            const float* src = ws + j * plane + r * N + c0;
+            if (cnt == 4 && (N % 4) == 0) {
+                const float4_t w = *reinterpret_cast<const float4_t*>(src);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] += w[q];
+            } else {
+                for (int q = 0; q < cnt; ++q) v[q] += src[q];
+            }
+        }
+        for (int q = 0; q < cnt; ++q) {
+            if (out_bf16)
+                reinterpret_cast<uint16_t*>(c)[r * ldc + c0 + q] = (uint16_t)f32_to_bf16_bits(v[q]);
+            else
+                reinterpret_cast<float*>(c)[r * ldc + c0 + q] = v[q];
+        }
+    }
+}
+
+// The operand's planes from element k0 of K on (k0 % 16 == 0).
+static GemmOperand k_slice(const GemmOperand& o, int64_t MN, int64_t k0)
+{
+    GemmOperand r = o;
+    if (o.k_major) {
+        // [MN, K]: k0 / 2 code bytes and k0 / 16 scale bytes into every row
+        r.codes = o.codes + k0 / 2;
+        r.scales = o.scales + k0 / 16;
+    } else {
+        // [K, MN]: k0 rows on; scales [K/16, MN] (1D) or [K/16, MN/16] (2D)
+        r.codes = o.codes + k0 * (MN / 2);
+        r.scales = o.scales + (k0 / 16) * (o.block2d ? MN / 16 : MN);
+    }
+    return r;
+}
+
+int gemm_k_slices(int64_t K, int64_t* slice_k)
+{
+    if (K <= kMaxChainK) {
+        *slice_k = K;
+        return 1;
+    }
+    const int64_t n = (K + kMaxChainK - 1) / kMaxChainK;
+    const int64_t q = 512;  // a multiple of every kernel's K step
+    *slice_k = ((K + n - 1) / n + q - 1) / q * q;
+    return (int)((K + *slice_k - 1) / *slice_k);
+}
+
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
+                       const GemmOperand& B, bool out_bf16, void* c, int64_t ldc, float* ws,
+                       hipStream_t s)
+{
+    int64_t ks;
+    const int nsl = gemm_k_slices(K, &ks);
+    if (nsl == 1) return launch_gemm_one(M, N, K, K, A, B, out_bf16, c, ldc, s, ws);
+    // K slices of at most kMaxChainK, each into its own FP32 plane, summed in order
+    for (int j = 0; j < nsl; ++j) {
+        const int64_t k0 = j * ks, kl = K - k0 < ks ? K - k0 : ks;
+        const GemmOperand a = k_slice(A, M, k0), b = k_slice(B, N, k0);
+        const hipError_t e =
+            launch_gemm_one(M, N, kl, K, a, b, false, ws + (int64_t)j * M * N, N, s);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t work = M * ((N + 3) / 4);
+    int grid = (int)((work + 255) / 256);
+    if (grid > 8192) grid = 8192;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(k_sum_slices, dim3(grid), dim3(256), 0, s, ws, nsl, M, N, out_bf16,
+                       static_cast<uint8_t*>(c), ldc);
+    return hipGetLastError();
+}
+
 
 // GEMM 1 of the MLP with the SwiGLU epilogue: H = s_A s_B A B^T (A [M, K],
 // B [N, K] with gate/up rows interleaved in blocks of 64, N % 128 == 0,
@@ -1471,7 +1669,7 @@ hipError_t launch_gemm_swiglu(int64_t M, int64_t N, int64_t K, const GemmOperand
                               float* amax_rht, hipStream_t s)
 {
     GemmParams p{};
-    p.M = M; p.N = N; p.K = K;
+    p.M = M; p.N = N; p.K = K; p.kp = K;
     p.a_codes = A.codes; p.a_scales = A.scales; p.a_ts = A.ts;
     p.b_codes = B.codes; p.b_scales = B.scales; p.b_ts = B.ts;
     p.a2d = A.block2d != 0;
@@ -1681,7 +1879,7 @@ hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_code
                           bool out_bf16, void* c, int64_t ldc, hipStream_t s)
 {
     GemmParams p;
-    p.M = M; p.N = N; p.K = K;
+    p.M = M; p.N = N; p.K = K; p.kp = K;
     p.a_bf16 = nullptr; p.lda = 0;
     p.a_codes = a_codes; p.a_scales = a_scales;
     p.b_codes = b_codes; p.b_scales = b_scales;
@@ -1707,7 +1905,7 @@ hipError_t launch_gemm_w4a16(int64_t M, int64_t N, int64_t K, const uint16_t* a,
                              hipStream_t s)
 {
     GemmParams p;
-    p.M = M; p.N = N; p.K = K;
+    p.M = M; p.N = N; p.K = K; p.kp = K;
     p.a_codes = nullptr; p.a_scales = nullptr; p.a_ts = nullptr;
     p.b_codes = B.codes; p.b_scales = B.scales; p.b_ts = B.ts;
     p.c = static_cast<uint8_t*>(c);

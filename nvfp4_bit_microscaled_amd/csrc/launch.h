@@ -80,8 +80,31 @@ struct GemmOperand {
     bool k_major;  // true: codes packed along K (storage [MN, K]); false: storage [K, MN]
 };
 
+// Longest K one chain of FP32 MFMA accumulations covers.  The matrix unit's
+// FP32 accumulation is not round-to-nearest (measured on the MI355X: about a
+// quarter of results differ from the correctly rounded sum, with a mean bias
+// of -0.02 to -0.2 ulp per instruction), so an all-positive dot product's
+// error grows with the chain length: 2e-5 of sum |a*b| at K = 106496, within
+// 1e-5 up to 32768.  A longer K is cut into slices of at most this length,
+// each accumulated separately and summed in FP32 with IEEE additions.
+constexpr int64_t kMaxChainK = 32768;
+
+// Number of K slices of a K-long GEMM and the slice length (a multiple of
+// 512; the last slice may be shorter).  1 slice when K <= kMaxChainK.
+int gemm_k_slices(int64_t K, int64_t* slice_k);
+
+// Workspace bytes for splitting the last, at most half-full round of output
+// tiles along K (both operands K-major); 0 when no split applies on the
+// current device.
+size_t gemm_split_bytes(bool both_kmajor, int64_t M, int64_t N, int64_t K);
+
+// C = A B^T etc. (layouts by GemmOperand::k_major).  When K > kMaxChainK, ws
+// holds gemm_k_slices(K) FP32 planes of M x N (16-byte aligned).  Otherwise
+// ws, when not null, holds gemm_split_bytes(...) bytes and the last round's
+// tiles are split along K (nullptr: no split).
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
-                       const GemmOperand& B, bool out_bf16, void* c, int64_t ldc, hipStream_t s);
+                       const GemmOperand& B, bool out_bf16, void* c, int64_t ldc, float* ws,
+                       hipStream_t s);
 
 // MXFP4 (E2M1 elements, E8M0 scale per 32 along the row): codes
 // [rows, cols/2], scales [rows, cols/32]; cols % 32 == 0.

@@ -36,7 +36,8 @@ def test_header_declares_the_abi():
                             "nvfp4_mx_dequantize", "nvfp4_mx_gemm", "nvfp4_gemm_w4a16",
                             "nvfp4_kv_cache_write", "nvfp4_kv_cache_read",
                             "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu",
-                            "nvfp4_transpose", "nvfp4_quantize_noalloc"])
+                            "nvfp4_transpose", "nvfp4_quantize_noalloc",
+                            "nvfp4_gemm_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -136,7 +137,7 @@ def test_swiglu_amax_validation(lib):
 
 def g(lib, **kw):
     args = dict(layout=0, M=64, N=64, K=64, ac=FAKE, asc=FAKE, ats=FAKE, ab=0, bc=FAKE, bsc=FAKE,
-                bts=FAKE, bb=1, odt=0, c=FAKE, ldc=64, stream=None)
+                bts=FAKE, bb=1, odt=0, c=FAKE, ldc=64, ws=None, wsb=0, stream=None)
     args.update(kw)
     return lib.nvfp4_gemm(*args.values())
 
@@ -155,6 +156,17 @@ def test_gemm_validation(lib):
     assert g(lib, ac=None) == 1
     assert g(lib, M=0) == 0                         # empty output: nothing to do
     assert g(lib, N=0) == 0
+    # K above one accumulation chain (32768): K slices need a workspace of one
+    # FP32 M x N plane per slice (slices of at most 32768, multiples of 512)
+    import nvfp4_bit_microscaled_amd as m
+    assert m.nvfp4_gemm_workspace_size(0, 64, 64, 32768) == 0
+    assert m.nvfp4_gemm_workspace_size(1, 64, 64, 32784) == 2 * 64 * 64 * 4
+    assert m.nvfp4_gemm_workspace_size(0, 8192, 16384, 106496) == 4 * 8192 * 16384 * 4
+    assert m.nvfp4_gemm_workspace_size(2, 0, 64, 106496) == 0
+    assert m.nvfp4_gemm_workspace_size(1, 4096, 14336, 32768) == 0   # no last-round split for NN
+    assert g(lib, K=106496) == 6                    # workspace missing
+    assert g(lib, K=106496, ws=FAKE, wsb=4 * 64 * 64 * 4 - 1) == 6
+    assert g(lib, K=106496, ws=MISALIGNED, wsb=4 * 64 * 64 * 4) == 3
 
 
 def test_rht_and_dequant_validation(lib):
@@ -219,6 +231,7 @@ def test_w4a16_validation(lib):
     assert w4(lib, c=ODD) == 3
     assert w4(lib, bts=None) == 1
     assert w4(lib, M=0) == 0
+    assert w4(lib, K=33280, lda=33280) == 5         # longer than one accumulation chain
 
 
 def kvw(lib, **kw):
@@ -337,6 +350,7 @@ def test_gemm_swiglu_validation(lib):
     assert gsw(lib, ld_act=120) == 2            # ld_act < N / 2
     assert gsw(lib, h=FAKE, ldh=200) == 2       # ldh < N
     assert gsw(lib, K=1 << 24) == 5             # 256-row records past 2^31 bytes
+    assert gsw(lib, K=32896) == 5               # longer than one accumulation chain
     assert gsw(lib, act=None) == 1
     assert gsw(lib, bc=MISALIGNED) == 3
     assert gsw(lib, act=ctypes.c_void_p(0x10004)) == 3

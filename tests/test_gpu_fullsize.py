@@ -299,7 +299,7 @@ def positive_nvfp4(nv, rng, rows, cols, ts, scale_lo, scale_hi):
 
 # the step's longest K (405B dgrad gate+up) and the 8B wgrad K; a narrow scale
 # band (E4M3 1.0 .. 2.0: similar-sized terms) and the full normal range
-@pytest.mark.parametrize("M,N,K", [(160, 96, 106496), (256, 256, 32768)])
+@pytest.mark.parametrize("M,N,K", [(160, 96, 106496), (128, 96, 53248), (256, 256, 32768)])
 @pytest.mark.parametrize("band", [(0x38, 0x40), (0x08, 0x7E)])
 def test_constant_sign_long_k(nv, M, N, K, band):
     rng = np.random.default_rng(K + band[0])

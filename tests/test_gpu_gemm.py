@@ -234,3 +234,98 @@ def test_skinny_decode_kernel(nv, M, N, K, b2d):
     a_or, a_g = random_operand(nv, rng, M, K, False, 1, 0.5)
     b_or, b_g = random_operand(nv, rng, N, K, b2d, 1, 0.75)
     run_and_check(nv, "NT", M, N, K, a_or, a_g, b_or, b_g)
+
+
+# K above one FP32 accumulation chain (32768): the library cuts K into slices
+# (multiples of 512, the last one shorter), each accumulated into its own FP32
+# plane and summed in order.  Every layout and kernel family: K-major x
+# K-major (256-tile and decode-size M), the NN/TN kernels, ragged M and N,
+# a last slice that is not a multiple of 128 (the general kernel), 2D blocks.
+LONG_K = [("NT", 144, 80, 33280, False, True), ("NT", 5, 64, 33280, False, False),
+          ("NN", 144, 96, 33280, False, True), ("TN", 96, 144, 33280, False, False),
+          ("NT", 256, 256, 49152, True, True), ("NT", 40, 48, 32784, False, False),
+          ("TN", 32, 48, 32784, True, False)]
+
+
+@pytest.mark.parametrize("layout,M,N,K,a2d,b2d", LONG_K)
+def test_long_k_slices(nv, layout, M, N, K, a2d, b2d):
+    rng = np.random.default_rng(M + N + K + 7 * a2d + b2d)
+    a_shape = (M, K) if layout != "TN" else (K, M)
+    b_shape = (N, K) if layout == "NT" else (K, N)
+    a_axis = 1 if layout != "TN" else 0
+    b_axis = 1 if layout == "NT" else 0
+    assert nv.nvfp4_gemm_workspace_size(nv.LAYOUT[layout], M, N, K) > 0
+    a_or, a_g = random_operand(nv, rng, *a_shape, a2d, a_axis, 0.5, scale_lo=0x20)
+    b_or, b_g = random_operand(nv, rng, *b_shape, b2d, b_axis, 0.25, scale_lo=0x20)
+    print("long K", layout, M, N, K, flush=True)
+    run_and_check(nv, layout, M, N, K, a_or, a_g, b_or, b_g)
+
+
+def tile_order(bid, nbm, nbn):
+    """The 256 x 256 output tile the K-major GEMM kernel gives workgroup `bid`
+    (its XCD-banded order: ids regrouped so each of the 8 XCDs owns a
+    contiguous band, bands walked in groups of 8 tile rows)."""
+    total = nbm * nbn
+    per = total // 8
+    i = (bid % 8) * per + bid // 8 if bid < per * 8 else bid
+    group = i // (8 * nbn)
+    first = group * 8
+    gsize = min(nbm - first, 8)
+    inn = i - group * 8 * nbn
+    return first + inn % gsize, inn // gsize
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_last_round_k_split(nv, out_dtype):
+    """A grid whose last round of 256 x 256 tiles would fill only 1/16 of the
+    compute units: with a workspace those tiles run as two K halves each.
+    Every output of the split tiles (and random others) against the oracle;
+    the whole result against the same GEMM without the split (FP32 sums of two
+    halves vs one chain: within the GEMM tolerance of each other)."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    nbn = 16
+    nbm = (ncu + ncu // 16 + nbn - 1) // nbn
+    M, N, K = 256 * nbm, 256 * nbn, 4096
+    t = nbm * nbn
+    tail = t % ncu
+    assert 0 < tail <= ncu // 2
+    assert nv.nvfp4_gemm_workspace_size(0, M, N, K) == 2 * M * N * 4
+    rng = np.random.default_rng(5)
+    a_or, a_g = random_operand(nv, rng, M, K, False, 1, 0.5, scale_lo=0x20)
+    b_or, b_g = random_operand(nv, rng, N, K, True, 1, 0.25, scale_lo=0x20)
+    print("last-round split", M, N, K, "tail", tail, flush=True)
+    y = nv.gemm("NT", a_g, b_g, out_dtype=out_dtype)
+    y_whole = torch.empty_like(y)
+    st = nv.nvfp4_gemm(0, M, N, K, a_g.codes, a_g.scales, a_g.tensor_scale, 0, b_g.codes,
+                       b_g.scales, b_g.tensor_scale, 1, nv._dtype_code(y_whole), y_whole, N)
+    assert st == 0
+    torch.cuda.synchronize()
+    ms, ns = [], []
+    for bid in range(t - tail, t):
+        tm, tn = tile_order(bid, nbm, nbn)
+        r = rng.integers(0, 256, 48)
+        c = rng.integers(0, 256, 48)
+        ms.append(256 * tm + r)
+        ns.append(256 * tn + c)
+        ms.append(np.array([256 * tm, 256 * tm + 255]))
+        ns.append(np.array([256 * tn + 255, 256 * tn]))
+    ms.append(rng.integers(0, M, 2048))
+    ns.append(rng.integers(0, N, 2048))
+    ms, ns = np.concatenate(ms).astype(np.int64), np.concatenate(ns).astype(np.int64)
+    ref, ab = oracle.gemm_pairs("NT", M, N, K, a_or, b_or, ms, ns)
+    mt, nt = torch.from_numpy(ms).cuda(), torch.from_numpy(ns).cuda()
+    got = y[mt, nt].float().cpu().numpy()
+    if out_dtype == torch.float32:
+        check_gemm(got, None, ref, ab, "last-round split")
+    else:
+        check_gemm(None, got, ref, ab, "last-round split")
+    # against the unsplit result everywhere: both within 1e-5 S of the exact
+    # value, so within 2e-5 S of each other (S = s_A s_B sum |a b|, from the
+    # dequantized magnitudes), plus a BF16 step for the BF16 output
+    S = torch.matmul(nv.dequantize(a_g, torch.float32).abs(),
+                     nv.dequantize(b_g, torch.float32).abs().t().contiguous())
+    d = (y.float() - y_whole.float()).abs()
+    bound = 2e-5 * S
+    if out_dtype == torch.bfloat16:
+        bound = bound + y_whole.float().abs() * 2.0 ** -7
+    assert bool((d <= bound).all())
