@@ -138,6 +138,44 @@ __device__ __forceinline__ void quotients(const float* x, const BlockDiv& b, flo
         y[i] = __uint_as_float(__float_as_uint(y[i]) | (__float_as_uint(x[i]) & 0x80000000u));
 }
 
+// True when y (FP32 bits u, either sign) lies within 8 units in the last
+// place of a number whose significand has at most 3 bits (the low 21 bits of
+// its mantissa field are 0).  Every E2M1 rounding boundary (0.25, 0.75, 1.25,
+// 1.75, 2.5, 3.5, 5) is such a number; so are the E2M1 values themselves and
+// a few others, which only costs an unneeded exact quotient.  Three
+// operations: a test of the boundaries alone measured slower overall.
+__device__ __forceinline__ bool near_e2m1_boundary(uint32_t u)
+{
+    return ((u + 8u) & 0x1FFFFFu) < 16u;
+}
+
+// Quotients for round-to-nearest E2M1 encoding: y[i] rounds to the same E2M1
+// code (RNE, saturating, sign kept) as RN(x[i] / d).  Worth it only where
+// quotients rarely sit on a boundary: on BF16 inputs without the Hadamard
+// transform, x / d is exactly 0.75, 1.75 or 3.5 for about 0.1-0.2 % of the
+// elements (x with amax's significand, scales 1.5 or 1.75 times a power of
+// two: 2688 = 21 * 2^7), which sends a quarter to two thirds of the waves
+// through the exact quotient as well, so those paths keep the exact one.  y0 = RN(x r) with
+// r = RN(1/d) is within 2.5 ulp of RN(x/d) (two roundings of relative size
+// 2^-24 each), so the two encode alike unless an E2M1 rounding boundary lies
+// between them or on one of them, i.e. unless y0 is within a few ulps of a
+// boundary; those lanes (and blocks whose d is outside Markstein's range)
+// take the exact quotient.  Values that underflow in x r are far below 0.25
+// and encode as (signed) zero either way.
+// The check is wave-wide (any lane near a boundary sends the whole wave
+// through the exact quotient), so the common path has no divergent branch.
+template <int n>
+__device__ __forceinline__ void quotients_rne(const float* x, const BlockDiv& b, float* y)
+{
+    bool exact = !b.fast;
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+        y[i] = x[i] * b.r;
+        exact |= near_e2m1_boundary(__float_as_uint(y[i]));
+    }
+    if (__builtin_amdgcn_ballot_w64(exact) != 0) quotients<n>(x, b, y);
+}
+
 // Single quotient (block-scale computation).
 __device__ __forceinline__ float quotient(float x, const BlockDiv& b)
 {

@@ -132,8 +132,9 @@ __device__ __forceinline__ void sr_values_mag(float* y, const float* x, const ui
     }
 }
 
-// Quantize 8 values sharing one block scale.
-template <bool kSR>
+// Quantize 8 values sharing one block scale (kRHT: Hadamard-transformed
+// values, for which round-to-nearest takes the reciprocal fast path).
+template <bool kSR, bool kRHT = false>
 __device__ __forceinline__ uint32_t encode8(const float v[8], const BlockDiv& bd, bool zero,
                                             const uint32_t r[8])
 {
@@ -142,6 +143,8 @@ __device__ __forceinline__ uint32_t encode8(const float v[8], const BlockDiv& bd
     if (kSR) {
         quotient_mags<8>(v, bd, y);
         sr_values_mag<8>(y, v, r);
+    } else if (kRHT) {
+        quotients_rne<8>(v, bd, y);
     } else {
         quotients<8>(v, bd, y);
     }
@@ -218,8 +221,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantParams p)
             }
         }
         u32x2 out;
-        out[0] = encode8<kSR>(v, bd, zero, r);
-        out[1] = encode8<kSR>(v + 8, bd, zero, r + 8);
+        out[0] = encode8<kSR, kRHT>(v, bd, zero, r);
+        out[1] = encode8<kSR, kRHT>(v + 8, bd, zero, r + 8);
         *reinterpret_cast<u32x2*>(p.codes + (int64_t)b * 8) = out;
         p.scales[b] = (uint8_t)e;
     }
@@ -296,7 +299,8 @@ __global__ __launch_bounds__(256) void k_quant_cols(QuantParams p)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) y[j][i] = 0.0f;
             } else {
-                quotients<16>(v[j], bd, y[j]);
+                if (!kSR && kRHT) quotients_rne<16>(v[j], bd, y[j]);
+                else quotients<16>(v[j], bd, y[j]);
             }
         }
         *reinterpret_cast<uint32_t*>(p.scales + rb * p.cols + c0) = sc;
@@ -520,7 +524,8 @@ void k_quant_t(QuantParams p)
                     for (int i = 0; i < 16; ++i) v[j][i] = 0.0f;
                 } else {
                     float y[16];
-                    quotients<16>(v[j], bd, y);
+                    if (!kSR && kRHT) quotients_rne<16>(v[j], bd, y);
+                    else quotients<16>(v[j], bd, y);
 #pragma unroll
                     for (int i = 0; i < 16; ++i) v[j][i] = y[i];
                 }

@@ -199,3 +199,94 @@ def test_debug_mode_reports_nonfinite_amax(nv, monkeypatch):
     torch.cuda.synchronize()
     assert st == 8, nv.status_string(st)
     assert torch.all(codes == 0x5A) and torch.all(scales == 0x5A)
+
+
+def h16():
+    i = np.arange(16)
+    return np.where(np.bitwise_count((i[:, None] & i[None, :]).astype(np.uint64)) % 2 == 1,
+                    -1.0, 1.0)
+
+
+def inverse_rht16(y, mask, axis):
+    """x with RHT16(x) = y up to FP32 rounding: x = D (1/4 H y) per group of 16
+    along `axis` (H symmetric, H H = 16 I, D = D^-1)."""
+    d = np.array([-1.0 if (mask >> i) & 1 else 1.0 for i in range(16)])
+    H = h16()
+    y = np.asarray(y, dtype=np.float64)
+    if axis == 1:
+        g = y.reshape(y.shape[0], -1, 16)
+        x = np.einsum("ij,rgj->rgi", H, g) * 0.25 * d
+        return x.reshape(y.shape).astype(np.float32)
+    g = y.reshape(-1, 16, y.shape[1])
+    x = np.einsum("ij,gjc->gic", H, g) * 0.25 * d[None, :, None]
+    return x.reshape(y.shape).astype(np.float32)
+
+
+@pytest.mark.parametrize("s_g", [1.0, 1.37, 2.0 ** -20 * 1.9])
+@pytest.mark.parametrize("mode", list(MODES) + ["rows_rht", "cols_rht", "cols_rht_t"])
+def test_quotients_around_every_e2m1_boundary(nv, s_g, mode):
+    """Elements whose quotient x/d lands on and within 6 FP32 ulps of every
+    E2M1 rounding boundary (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5), both signs,
+    under every positive normal E4M3 block scale: the round-to-nearest path
+    (which multiplies by the block's reciprocal and takes the exact quotient
+    only near a boundary) must encode exactly as the oracle's correctly
+    rounded quotient.  FP32 input; the tensor amax sits in the first block.
+    The *_rht modes feed the inverse transform of these values, so the
+    Hadamard-transformed quotients land on or next to the boundaries (exactly
+    where the inverse is exact in FP32); cols_rht_t writes transposed
+    storage."""
+    f32 = np.float32
+    amax = f32(2688.0) * f32(s_g)
+    sg = f32(amax / f32(2688.0))
+    d6 = f32(f32(6.0) * sg)
+    probes = []
+    for m in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0):
+        for j in range(-6, 7):
+            probes.append((m, j))
+    blocks = []
+    for code in range(0x08, 0x7F):              # normal E4M3 scales 2^-6 .. 448
+        e = f32(oracle.e4m3_value(code))
+        aB = f32(e * d6)                         # block amax giving this scale
+        d = f32(e * sg)
+        vals = []
+        for sign in (1.0, -1.0):
+            for m, j in probes:
+                x = np.nextafter(f32(f32(m) * d), f32(np.inf) if j > 0 else f32(-np.inf),
+                                 dtype=np.float32) if j else f32(f32(m) * d)
+                for _ in range(abs(j) - 1):
+                    x = np.nextafter(x, f32(np.inf) if j > 0 else f32(-np.inf), dtype=np.float32)
+                vals.append(f32(sign) * x)
+        for k in range(0, len(vals), 15):
+            blk = [aB] + vals[k:k + 15]
+            blk += [f32(0.0)] * (16 - len(blk))
+            blocks.append(blk)
+    nb = len(blocks)
+    cols = 256
+    rows = (nb * 16 + cols - 1) // cols
+    rows = (rows + 15) // 16 * 16
+    flat = np.zeros(rows * cols, dtype=np.float32)
+    flat[0] = amax
+    flat[16:16 + nb * 16] = np.asarray(blocks, dtype=np.float32).ravel()
+    x = torch.from_numpy(flat.reshape(rows, cols))
+    if mode.startswith("cols"):     # the same blocks down the columns
+        x = x.reshape(rows // 16, 16, cols // 16, 16).permute(0, 3, 2, 1).reshape(rows, cols)
+        x = x.contiguous()
+    if not mode.endswith(("rht", "rht_t")):
+        compare(nv, x, mode)
+        return
+    mask = 0x5A3C
+    axis = 1 if mode == "rows_rht" else 0
+    x = torch.from_numpy(inverse_rht16(x.numpy(), mask, axis))
+    if mode == "cols_rht_t":
+        q = nv.quantize(x.cuda(), axis=0, rht=True, mask=mask, transpose=True)
+        torch.cuda.synchronize()
+        oc, osc, ots, _ = oracle.quantize(to_oracle_input(x), axis=0, rht=True, mask=mask)
+        assert q.tensor_scale.item() == ots
+        qc = q.codes.cpu().numpy()
+        tq = np.empty((qc.shape[0], qc.shape[1] * 2), dtype=np.uint8)
+        tq[:, 0::2], tq[:, 1::2] = qc & 0xF, qc >> 4
+        oq = np.empty((oc.shape[0], oc.shape[1] * 2), dtype=np.uint8)
+        oq[:, 0::2], oq[:, 1::2] = oc & 0xF, oc >> 4
+        assert np.array_equal(tq, oq.T) and np.array_equal(q.scales.cpu().numpy(), osc.T)
+        return
+    compare(nv, x, "rows" if axis == 1 else "cols", rht=True, mask=mask)
