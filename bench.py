@@ -25,8 +25,11 @@ of the column RHT) from one read (nvfp4_amax).
 
 Inputs are resident in HBM before timing starts.  The JSON line reports the
 step's NVFP4 GEMM throughput (GEMM FLOPs / step time), per-kernel HIP-event
-timings, the roofline of the dominant GEMM kernel and the CPU oracle's
-throughput on a bounded sample of the same work.
+timings (inside the step and alone), the roofline of the dominant GEMM kernel
+and the CPU oracle's throughput on bounded samples of the same work.  Beside
+it (unless --step-only): the decode GEMMs, the MXFP4 comparison, the KV cache,
+dequantize/RHT16, and the same step at one GPU's token share of a
+Llama-3.1-405B MLP (8192 tokens, hidden 16384, intermediate 53248).
 """
 from __future__ import annotations
 
@@ -64,6 +67,9 @@ def parse():
                     help="one untimed step, then only the isolated replay of its quantize, "
                          "amax, transpose and SwiGLU calls (for per-kernel counters); prints "
                          "the calls in replay order with their times")
+    ap.add_argument("--c5-only", action="store_true",
+                    help="print only the Llama-3.1-405B token-share step object (for "
+                         "profiling its kernels)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode-shape GEMMs and print their JSON object "
                          "(for profiling the skinny kernel; not the bench line)")
@@ -132,7 +138,6 @@ def main():
         sys.exit(2)
 
     import torch
-    import torch.nn.functional as F
 
     import nvfp4_bit_microscaled_amd as nv
     import workloads
@@ -151,121 +156,12 @@ def main():
         W_gu = workloads.weights(2 * cfg["ffn"], cfg["hidden"], cfg["wgu_seed"], device="cuda")
         print(json.dumps({"mxfp4": mxfp4_bench(torch, nv, X, W_gu)}), flush=True)
         return
-    cfg = workloads.LLAMA8B
-    T, D, Fh = cfg["tokens"], cfg["hidden"], cfg["ffn"]
-    mask = workloads.sign_mask(cfg["mask_seed"])
-    sr_seed = cfg["sr_seed"]
+    if args.c5_only:
+        print(json.dumps({"llama405b_share": c5_bench(torch, nv, workloads, dev)}), flush=True)
+        return
 
     print("generating inputs on the GPU", file=sys.stderr, flush=True)
-    X = workloads.activations(T, D, cfg["x_seed"], device="cuda")
-    W_gu = workloads.weights(2 * Fh, D, cfg["wgu_seed"], device="cuda")
-    W_down = workloads.weights(D, Fh, cfg["wdown_seed"], device="cuda")
-    dY = workloads.gradients(T, D, cfg["dy_seed"], device="cuda")
-    dH = workloads.gradients(T, 2 * Fh, cfg["dh_seed"], device="cuda")
-    torch.cuda.synchronize()
-
-    timer = Timer(torch)
-    gemm_flops = {}   # (name) -> flops per call
-    qbytes = {}       # (name) -> algorithmic HBM bytes per call
-    swbytes = {}      # the fused SwiGLU + amax pass
-
-    def qb(rows, cols, in_bytes=2, amax_pass=True, block2d=False):
-        # read input (twice when the amax pass runs) + codes + scales (one
-        # byte per 16 elements in 1x16 blocks, per 256 in 16x16 blocks)
-        return rows * cols * (in_bytes * (2 if amax_pass else 1) + 0.5
-                              + (1 / 256 if block2d else 1 / 16))
-
-    def Q(name, x, **kw):
-        qbytes[name] = qb(*x.shape, amax_pass=kw.get("amax_in") is None,
-                          block2d=kw.get("block2d", False))
-        return timer.run("quantize", nv.quantize, x, name=name, **kw)
-
-    def TR(name, q):
-        # storage transpose of a 16x16-block operand: codes and scales read
-        # and written once
-        qbytes[name] = q.rows * q.cols * 2 * (0.5 + 1 / 256)
-        return timer.run("quantize", nv.transpose, q, name=name)
-
-    def AMX(name, x):
-        # max |x| and max |RHT16 down the columns of x| in one read
-        qbytes[name] = x.shape[0] * x.shape[1] * 2
-        return timer.run("quantize", nv.amax, x, rht_mask=mask, name=name)
-
-    def SWIGLU(name, h):
-        # act = silu(gate) * up with both amaxes of act: reads H, writes act
-        swbytes[name] = h.shape[0] * h.shape[1] * 2 + h.shape[0] * (h.shape[1] // 2) * 2
-        return timer.run("swiglu", nv.swiglu_amax, h, mask, name=name,
-                         out=buf("Act", (h.shape[0], h.shape[1] // 2)))
-
-    def G(name, role, a, b, M, N, K, out=None):
-        gemm_flops[name] = 2.0 * M * N * K
-        return timer.run("gemm_" + role, nv.gemm, "NT", a, b, out_dtype=torch.bfloat16,
-                         out=out)
-
-    bufs = {}
-
-    def buf(name, shape):
-        t = bufs.get(name)
-        if t is None:
-            t = bufs[name] = torch.empty(*shape, dtype=torch.bfloat16, device=dev)
-        return t
-
-    # A second stream (default priority) takes the HBM-bound quantizations of
-    # each phase while the main stream runs the VALU-bound ones; the streams
-    # meet before every GEMM, so GEMMs always run alone.  side waits for the
-    # main stream at each fork, so memory the caching allocator hands out
-    # again is never reused while the other stream may still read it.
-    side = torch.cuda.Stream(device=dev)
-
-    def fork():
-        e = torch.cuda.Event()
-        e.record(torch.cuda.current_stream())
-        side.wait_event(e)
-
-    def join():
-        e = torch.cuda.Event()
-        e.record(side)
-        torch.cuda.current_stream().wait_event(e)
-
-    def step():
-        # ---- fprop: weights on the side stream, X on the main one
-        fork()
-        with torch.cuda.stream(side):
-            wgu = Q("Wgu_2d", W_gu, block2d=True)
-            wdn = Q("Wdown_2d", W_down, block2d=True)
-        ax, axt = AMX("X_amax2", X)
-        xq = Q("X_rows", X, amax_in=ax)
-        join()
-        H = G("fprop_gu", "fprop", xq, wgu, T, 2 * Fh, D, out=buf("H", (T, 2 * Fh)))
-        act, aa, aat = SWIGLU("Act_swiglu_amax2", H)
-        aq = Q("Act_rows", act, amax_in=aa)
-        G("fprop_down", "fprop", aq, wdn, T, D, Fh, out=buf("Y", (T, D)))
-        # ---- backward, down projection: both dY quantizations (stochastic
-        # rounding, VALU-bound) beside W_down^T and Act^T (HBM-bound)
-        ady, adyt = AMX("dY_amax2", dY)
-        fork()
-        with torch.cuda.stream(side):
-            wdn_t = TR("Wdown_2d_T", wdn)
-            at = Q("Act_cols_rht_T", act, axis=0, rht=True, mask=mask, transpose=True, amax_in=aat)
-        dyq = Q("dY_rows_sr", dY, sr=True, seed=sr_seed, stream_id=0, amax_in=ady)
-        dyt = Q("dY_cols_rht_sr_T", dY, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,
-                stream_id=1, transpose=True, amax_in=adyt)
-        join()
-        G("dgrad_down", "dgrad", dyq, wdn_t, T, Fh, D, out=buf("dAct", (T, Fh)))
-        G("wgrad_down", "wgrad", dyt, at, D, Fh, T, out=buf("dWdown", (D, Fh)))
-        # ---- backward, gate/up projection: the same split
-        adh, adht = AMX("dH_amax2", dH)
-        fork()
-        with torch.cuda.stream(side):
-            wgu_t = TR("Wgu_2d_T", wgu)
-            xt = Q("X_cols_rht_T", X, axis=0, rht=True, mask=mask, transpose=True, amax_in=axt)
-        dhq = Q("dH_rows_sr", dH, sr=True, seed=sr_seed, stream_id=0, amax_in=adh)
-        dht = Q("dH_cols_rht_sr_T", dH, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,
-                stream_id=1, transpose=True, amax_in=adht)
-        join()
-        G("dgrad_gu", "dgrad", dhq, wgu_t, T, D, 2 * Fh, out=buf("dX", (T, D)))
-        G("wgrad_gu", "wgrad", dht, xt, 2 * Fh, D, T, out=buf("dWgu", (2 * Fh, D)))
-
+    ms = MlpStep(torch, nv, workloads, workloads.LLAMA8B, dev)
     if args.calibration_copy:
         # a plain elementwise copy of known size: reads 1 GiB, writes 1 GiB
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -275,142 +171,319 @@ def main():
         del src, dst
 
     if args.quant_only:
-        step()
+        ms.step()
         torch.cuda.synchronize()
-        timer.recorded = []
-        step()
-        torch.cuda.synchronize()
-        calls = timer.recorded
-        timer.recorded = None
+        calls = ms.record_calls()
         iso = isolated_times(torch, calls, dev, reps=3)
         print(json.dumps({"quant_only": {
             "replay": "each call once untimed, then a 1 GiB cache-evicting read, then 3 "
                       "times back to back (timed), in this order",
             "order": [name for _, name, _, _, _ in calls],
             "isolated_us": {k: round(v, 2) for k, v in iso.items()},
-            "bytes": {k: int(v) for k, v in qbytes.items()}}}), flush=True)
+            "bytes": {k: int(v) for k, v in ms.qbytes.items()}}}), flush=True)
         return
 
     print("warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region: K steps, bracketed by synchronizations
-    timer.enabled = True
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    totals = timer.totals()
-    print("timed %d steps: %.3f ms/step (host wall %.3f s)" % (args.steps, ms_step, wall),
+    r = run_step_bench(torch, ms, args.steps, args.warmup, dev, isolated=True)
+    print("timed %d steps: %.3f ms/step (host wall %.3f s)" % (args.steps, r["ms_per_step"],
+                                                             r["host_wall_s"]),
           file=sys.stderr, flush=True)
-
-    # every quantize, amax, transpose and SwiGLU call of one more step, replayed
-    # one at a time on one stream (nothing beside it), each after a cache-evicting
-    # write: the per-kernel times the two-stream step cannot give
-    timer.enabled = False
-    timer.recorded = []
-    step()
-    torch.cuda.synchronize()
-    iso = isolated_times(torch, timer.recorded, dev)
-    timer.recorded = None
-
-    flops_step = sum(gemm_flops.values())
-    value = flops_step / (ms_step * 1e-3) / 1e12
-    per_kind = {k: {"ms_per_step": t / args.steps, "calls_per_step": n / args.steps}
-                for k, (t, n) in totals.items()}
-    # the six GEMMs by role (all the NT kernel): flops and average launch time
-    role_flops = {"fprop": gemm_flops["fprop_gu"] + gemm_flops["fprop_down"],
-                  "dgrad": gemm_flops["dgrad_down"] + gemm_flops["dgrad_gu"],
-                  "wgrad": gemm_flops["wgrad_down"] + gemm_flops["wgrad_gu"]}
-    gemm_roles = {}
-    for role, fl in role_flops.items():
-        t, n = totals["gemm_" + role]
-        gemm_roles[role] = {"tflops": fl * args.steps / (t * 1e-3) / 1e12,
-                            "avg_launch_ms": t / n, "launches": n}
-    # each quantize / amax call: time, algorithmic GB/s, and what bounds it
-    # (the stochastic-rounding calls are bound by VALU work: Philox and the
-    # exact SR selection; the others stream HBM)
-    q_calls = {}
-    counters = quantize_counters()
-    for name, (t, n) in timer.totals(by_name=True).items():
-        if name not in qbytes:
-            continue
-        it = iso[name]
-        q_calls[name] = {"us_in_step": round(t / n * 1e3, 1),
-                         "isolated_us": round(it, 1),
-                         "isolated_GBps": round(qbytes[name] / (it * 1e-6) / 1e9, 1),
-                         "isolated_frac_of_hbm": round(qbytes[name] / (it * 1e-6) / 1e9
-                                                       / HBM_PEAK_GBPS, 4),
-                         "bytes": int(qbytes[name])}
-        if counters is not None and name in counters:
-            q_calls[name]["bound"] = counters[name]["bound"]
-            q_calls[name]["counters"] = counters[name]
-    q_bytes = sum(qbytes.values()) * args.steps
-    q_iso = sum(iso[k] for k in qbytes)
-    gemm_t = sum(totals["gemm_" + k][0] for k in role_flops)
-    # the quantize phases' wall time: the step outside the GEMMs and the
-    # SwiGLU pass, which run alone on the main stream (the per-call times
-    # overlap across the two streams, so their sum is not a duration)
-    q_wall = ms_step * args.steps - gemm_t - totals["swiglu"][0]
-    gemm_n = sum(totals["gemm_" + k][1] for k in role_flops)
-    achieved = flops_step * args.steps / (gemm_t * 1e-3) / 1e12
+    cfg = workloads.LLAMA8B
     line = {
         "metric": "NVFP4 GEMM TFLOPS (8B MLP shapes) + quantize GB/s, % of MI355X roofline",
-        "value": round(value, 2),
+        "value": round(r["tflops_step"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "nvfp4 operands, f16 mfma, f32 accumulate",
         "data": "synthetic (seeded activations/weights/Student-t gradients, HBM-resident)",
-        "config": {"workload": "llama3-8b-mlp-fwd+bwd-step", "tokens": T, "hidden": D,
-                   "ffn": Fh, "gemm_tflop_per_step": round(flops_step / 1e12, 4),
+        "config": {"workload": "llama3-8b-mlp-fwd+bwd-step", "tokens": cfg["tokens"],
+                   "hidden": cfg["hidden"], "ffn": cfg["ffn"],
+                   "gemm_tflop_per_step": round(r["flops_step"] / 1e12, 4),
                    "parallelism": "none (1 GPU)"},
-        "gemm_only_tflops": round(achieved, 2),
-        "gemm_by_role": {k: {kk: round(vv, 4) for kk, vv in v.items()}
-                         for k, v in gemm_roles.items()},
-        "quantize_GBps": round(q_bytes / (q_wall * 1e-3) / 1e9, 1),
-        "quantize_frac_of_hbm": round(q_bytes / (q_wall * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "quantize_wall_ms_per_step": round(q_wall / args.steps, 4),
-        "quantize_isolated_GBps": round(sum(qbytes.values()) / (q_iso * 1e-6) / 1e9, 1),
-        "quantize_isolated_frac_of_hbm": round(sum(qbytes.values()) / (q_iso * 1e-6) / 1e9
-                                               / HBM_PEAK_GBPS, 4),
-        "quantize_isolated_ms_per_step": round(q_iso / 1e3, 4),
-        "quantize_by_call": q_calls,
-        "swiglu_isolated_us": round(iso["Act_swiglu_amax2"], 1),
-        "swiglu_GBps": round(sum(swbytes.values()) * args.steps / (totals["swiglu"][0] * 1e-3) / 1e9, 1),
-        "time_breakdown_ms_per_step": {("quantize_calls_sum" if k == "quantize" else k):
-                                       round(v["ms_per_step"], 4) for k, v in per_kind.items()},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm_kk (K-major x K-major, all six MLP GEMMs)",
-                     "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                     "avg_launch_ms": round(gemm_t / gemm_n, 4),
-                     "traffic": gemm_traffic()},
     }
-    del bufs
+    line.update(r["report"])
+    line["roofline"] = {"bound": "mfma",
+                        "kernel": "k_gemm_kk (K-major x K-major, all six MLP GEMMs)",
+                        "achieved": round(r["gemm_tflops"], 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s",
+                        "frac": round(r["gemm_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                        "avg_launch_ms": round(r["gemm_avg_launch_ms"], 4),
+                        "traffic": gemm_traffic()}
+    X, W_gu, mask = ms.X, ms.W_gu, ms.mask
+    ms.free_buffers()
     torch.cuda.empty_cache()
     if not args.step_only:
         line["decode"] = decode_bench(torch, nv, workloads)
         line["mxfp4"] = mxfp4_bench(torch, nv, X, W_gu)
         line["kv_cache"] = kv_bench(torch, nv, workloads)
         line["dequantize_rht16"] = dequant_rht_bench(torch, nv, X, mask)
+        del ms
+        torch.cuda.empty_cache()
+        line["llama405b_share"] = c5_bench(torch, nv, workloads, dev)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, torch, nv, workloads, X, W_gu)
     print(json.dumps(line), flush=True)
+
+
+class MlpStep:
+    """One NVFP4 MLP training step (fprop, dgrad, wgrad of both projections)
+    over seeded synthetic inputs resident in HBM, with every library call
+    named and timed through a Timer.  cfg: tokens, hidden, ffn and seeds
+    (workloads.LLAMA8B or workloads.LLAMA405B)."""
+
+    def __init__(self, torch, nv, workloads, cfg, dev):
+        self.torch, self.nv, self.cfg, self.dev = torch, nv, cfg, dev
+        T, D, Fh = cfg["tokens"], cfg["hidden"], cfg["ffn"]
+        self.T, self.D, self.Fh = T, D, Fh
+        self.mask = workloads.sign_mask(cfg["mask_seed"])
+        self.sr_seed = cfg["sr_seed"]
+        self.X = workloads.activations(T, D, cfg["x_seed"], device="cuda")
+        self.W_gu = workloads.weights(2 * Fh, D, cfg["wgu_seed"], device="cuda")
+        self.W_down = workloads.weights(D, Fh, cfg["wdown_seed"], device="cuda")
+        self.dY = workloads.gradients(T, D, cfg["dy_seed"], device="cuda")
+        self.dH = workloads.gradients(T, 2 * Fh, cfg["dh_seed"], device="cuda")
+        torch.cuda.synchronize()
+        self.timer = Timer(torch)
+        self.gemm_flops = {}   # name -> flops per call
+        self.qbytes = {}       # name -> algorithmic HBM bytes per call
+        self.swbytes = {}      # the fused SwiGLU + amax pass
+        self.bufs = {}
+        # A second stream (default priority) takes the HBM-bound quantizations
+        # of each phase while the main stream runs the VALU-bound ones; the
+        # streams meet before every GEMM, so GEMMs always run alone.  side
+        # waits for the main stream at each fork, so memory the caching
+        # allocator hands out again is never reused while the other stream
+        # may still read it.
+        self.side = torch.cuda.Stream(device=dev)
+
+    # ---- named library calls (bytes / flops recorded per call)
+    @staticmethod
+    def qb(rows, cols, in_bytes=2, amax_pass=True, block2d=False):
+        # read input (twice when the amax pass runs) + codes + scales (one
+        # byte per 16 elements in 1x16 blocks, per 256 in 16x16 blocks)
+        return rows * cols * (in_bytes * (2 if amax_pass else 1) + 0.5
+                              + (1 / 256 if block2d else 1 / 16))
+
+    def Q(self, name, x, **kw):
+        self.qbytes[name] = self.qb(*x.shape, amax_pass=kw.get("amax_in") is None,
+                                    block2d=kw.get("block2d", False))
+        return self.timer.run("quantize", self.nv.quantize, x, name=name, **kw)
+
+    def TR(self, name, q):
+        # storage transpose of a 16x16-block operand: codes and scales read
+        # and written once
+        self.qbytes[name] = q.rows * q.cols * 2 * (0.5 + 1 / 256)
+        return self.timer.run("quantize", self.nv.transpose, q, name=name)
+
+    def AMX(self, name, x):
+        # max |x| and max |RHT16 down the columns of x| in one read
+        self.qbytes[name] = x.shape[0] * x.shape[1] * 2
+        return self.timer.run("quantize", self.nv.amax, x, rht_mask=self.mask, name=name)
+
+    def SWIGLU(self, name, h):
+        # act = silu(gate) * up with both amaxes of act: reads H, writes act
+        self.swbytes[name] = h.shape[0] * h.shape[1] * 2 + h.shape[0] * (h.shape[1] // 2) * 2
+        return self.timer.run("swiglu", self.nv.swiglu_amax, h, self.mask, name=name,
+                              out=self.buf("Act", (h.shape[0], h.shape[1] // 2)))
+
+    def G(self, name, role, a, b, M, N, K, out=None):
+        self.gemm_flops[name] = 2.0 * M * N * K
+        return self.timer.run("gemm_" + role, self.nv.gemm, "NT", a, b,
+                              out_dtype=self.torch.bfloat16, out=out)
+
+    def buf(self, name, shape):
+        t = self.bufs.get(name)
+        if t is None:
+            t = self.bufs[name] = self.torch.empty(*shape, dtype=self.torch.bfloat16,
+                                                   device=self.dev)
+        return t
+
+    def free_buffers(self):
+        self.bufs = {}
+
+    def fork(self):
+        e = self.torch.cuda.Event()
+        e.record(self.torch.cuda.current_stream())
+        self.side.wait_event(e)
+
+    def join(self):
+        e = self.torch.cuda.Event()
+        e.record(self.side)
+        self.torch.cuda.current_stream().wait_event(e)
+
+    def step(self):
+        torch, T, D, Fh, mask, sr_seed = self.torch, self.T, self.D, self.Fh, self.mask, self.sr_seed
+        Q, TR, AMX, G, buf = self.Q, self.TR, self.AMX, self.G, self.buf
+        X, W_gu, W_down, dY, dH = self.X, self.W_gu, self.W_down, self.dY, self.dH
+        # ---- fprop: weights on the side stream, X on the main one
+        self.fork()
+        with torch.cuda.stream(self.side):
+            wgu = Q("Wgu_2d", W_gu, block2d=True)
+            wdn = Q("Wdown_2d", W_down, block2d=True)
+        ax, axt = AMX("X_amax2", X)
+        xq = Q("X_rows", X, amax_in=ax)
+        self.join()
+        H = G("fprop_gu", "fprop", xq, wgu, T, 2 * Fh, D, out=buf("H", (T, 2 * Fh)))
+        act, aa, aat = self.SWIGLU("Act_swiglu_amax2", H)
+        aq = Q("Act_rows", act, amax_in=aa)
+        G("fprop_down", "fprop", aq, wdn, T, D, Fh, out=buf("Y", (T, D)))
+        # ---- backward, down projection: both dY quantizations (stochastic
+        # rounding, VALU-bound) beside W_down^T and Act^T
+        ady, adyt = AMX("dY_amax2", dY)
+        self.fork()
+        with torch.cuda.stream(self.side):
+            wdn_t = TR("Wdown_2d_T", wdn)
+            at = Q("Act_cols_rht_T", act, axis=0, rht=True, mask=mask, transpose=True,
+                   amax_in=aat)
+        dyq = Q("dY_rows_sr", dY, sr=True, seed=sr_seed, stream_id=0, amax_in=ady)
+        dyt = Q("dY_cols_rht_sr_T", dY, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,
+                stream_id=1, transpose=True, amax_in=adyt)
+        self.join()
+        G("dgrad_down", "dgrad", dyq, wdn_t, T, Fh, D, out=buf("dAct", (T, Fh)))
+        G("wgrad_down", "wgrad", dyt, at, D, Fh, T, out=buf("dWdown", (D, Fh)))
+        # ---- backward, gate/up projection: the same split
+        adh, adht = AMX("dH_amax2", dH)
+        self.fork()
+        with torch.cuda.stream(self.side):
+            wgu_t = TR("Wgu_2d_T", wgu)
+            xt = Q("X_cols_rht_T", X, axis=0, rht=True, mask=mask, transpose=True, amax_in=axt)
+        dhq = Q("dH_rows_sr", dH, sr=True, seed=sr_seed, stream_id=0, amax_in=adh)
+        dht = Q("dH_cols_rht_sr_T", dH, axis=0, rht=True, mask=mask, sr=True, seed=sr_seed,
+                stream_id=1, transpose=True, amax_in=adht)
+        self.join()
+        G("dgrad_gu", "dgrad", dhq, wgu_t, T, D, 2 * Fh, out=buf("dX", (T, D)))
+        G("wgrad_gu", "wgrad", dht, xt, 2 * Fh, D, T, out=buf("dWgu", (2 * Fh, D)))
+
+    def record_calls(self):
+        """Run one step untimed and return its named non-GEMM calls."""
+        self.timer.enabled = False
+        self.timer.recorded = []
+        self.step()
+        self.torch.cuda.synchronize()
+        calls = self.timer.recorded
+        self.timer.recorded = None
+        return calls
+
+
+def run_step_bench(torch, ms, steps, warmup, dev, isolated=True):
+    """Warm up, time `steps` steps between two synchronizations, then (when
+    `isolated`) replay every quantize, amax, transpose and SwiGLU call of one
+    more step alone: the per-kernel times the two-stream step cannot give."""
+    for _ in range(warmup):
+        ms.step()
+    torch.cuda.synchronize()
+    timer = ms.timer
+    timer.pending = []
+    timer.enabled = True
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        ms.step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / steps
+    timer.enabled = False
+    totals = timer.totals()
+    by_name = timer.totals(by_name=True)
+    iso = isolated_times(torch, ms.record_calls(), dev) if isolated else None
+
+    gemm_flops, qbytes, swbytes = ms.gemm_flops, ms.qbytes, ms.swbytes
+    flops_step = sum(gemm_flops.values())
+    role_flops = {"fprop": gemm_flops["fprop_gu"] + gemm_flops["fprop_down"],
+                  "dgrad": gemm_flops["dgrad_down"] + gemm_flops["dgrad_gu"],
+                  "wgrad": gemm_flops["wgrad_down"] + gemm_flops["wgrad_gu"]}
+    gemm_roles = {}
+    for role, fl in role_flops.items():
+        t, n = totals["gemm_" + role]
+        gemm_roles[role] = {"tflops": round(fl * steps / (t * 1e-3) / 1e12, 2),
+                            "avg_launch_ms": round(t / n, 4), "launches": n}
+    # each quantize / amax / transpose call: its time inside the step, its
+    # time alone, its algorithmic bytes and (from the committed counter
+    # summary, while it matches the source) what bounds it
+    q_calls = {}
+    counters = quantize_counters()
+    for name, (t, n) in by_name.items():
+        if name not in qbytes:
+            continue
+        c = {"us_in_step": round(t / n * 1e3, 1), "bytes": int(qbytes[name])}
+        if iso is not None:
+            it = iso[name]
+            c.update({"isolated_us": round(it, 1),
+                      "isolated_GBps": round(qbytes[name] / (it * 1e-6) / 1e9, 1),
+                      "isolated_frac_of_hbm": round(qbytes[name] / (it * 1e-6) / 1e9
+                                                    / HBM_PEAK_GBPS, 4)})
+        if counters is not None and name in counters:
+            c["bound"] = counters[name]["bound"]
+            c["counters"] = counters[name]
+        q_calls[name] = c
+    q_bytes = sum(qbytes.values()) * steps
+    gemm_t = sum(totals["gemm_" + k][0] for k in role_flops)
+    gemm_n = sum(totals["gemm_" + k][1] for k in role_flops)
+    # the quantize phases' wall time: the step outside the GEMMs and the
+    # SwiGLU pass, which run alone on the main stream (the per-call times
+    # overlap across the two streams, so their sum is not a duration)
+    q_wall = ms_step * steps - gemm_t - totals["swiglu"][0]
+    achieved = flops_step * steps / (gemm_t * 1e-3) / 1e12
+    report = {
+        "gemm_only_tflops": round(achieved, 2),
+        "gemm_by_role": gemm_roles,
+        "quantize_GBps": round(q_bytes / (q_wall * 1e-3) / 1e9, 1),
+        "quantize_frac_of_hbm": round(q_bytes / (q_wall * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "quantize_wall_ms_per_step": round(q_wall / steps, 4),
+    }
+    if iso is not None:
+        q_iso = sum(iso[k] for k in qbytes)
+        report.update({
+            "quantize_isolated_GBps": round(sum(qbytes.values()) / (q_iso * 1e-6) / 1e9, 1),
+            "quantize_isolated_frac_of_hbm": round(sum(qbytes.values()) / (q_iso * 1e-6) / 1e9
+                                                   / HBM_PEAK_GBPS, 4),
+            "quantize_isolated_ms_per_step": round(q_iso / 1e3, 4),
+            "swiglu_isolated_us": round(iso["Act_swiglu_amax2"], 1)})
+    report.update({
+        "quantize_by_call": q_calls,
+        "swiglu_GBps": round(sum(swbytes.values()) * steps / (totals["swiglu"][0] * 1e-3)
+                             / 1e9, 1),
+        "time_breakdown_ms_per_step": {("quantize_calls_sum" if k == "quantize" else k):
+                                       round(t / steps, 4) for k, (t, n) in totals.items()},
+    })
+    return {"ms_per_step": ms_step, "host_wall_s": wall, "flops_step": flops_step,
+            "tflops_step": flops_step / (ms_step * 1e-3) / 1e12, "gemm_tflops": achieved,
+            "gemm_avg_launch_ms": gemm_t / gemm_n, "report": report}
+
+
+def c5_bench(torch, nv, workloads, dev, steps=3, warmup=1):
+    """The same fwd+bwd step at one GPU's token share of a Llama-3.1-405B MLP
+    (8192 tokens, hidden 16384, intermediate 53248): the benchmark paragraph
+    of the readjensen.com NVFP4 training-recipe page, where the pages report
+    the largest gain.  Two of its GEMMs have K above one FP32 accumulation
+    chain (dgrad gate+up 106496, fprop down 53248) and run as K slices."""
+    cfg = workloads.LLAMA405B
+    ms = MlpStep(torch, nv, workloads, cfg, dev)
+    r = run_step_bench(torch, ms, steps, warmup, dev, isolated=False)
+    out = {"workload": "llama3.1-405b-mlp-fwd+bwd-step, one GPU's token share",
+           "tokens": cfg["tokens"], "hidden": cfg["hidden"], "ffn": cfg["ffn"],
+           "steps": steps, "warmup": warmup,
+           "ms_per_step": round(r["ms_per_step"], 3),
+           "tflops_step": round(r["tflops_step"], 2),
+           "gemm_tflop_per_step": round(r["flops_step"] / 1e12, 3),
+           "gemm_frac_of_mfma_peak": round(r["gemm_tflops"] / MFMA_F16_PEAK_TFLOPS, 4)}
+    out.update({k: v for k, v in r["report"].items() if k != "quantize_by_call"})
+    out["quantize_us_in_step"] = {k: v["us_in_step"] for k, v in
+                                  r["report"]["quantize_by_call"].items()}
+    del ms
+    torch.cuda.empty_cache()
+    return out
 
 
 def isolated_times(torch, calls, dev, reps=10):
@@ -658,50 +731,89 @@ def cpu_model():
 
 
 def cpu_baseline(args, torch, nv, workloads, X, W_gu):
-    """The oracle, as it stands, on a bounded sample of the step: fprop GEMM 1
-    for the first `rows` tokens (all 28672 outputs, full K = 4096)."""
+    """The oracle, as it stands, on bounded samples of the same work (all host
+    cores unless stated):
+      - value: fprop GEMM 1 for the first `rows` tokens (all 28672 outputs,
+        full K = 4096), FP64 dot products of the quantized operands;
+      - single_thread_value: the same on rows / cores tokens, one thread;
+      - quantize: the whole of X (32768 x 4096, 1x16 RNE with its amax pass)
+        and W_gu (16x16 with its amax pass);
+      - tiny: the 256 x 256 quantize / dequantize and the 128 x 128 x 256 GEMM
+        in full;
+      - decode_m1: the decode weight (28672 x 8192, 1x16) quantized and the
+        M = 1 GEMM in full."""
     import numpy as np
 
     import oracle
     rows = args.cpu_sample_rows
     cores = len(os.sched_getaffinity(0))
     oracle.set_num_threads(cores)
-    x = X[:rows].cpu()
+    out = {"unit": "TFLOP/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model()}
+    # quantize: all of X and W_gu (2.56 B/elem with the amax pass read: 4.56)
+    xc_all = X.cpu()
     w = W_gu.cpu()
     t0 = time.perf_counter()
-    xc, xs, xts, _ = oracle.quantize(workloads.bf16_bits(x),
-                                     amax_in=float(X.abs().max().item()))
+    oracle.quantize(workloads.bf16_bits(xc_all))
     wc, wsc, wts, _ = oracle.quantize(workloads.bf16_bits(w), block2d=True)
     tq = time.perf_counter() - t0
+    qbytes = (xc_all.numel() + w.numel()) * (2 * 2 + 0.5) + xc_all.numel() / 16 + w.numel() / 256
+    out["quantize_GBps"] = round(qbytes / tq / 1e9, 4)
+    out["quantize_sample"] = ("all of X (32768 x 4096, 1x16 RNE) and W_gu (28672 x 4096, "
+                              "16x16 RNE), each with its amax pass, %.1f s" % tq)
+    # GEMM: fprop GEMM 1 on the first `rows` tokens
+    x = X[:rows].cpu()
+    xc, xs, xts, _ = oracle.quantize(workloads.bf16_bits(x), amax_in=float(X.abs().max().item()))
     N, K = w.shape
-    ms, ns = np.meshgrid(np.arange(rows), np.arange(N), indexing="ij")
+    m_, n_ = np.meshgrid(np.arange(rows), np.arange(N), indexing="ij")
     t1 = time.perf_counter()
-    oracle.gemm_pairs("NT", rows, N, K, (xc, xs, xts, False), (wc, wsc, wts, True), ms.ravel(),
-                      ns.ravel())
+    oracle.gemm_pairs("NT", rows, N, K, (xc, xs, xts, False), (wc, wsc, wts, True), m_.ravel(),
+                      n_.ravel())
     tg = time.perf_counter() - t1
+    flops = 2.0 * rows * N * K
+    out["value"] = round(flops / tg / 1e12, 6)
+    out["sample"] = ("fprop GEMM 1 (NT, 2D-quantized W_gu) on the first %d tokens: "
+                     "%d x %d x %d FP64 dot products (%.2f GFLOP) in %.1f s"
+                     % (rows, rows, N, K, flops / 1e9, tg))
     # the same on one thread, over rows / cores tokens (about the same wall time)
     rows1 = max(1, rows // cores)
-    ms1, ns1 = np.meshgrid(np.arange(rows1), np.arange(N), indexing="ij")
+    m1, n1 = np.meshgrid(np.arange(rows1), np.arange(N), indexing="ij")
     oracle.set_num_threads(1)
     t2 = time.perf_counter()
-    oracle.gemm_pairs("NT", rows1, N, K, (xc, xs, xts, False), (wc, wsc, wts, True), ms1.ravel(),
-                      ns1.ravel())
+    oracle.gemm_pairs("NT", rows1, N, K, (xc, xs, xts, False), (wc, wsc, wts, True), m1.ravel(),
+                      n1.ravel())
     t1s = time.perf_counter() - t2
     oracle.set_num_threads(cores)
-    flops = 2.0 * rows * N * K
-    flops1 = 2.0 * rows1 * N * K
-    qbytes = (x.numel() + w.numel()) * (2 + 0.5 + 1 / 16) + w.numel() * 2
-    return {"value": round(flops / tg / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle", "cpu_model": cpu_model(),
-            "sample": "fprop GEMM 1 (NT, 2D-quantized W_gu) on the first %d tokens: "
-                      "%d x %d x %d FP64 dot products (%.2f GFLOP) in %.1f s"
-                      % (rows, rows, N, K, flops / 1e9, tg),
-            "single_thread_value": round(flops1 / t1s / 1e12, 6),
-            "single_thread_sample": "the same GEMM on the first %d tokens, one thread, %.1f s"
-                                    % (rows1, t1s),
-            "quantize_GBps": round(qbytes / tq / 1e9, 4),
-            "quantize_sample": "X rows 0-%d (1x16 RNE) and W_gu (16x16 RNE, amax pass), %.1f s"
-                               % (rows - 1, tq)}
+    out["single_thread_value"] = round(2.0 * rows1 * N * K / t1s / 1e12, 6)
+    out["single_thread_sample"] = "the same GEMM on the first %d tokens, one thread, %.1f s" % (
+        rows1, t1s)
+    # the tiny workload in full
+    cfg = workloads.TINY
+    t3 = time.perf_counter()
+    a_c, a_s, a_t, _ = oracle.quantize(workloads.bf16_bits(
+        workloads.activations(*cfg["act"], seed=cfg["act_seed"])))
+    oracle.dequantize(a_c, a_s, a_t, *cfg["act"])
+    b_c, b_s, b_t, _ = oracle.quantize(workloads.bf16_bits(
+        workloads.weights(*cfg["w"], seed=cfg["w_seed"])), block2d=True)
+    M_, N_, K_ = cfg["gemm"]
+    oracle.gemm_full("NT", M_, N_, K_, (a_c[:M_], a_s[:M_], a_t, False), (b_c, b_s, b_t, True))
+    out["tiny_full_s"] = round(time.perf_counter() - t3, 4)
+    # decode M = 1 in full: quantize the weight, then the 1 x 28672 x 8192 GEMM
+    dc = workloads.DECODE
+    wd = workloads.weights(dc["n"], dc["k"], seed=dc["w_seed"])
+    ad = workloads.activations(64, dc["k"], seed=dc["act_seed"])[:1]
+    t4 = time.perf_counter()
+    dw = oracle.quantize(workloads.bf16_bits(wd))
+    tqd = time.perf_counter() - t4
+    da = oracle.quantize(workloads.bf16_bits(ad))
+    t5 = time.perf_counter()
+    oracle.gemm_full("NT", 1, dc["n"], dc["k"], (da[0], da[1], da[2], False),
+                     (dw[0], dw[1], dw[2], False))
+    tgd = time.perf_counter() - t5
+    out["decode_m1"] = {"weight_quantize_s": round(tqd, 3), "gemm_s": round(tgd, 3),
+                        "gemm_GFLOPs": round(2.0 * dc["n"] * dc["k"] / tgd / 1e9, 3),
+                        "sample": "28672 x 8192 weight (1x16 RNE with amax pass), then the "
+                                  "M = 1 GEMM over all 28672 outputs"}
+    return out
 
 
 if __name__ == "__main__":
