@@ -390,8 +390,9 @@ nvfp4_status nvfp4_gemm_swiglu(int64_t M, int64_t N, int64_t K, const uint8_t* a
  *   output rounded to nearest-even.  cols % 32 == 0; ld_out >= cols.
  * nvfp4_mx_gemm: C[M, N] = A[M, K] * B[N, K]^T (NT: both stored K-major)
  *   with FP32 accumulation on the native scaled FP4 MFMA, BF16 (RNE) or
- *   FP32 out.  K % 128 == 0; K / 2 * 256 < 2^31; ldc >= N; c element-aligned,
- *   operand planes 16-byte aligned.  K == 0 writes zeros.
+ *   FP32 out.  K % 128 == 0; K <= 32768 (one FP32 accumulation chain; see
+ *   nvfp4_gemm); ldc >= N; c element-aligned, operand planes 16-byte
+ *   aligned.  K == 0 writes zeros.
  * All pointers are caller-owned device memory; launches are asynchronous on
  * `stream`; argument errors return before anything is enqueued.
  */

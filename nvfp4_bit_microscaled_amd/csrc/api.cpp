@@ -414,8 +414,10 @@ nvfp4_status nvfp4_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_cod
     if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_INVALID_ARG;
     if (ldc < N) return NVFP4_ERR_SHAPE;
     if (K % 128) return NVFP4_ERR_SHAPE;
-    // buffer records of a 256-row tile (and the C offsets) in 32 bits
+    // buffer records of a 256-row tile (and the C offsets) in 32 bits; one
+    // FP32 accumulation chain over K
     if ((uint64_t)K / 2 * 256 >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
+    if (K > kMaxChainK) return NVFP4_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return NVFP4_OK;
     if (!c) return NVFP4_ERR_INVALID_ARG;
     const size_t esz = out_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;

@@ -1878,7 +1878,7 @@ hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_code
                           const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
                           bool out_bf16, void* c, int64_t ldc, hipStream_t s)
 {
-    GemmParams p;
+    GemmParams p{};
     p.M = M; p.N = N; p.K = K; p.kp = K;
     p.a_bf16 = nullptr; p.lda = 0;
     p.a_codes = a_codes; p.a_scales = a_scales;
@@ -1904,7 +1904,7 @@ hipError_t launch_gemm_w4a16(int64_t M, int64_t N, int64_t K, const uint16_t* a,
                              const GemmOperand& B, bool out_bf16, void* c, int64_t ldc,
                              hipStream_t s)
 {
-    GemmParams p;
+    GemmParams p{};
     p.M = M; p.N = N; p.K = K; p.kp = K;
     p.a_codes = nullptr; p.a_scales = nullptr; p.a_ts = nullptr;
     p.b_codes = B.codes; p.b_scales = B.scales; p.b_ts = B.ts;

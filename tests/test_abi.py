@@ -207,6 +207,7 @@ def test_mx_validation(lib):
     assert mxg(lib, ac=MISALIGNED) == 3
     assert mxg(lib, bsc=None) == 1
     assert mxg(lib, K=1 << 24) == 5                  # 256 rows of codes past 2^31 bytes
+    assert mxg(lib, K=32896) == 5                    # longer than one accumulation chain
     assert mxg(lib, M=0) == 0
 
 
