@@ -72,7 +72,7 @@ def parse():
                          "profiling its kernels)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode-shape GEMMs and print their JSON object "
-                         "(for profiling the skinny kernel; not the bench line)")
+                         "(for profiling the decode kernels; not the bench line)")
     return ap.parse_args()
 
 
@@ -564,7 +564,7 @@ def dequant_rht_bench(torch, nv, X, mask, reps=20):
 
 
 def decode_bench(torch, nv, workloads):
-    """Decode-style skinny NT GEMM: activations [M, 8192] x weights [28672, 8192],
+    """Decode-shape NT GEMM: activations [M, 8192] x weights [28672, 8192],
     both 1x16 RNE.  HBM-bound on the packed weights (codes + scales).  Four
     copies of the quantized weights (4 x 132 MB, twice the 256 MB Infinity
     Cache) are cycled through 40 back-to-back launches, so every launch reads

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libnvfp4.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemm_decode.hip"]
 ARCH = os.environ.get("NVFP4_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -20,55 +20,11 @@
 // equal; both hold the scaled products exactly.
 #include <type_traits>
 
-#include "device_common.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace nvfp4 {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float16_t __attribute__((ext_vector_type(16)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// BF16 bits of two FP32 values rounded to nearest even, a in the low half:
-// one v_cvt_pk_bf16_f32 (these kernels keep FP32 denormals, so those round
-// like any other value).
-__device__ __forceinline__ uint32_t bf16_pair(float a, float b)
-{
-    const float2_t v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
-struct GemmParams {
-    int64_t M, N, K;
-    int64_t kp;   // K-major operands: K extent of a row of the planes (>= K; > K for a K slice)
-    const uint8_t* a_codes;
-    const uint8_t* a_scales;
-    const uint8_t* b_codes;
-    const uint8_t* b_scales;
-    const float* a_ts;
-    const float* b_ts;
-    uint8_t* c;
-    int64_t ldc;
-    bool a2d, b2d, out_bf16;
-    bool vec_out;  // C rows allow 8-byte (BF16) / 16-byte (FP32) stores
-    const uint16_t* a_bf16;  // weight-only GEMM: BF16 activations [M, K], row pitch lda
-    int64_t lda;
-    bool vec16;    // C base and row pitch are 16-byte aligned (whole-line epilogue)
-    // SwiGLU epilogue (k_gemm_kk<true>): act [M, N/2] BF16, row pitch ld_act;
-    // H itself (through c) only when store_h; two amax partials per workgroup
-    uint8_t* act;
-    int64_t ld_act;
-    uint32_t rht_mask;
-    float* partials;   // [grid] max|act|, then [grid] max|RHT16 of act down columns|
-    bool store_h, act_vec16;
-    // K-split of the last round of tiles (k_gemm_kk<.., true>): workgroup b
-    // takes K half b % 2 of tile tile_base + b / 2 (K = the half's length,
-    // kp the whole K) and writes the FP32 partial to c (half 0) or c2 (half 1)
-    uint32_t tile_base;
-    uint8_t* c2;
-};
 
 // 8x8 nibble transpose: in[k] holds element (k, j) in nibble j; out[j] gets
 // element (k, j) in nibble k.  Recursive block transpose: swap the off-
@@ -298,39 +254,6 @@ __device__ __forceinline__ void stage_store(const Staged& st, uint8_t* tile)
     w[0] = __builtin_amdgcn_perm(s1, s0, 0x05040100u);  // b0 b1 b4 b5
     w[1] = __builtin_amdgcn_perm(s1, s0, 0x07060302u);  // b2 b3 b6 b7
     *reinterpret_cast<u32x2*>(sct + t * 8) = w;
-}
-
-// 8 FP16 operand values from 8 codes (one 32-bit word) and the block scale.
-__device__ __forceinline__ half8_t dequant_word(uint32_t w, _Float16 e)
-{
-    half2_t s2 = {e, e};
-    half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
-    half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
-    half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
-    half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
-    half8_t r;
-    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-    return r;
-}
-
-// Eight E2M1 codes times the block scale e as BF16, for the weight-only
-// (BF16-activation) GEMM.  val * e needs at most 6 significant bits, so it
-// is exact in FP32 and its low 16 bits are zero: the BF16 value is the upper
-// half, taken with one v_perm per pair.
-__device__ __forceinline__ bf16x8_t dequant_word_bf16(uint32_t w, float e)
-{
-    u32x4 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        float2_t v = q == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
-                   : q == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
-                   : q == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
-                            : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-        r[q] = __builtin_amdgcn_perm(__float_as_uint(v[1] * e), __float_as_uint(v[0] * e),
-                                     0x07060302u);
-    }
-    return __builtin_bit_cast(bf16x8_t, r);
 }
 
 // Output tile index for workgroup `bid`: consecutive ids go round-robin to
@@ -654,15 +577,7 @@ constexpr int kKKLds = 3 * kKKStage;             // 110592 bytes
 constexpr int kKKLdsReserve = 4 * 32 * (256 + 16) + 4 * 32 * (128 + 16);
 static_assert(kKKLdsReserve + 32 <= kKKLds, "epilogue LDS fits the operand ring");
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-#define NVFP4_WAIT_VMCNT(n) \
-    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
-// ... and with only the LDS / scalar-memory counter drained (vmcnt left at its
-// maximum 63)
-#define NVFP4_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 // SwiGLU epilogue of a 256 x 256 tile of H = s_A s_B A B^T whose B rows are
 // interleaved in blocks of 64: rows 128 q .. 128 q + 63 are gate rows
@@ -1113,278 +1028,6 @@ __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
     }
 }
 
-// ---------------------------------------------------------------------------
-// Skinny NT kernel for decode-style shapes (M <= 64, K a multiple of the K
-// chunk KC = 512): C[M, N] = A[M, K]
-// B[N, K]^T.  The packed weights B dominate the traffic (4.5 bits per element)
-// and are streamed once: each wave owns 16 rows of B (16 output columns) over
-// all of K.  Inside a chunk, lane group g = lane / 16 owns the contiguous K
-// quarter g KC/4 .. +KC/4 (one 16-byte code load per 128 K, and its scale
-// bytes for the whole chunk in one or two wide loads: the load path is
-// limited by accesses per lane, so 2-byte scale loads per step would cost as
-// much as the codes).  The few activation rows are dequantized once per
-// workgroup into LDS as FP16, one chunk at a time, in the same lane-quarter
-// order (16 bytes of padding per quarter keep the quarters on different
-// banks).  Both operands are prefetched into registers one chunk ahead,
-// issued after everything the current chunk waits for (vector-memory
-// counters drain in order).  Short chunks stream best: with 2048 or 1024
-// the same weights took 15-25% longer (more bytes in flight per wave, in
-// larger bursts).  Rows past M or N are clamped to the last valid
-// row (never stored).  v_mfma_f32_16x16x32_f16: at step s lane (row l % 16,
-// group g) supplies k = kc + g KC/4 + 32 st + 8 s + [0, 8) for both operands.
-// ---------------------------------------------------------------------------
-constexpr int kSkN = 64;  // output columns per workgroup
-
-// kA16: the weight-only variant, BF16 activations (no activation scales;
-// 32-element pieces copied to LDS as they are), weights dequantized to BF16
-// and v_mfma_f32_16x16x32_bf16.
-template <int KC, int RMAX, bool kA16>
-__global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
-{
-    constexpr int kSteps = KC / 128;                 // B steps per chunk
-    constexpr int kQ = KC / 4;                       // K of one lane quarter per chunk
-    constexpr int kQStride = kQ * 2 + 16;            // LDS bytes per activation row quarter
-    constexpr int kRow = 4 * kQStride;               // LDS bytes per activation row
-    constexpr int kAPer = RMAX * 16 * KC / 32 / 256; // 32-code activation pieces per thread
-    constexpr int kSB = 2 * kSteps;                  // scale bytes per lane and chunk
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lr = lane & 15, g = lane >> 4;
-    const int64_t n = (int64_t)blockIdx.x * kSkN + wave * 16 + lr;  // B row of this lane
-    const int64_t nc = n < p.N ? n : p.N - 1;                       // clamped for loads
-    const int64_t K = p.K, lds_b = K / 16;
-    // B through buffer resources over the whole code / scale planes (below
-    // 2 GiB): per-lane offsets in VGPRs, the chunk offset scalar, the step
-    // offset an immediate.  Past the last chunk the prefetch goes through
-    // resources with no records (out-of-range loads return zeros, touching no
-    // memory), so the loop body has no branch around it.
-    const __amdgpu_buffer_rsrc_t rc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, (short)0, 0x7FFFFFFF, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.b_scales, (short)0, 0x7FFFFFFF, 0x00020000);
-    const __amdgpu_buffer_rsrc_t none =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, (short)0, 0, 0x00020000);
-    // kLines (one activation row block): B codes in whole 128-byte lines.
-    // Load instruction (h, ln) of a chunk reads line ln of rows 8 h .. 8 h + 7
-    // of the wave's 16 (lane l: row 8 h + l / 8, bytes 16 (l % 8) of the
-    // line), and the bytes go through a wave-private LDS buffer into the
-    // fragment layout.  Measured on 28672 x 8192 weights this streams 6-11%
-    // faster for M <= 16 than loading the fragment layout directly (16 bytes
-    // from each of 64 lines per instruction); with more activation rows the
-    // extra LDS costs a workgroup per CU and loses.  Otherwise lane group g
-    // loads its quarter of the chunk directly, 16 bytes per step.
-    constexpr bool kLines = RMAX == 1;
-    static_assert(!kLines || KC == 512, "two 128-byte lines per row and chunk");
-    int bo[2];
-    if constexpr (kLines) {
-        const int64_t brow0 = (int64_t)blockIdx.x * kSkN + wave * 16;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            int64_t r = brow0 + 8 * h + (lane >> 3);
-            r = r < p.N ? r : p.N - 1;
-            bo[h] = (int)(r * (K / 2)) + 16 * (lane & 7);
-        }
-    } else {
-        bo[0] = bo[1] = (int)(nc * (K / 2)) + (kQ / 2) * g;
-    }
-    uint8_t* const bl = lds + RMAX * 16 * kRow + wave * 16 * (KC / 2 + 16);  // 16 rows x 272 B
-    const int bso = (int)(p.b2d ? (nc / 16) * lds_b : nc * lds_b) + (kQ / 16) * g;
-    // Workgroups walk K starting at different chunks: rows are K/2 bytes
-    // apart, so if every workgroup read the same chunk at once, all reads
-    // would fall in the same few byte ranges of the row pitch (the same
-    // memory channels).  The sum over chunks is the same in any order.
-    const int nchunks = (int)(K / KC);
-    const int rot = (int)(blockIdx.x % (unsigned)nchunks) * KC;
-    auto kpos = [&](int kc) { return kc + rot >= (int)K ? kc + rot - (int)K : kc + rot; };
-    float4_t acc[RMAX];
-#pragma unroll
-    for (int r = 0; r < RMAX; ++r) acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-    // B: lane g owns the contiguous quarter kc + g KC/4 .. +KC/4 of each chunk,
-    // 32 codes per step, so its scale bytes for the chunk are one contiguous
-    // run of kSB bytes
-    u32x4 ac[kA16 ? 1 : kAPer], bc[kSteps], bn[kSteps];
-    uint32_t as[kA16 ? 1 : kAPer];
-    u32x4 aw[kA16 ? kAPer : 1][4];  // BF16 pieces (64 bytes each)
-    uint32_t bs[kSB / 4], bsn[kSB / 4];
-    auto load_a = [&](int64_t kc) {
-#pragma unroll
-        for (int i = 0; i < kAPer; ++i) {
-            int idx = threadIdx.x + 256 * i;
-            int m = idx / (KC / 32), c = idx % (KC / 32);
-            int64_t mc = m < p.M ? m : p.M - 1;
-            int64_t k = kc + 32 * c;
-            k = k < K ? k : K - 32;  // the prefetch past the last chunk reads a valid piece
-            if constexpr (kA16) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(p.a_bf16 + mc * p.lda + k);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) aw[i][q] = src[q];
-            } else {
-                ac[i] = *reinterpret_cast<const u32x4*>(p.a_codes + mc * (K / 2) + k / 2);
-                const uint8_t* sp =
-                    p.a_scales + (p.a2d ? (mc / 16) * lds_b : mc * lds_b) + k / 16;
-                as[i] = *reinterpret_cast<const uint16_t*>(sp);
-            }
-        }
-    };
-    auto load_b = [&](__amdgpu_buffer_rsrc_t c_rsrc, __amdgpu_buffer_rsrc_t s_rsrc, int kc,
-                      u32x4* c, uint32_t* sc) {
-#pragma unroll
-        for (int st = 0; st < kSteps; ++st) {  // kLines: st = 2 h + ln
-            if constexpr (kLines)
-                c[st] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, bo[st >> 1],
-                                                                 kc / 2 + 128 * (st & 1), 0));
-            else
-                c[st] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, bo[0] + 16 * st, kc / 2, 0));
-        }
-#pragma unroll
-        for (int q = 0; q < kSB / 4; q += (kSB >= 16 ? 4 : 2)) {
-            if (kSB >= 16) {
-                u32x4 w = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(s_rsrc, bso + 4 * q, kc / 16, 0));
-                sc[q] = w[0]; sc[q + 1] = w[1]; sc[q + 2] = w[2]; sc[q + 3] = w[3];
-            } else {
-                u32x2 w = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(s_rsrc, bso + 4 * q, kc / 16, 0));
-                sc[q] = w[0]; sc[q + 1] = w[1];
-            }
-        }
-    };
-
-    // one chunk: its activations into LDS, the next chunk's operands issued,
-    // then the products with the B registers loaded one chunk earlier.  The
-    // chunk loop runs in pairs with the two B register sets swapping roles,
-    // so no register copy (and no wait for the prefetch) sits in the loop.
-    auto chunk = [&](int kc, const u32x4 (&cb)[kSteps], const uint32_t (&cs)[kSB / 4],
-                     u32x4 (&nb)[kSteps], uint32_t (&ns)[kSB / 4]) {
-        // activations of this chunk -> FP16 in LDS, row-major by lane quarter
-        // (the previous chunk's readers are done); rows past M hold the last
-        // row again and are never stored.  The barriers only order LDS
-        // accesses: a plain s_barrier after draining this wave's LDS counter
-        // (a __syncthreads fence would also wait for the prefetch in flight).
-        NVFP4_WAIT_LGKMCNT0();
-        __builtin_amdgcn_s_barrier();
-#pragma unroll
-        for (int i = 0; i < kAPer; ++i) {
-            int idx = threadIdx.x + 256 * i;
-            int m = idx / (KC / 32), c = idx % (KC / 32);
-            const int kl = 32 * c;  // K offset inside the chunk
-            uint8_t* dst = lds + m * kRow + (kl / kQ) * kQStride + (kl % kQ) * 2;
-            if constexpr (kA16) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(dst + 16 * q) = aw[i][q];
-            } else {
-                half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as[i], 1.0f, false);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<half8_t*>(dst + 16 * q) = dequant_word(ac[i][q], e2[q >> 1]);
-            }
-        }
-        NVFP4_WAIT_LGKMCNT0();
-        __builtin_amdgcn_s_barrier();
-        // next chunk's operands, A strictly before B (the next chunk's
-        // dequantization then waits for A alone); past the end through the
-        // record-less resources
-        const bool more = kc + KC < (int)K;
-        __builtin_amdgcn_sched_barrier(0);
-        load_a(kpos(kc + KC));
-        __builtin_amdgcn_sched_barrier(0);
-        load_b(more ? rc : none, more ? rs : none, more ? kpos(kc + KC) : 0, nb, ns);
-        __builtin_amdgcn_sched_barrier(0);
-        // this chunk's weight lines into the wave's LDS buffer (row pitch 272
-        // bytes), then each lane takes 16 bytes of its row's quarter g per
-        // step: one wave's LDS accesses complete in order, so no barrier
-        u32x4 cq[kSteps];
-        if constexpr (kLines) {
-#pragma unroll
-            for (int st = 0; st < kSteps; ++st)
-                *reinterpret_cast<u32x4*>(bl + (8 * (st >> 1) + (lane >> 3)) * (KC / 2 + 16) +
-                                          128 * (st & 1) + 16 * (lane & 7)) = cb[st];
-#pragma unroll
-            for (int st = 0; st < kSteps; ++st)
-                cq[st] = *reinterpret_cast<const u32x4*>(bl + lr * (KC / 2 + 16) + (kQ / 2) * g +
-                                                         16 * st);
-        } else {
-#pragma unroll
-            for (int st = 0; st < kSteps; ++st) cq[st] = cb[st];
-        }
-#pragma unroll
-        for (int st = 0; st < kSteps; ++st) {
-            // the step's A fragments first (one LDS latency per step), then
-            // its four B dequantizations and MFMAs
-            half8_t af[4][RMAX];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int r = 0; r < RMAX; ++r)
-                    af[s][r] = *reinterpret_cast<const half8_t*>(
-                        lds + (16 * r + lr) * kRow + g * kQStride + (32 * st + 8 * s) * 2);
-            // scale bytes 2 st, 2 st + 1 of the lane's run
-            const uint32_t sw = cs[st >> 1] >> (16 * (st & 1));
-            if constexpr (kA16) {
-                const float e0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
-                const float e1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    bf16x8_t bf = dequant_word_bf16(cq[st][s], s < 2 ? e0 : e1);
-#pragma unroll
-                    for (int r = 0; r < RMAX; ++r)
-                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, af[s][r]), bf, acc[r], 0, 0, 0);
-                }
-            } else {
-                half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    half8_t bf = dequant_word(cq[st][s], e2[s >> 1]);
-#pragma unroll
-                    for (int r = 0; r < RMAX; ++r)
-                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s][r], bf, acc[r], 0, 0, 0);
-                }
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4 * RMAX, 0);   // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);         // scale + B dequant
-            __builtin_amdgcn_sched_group_barrier(0x008, 4 * RMAX, 0);   // MFMAs
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(kpos(0));
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(rc, rs, kpos(0), bc, bs);
-    __builtin_amdgcn_sched_barrier(0);
-    // both exits leave the loop, so the loop head is reached only after the
-    // second chunk of a pair (its registers are the live ones there)
-    for (int kc = 0;; kc += 2 * KC) {
-        chunk(kc, bc, bs, bn, bsn);
-        if (kc + KC >= (int)K) break;
-        chunk(kc + KC, bn, bsn, bc, bs);
-        if (kc + 2 * KC >= (int)K) break;
-    }
-    // lane holds C[16 r + 4 g + j][n] in acc[r][j]
-    const float sab = kA16 ? *p.b_ts : (*p.a_ts) * (*p.b_ts);
-#pragma unroll
-    for (int r = 0; r < RMAX; ++r) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int64_t row = 16 * r + 4 * g + j;
-            if (row < p.M && n < p.N) {
-                float v = acc[r][j] * sab;
-                if (p.out_bf16) {
-                    uint32_t u = __float_as_uint(v);
-                    u += 0x7FFFu + ((u >> 16) & 1u);
-                    reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + n] = (uint16_t)(u >> 16);
-                } else {
-                    reinterpret_cast<float*>(p.c)[row * p.ldc + n] = v;
-                }
-            }
-        }
-    }
-}
-
 __global__ void k_fill_zero(uint8_t* c, int64_t M, int64_t N, int64_t ldc, int esz)
 {
     int64_t total = M * N;
@@ -1454,35 +1097,58 @@ uint64_t gemm_tail_tiles(int64_t M, int64_t N, int64_t K, int64_t kp)
 size_t gemm_split_bytes(bool both_kmajor, int64_t M, int64_t N, int64_t K)
 {
     if (!both_kmajor || K % kTK != 0 || K > kMaxChainK) return 0;
-    if (M <= 64 && K % 512 == 0 && (uint64_t)N * (uint64_t)K / 2 < (1ull << 31)) return 0;
+    if (gemm_decode_shape(M, N, K)) return 0;
     if (K / 2 * kTM >= (1ll << 31)) return 0;
     return gemm_tail_tiles(M, N, K, K) ? (size_t)2 * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 // C over the split tiles: the two FP32 halves (planes [M, N]) summed, then
-// rounded to BF16 or stored as FP32.  One workgroup per tile (tile ids as
-// the K-major kernel maps them); thread t covers 4 columns of rows t / 64,
-// t / 64 + 4, ...
+// rounded to BF16 or stored as FP32.  Four workgroups per tile (tile ids as
+// the K-major kernel maps them), 64 rows each; thread t covers 4 consecutive
+// columns of rows t / 64, t / 64 + 4, ... (16-byte loads when the rows
+// allow them).
 __global__ __launch_bounds__(256) void k_sum_tail_tiles(const float* h0, const float* h1,
                                                         int64_t M, int64_t N, uint32_t tile_base,
                                                         bool out_bf16, uint8_t* c, int64_t ldc)
 {
     const uint32_t nbm = (uint32_t)((M + kTM - 1) / kTM), nbn = (uint32_t)((N + kTN - 1) / kTN);
     uint32_t tm, tn;
-    tile_of(tile_base + blockIdx.x, nbm, nbn, tm, tn);
-    const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
+    tile_of(tile_base + (blockIdx.x >> 2), nbm, nbn, tm, tn);
+    const int64_t m0 = (int64_t)tm * kTM + 64 * (blockIdx.x & 3), n0 = (int64_t)tn * kTN;
     const int t = threadIdx.x;
     const int64_t col = n0 + 4 * (t & 63);
-    for (int r = t >> 6; r < kTM; r += 4) {
+    const bool vec = (N % 4) == 0 && col + 4 <= N;
+    const bool vec_c = vec && (ldc % 4) == 0 && (reinterpret_cast<uintptr_t>(c) & 15u) == 0;
+#pragma unroll 4
+    for (int r = t >> 6; r < 64; r += 4) {
         const int64_t row = m0 + r;
-        if (row >= M) break;
-        for (int q = 0; q < 4; ++q) {
-            if (col + q >= N) break;
-            const float v = h0[row * N + col + q] + h1[row * N + col + q];
-            if (out_bf16)
-                reinterpret_cast<uint16_t*>(c)[row * ldc + col + q] = (uint16_t)f32_to_bf16_bits(v);
-            else
-                reinterpret_cast<float*>(c)[row * ldc + col + q] = v;
+        if (row >= M || col >= N) break;
+        float v[4];
+        if (vec) {
+            const float4_t a = *reinterpret_cast<const float4_t*>(h0 + row * N + col);
+            const float4_t b = *reinterpret_cast<const float4_t*>(h1 + row * N + col);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = a[q] + b[q];
+        } else {
+            for (int q = 0; q < 4; ++q)
+                v[q] = col + q < N ? h0[row * N + col + q] + h1[row * N + col + q] : 0.0f;
+        }
+        if (vec_c && out_bf16) {
+            u32x2 w;
+            w[0] = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+            w[1] = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(c) + row * ldc + col) = w;
+        } else if (vec_c) {
+            *reinterpret_cast<float4_t*>(reinterpret_cast<float*>(c) + row * ldc + col) =
+                float4_t{v[0], v[1], v[2], v[3]};
+        } else {
+            for (int q = 0; q < 4 && col + q < N; ++q) {
+                if (out_bf16)
+                    reinterpret_cast<uint16_t*>(c)[row * ldc + col + q] =
+                        (uint16_t)f32_to_bf16_bits(v[q]);
+                else
+                    reinterpret_cast<float*>(c)[row * ldc + col + q] = v[q];
+            }
         }
     }
 }
@@ -1505,25 +1171,9 @@ static hipError_t launch_gemm_one(int64_t M, int64_t N, int64_t K, int64_t kp,
     const int esz = out_bf16 ? 2 : 4;
     p.vec_out = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(c) % (4 * esz) == 0;
     p.vec16 = (ldc * esz) % 16 == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0;
-    // decode-style shapes (M <= 64): stream the weights with a dedicated
-    // kernel; its K chunk must divide K
-    const int skinny_kc = 512;
-    const bool b_small = (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);  // 32-bit buffer offsets
-    if (A.k_major && B.k_major && M <= 64 && K % skinny_kc == 0 && b_small && kp == K) {
-        dim3 g((unsigned)((N + kSkN - 1) / kSkN));
-#define NVFP4_SKINNY(KC, RMAX)                                                                 \
-    {                                                                                          \
-        auto kern = k_gemm_skinny<KC, RMAX, false>;                                            \
-        const int lds = RMAX * 16 * (KC * 2 + 64) + (RMAX == 1 ? 4 * 16 * (KC / 2 + 16) : 0);  \
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
-        hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
-    }
-        if (M <= 16) NVFP4_SKINNY(512, 1)
-        else if (M <= 32) NVFP4_SKINNY(512, 2)
-        else NVFP4_SKINNY(512, 4)
-#undef NVFP4_SKINNY
-        return hipGetLastError();
-    }
+    // decode-style shapes (M <= 64): the weight-streaming kernels
+    if (A.k_major && B.k_major && kp == K && gemm_decode_shape(M, N, K))
+        return launch_gemm_decode(p, s);
     if (A.k_major && B.k_major && K % kTK == 0 && kp / 2 * kTM < (1ll << 31)) {
         const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
         const bool all_full = M % kTM == 0 && N % kTN == 0 && p.vec16;
@@ -1549,7 +1199,7 @@ static hipError_t launch_gemm_one(int64_t M, int64_t N, int64_t K, int64_t kp,
         auto ks = full_q ? k_gemm_kk<false, kKKEpiF32, true> : k_gemm_kk<false, kKKEpiAny, true>;
         hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, kKKLds);
         hipLaunchKernelGGL(ks, dim3((unsigned)(2 * tail)), dim3(256), kKKLds, s, q);
-        hipLaunchKernelGGL(k_sum_tail_tiles, dim3((unsigned)tail), dim3(256), 0, s, split_ws,
+        hipLaunchKernelGGL(k_sum_tail_tiles, dim3((unsigned)(4 * tail)), dim3(256), 0, s, split_ws,
                            split_ws + M * N, M, N, (uint32_t)(t - tail), out_bf16, p.c, ldc);
         return hipGetLastError();
     }
@@ -1897,37 +1547,6 @@ hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_code
                           : (out_bf16 ? k_gemm_mx<kKKEpiBF16> : k_gemm_mx<kKKEpiF32>);
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
     hipLaunchKernelGGL(kern, dim3((unsigned)t), dim3(256), kMxLds, s, p);
-    return hipGetLastError();
-}
-
-hipError_t launch_gemm_w4a16(int64_t M, int64_t N, int64_t K, const uint16_t* a, int64_t lda,
-                             const GemmOperand& B, bool out_bf16, void* c, int64_t ldc,
-                             hipStream_t s)
-{
-    GemmParams p{};
-    p.M = M; p.N = N; p.K = K; p.kp = K;
-    p.a_codes = nullptr; p.a_scales = nullptr; p.a_ts = nullptr;
-    p.b_codes = B.codes; p.b_scales = B.scales; p.b_ts = B.ts;
-    p.c = static_cast<uint8_t*>(c);
-    p.ldc = ldc;
-    p.a2d = false;
-    p.b2d = B.block2d != 0;
-    p.out_bf16 = out_bf16;
-    p.vec_out = false;
-    p.a_bf16 = a;
-    p.lda = lda;
-    dim3 g((unsigned)((N + kSkN - 1) / kSkN));
-#define NVFP4_SKINNY16(RMAX)                                                                   \
-    {                                                                                          \
-        auto kern = k_gemm_skinny<512, RMAX, true>;                                            \
-        const int lds = RMAX * 16 * (512 * 2 + 64) + (RMAX == 1 ? 4 * 16 * (512 / 2 + 16) : 0);\
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
-        hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
-    }
-    if (M <= 16) NVFP4_SKINNY16(1)
-    else if (M <= 32) NVFP4_SKINNY16(2)
-    else NVFP4_SKINNY16(4)
-#undef NVFP4_SKINNY16
     return hipGetLastError();
 }
 

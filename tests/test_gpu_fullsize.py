@@ -9,7 +9,7 @@ tiles plus 4096 seeded random outputs, each a full-K FP64 dot product.
 Workloads: Llama-3-8B MLP at 32768 tokens (fprop and backward, in the NN/TN
 storage layouts and in the all-K-major configuration the training step
 times), decode-style
-skinny GEMMs (M in {1, 16, 64}, K 8192, N 28672) and one GPU's token share of
+GEMMs (M in {1, 16, 32, 64}, K 8192, N 28672) and one GPU's token share of
 a Llama-3.1-405B MLP (8192 tokens, hidden 16384, intermediate 53248).  The
 token count follows the benchmark paragraph of the readjensen.com NVFP4
 training-recipe page; the recipe (2D weights, RHT + SR on wgrad inputs, SR on
@@ -318,7 +318,7 @@ DEC = workloads.DECODE
 
 
 @pytest.mark.parametrize("M", list(DEC["ms"]))
-def test_decode_skinny_gemm(nv, M):
+def test_decode_gemm(nv, M):
     """Activations [M, 8192] and weights [28672, 8192], both 1x16 RNE along K."""
     K, N = DEC["k"], DEC["n"]
     x = workloads.activations(64, K, seed=DEC["act_seed"])[:M]

@@ -217,17 +217,20 @@ def test_nt_kmajor_odd_rows(nv):
     run_and_check(nv, "NT", M, N, K, a_or, a_g, b_or, b_g)
 
 
-# decode-style NT shapes (M <= 64, K a multiple of the kernel's 512 K chunk):
-# the skinny kernel, with M and N ragged and one, an odd number and an even
-# number of chunks (its chunk loop runs in pairs)
+# decode-style NT shapes (M <= 64, K a multiple of 512): the weight-streaming
+# kernel (512-K chunks through a three-stage LDS ring, its chunk loop runs in
+# pairs; 1, 2 or 4 activation row tiles).  M and N ragged (partial last
+# workgroup), one, an odd and an even number of chunks, 2D weight blocks.
 SKINNY = [(1, 64, 2048, False), (5, 100, 4096, True), (16, 1000, 2048, False),
           (17, 200, 1024, True), (32, 77, 3072, False), (33, 130, 1536, False),
           (64, 96, 512, True), (64, 64, 8192, False), (1, 300, 2560, False),
-          (7, 48, 512, True), (12, 4200, 1536, False)]
+          (7, 48, 512, True), (12, 4200, 1536, False), (20, 130, 512, False),
+          (24, 64, 2560, False), (40, 64, 1536, True), (48, 200, 2560, False),
+          (63, 1000, 1024, False)]
 
 
 @pytest.mark.parametrize("M,N,K,b2d", SKINNY)
-def test_skinny_decode_kernel(nv, M, N, K, b2d):
+def test_decode_kernel(nv, M, N, K, b2d):
     rng = np.random.default_rng(M * 1000 + N + K)
     if b2d:
         N = (N + 15) // 16 * 16
@@ -275,8 +278,9 @@ def tile_order(bid, nbm, nbn):
     return first + inn % gsize, inn // gsize
 
 
-@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_last_round_k_split(nv, out_dtype):
+@pytest.mark.parametrize("out_dtype,ragged", [(torch.bfloat16, False), (torch.float32, False),
+                                               (torch.bfloat16, True), (torch.float32, True)])
+def test_last_round_k_split(nv, out_dtype, ragged):
     """A grid whose last round of 256 x 256 tiles would fill only 1/16 of the
     compute units: with a workspace those tiles run as two K halves each.
     Every output of the split tiles (and random others) against the oracle;
@@ -286,18 +290,21 @@ def test_last_round_k_split(nv, out_dtype):
     nbn = 16
     nbm = (ncu + ncu // 16 + nbn - 1) // nbn
     M, N, K = 256 * nbm, 256 * nbn, 4096
+    if ragged:  # partial last tile row and column, N % 4 != 0 (unvectorized sum)
+        M, N = M - 37, N - 6
     t = nbm * nbn
     tail = t % ncu
     assert 0 < tail <= ncu // 2
     assert nv.nvfp4_gemm_workspace_size(0, M, N, K) == 2 * M * N * 4
     rng = np.random.default_rng(5)
     a_or, a_g = random_operand(nv, rng, M, K, False, 1, 0.5, scale_lo=0x20)
-    b_or, b_g = random_operand(nv, rng, N, K, True, 1, 0.25, scale_lo=0x20)
+    b_or, b_g = random_operand(nv, rng, N, K, not ragged, 1, 0.25, scale_lo=0x20)
     print("last-round split", M, N, K, "tail", tail, flush=True)
     y = nv.gemm("NT", a_g, b_g, out_dtype=out_dtype)
     y_whole = torch.empty_like(y)
     st = nv.nvfp4_gemm(0, M, N, K, a_g.codes, a_g.scales, a_g.tensor_scale, 0, b_g.codes,
-                       b_g.scales, b_g.tensor_scale, 1, nv._dtype_code(y_whole), y_whole, N)
+                       b_g.scales, b_g.tensor_scale, 0 if ragged else 1, nv._dtype_code(y_whole),
+                       y_whole, N)
     assert st == 0
     torch.cuda.synchronize()
     ms, ns = [], []
@@ -312,6 +319,8 @@ def test_last_round_k_split(nv, out_dtype):
     ms.append(rng.integers(0, M, 2048))
     ns.append(rng.integers(0, N, 2048))
     ms, ns = np.concatenate(ms).astype(np.int64), np.concatenate(ns).astype(np.int64)
+    keep = (ms < M) & (ns < N)
+    ms, ns = ms[keep], ns[keep]
     ref, ab = oracle.gemm_pairs("NT", M, N, K, a_or, b_or, ms, ns)
     mt, nt = torch.from_numpy(ms).cuda(), torch.from_numpy(ns).cuda()
     got = y[mt, nt].float().cpu().numpy()
