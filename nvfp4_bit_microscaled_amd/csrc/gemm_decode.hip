@@ -286,7 +286,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
 // walks K in 512-K chunks.  The weights are read the way HBM streams them
 // best: each copy instruction moves four whole 256-byte row pieces (1 KB,
 // contiguous per row) straight into LDS (buffer loads with the LDS flag),
-// two chunks ahead of use in a three-stage ring.  Each lane loads the 16-byte
+// two chunks ahead of use in a three-stage ring (the activations one chunk
+// ahead, in registers; a four-stage ring measured slower at every M).  Each
+// lane loads the 16-byte
 // piece that its LDS slot holds, so the row pieces land XOR-swizzled (piece p
 // of row r at position p ^ (r % 16)) and a fragment read's 16 lanes of one
 // lane group (16 rows, one piece) hit 16 different bank groups.  Inside a chunk the four waves split
@@ -304,18 +306,24 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
 constexpr int kDlKC = 512;                   // K per chunk
 constexpr int kDlCodes = 64 * 256;           // code bytes per stage (64 rows x 256 B)
 constexpr int kDlStage = kDlCodes + 64 * 32; // + 32 scale bytes per row
-constexpr int kDlRing = 3 * kDlStage;        // 55296 bytes
 constexpr int kDlStride = 64 + 4;            // LDS row pitch (floats) of the partial tiles
 
-__host__ __device__ constexpr int decode_lds_bytes(int rmax)
+// LDS of the kernel: the ring of nst stages, reused at the end for the
+// partial tiles
+__host__ __device__ constexpr int decode_lds_bytes(int rmax, int nst)
 {
-    return kDlRing > 4 * 16 * rmax * kDlStride * 4 ? kDlRing : 4 * 16 * rmax * kDlStride * 4;
+    return nst * kDlStage > 4 * 16 * rmax * kDlStride * 4 ? nst * kDlStage
+                                                          : 4 * 16 * rmax * kDlStride * 4;
 }
 
-template <int RMAX>
+// NST ring stages: chunk i + NST - 1 is copied while chunk i is computed, and
+// the activations of chunk i + NST - 2 are loaded then (NST - 1 register sets).
+template <int RMAX, int NST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_decode_lds(GemmParams p)
 {
+    static_assert(NST == 3 || NST == 4, "three or four ring stages");
+    constexpr int NA = NST - 1;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -381,8 +389,8 @@ void k_gemm_decode_lds(GemmParams p)
                 rs, (lds_void_t*)(base + kDlCodes + (16 * wave + 8 * h) * 32), 4, sof[h], kc / 16,
                 0, 0);
     };
-    u32x4 a0c[RMAX], a1c[RMAX];
-    uint32_t a0s[RMAX], a1s[RMAX];
+    u32x4 ac[NA][RMAX];
+    uint32_t as[NA][RMAX];
     auto load_a = [&](int i, u32x4 (&c)[RMAX], uint32_t (&sc)[RMAX]) {
         const bool live = i < nch;
         const __amdgpu_buffer_rsrc_t rc = live ? rac : none, rs = live ? ras : none;
@@ -434,48 +442,50 @@ void k_gemm_decode_lds(GemmParams p)
             }
         }
     };
-    // prologue: chunk 0, its activations, chunk 1; in iteration i the
-    // activations of chunk i + 1 are loaded before the copies of chunk i + 2,
-    // so at the top of every iteration the six copies of the next chunk are
-    // the only memory operations that may still be in flight
-    copy(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(0, a0c, a0s);
-    __builtin_amdgcn_sched_barrier(0);
-    copy(1, 1);
-    int st = 0;
+    // Issue order: copy(0), A(0), copy(1), A(1), ... (the activations of chunk
+    // j right after the copies of chunk j, before those of chunk j + 1): the
+    // prologue issues up to copy(NST - 2), iteration i then A(i + NST - 2) and
+    // copy(i + NST - 1).  At the top of iteration i, chunk i's copies and
+    // activations have landed once at most the later NST - 2 chunks' copies
+    // and NST - 3 chunks' activations (two loads per row tile) are in flight.
     // The scheduling barriers keep this order: the compiler would otherwise
     // sink the activation loads below the products and hoist the products'
-    // first dequantizations above the wait, which leaves the next chunk's
-    // copies behind loads the next iteration needs at once (in-order
-    // counters), so each iteration would wait for the copies of two chunks on.
-    for (int i = 0; i < nch; i += 2) {
-        // chunk i's copies (this wave's) and activations have landed; after
-        // the barrier every wave's have, and stage (i + 2) % 3 (read in
-        // iteration i - 1) is free
+    // first dequantizations above the wait, leaving the next chunk's copies
+    // behind loads an iteration needs at once (in-order counters).
+    constexpr int kInFlight = 6 * (NST - 2) + 2 * RMAX * (NST - 3);
+#pragma unroll
+    for (int j = 0; j <= NST - 2; ++j) {
+        copy(j, j);
         __builtin_amdgcn_sched_barrier(0);
-        NVFP4_WAIT_VMCNT(6);
-        NVFP4_WAIT_LGKMCNT0();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        load_a(i + 1, a1c, a1s);
-        __builtin_amdgcn_sched_barrier(0);
-        copy(i + 2, st == 0 ? 2 : st - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(st, a0c, a0s);
-        st = st == 2 ? 0 : st + 1;
-        if (i + 1 >= nch) break;
-        __builtin_amdgcn_sched_barrier(0);
-        NVFP4_WAIT_VMCNT(6);
-        NVFP4_WAIT_LGKMCNT0();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        load_a(i + 2, a0c, a0s);
-        __builtin_amdgcn_sched_barrier(0);
-        copy(i + 3, st == 0 ? 2 : st - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(st, a1c, a1s);
-        st = st == 2 ? 0 : st + 1;
+        if (j <= NST - 3) {
+            load_a(j, ac[j], as[j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    int st = 0;
+    // NA iterations per trip, so every activation set index is a constant
+    // (chunk i computes with set i % NA and loads chunk i + NA - 1's into set
+    // (i + NA - 1) % NA, the one chunk i - 1 used): no register copies
+    for (int i0 = 0; i0 < nch; i0 += NA) {
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int i = i0 + u;
+            if (i >= nch) break;
+            // after the barrier every wave's copies of chunk i have landed,
+            // and the stage of chunk i - 1 (read in the previous iteration)
+            // is free
+            __builtin_amdgcn_sched_barrier(0);
+            NVFP4_WAIT_VMCNT(kInFlight);
+            NVFP4_WAIT_LGKMCNT0();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            load_a(i + NST - 2, ac[(u + NA - 1) % NA], as[(u + NA - 1) % NA]);
+            __builtin_amdgcn_sched_barrier(0);
+            copy(i + NST - 1, st == 0 ? NST - 1 : st - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st, ac[u], as[u]);
+            st = st == NST - 1 ? 0 : st + 1;
+        }
     }
     // every wave is done with the ring (and the copies past the end, which
     // write zeros into it, have landed) before it holds the partial tiles:
@@ -524,16 +534,16 @@ hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s)
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
     }
-#define NVFP4_DECODE_LDS(RMAX)                                                                 \
+#define NVFP4_DECODE_LDS(RMAX, NST)                                                            \
     {                                                                                          \
-        auto kern = k_gemm_decode_lds<RMAX>;                                                   \
-        const int lds = decode_lds_bytes(RMAX);                                                \
+        auto kern = k_gemm_decode_lds<RMAX, NST>;                                              \
+        const int lds = decode_lds_bytes(RMAX, NST);                                           \
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
     }
-    if (p.M <= 16) NVFP4_DECODE_LDS(1)
-    else if (p.M <= 32) NVFP4_DECODE_LDS(2)
-    else NVFP4_DECODE_LDS(4)
+    if (p.M <= 16) NVFP4_DECODE_LDS(1, 3)
+    else if (p.M <= 32) NVFP4_DECODE_LDS(2, 3)
+    else NVFP4_DECODE_LDS(4, 3)
 #undef NVFP4_SKINNY
 #undef NVFP4_DECODE_LDS
     return hipGetLastError();
