@@ -658,7 +658,28 @@ def mxfp4_bench(torch, nv, X, W):
     t_mx = timed(lambda: nv.mx_gemm(xm, wm, out=y))
     xn, wn = nv.quantize(X), nv.quantize(W, block2d=True)
     t_nv = timed(lambda: nv.gemm("NT", xn, wn, out=y))
-    del y
+    # NVFP4 operands whose block scales are powers of two, equal across each
+    # 32-K pair (random codes; A 1x16, W 16x16): nvfp4_gemm_native takes the
+    # native scaled FP4 MFMA for them (check, E8M0 planes and GEMM timed
+    # together), against nvfp4_gemm's FP16 path on the same operands
+    g = torch.Generator(device="cuda").manual_seed(12)
+    pow2 = torch.tensor([e << 3 for e in range(5, 12)], dtype=torch.uint8, device="cuda")
+
+    def pow2_operand(rows, block2d):
+        codes = torch.randint(0, 256, (rows, D // 2), dtype=torch.uint8, device="cuda",
+                              generator=g)
+        srows = rows // 16 if block2d else rows
+        idx = torch.randint(0, len(pow2), (srows, D // 32), device="cuda", generator=g)
+        scales = pow2[idx].repeat_interleave(2, dim=1).contiguous()
+        return nv.NVFP4Tensor(codes, scales, torch.ones(1, device="cuda"),
+                              torch.zeros(1, device="cuda"), rows, D, block2d, 1)
+
+    xp, wp = pow2_operand(T, False), pow2_operand(N, True)
+    used = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t_native = timed(lambda: nv.gemm_native(xp, wp, out=y, used_native=used))
+    native_used = int(used.item())
+    t_fp16 = timed(lambda: nv.gemm("NT", xp, wp, out=y))
+    del y, xp, wp
     fl = 2.0 * T * N * D
     xf = X.float()
     mse_mx = ((nv.mx_dequantize(xm, torch.float32) - xf) ** 2).mean().item()
@@ -670,6 +691,13 @@ def mxfp4_bench(torch, nv, X, W):
             "mx_frac_of_fp4_peak": round(fl / t_mx / 1e9 / MFMA_FP4_PEAK_TFLOPS, 4),
             "nvfp4_gemm_ms": round(t_nv, 4), "nvfp4_gemm_tflops": round(fl / t_nv / 1e9, 1),
             "mx_quantize_GBps": round(qb / (t_q * 1e-3) / 1e9, 1),
+            "nvfp4_native_pow2_scales": {
+                "call": "nvfp4_gemm_native on NVFP4 operands with power-of-two block scales "
+                        "(check + E8M0 planes + k_gemm_mx)",
+                "used_native": native_used, "ms": round(t_native, 4),
+                "tflops": round(fl / t_native / 1e9, 1),
+                "fp16_path_ms": round(t_fp16, 4),
+                "fp16_path_tflops": round(fl / t_fp16 / 1e9, 1)},
             "mse_on_X": {"mxfp4": mse_mx, "nvfp4": mse_nv,
                          "nvfp4_less_error": round(1 - mse_nv / mse_mx, 4)}}
 

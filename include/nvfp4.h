@@ -369,6 +369,45 @@ nvfp4_status nvfp4_gemm_swiglu(int64_t M, int64_t N, int64_t K, const uint8_t* a
                                void* stream);
 
 /*
+ * NVFP4 GEMM on the native scaled FP4 matrix instruction, where that is
+ * exact.  The pages note that CDNA 4's matrix cores support FP4 natively
+ * (guiahardware.es, "NVFP4: cos'e e come supera FP8 e BF16", section "Roadmap
+ * e disponibilita").  That instruction multiplies each 32 K-consecutive E2M1
+ * codes of an operand row by one power of two (E8M0), while NVFP4 scales
+ * each 16 with an E4M3 value.  The two agree exactly on a row's 32-K block
+ * when each of its two 16-element scales is a power of two or is zero over
+ * all-zero codes, and the non-zero ones are equal: then every element's
+ * value q * e * s_g is code * 2^k * s_g with one k per 32, and s_A * s_B
+ * goes to the epilogue.  Real tensors' E4M3 scales are rarely like that, so
+ * this is a path for data that is (for instance quantized with power-of-two
+ * block scales), not a replacement for nvfp4_gemm.
+ *
+ * nvfp4_gemm_native: C[M, N] = s_A s_B sum_k (q e)_A (q e)_B, NT (A [M, K],
+ *   B [N, K], both with blocks along K, 1D or 2D), FP32 accumulation, BF16
+ *   (RNE) or FP32 out.  The call checks every 32-K block of both operands on
+ *   the device, writes the E8M0 planes into the workspace, and runs the
+ *   native kernel when every block passes, else the FP16 kernel of
+ *   nvfp4_gemm (both are launched; each exits at once unless chosen).  The
+ *   result is that of nvfp4_gemm either way, to the same tolerance.
+ *   *used_native (device int32, caller-owned) ends as 1 when the native path
+ *   ran, 0 otherwise; calls that overlap on one stream must not share it.
+ *   Shape rules: K % 128 == 0; K <= 32768 (one FP32 accumulation chain);
+ *   2D operands need their rows % 16 == 0; ldc >= N; operand planes and the
+ *   workspace 16-byte aligned, used_native 4-byte aligned, c element-aligned.
+ *   K == 0 writes zeros and leaves *used_native unchanged.
+ * nvfp4_gemm_native_workspace_size: the E8M0 planes, M * K/32 (rounded up to
+ *   16) + N * K/32 bytes.
+ */
+size_t nvfp4_gemm_native_workspace_size(int64_t M, int64_t N, int64_t K);
+nvfp4_status nvfp4_gemm_native(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                               const uint8_t* a_scales, const float* a_tensor_scale,
+                               nvfp4_block a_block, const uint8_t* b_codes,
+                               const uint8_t* b_scales, const float* b_tensor_scale,
+                               nvfp4_block b_block, nvfp4_dtype out_dtype, void* c, int64_t ldc,
+                               int32_t* used_native, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * MXFP4, the power-of-two-scaled format the pages compare NVFP4 with
  * ("NVFP4: cos'e e come supera FP8 e BF16", guiahardware.es, section "Cos'e
  * NVFP4": NVFP4's E4M3 scales against power-of-two scaling such as MXFP4;

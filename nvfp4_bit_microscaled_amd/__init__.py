@@ -38,7 +38,8 @@ EXPORTS = ("nvfp4_version", "nvfp4_status_string", "nvfp4_quantize_workspace_siz
            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize",
            "nvfp4_mx_gemm", "nvfp4_gemm_w4a16", "nvfp4_kv_cache_write",
            "nvfp4_kv_cache_read", "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu",
-           "nvfp4_transpose", "nvfp4_quantize_noalloc", "nvfp4_gemm_workspace_size")
+           "nvfp4_transpose", "nvfp4_quantize_noalloc", "nvfp4_gemm_workspace_size",
+           "nvfp4_gemm_native_workspace_size", "nvfp4_gemm_native")
 
 
 class NVFP4Error(RuntimeError):
@@ -83,6 +84,11 @@ def _load():
                              ctypes.c_size_t, vp]
     L.nvfp4_gemm_workspace_size.restype = ctypes.c_size_t
     L.nvfp4_gemm_workspace_size.argtypes = [ci, i64, i64, i64]
+    L.nvfp4_gemm_native_workspace_size.restype = ctypes.c_size_t
+    L.nvfp4_gemm_native_workspace_size.argtypes = [i64, i64, i64]
+    L.nvfp4_gemm_native.restype = ci
+    L.nvfp4_gemm_native.argtypes = [i64, i64, i64, vp, vp, vp, ci, vp, vp, vp, ci, ci, vp, i64, vp,
+                                    vp, ctypes.c_size_t, vp]
     L.nvfp4_gemm_w4a16.restype = ci
     L.nvfp4_gemm_w4a16.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, ci, ci, vp, i64, vp]
     L.nvfp4_mx_quantize.restype = ci
@@ -197,6 +203,19 @@ def nvfp4_gemm(layout, M, N, K, a_codes, a_scales, a_tensor_scale, a_block, b_co
     return lib.nvfp4_gemm(layout, M, N, K, _p(a_codes), _p(a_scales), _p(a_tensor_scale), a_block,
                           _p(b_codes), _p(b_scales), _p(b_tensor_scale), b_block, out_dtype,
                           _p(c), ldc, _p(workspace), workspace_bytes, _stream(stream))
+
+
+def nvfp4_gemm_native_workspace_size(M, N, K) -> int:
+    return lib.nvfp4_gemm_native_workspace_size(M, N, K)
+
+
+def nvfp4_gemm_native(M, N, K, a_codes, a_scales, a_tensor_scale, a_block, b_codes, b_scales,
+                      b_tensor_scale, b_block, out_dtype, c, ldc, used_native, workspace=None,
+                      workspace_bytes=0, stream=None) -> int:
+    return lib.nvfp4_gemm_native(M, N, K, _p(a_codes), _p(a_scales), _p(a_tensor_scale), a_block,
+                                 _p(b_codes), _p(b_scales), _p(b_tensor_scale), b_block,
+                                 out_dtype, _p(c), ldc, _p(used_native), _p(workspace),
+                                 workspace_bytes, _stream(stream))
 
 
 def nvfp4_gemm_w4a16(M, N, K, a, lda, b_codes, b_scales, b_tensor_scale, b_block, out_dtype, c,
@@ -444,6 +463,43 @@ def gemm(layout: str, a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16,
         BLOCK_2D if b.block2d else BLOCK_1D, _dtype_code(out), out, out.stride(0), ws,
         0 if ws is None else ws.numel()))
     return out
+
+
+def gemm_native(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16,
+                out: torch.Tensor | None = None, used_native: torch.Tensor | None = None):
+    """NT GEMM (a [M, K], b [N, K], blocks along K) on the native scaled FP4
+    instruction when every 32-K block of both operands maps onto one
+    power-of-two scale exactly, else on the FP16 path.  Returns (out,
+    used_native): an int32 device tensor holding 1 or 0 for the path taken."""
+    M, K = a.rows, a.cols
+    N, Kb = b.rows, b.cols
+    if Kb != K:
+        raise ValueError("gemm_native: A has K = %d but B has K = %d" % (K, Kb))
+    for name, op in (("A", a), ("B", b)):
+        if not op.block2d and op.axis != 1:
+            raise ValueError("gemm_native: operand %s has 1D blocks along rows, not along K" % name)
+        if tuple(op.codes.shape) != (op.rows, op.cols // 2) or not op.codes.is_contiguous():
+            raise ValueError("gemm_native: operand %s codes are not a dense plane" % name)
+        if tuple(op.scales.shape) != scale_shape(op.rows, op.cols, op.block2d, op.axis) \
+                or not op.scales.is_contiguous():
+            raise ValueError("gemm_native: operand %s scales do not match its block layout" % name)
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=a.codes.device)
+    if tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise ValueError("gemm_native: out must be [%d, %d] with unit column stride" % (M, N))
+    if used_native is None:
+        used_native = torch.zeros(1, dtype=torch.int32, device=out.device)
+    nws = nvfp4_gemm_native_workspace_size(M, N, K)
+    key = ("gemm_native", str(out.device), torch.cuda.current_stream(out.device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < max(nws, 16):
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=out.device)
+        _workspaces[key] = ws
+    _check("nvfp4_gemm_native", nvfp4_gemm_native(
+        M, N, K, a.codes, a.scales, a.tensor_scale, BLOCK_2D if a.block2d else BLOCK_1D,
+        b.codes, b.scales, b.tensor_scale, BLOCK_2D if b.block2d else BLOCK_1D,
+        _dtype_code(out), out, out.stride(0), used_native, ws, ws.numel()))
+    return out, used_native
 
 
 def interleave_gate_up(w: torch.Tensor) -> torch.Tensor:

@@ -431,6 +431,50 @@ nvfp4_status nvfp4_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_cod
                                    out_dtype == NVFP4_DTYPE_BF16, c, ldc, s));
 }
 
+size_t nvfp4_gemm_native_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || K % 128) return 0;
+    return gemm_native_bytes(M, N, K);
+}
+
+nvfp4_status nvfp4_gemm_native(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                               const uint8_t* a_scales, const float* a_tensor_scale,
+                               nvfp4_block a_block, const uint8_t* b_codes,
+                               const uint8_t* b_scales, const float* b_tensor_scale,
+                               nvfp4_block b_block, nvfp4_dtype out_dtype, void* c, int64_t ldc,
+                               int32_t* used_native, void* workspace, size_t workspace_bytes,
+                               void* stream)
+{
+    if (a_block != NVFP4_BLOCK_1D && a_block != NVFP4_BLOCK_2D) return NVFP4_ERR_INVALID_ARG;
+    if (b_block != NVFP4_BLOCK_1D && b_block != NVFP4_BLOCK_2D) return NVFP4_ERR_INVALID_ARG;
+    if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_FP32) return NVFP4_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_INVALID_ARG;
+    if (ldc < N) return NVFP4_ERR_SHAPE;
+    if (K % 128) return NVFP4_ERR_SHAPE;
+    if (a_block == NVFP4_BLOCK_2D && M % 16) return NVFP4_ERR_LAYOUT;
+    if (b_block == NVFP4_BLOCK_2D && N % 16) return NVFP4_ERR_LAYOUT;
+    if ((uint64_t)K / 2 * 256 >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
+    if (K > kMaxChainK) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return NVFP4_OK;
+    if (!c) return NVFP4_ERR_INVALID_ARG;
+    const size_t esz = out_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+    if ((reinterpret_cast<uintptr_t>(c) & (esz - 1)) != 0) return NVFP4_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) return from_hip(launch_fill_zero(c, out_dtype == NVFP4_DTYPE_BF16, M, N, ldc, s));
+    if (!a_codes || !a_scales || !a_tensor_scale || !b_codes || !b_scales || !b_tensor_scale ||
+        !used_native)
+        return NVFP4_ERR_INVALID_ARG;
+    if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) || !aligned16(b_scales))
+        return NVFP4_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(used_native) & 3u) != 0) return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < gemm_native_bytes(M, N, K)) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    GemmOperand A{a_codes, a_scales, a_tensor_scale, a_block == NVFP4_BLOCK_2D, true};
+    GemmOperand B{b_codes, b_scales, b_tensor_scale, b_block == NVFP4_BLOCK_2D, true};
+    return from_hip(launch_gemm_native(M, N, K, A, B, out_dtype == NVFP4_DTYPE_BF16, c, ldc,
+                                       used_native, static_cast<uint8_t*>(workspace), s));
+}
+
 nvfp4_status nvfp4_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
                               const uint8_t* b_codes, const uint8_t* b_scales,
                               const float* b_tensor_scale, nvfp4_block b_block,

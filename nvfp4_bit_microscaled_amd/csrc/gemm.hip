@@ -806,6 +806,7 @@ constexpr int kKKEpiAny = 0, kKKEpiBF16 = 1, kKKEpiF32 = 2;
 template <bool kSwiGLU, int kEpi = kKKEpiAny, bool kSplit = false>
 __global__ __launch_bounds__(256) void k_gemm_kk(GemmParams p)
 {
+    if (p.gate != nullptr && *p.gate != p.gate_want) return;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const uint32_t nbm = (uint32_t)((p.M + kTM - 1) / kTM), nbn = (uint32_t)((p.N + kTN - 1) / kTN);
     uint32_t tm, tn;
@@ -1156,7 +1157,8 @@ __global__ __launch_bounds__(256) void k_sum_tail_tiles(const float* h0, const f
 // One GEMM launch over K (<= kp: a K slice when kp > K).
 static hipError_t launch_gemm_one(int64_t M, int64_t N, int64_t K, int64_t kp,
                                   const GemmOperand& A, const GemmOperand& B, bool out_bf16,
-                                  void* c, int64_t ldc, hipStream_t s, float* split_ws = nullptr)
+                                  void* c, int64_t ldc, hipStream_t s, float* split_ws = nullptr,
+                                  const int32_t* gate = nullptr)
 {
     GemmParams p{};
     p.M = M; p.N = N; p.K = K; p.kp = kp;
@@ -1171,8 +1173,13 @@ static hipError_t launch_gemm_one(int64_t M, int64_t N, int64_t K, int64_t kp,
     const int esz = out_bf16 ? 2 : 4;
     p.vec_out = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(c) % (4 * esz) == 0;
     p.vec16 = (ldc * esz) % 16 == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0;
+    // gated (the FP16 path beside the native FP4 one): the 256 x 256 kernel
+    // alone, every tile in one launch, run only when *gate == 0
+    p.gate = gate;
+    p.gate_want = 0;
+    if (gate != nullptr) split_ws = nullptr;
     // decode-style shapes (M <= 64): the weight-streaming kernels
-    if (A.k_major && B.k_major && kp == K && gemm_decode_shape(M, N, K))
+    if (gate == nullptr && A.k_major && B.k_major && kp == K && gemm_decode_shape(M, N, K))
         return launch_gemm_decode(p, s);
     if (A.k_major && B.k_major && K % kTK == 0 && kp / 2 * kTM < (1ll << 31)) {
         const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
@@ -1420,6 +1427,7 @@ __device__ __forceinline__ void mx_copy(const MxOperand& o, int kt, uint8_t* dst
 template <int kEpi>
 __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p)
 {
+    if (p.gate != nullptr && *p.gate != p.gate_want) return;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const uint32_t nbm = (uint32_t)((p.M + kTM - 1) / kTM), nbn = (uint32_t)((p.N + kTN - 1) / kTN);
     uint32_t tm, tn;
@@ -1504,23 +1512,25 @@ __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p)
                 }
         }
     }
+    // MXFP4 has no tensor scale; the native NVFP4 path passes s_A and s_B
+    const float sab = p.a_ts != nullptr ? (*p.a_ts) * (*p.b_ts) : 1.0f;
     if constexpr (kEpi != kKKEpiAny) {
         NVFP4_WAIT_VMCNT(0);
         NVFP4_WAIT_LGKMCNT0();
         __builtin_amdgcn_s_barrier();
-        store_tile_lds<kEpi == kKKEpiBF16>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f, lds);
+        store_tile_lds<kEpi == kKKEpiBF16>(p, acc, m0, n0, wm, wn, lr, lk, sab, lds);
     } else if (m0 + kTM <= p.M && n0 + kTN <= p.N) {
         if (p.vec16) {
             NVFP4_WAIT_VMCNT(0);
             NVFP4_WAIT_LGKMCNT0();
             __builtin_amdgcn_s_barrier();
-            if (p.out_bf16) store_tile_lds<true>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f, lds);
-            else store_tile_lds<false>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f, lds);
+            if (p.out_bf16) store_tile_lds<true>(p, acc, m0, n0, wm, wn, lr, lk, sab, lds);
+            else store_tile_lds<false>(p, acc, m0, n0, wm, wn, lr, lk, sab, lds);
         } else {
-            store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f);
+            store_tile<true>(p, acc, m0, n0, wm, wn, lr, lk, sab);
         }
     } else {
-        store_tile<false>(p, acc, m0, n0, wm, wn, lr, lk, 1.0f);
+        store_tile<false>(p, acc, m0, n0, wm, wn, lr, lk, sab);
     }
 }
 
@@ -1548,6 +1558,114 @@ hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_code
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
     hipLaunchKernelGGL(kern, dim3((unsigned)t), dim3(256), kMxLds, s, p);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 on the native scaled FP4 MFMA, where that is exact.  The instruction
+// multiplies each 32 K-consecutive E2M1 codes of an operand row by one power
+// of two (an E8M0 byte).  An NVFP4 row maps onto it exactly when, in every
+// 32-K block, each of its two 16-element E4M3 scales is a power of two or is
+// zero over all-zero codes (a zero block contributes nothing under any
+// scale), and the non-zero ones are equal; s_A s_B then goes to the
+// epilogue.  k_native_scales checks that for one operand and writes the E8M0
+// plane [rows, K/32] the MXFP4 kernel reads; any block that fails clears
+// *gate, and the FP16 path runs instead (both are launched, each gated).
+// ---------------------------------------------------------------------------
+
+__global__ void k_set_gate(int32_t* gate)
+{
+    if (threadIdx.x == 0) *gate = 1;
+}
+
+// E8M0 byte of an E4M3 scale byte that is a power of two, else -1 (0 maps
+// to -2: zero).  E4M3 normals 2^(E-7) (mantissa 0), subnormals m 2^-9 with
+// m in {1, 2, 4}; E8M0 u encodes 2^(u-127).
+__device__ __forceinline__ int e8m0_of_pow2_e4m3(uint32_t s)
+{
+    if (s == 0) return -2;
+    const uint32_t e = s >> 3, m = s & 7u;
+    if (e != 0) return m == 0 ? (int)(e + 120) : -1;
+    return m == 1 ? 118 : (m == 2 ? 119 : (m == 4 ? 120 : -1));
+}
+
+// One thread per (row, 32-K block).  scales: 1D [rows, K/16] or 2D
+// [rows/16, K/16]; codes [rows, K/2].
+__global__ __launch_bounds__(256) void k_native_scales(const uint8_t* scales, const uint8_t* codes,
+                                                       int64_t rows, int64_t K, bool two_d,
+                                                       uint8_t* e8, int32_t* gate)
+{
+    const int64_t nb = K / 32;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * nb) return;
+    const int64_t row = idx / nb, j = idx % nb;
+    const int64_t srow = two_d ? row / 16 : row;
+    const uint8_t* sp = scales + srow * (K / 16) + 2 * j;
+    int u[2];
+    bool ok = true;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        u[h] = e8m0_of_pow2_e4m3(sp[h]);
+        if (u[h] == -1) ok = false;
+        if (u[h] == -2) {  // zero scale: exact only over all-zero codes
+            const uint32_t* cp =
+                reinterpret_cast<const uint32_t*>(codes + row * (K / 2) + (2 * j + h) * 8);
+            if ((cp[0] | cp[1]) != 0u) ok = false;
+        }
+    }
+    int out = 127;
+    if (ok) {
+        if (u[0] >= 0 && u[1] >= 0) {
+            if (u[0] != u[1]) ok = false;
+            out = u[0];
+        } else if (u[0] >= 0) {
+            out = u[0];
+        } else if (u[1] >= 0) {
+            out = u[1];
+        }
+    }
+    e8[idx] = (uint8_t)out;
+    if (!ok) *gate = 0;
+}
+
+size_t gemm_native_bytes(int64_t M, int64_t N, int64_t K)
+{
+    const size_t a = ((size_t)M * (size_t)(K / 32) + 15) & ~(size_t)15;
+    return a + (size_t)N * (size_t)(K / 32);
+}
+
+hipError_t launch_gemm_native(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
+                              const GemmOperand& B, bool out_bf16, void* c, int64_t ldc,
+                              int32_t* gate, uint8_t* ws, hipStream_t s)
+{
+    uint8_t* e8a = ws;
+    uint8_t* e8b = ws + (((size_t)M * (size_t)(K / 32) + 15) & ~(size_t)15);
+    hipLaunchKernelGGL(k_set_gate, dim3(1), dim3(64), 0, s, gate);
+    const int64_t na = M * (K / 32), nbb = N * (K / 32);
+    hipLaunchKernelGGL(k_native_scales, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, s,
+                       A.scales, A.codes, M, K, A.block2d != 0, e8a, gate);
+    hipLaunchKernelGGL(k_native_scales, dim3((unsigned)((nbb + 255) / 256)), dim3(256), 0, s,
+                       B.scales, B.codes, N, K, B.block2d != 0, e8b, gate);
+    // the native kernel (runs when every block passed)
+    GemmParams p{};
+    p.M = M; p.N = N; p.K = K; p.kp = K;
+    p.a_codes = A.codes; p.a_scales = e8a; p.a_ts = A.ts;
+    p.b_codes = B.codes; p.b_scales = e8b; p.b_ts = B.ts;
+    p.c = static_cast<uint8_t*>(c);
+    p.ldc = ldc;
+    p.out_bf16 = out_bf16;
+    const int esz = out_bf16 ? 2 : 4;
+    p.vec_out = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(c) % (4 * esz) == 0;
+    p.vec16 = (ldc * esz) % 16 == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0;
+    p.gate = gate;
+    p.gate_want = 1;
+    const uint64_t t = (uint64_t)((M + kTM - 1) / kTM) * (uint64_t)((N + kTN - 1) / kTN);
+    const bool all_full = M % kTM == 0 && N % kTN == 0 && p.vec16;
+    auto kern = !all_full ? k_gemm_mx<kKKEpiAny>
+                          : (out_bf16 ? k_gemm_mx<kKKEpiBF16> : k_gemm_mx<kKKEpiF32>);
+    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+    hipLaunchKernelGGL(kern, dim3((unsigned)t), dim3(256), kMxLds, s, p);
+    // the FP16 path (runs when a block failed)
+    return launch_gemm_one(M, N, K, K, A, B, out_bf16, c, ldc, s, nullptr, gate);
 }
 
 }  // namespace nvfp4

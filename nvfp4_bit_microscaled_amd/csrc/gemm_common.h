@@ -49,6 +49,10 @@ struct GemmParams {
     // kp the whole K) and writes the FP32 partial to c (half 0) or c2 (half 1)
     uint32_t tile_base;
     uint8_t* c2;
+    // k_gemm_kk and k_gemm_mx: when gate is set, the kernel runs only if
+    // *gate == gate_want (device-side choice between two launched paths)
+    const int32_t* gate;
+    int32_t gate_want;
 };
 
 // LDS pointer type of the buffer-load-to-LDS builtin

@@ -106,6 +106,16 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
                        const GemmOperand& B, bool out_bf16, void* c, int64_t ldc, float* ws,
                        hipStream_t s);
 
+// NVFP4 GEMM (NT, both K-major, K % 128 == 0, K <= kMaxChainK) on the native
+// scaled FP4 MFMA when every 32-K block of both operands maps onto one
+// power-of-two scale exactly, else on the FP16 path; *gate (device) ends as 1
+// or 0 for the path taken.  ws: gemm_native_bytes(M, N, K) bytes of E8M0
+// planes (16-byte aligned).
+size_t gemm_native_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_native(int64_t M, int64_t N, int64_t K, const GemmOperand& A,
+                              const GemmOperand& B, bool out_bf16, void* c, int64_t ldc,
+                              int32_t* gate, uint8_t* ws, hipStream_t s);
+
 // MXFP4 (E2M1 elements, E8M0 scale per 32 along the row): codes
 // [rows, cols/2], scales [rows, cols/32]; cols % 32 == 0.
 hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld,

@@ -37,7 +37,8 @@ def test_header_declares_the_abi():
                             "nvfp4_kv_cache_write", "nvfp4_kv_cache_read",
                             "nvfp4_gemm_swiglu_workspace_size", "nvfp4_gemm_swiglu",
                             "nvfp4_transpose", "nvfp4_quantize_noalloc",
-                            "nvfp4_gemm_workspace_size"])
+                            "nvfp4_gemm_workspace_size", "nvfp4_gemm_native_workspace_size",
+                            "nvfp4_gemm_native"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -209,6 +210,37 @@ def test_mx_validation(lib):
     assert mxg(lib, K=1 << 24) == 5                  # 256 rows of codes past 2^31 bytes
     assert mxg(lib, K=32896) == 5                    # longer than one accumulation chain
     assert mxg(lib, M=0) == 0
+
+
+def ng(lib, **kw):
+    args = dict(M=64, N=64, K=256, ac=FAKE, asc=FAKE, ats=FAKE, ab=0, bc=FAKE, bsc=FAKE, bts=FAKE,
+                bb=0, odt=0, c=FAKE, ldc=64, used=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    args.update(kw)
+    return lib.nvfp4_gemm_native(*args.values())
+
+
+def test_gemm_native_validation(lib):
+    import nvfp4_bit_microscaled_amd as m
+    # E8M0 planes: M x K/32 (rounded up to 16 bytes) + N x K/32
+    assert m.nvfp4_gemm_native_workspace_size(64, 64, 256) == 64 * 8 + 64 * 8
+    assert m.nvfp4_gemm_native_workspace_size(5, 7, 128) == 32 + 28
+    assert m.nvfp4_gemm_native_workspace_size(5, 7, 100) == 0
+    assert ng(lib, ab=2) == 1
+    assert ng(lib, odt=5) == 1
+    assert ng(lib, N=-1) == 1
+    assert ng(lib, K=192) == 2                       # K % 128
+    assert ng(lib, ldc=32) == 2
+    assert ng(lib, ab=1, M=40) == 4                  # 2D operand with M % 16
+    assert ng(lib, K=32896) == 5                     # longer than one accumulation chain
+    assert ng(lib, c=ODD) == 3
+    assert ng(lib, used=None) == 1
+    assert ng(lib, ats=None) == 1
+    assert ng(lib, bsc=MISALIGNED) == 3
+    assert ng(lib, used=ODD) == 3
+    assert ng(lib, ws=None) == 6
+    assert ng(lib, wsb=64 * 8 + 64 * 8 - 1) == 6
+    assert ng(lib, ws=MISALIGNED) == 3
+    assert ng(lib, M=0) == 0
 
 
 def w4(lib, **kw):
