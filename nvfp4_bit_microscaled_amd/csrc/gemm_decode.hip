@@ -9,32 +9,30 @@
 namespace nvfp4 {
 
 // ---------------------------------------------------------------------------
-// Skinny NT kernel for decode-style shapes (M <= 64, K a multiple of the K
-// chunk KC = 512): C[M, N] = A[M, K]
-// B[N, K]^T.  The packed weights B dominate the traffic (4.5 bits per element)
-// and are streamed once: each wave owns 16 rows of B (16 output columns) over
-// all of K.  Inside a chunk, lane group g = lane / 16 owns the contiguous K
-// quarter g KC/4 .. +KC/4 (one 16-byte code load per 128 K, and its scale
-// bytes for the whole chunk in one or two wide loads: the load path is
-// limited by accesses per lane, so 2-byte scale loads per step would cost as
-// much as the codes).  The few activation rows are dequantized once per
-// workgroup into LDS as FP16, one chunk at a time, in the same lane-quarter
-// order (16 bytes of padding per quarter keep the quarters on different
-// banks).  Both operands are prefetched into registers one chunk ahead,
-// issued after everything the current chunk waits for (vector-memory
-// counters drain in order).  Short chunks stream best: with 2048 or 1024
-// the same weights took 15-25% longer (more bytes in flight per wave, in
-// larger bursts).  Rows past M or N are clamped to the last valid
-// row (never stored).  v_mfma_f32_16x16x32_f16: at step s lane (row l % 16,
-// group g) supplies k = kc + g KC/4 + 32 st + 8 s + [0, 8) for both operands.
+// Weight-only decode GEMM (BF16 activations x NVFP4 weights, M <= 64, K a
+// multiple of the K chunk KC = 512): C[M, N] = A[M, K] B[N, K]^T.  The packed
+// weights B dominate the traffic (4.5 bits per element) and are streamed
+// once: each wave owns 16 rows of B (16 output columns) over all of K.  Inside
+// a chunk, lane group g = lane / 16 owns the contiguous K quarter g KC/4 ..
+// +KC/4 (one 16-byte code load per 128 K, and its scale bytes for the whole
+// chunk in one or two wide loads: the load path is limited by accesses per
+// lane, so 2-byte scale loads per step would cost as much as the codes).  The
+// few activation rows are copied into LDS as they are (32-element BF16
+// pieces, no activation scales), one chunk at a time, in the same
+// lane-quarter order (16 bytes of padding per quarter keep the quarters on
+// different banks).  Both operands are prefetched into registers one chunk
+// ahead, issued after everything the current chunk waits for (vector-memory
+// counters drain in order).  Short chunks stream best: with 2048 or 1024 the
+// same weights took 15-25% longer (more bytes in flight per wave, in larger
+// bursts).  Each weight word is dequantized to BF16 exactly for
+// v_mfma_f32_16x16x32_bf16: at step s lane (row l % 16, group g) supplies
+// k = kc + g KC/4 + 32 st + 8 s + [0, 8) for both operands.  Rows past M or N
+// are clamped to the last valid row (never stored).
 // ---------------------------------------------------------------------------
 constexpr int kSkN = 64;  // output columns per workgroup
 
-// kA16: the weight-only variant, BF16 activations (no activation scales;
-// 32-element pieces copied to LDS as they are), weights dequantized to BF16
-// and v_mfma_f32_16x16x32_bf16.
-template <int KC, int RMAX, bool kA16>
-__global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
+template <int KC, int RMAX>
+__global__ __launch_bounds__(256) void k_gemm_w4a16(GemmParams p)
 {
     constexpr int kSteps = KC / 128;                 // B steps per chunk
     constexpr int kQ = KC / 4;                       // K of one lane quarter per chunk
@@ -98,9 +96,8 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
     // B: lane g owns the contiguous quarter kc + g KC/4 .. +KC/4 of each chunk,
     // 32 codes per step, so its scale bytes for the chunk are one contiguous
     // run of kSB bytes
-    u32x4 ac[kA16 ? 1 : kAPer], bc[kSteps], bn[kSteps];
-    uint32_t as[kA16 ? 1 : kAPer];
-    u32x4 aw[kA16 ? kAPer : 1][4];  // BF16 pieces (64 bytes each)
+    u32x4 bc[kSteps], bn[kSteps];
+    u32x4 aw[kAPer][4];  // BF16 pieces (64 bytes each)
     uint32_t bs[kSB / 4], bsn[kSB / 4];
     auto load_a = [&](int64_t kc) {
 #pragma unroll
@@ -110,16 +107,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
             int64_t mc = m < p.M ? m : p.M - 1;
             int64_t k = kc + 32 * c;
             k = k < K ? k : K - 32;  // the prefetch past the last chunk reads a valid piece
-            if constexpr (kA16) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(p.a_bf16 + mc * p.lda + k);
+            const u32x4* src = reinterpret_cast<const u32x4*>(p.a_bf16 + mc * p.lda + k);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) aw[i][q] = src[q];
-            } else {
-                ac[i] = *reinterpret_cast<const u32x4*>(p.a_codes + mc * (K / 2) + k / 2);
-                const uint8_t* sp =
-                    p.a_scales + (p.a2d ? (mc / 16) * lds_b : mc * lds_b) + k / 16;
-                as[i] = *reinterpret_cast<const uint16_t*>(sp);
-            }
+            for (int q = 0; q < 4; ++q) aw[i][q] = src[q];
         }
     };
     auto load_b = [&](__amdgpu_buffer_rsrc_t c_rsrc, __amdgpu_buffer_rsrc_t s_rsrc, int kc,
@@ -167,15 +157,8 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
             int m = idx / (KC / 32), c = idx % (KC / 32);
             const int kl = 32 * c;  // K offset inside the chunk
             uint8_t* dst = lds + m * kRow + (kl / kQ) * kQStride + (kl % kQ) * 2;
-            if constexpr (kA16) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(dst + 16 * q) = aw[i][q];
-            } else {
-                half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as[i], 1.0f, false);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<half8_t*>(dst + 16 * q) = dequant_word(ac[i][q], e2[q >> 1]);
-            }
+            for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(dst + 16 * q) = aw[i][q];
         }
         NVFP4_WAIT_LGKMCNT0();
         __builtin_amdgcn_s_barrier();
@@ -209,35 +192,24 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
         for (int st = 0; st < kSteps; ++st) {
             // the step's A fragments first (one LDS latency per step), then
             // its four B dequantizations and MFMAs
-            half8_t af[4][RMAX];
+            bf16x8_t af[4][RMAX];
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int r = 0; r < RMAX; ++r)
-                    af[s][r] = *reinterpret_cast<const half8_t*>(
+                    af[s][r] = *reinterpret_cast<const bf16x8_t*>(
                         lds + (16 * r + lr) * kRow + g * kQStride + (32 * st + 8 * s) * 2);
             // scale bytes 2 st, 2 st + 1 of the lane's run
             const uint32_t sw = cs[st >> 1] >> (16 * (st & 1));
-            if constexpr (kA16) {
-                const float e0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
-                const float e1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
+            const float e0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
+            const float e1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    bf16x8_t bf = dequant_word_bf16(cq[st][s], s < 2 ? e0 : e1);
+            for (int s = 0; s < 4; ++s) {
+                bf16x8_t bf = dequant_word_bf16(cq[st][s], s < 2 ? e0 : e1);
 #pragma unroll
-                    for (int r = 0; r < RMAX; ++r)
-                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, af[s][r]), bf, acc[r], 0, 0, 0);
-                }
-            } else {
-                half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    half8_t bf = dequant_word(cq[st][s], e2[s >> 1]);
-#pragma unroll
-                    for (int r = 0; r < RMAX; ++r)
-                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s][r], bf, acc[r], 0, 0, 0);
-                }
+                for (int r = 0; r < RMAX; ++r)
+                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        af[s][r], bf, acc[r], 0, 0, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x100, 4 * RMAX, 0);   // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);         // scale + B dequant
@@ -260,7 +232,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p)
         if (kc + 2 * KC >= (int)K) break;
     }
     // lane holds C[16 r + 4 g + j][n] in acc[r][j]
-    const float sab = kA16 ? *p.b_ts : (*p.a_ts) * (*p.b_ts);
+    const float sab = *p.b_ts;
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
 #pragma unroll
@@ -527,13 +499,6 @@ bool gemm_decode_shape(int64_t M, int64_t N, int64_t K)
 hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s)
 {
     dim3 g((unsigned)((p.N + kSkN - 1) / kSkN));
-#define NVFP4_SKINNY(KC, RMAX)                                                                 \
-    {                                                                                          \
-        auto kern = k_gemm_skinny<KC, RMAX, false>;                                            \
-        const int lds = RMAX * 16 * (KC * 2 + 64) + (RMAX == 1 ? 4 * 16 * (KC / 2 + 16) : 0);  \
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
-        hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
-    }
 #define NVFP4_DECODE_LDS(RMAX, NST)                                                            \
     {                                                                                          \
         auto kern = k_gemm_decode_lds<RMAX, NST>;                                              \
@@ -544,7 +509,6 @@ hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s)
     if (p.M <= 16) NVFP4_DECODE_LDS(1, 3)
     else if (p.M <= 32) NVFP4_DECODE_LDS(2, 3)
     else NVFP4_DECODE_LDS(4, 3)
-#undef NVFP4_SKINNY
 #undef NVFP4_DECODE_LDS
     return hipGetLastError();
 }
@@ -568,7 +532,7 @@ hipError_t launch_gemm_w4a16(int64_t M, int64_t N, int64_t K, const uint16_t* a,
     dim3 g((unsigned)((N + kSkN - 1) / kSkN));
 #define NVFP4_SKINNY16(RMAX)                                                                   \
     {                                                                                          \
-        auto kern = k_gemm_skinny<512, RMAX, true>;                                            \
+        auto kern = k_gemm_w4a16<512, RMAX>;                                            \
         const int lds = RMAX * 16 * (512 * 2 + 64) + (RMAX == 1 ? 4 * 16 * (512 / 2 + 16) : 0);\
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
