@@ -9,8 +9,9 @@
 namespace nvfp4 {
 
 // ---------------------------------------------------------------------------
-// Weight-only decode GEMM (BF16 activations x NVFP4 weights, M <= 64, K a
-// multiple of the K chunk KC = 512): C[M, N] = A[M, K] B[N, K]^T.  The packed
+// Weight-only decode GEMM for 17..64 rows (BF16 activations x NVFP4 weights,
+// K a multiple of the K chunk KC = 512): C[M, N] = A[M, K] B[N, K]^T.  (Up to
+// 16 rows the weight-streaming kernel below takes the weight-only GEMM too.)  The packed
 // weights B dominate the traffic (4.5 bits per element) and are streamed
 // once: each wave owns 16 rows of B (16 output columns) over all of K.  Inside
 // a chunk, lane group g = lane / 16 owns the contiguous K quarter g KC/4 ..
@@ -57,30 +58,8 @@ __global__ __launch_bounds__(256) void k_gemm_w4a16(GemmParams p)
         __builtin_amdgcn_make_buffer_rsrc((void*)p.b_scales, (short)0, 0x7FFFFFFF, 0x00020000);
     const __amdgpu_buffer_rsrc_t none =
         __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, (short)0, 0, 0x00020000);
-    // kLines (one activation row block): B codes in whole 128-byte lines.
-    // Load instruction (h, ln) of a chunk reads line ln of rows 8 h .. 8 h + 7
-    // of the wave's 16 (lane l: row 8 h + l / 8, bytes 16 (l % 8) of the
-    // line), and the bytes go through a wave-private LDS buffer into the
-    // fragment layout.  Measured on 28672 x 8192 weights this streams 6-11%
-    // faster for M <= 16 than loading the fragment layout directly (16 bytes
-    // from each of 64 lines per instruction); with more activation rows the
-    // extra LDS costs a workgroup per CU and loses.  Otherwise lane group g
-    // loads its quarter of the chunk directly, 16 bytes per step.
-    constexpr bool kLines = RMAX == 1;
-    static_assert(!kLines || KC == 512, "two 128-byte lines per row and chunk");
-    int bo[2];
-    if constexpr (kLines) {
-        const int64_t brow0 = (int64_t)blockIdx.x * kSkN + wave * 16;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            int64_t r = brow0 + 8 * h + (lane >> 3);
-            r = r < p.N ? r : p.N - 1;
-            bo[h] = (int)(r * (K / 2)) + 16 * (lane & 7);
-        }
-    } else {
-        bo[0] = bo[1] = (int)(nc * (K / 2)) + (kQ / 2) * g;
-    }
-    uint8_t* const bl = lds + RMAX * 16 * kRow + wave * 16 * (KC / 2 + 16);  // 16 rows x 272 B
+    // lane group g loads its quarter of the chunk directly, 16 bytes per step
+    const int bo = (int)(nc * (K / 2)) + (kQ / 2) * g;
     const int bso = (int)(p.b2d ? (nc / 16) * lds_b : nc * lds_b) + (kQ / 16) * g;
     // Workgroups walk K starting at different chunks: rows are K/2 bytes
     // apart, so if every workgroup read the same chunk at once, all reads
@@ -115,15 +94,9 @@ __global__ __launch_bounds__(256) void k_gemm_w4a16(GemmParams p)
     auto load_b = [&](__amdgpu_buffer_rsrc_t c_rsrc, __amdgpu_buffer_rsrc_t s_rsrc, int kc,
                       u32x4* c, uint32_t* sc) {
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) {  // kLines: st = 2 h + ln
-            if constexpr (kLines)
-                c[st] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, bo[st >> 1],
-                                                                 kc / 2 + 128 * (st & 1), 0));
-            else
-                c[st] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, bo[0] + 16 * st, kc / 2, 0));
-        }
+        for (int st = 0; st < kSteps; ++st)
+            c[st] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, bo + 16 * st, kc / 2, 0));
 #pragma unroll
         for (int q = 0; q < kSB / 4; q += (kSB >= 16 ? 4 : 2)) {
             if (kSB >= 16) {
@@ -171,23 +144,9 @@ __global__ __launch_bounds__(256) void k_gemm_w4a16(GemmParams p)
         __builtin_amdgcn_sched_barrier(0);
         load_b(more ? rc : none, more ? rs : none, more ? kpos(kc + KC) : 0, nb, ns);
         __builtin_amdgcn_sched_barrier(0);
-        // this chunk's weight lines into the wave's LDS buffer (row pitch 272
-        // bytes), then each lane takes 16 bytes of its row's quarter g per
-        // step: one wave's LDS accesses complete in order, so no barrier
         u32x4 cq[kSteps];
-        if constexpr (kLines) {
 #pragma unroll
-            for (int st = 0; st < kSteps; ++st)
-                *reinterpret_cast<u32x4*>(bl + (8 * (st >> 1) + (lane >> 3)) * (KC / 2 + 16) +
-                                          128 * (st & 1) + 16 * (lane & 7)) = cb[st];
-#pragma unroll
-            for (int st = 0; st < kSteps; ++st)
-                cq[st] = *reinterpret_cast<const u32x4*>(bl + lr * (KC / 2 + 16) + (kQ / 2) * g +
-                                                         16 * st);
-        } else {
-#pragma unroll
-            for (int st = 0; st < kSteps; ++st) cq[st] = cb[st];
-        }
+        for (int st = 0; st < kSteps; ++st) cq[st] = cb[st];
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) {
             // the step's A fragments first (one LDS latency per step), then
@@ -290,12 +249,18 @@ __host__ __device__ constexpr int decode_lds_bytes(int rmax, int nst)
 
 // NST ring stages: chunk i + NST - 1 is copied while chunk i is computed, and
 // the activations of chunk i + NST - 2 are loaded then (NST - 1 register sets).
-template <int RMAX, int NST>
+// kA16: the weight-only GEMM (BF16 activations [M, K], row pitch lda; no
+// activation scales): the lane's 32 activation values come as four 16-byte
+// loads used as they are, the weight words are dequantized to BF16 exactly
+// (dequant_word_bf16) and the products are v_mfma_f32_16x16x32_bf16.
+template <int RMAX, int NST, bool kA16 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_decode_lds(GemmParams p)
 {
     static_assert(NST == 3 || NST == 4, "three or four ring stages");
     constexpr int NA = NST - 1;
+    constexpr int AW = kA16 ? 4 : 1;             // 16-byte activation loads per row tile
+    constexpr int kAOps = RMAX * (AW + (kA16 ? 0 : 1));  // activation loads per chunk
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -306,10 +271,10 @@ void k_gemm_decode_lds(GemmParams p)
         __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, (short)0, 0x7FFFFFFF, 0x00020000);
     const __amdgpu_buffer_rsrc_t rbs =
         __builtin_amdgcn_make_buffer_rsrc((void*)p.b_scales, (short)0, 0x7FFFFFFF, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rac =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.a_codes, (short)0, 0x7FFFFFFF, 0x00020000);
-    const __amdgpu_buffer_rsrc_t ras =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.a_scales, (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rac = __builtin_amdgcn_make_buffer_rsrc(
+        kA16 ? (void*)p.a_bf16 : (void*)p.a_codes, (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc(
+        kA16 ? (void*)p.a_bf16 : (void*)p.a_scales, (short)0, 0x7FFFFFFF, 0x00020000);
     // no records: loads through it return zeros and touch no memory (the
     // copies past the last chunk, which keep the wait counts uniform)
     const __amdgpu_buffer_rsrc_t none =
@@ -335,8 +300,13 @@ void k_gemm_decode_lds(GemmParams p)
     for (int r = 0; r < RMAX; ++r) {
         int64_t m = 16 * r + lr;
         m = m < p.M ? m : p.M - 1;
-        aco[r] = (int)(m * (K / 2)) + 64 * wave + 16 * g;
-        aso[r] = (int)((p.a2d ? m / 16 : m) * (K / 16)) + 8 * wave + 2 * g;
+        if constexpr (kA16) {
+            aco[r] = (int)(m * p.lda * 2) + 256 * wave + 64 * g;  // bytes of BF16
+            aso[r] = 0;
+        } else {
+            aco[r] = (int)(m * (K / 2)) + 64 * wave + 16 * g;
+            aso[r] = (int)((p.a2d ? m / 16 : m) * (K / 16)) + 8 * wave + 2 * g;
+        }
     }
     // chunks start at a per-workgroup offset so the workgroups do not all
     // read the same byte ranges of the row pitch at once
@@ -361,20 +331,25 @@ void k_gemm_decode_lds(GemmParams p)
                 rs, (lds_void_t*)(base + kDlCodes + (16 * wave + 8 * h) * 32), 4, sof[h], kc / 16,
                 0, 0);
     };
-    u32x4 ac[NA][RMAX];
+    u32x4 ac[NA][RMAX][AW];
     uint32_t as[NA][RMAX];
-    auto load_a = [&](int i, u32x4 (&c)[RMAX], uint32_t (&sc)[RMAX]) {
+    auto load_a = [&](int i, u32x4 (&c)[RMAX][AW], uint32_t (&sc)[RMAX]) {
         const bool live = i < nch;
         const __amdgpu_buffer_rsrc_t rc = live ? rac : none, rs = live ? ras : none;
         const int kc = live ? kpos(i) : 0;
 #pragma unroll
         for (int r = 0; r < RMAX; ++r)
-            c[r] = __builtin_bit_cast(u32x4,
-                                      __builtin_amdgcn_raw_buffer_load_b128(rc, aco[r], kc / 2, 0));
-        __builtin_amdgcn_sched_barrier(0);  // the same load order in the prologue and the loop
 #pragma unroll
-        for (int r = 0; r < RMAX; ++r)
-            sc[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, aso[r], kc / 16, 0);
+            for (int h = 0; h < AW; ++h)
+                c[r][h] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, aco[r] + 16 * h,
+                                                                 kA16 ? 2 * kc : kc / 2, 0));
+        __builtin_amdgcn_sched_barrier(0);  // the same load order in the prologue and the loop
+        if constexpr (!kA16) {
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r)
+                sc[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, aso[r], kc / 16, 0);
+        }
     };
     float4_t acc[4][RMAX];
 #pragma unroll
@@ -382,7 +357,7 @@ void k_gemm_decode_lds(GemmParams p)
 #pragma unroll
         for (int r = 0; r < RMAX; ++r) acc[t][r] = float4_t{0.f, 0.f, 0.f, 0.f};
     // chunk i from ring stage st with the activation registers of chunk i
-    auto compute = [&](int st, const u32x4 (&ac)[RMAX], const uint32_t (&as)[RMAX]) {
+    auto compute = [&](int st, const u32x4 (&ac)[RMAX][AW], const uint32_t (&as)[RMAX]) {
         const uint8_t* base = lds + st * kDlStage;
         u32x4 bc[4];
         uint32_t bs[4];
@@ -395,6 +370,28 @@ void k_gemm_decode_lds(GemmParams p)
         }
         // all eight LDS reads in flight before the activations' dequantization
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kA16) {
+            // word s of the lane's 32 K: activation load s as it is, weight word
+            // s in BF16 with scale byte s / 2 of the pair
+            float e[4][2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                e[t][0] = __builtin_amdgcn_cvt_f32_fp8((int)bs[t], 0);
+                e[t][1] = __builtin_amdgcn_cvt_f32_fp8((int)bs[t], 1);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const bf16x8_t bf = dequant_word_bf16(bc[t][s], e[t][s >> 1]);
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r)
+                        acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, ac[r][s]), bf, acc[t][r], 0, 0, 0);
+                }
+            }
+            return;
+        } else {
         half2_t ae[RMAX];
 #pragma unroll
         for (int r = 0; r < RMAX; ++r)
@@ -403,7 +400,7 @@ void k_gemm_decode_lds(GemmParams p)
         for (int s = 0; s < 4; ++s) {
             half8_t af[RMAX];
 #pragma unroll
-            for (int r = 0; r < RMAX; ++r) af[r] = dequant_word(ac[r][s], ae[r][s >> 1]);
+            for (int r = 0; r < RMAX; ++r) af[r] = dequant_word(ac[r][0][s], ae[r][s >> 1]);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const half2_t be = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[t], 1.0f, false);
@@ -413,18 +410,19 @@ void k_gemm_decode_lds(GemmParams p)
                     acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[r], bf, acc[t][r], 0, 0, 0);
             }
         }
+        }
     };
     // Issue order: copy(0), A(0), copy(1), A(1), ... (the activations of chunk
     // j right after the copies of chunk j, before those of chunk j + 1): the
     // prologue issues up to copy(NST - 2), iteration i then A(i + NST - 2) and
     // copy(i + NST - 1).  At the top of iteration i, chunk i's copies and
     // activations have landed once at most the later NST - 2 chunks' copies
-    // and NST - 3 chunks' activations (two loads per row tile) are in flight.
+    // and NST - 3 chunks' activation loads are in flight.
     // The scheduling barriers keep this order: the compiler would otherwise
     // sink the activation loads below the products and hoist the products'
     // first dequantizations above the wait, leaving the next chunk's copies
     // behind loads an iteration needs at once (in-order counters).
-    constexpr int kInFlight = 6 * (NST - 2) + 2 * RMAX * (NST - 3);
+    constexpr int kInFlight = 6 * (NST - 2) + kAOps * (NST - 3);
 #pragma unroll
     for (int j = 0; j <= NST - 2; ++j) {
         copy(j, j);
@@ -474,7 +472,7 @@ void k_gemm_decode_lds(GemmParams p)
             for (int j = 0; j < 4; ++j)
                 red[(wave * 16 * RMAX + 16 * r + 4 * g + j) * kDlStride + 16 * t + lr] = acc[t][r][j];
     __syncthreads();
-    const float sab = (*p.a_ts) * (*p.b_ts);
+    const float sab = kA16 ? *p.b_ts : (*p.a_ts) * (*p.b_ts);
     const int col = threadIdx.x & 63;
     const int64_t n = n0 + col;
     for (int row = threadIdx.x >> 6; row < 16 * RMAX && row < p.M; row += 4) {
@@ -529,16 +527,25 @@ hipError_t launch_gemm_w4a16(int64_t M, int64_t N, int64_t K, const uint16_t* a,
     p.vec_out = false;
     p.a_bf16 = a;
     p.lda = lda;
-    dim3 g((unsigned)((N + kSkN - 1) / kSkN));
+    dim3 g((unsigned)((N + 63) / 64));
+    // up to 16 rows the weight-streaming kernel (its 16-byte BF16 activation
+    // loads are few); with more rows they cost more than the skinny kernel's
+    // shared LDS copy of the activations (measured at 32 and 64 rows)
+    if (M <= 16) {
+        auto kern = k_gemm_decode_lds<1, 3, true>;
+        const int lds = decode_lds_bytes(1, 3);
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);
+        return hipGetLastError();
+    }
 #define NVFP4_SKINNY16(RMAX)                                                                   \
     {                                                                                          \
-        auto kern = k_gemm_w4a16<512, RMAX>;                                            \
-        const int lds = RMAX * 16 * (512 * 2 + 64) + (RMAX == 1 ? 4 * 16 * (512 / 2 + 16) : 0);\
+        auto kern = k_gemm_w4a16<512, RMAX>;                                                   \
+        const int lds = RMAX * 16 * (512 * 2 + 64);                                            \
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
     }
-    if (M <= 16) NVFP4_SKINNY16(1)
-    else if (M <= 32) NVFP4_SKINNY16(2)
+    if (M <= 32) NVFP4_SKINNY16(2)
     else NVFP4_SKINNY16(4)
 #undef NVFP4_SKINNY16
     return hipGetLastError();

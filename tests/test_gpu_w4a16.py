@@ -23,11 +23,12 @@ def nv():
     return m
 
 
-# M <= 16, 17..32, 33..64 (the three kernel instances); ragged N; one, an odd
-# and an even number of 512-K chunks
+# M <= 16, 17..32, 33..64 (the three kernel instances); ragged N (partial
+# last workgroup of 64 columns); one, an odd and an even number of 512-K chunks
 SHAPES = [(1, 64, 512, False), (5, 100, 1536, True), (16, 1000, 2048, False),
           (17, 200, 1024, True), (32, 77, 2560, False), (33, 130, 512, False),
-          (64, 96, 4096, True)]
+          (64, 96, 4096, True), (24, 64, 512, False), (40, 64, 1536, True),
+          (63, 200, 2560, False)]
 
 
 @pytest.mark.parametrize("M,N,K,b2d", SHAPES)
