@@ -932,7 +932,9 @@ __device__ __forceinline__ void dequant8_store(uint32_t w, const float e[8], flo
             b += 0x7FFFu + ((b >> 16) & 1u);
             o[j] = (a >> 16) | (b & 0xFFFF0000u);
         }
-        *reinterpret_cast<u32x4*>(dst) = o;
+        // a wave's 64 stores are 1 KB of consecutive bytes: streaming stores,
+        // which skip the caches (the output is written once per call)
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst));
     } else {
         u32x4 a, b;
 #pragma unroll
@@ -940,6 +942,8 @@ __device__ __forceinline__ void dequant8_store(uint32_t w, const float e[8], flo
             a[j] = __float_as_uint(v[j]);
             b[j] = __float_as_uint(v[4 + j]);
         }
+        // two 16-byte halves per lane: plain stores, which L2 merges into whole
+        // lines (streaming stores of half lines measured 40% slower)
         u32x4* d = reinterpret_cast<u32x4*>(dst);
         d[0] = a;
         d[1] = b;
@@ -957,32 +961,59 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* codes, const uin
 {
     const float s_g = kMode == 3 ? 1.0f : *ts;
     const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < items; t += stride) {
-        uint32_t row = fdiv(t, div);
-        uint32_t cq = t - row * div.d;
-        int64_t c0 = (int64_t)cq * 8;
-        uint32_t w = *reinterpret_cast<const uint32_t*>(codes + (int64_t)row * (cols / 2) + c0 / 2);
-        float e[8];
-        if (kMode == 3) {
-            const uint32_t u = scales[(int64_t)row * (cols / 32) + c0 / 32];
-            const float ev = __uint_as_float(u == 0 ? 0x00400000u : (u == 255 ? 0x7FC00000u : u << 23));
+    // kU items per trip, all their loads issued before any store, so each
+    // lane keeps kU code words in flight
+    constexpr int kU = 4;
+    for (uint32_t t0 = blockIdx.x * blockDim.x + threadIdx.x; t0 < items; t0 += kU * stride) {
+        uint32_t w[kU], row[kU];
+        int64_t c0[kU];
+        uint32_t sraw[kU][2];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) e[j] = ev;
-        } else if (kMode == 1) {
-            u32x2 s = *reinterpret_cast<const u32x2*>(scales + (int64_t)(row / 16) * cols + c0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                e[j] = e4m3_decode(s[0] >> (8 * j));
-                e[4 + j] = e4m3_decode(s[1] >> (8 * j));
+        for (int u = 0; u < kU; ++u) {
+            const uint32_t t = t0 + u * stride;
+            const bool ok = t < items;
+            const uint32_t tc = ok ? t : t0;  // a valid item, stored only when ok
+            row[u] = fdiv(tc, div);
+            c0[u] = (int64_t)(tc - row[u] * div.d) * 8;
+            w[u] = *reinterpret_cast<const uint32_t*>(codes + (int64_t)row[u] * (cols / 2) +
+                                                      c0[u] / 2);
+            if (kMode == 3) {
+                sraw[u][0] = scales[(int64_t)row[u] * (cols / 32) + c0[u] / 32];
+            } else if (kMode == 1) {
+                const u32x2 sv = *reinterpret_cast<const u32x2*>(
+                    scales + (int64_t)(row[u] / 16) * cols + c0[u]);
+                sraw[u][0] = sv[0];
+                sraw[u][1] = sv[1];
+            } else {
+                const int64_t si = (kMode == 0) ? (int64_t)row[u] * (cols / 16) + c0[u] / 16
+                                                : (int64_t)(row[u] / 16) * (cols / 16) + c0[u] / 16;
+                sraw[u][0] = scales[si];
             }
-        } else {
-            int64_t si = (kMode == 0) ? (int64_t)row * (cols / 16) + c0 / 16
-                                      : (int64_t)(row / 16) * (cols / 16) + c0 / 16;
-            float ev = e4m3_decode(scales[si]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) e[j] = ev;
         }
-        dequant8_store<kOutBF16>(w, e, s_g, out + ((int64_t)row * ld_out + c0) * (kOutBF16 ? 2 : 4));
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (t0 + u * stride >= items) break;
+            float e[8];
+            if (kMode == 3) {
+                const uint32_t v = sraw[u][0];
+                const float ev = __uint_as_float(v == 0 ? 0x00400000u
+                                                        : (v == 255 ? 0x7FC00000u : v << 23));
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) e[jj] = ev;
+            } else if (kMode == 1) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    e[jj] = e4m3_decode(sraw[u][0] >> (8 * jj));
+                    e[4 + jj] = e4m3_decode(sraw[u][1] >> (8 * jj));
+                }
+            } else {
+                const float ev = e4m3_decode(sraw[u][0]);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) e[jj] = ev;
+            }
+            dequant8_store<kOutBF16>(w[u], e, s_g,
+                                     out + ((int64_t)row[u] * ld_out + c0[u]) * (kOutBF16 ? 2 : 4));
+        }
     }
 }
 
