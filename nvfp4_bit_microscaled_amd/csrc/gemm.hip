@@ -413,7 +413,8 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams& p, float16_t (&
             for (int r0 = 0; r0 < 32; r0 += 4) {
                 const int r = r0 + rr;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(wl + r * kPitch + 16 * cc);
-                *reinterpret_cast<u32x4*>(cbase + (int64_t)(32 * i + r) * p.ldc * esz + jp * 256) = v;
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<u32x4*>(cbase + (int64_t)(32 * i + r) * p.ldc * esz + jp * 256));
             }
         }
 }

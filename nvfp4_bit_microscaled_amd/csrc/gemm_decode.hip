@@ -392,23 +392,50 @@ void k_gemm_decode_lds(GemmParams p)
             }
             return;
         } else {
-        half2_t ae[RMAX];
+        // Software-pipelined over the four words s: the operands of word
+        // s + 1 are dequantized (into the other register set) while the
+        // MFMAs of word s run, one MFMA then kV VALU instructions at a time.
+        // With one set, each dequantization would overwrite registers that
+        // the MFMAs before it still read, and wait for them.
+        constexpr int kV = (RMAX + 4) * 8 / (4 * RMAX);  // VALU per MFMA
+        half2_t ae[RMAX], be[4];
 #pragma unroll
         for (int r = 0; r < RMAX; ++r)
             ae[r] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as[r], 1.0f, false);
 #pragma unroll
+        for (int t = 0; t < 4; ++t)
+            be[t] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[t], 1.0f, false);
+        half8_t af[2][RMAX], bf[2][4];
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r) af[0][r] = dequant_word(ac[r][0][0], ae[r][0]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bf[0][t] = dequant_word(bc[t][0], be[t][0]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
         for (int s = 0; s < 4; ++s) {
-            half8_t af[RMAX];
-#pragma unroll
-            for (int r = 0; r < RMAX; ++r) af[r] = dequant_word(ac[r][0][s], ae[r][s >> 1]);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const half2_t be = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[t], 1.0f, false);
-                const half8_t bf = dequant_word(bc[t][s], be[s >> 1]);
+            const int c = s & 1, n = c ^ 1;
+            if (s < 3) {
 #pragma unroll
                 for (int r = 0; r < RMAX; ++r)
-                    acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[r], bf, acc[t][r], 0, 0, 0);
+                    af[n][r] = dequant_word(ac[r][0][s + 1], ae[r][(s + 1) >> 1]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    bf[n][t] = dequant_word(bc[t][s + 1], be[t][(s + 1) >> 1]);
             }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r)
+                    acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[c][r], bf[c][t], acc[t][r],
+                                                                      0, 0, 0);
+            if (s < 3) {
+#pragma unroll
+                for (int q = 0; q < 4 * RMAX; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         }
     };
