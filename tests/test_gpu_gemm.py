@@ -338,3 +338,32 @@ def test_last_round_k_split(nv, out_dtype, ragged):
     if out_dtype == torch.bfloat16:
         bound = bound + y_whole.float().abs() * 2.0 ** -7
     assert bool((d <= bound).all())
+
+
+@pytest.mark.parametrize("rounds,K,b2d", [(1.25, 256, True), (2.25, 4096, False), (3.125, 512, False)])
+def test_multi_round_grids(nv, rounds, K, b2d):
+    """Grids of full 256 x 256 tiles with more tiles than compute units (up to
+    four rounds; K = 256 is the two-k-tile minimum of the pipeline).  Outputs
+    of tiles of the second and later rounds (corners and random points) and
+    random others against the oracle, FP32 and BF16 (the BF16 result the FP32
+    one rounded); at K = 4096 the last round is also split along K."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    nbn = 16
+    nbm = int(np.ceil(rounds * ncu / nbn))
+    M, N = 256 * nbm, 256 * nbn
+    t = nbm * nbn
+    assert t > ncu
+    rng = np.random.default_rng(int(rounds * 8) + K)
+    a_or, a_g = random_operand(nv, rng, M, K, False, 1, 0.5, scale_lo=0x20)
+    b_or, b_g = random_operand(nv, rng, N, K, b2d, 1, 0.25, scale_lo=0x20)
+    print("multi-round grid", M, N, K, "tiles", t, flush=True)
+    ms, ns = [], []
+    later = list(range(ncu, t))
+    for bid in [later[i] for i in sorted(rng.choice(len(later), min(len(later), 48), replace=False))]:
+        tm, tn = tile_order(bid, nbm, nbn)
+        ms.append(256 * tm + np.concatenate([[0, 0, 255, 255], rng.integers(0, 256, 20)]))
+        ns.append(256 * tn + np.concatenate([[0, 255, 0, 255], rng.integers(0, 256, 20)]))
+    ms.append(rng.integers(0, M, 2048))
+    ns.append(rng.integers(0, N, 2048))
+    pairs = (np.concatenate(ms).astype(np.int64), np.concatenate(ns).astype(np.int64))
+    run_and_check(nv, "NT", M, N, K, a_or, a_g, b_or, b_g, pairs=pairs)
