@@ -211,6 +211,17 @@ __global__ __launch_bounds__(256) void k_gemm_w4a16(GemmParams p)
     }
 }
 
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+// The E4M3 value of byte e of w, as FP32 (exact).
+__device__ __forceinline__ float e4m3_value(uint32_t w, int e)
+{
+    return e == 0 ? __builtin_amdgcn_cvt_f32_fp8((int)w, 0)
+         : e == 1 ? __builtin_amdgcn_cvt_f32_fp8((int)w, 1)
+         : e == 2 ? __builtin_amdgcn_cvt_f32_fp8((int)w, 2)
+                  : __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+}
+
 // ---------------------------------------------------------------------------
 // Weight-streaming decode kernel: C[M, N] = A[M, K] B[N, K]^T for M <= 16 RMAX
 // activation rows.  A workgroup owns 64 weight rows (64 output columns) and
@@ -253,11 +264,21 @@ __host__ __device__ constexpr int decode_lds_bytes(int rmax, int nst)
 // activation scales): the lane's 32 activation values come as four 16-byte
 // loads used as they are, the weight words are dequantized to BF16 exactly
 // (dequant_word_bf16) and the products are v_mfma_f32_16x16x32_bf16.
-template <int RMAX, int NST, bool kA16 = false>
+// kRow1: one activation row (M == 1), contracted on the FP4 MFMA with the
+// block scales applied to its output: the activation operand's 16 rows are
+// the wave's 8 K blocks (row i keeps block i's 16 codes and zeros elsewhere;
+// rows 8-15 are zero), so the MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, both
+// operands E2M1, unit scales) returns the per-block code dot products
+// sum_k a_k w_nk of 16 weight rows exactly (each at most 16 products of
+// E2M1 values: multiples of 1/4 below 2^10), and each is then multiplied by
+// its block's scale product s_a s_w (exact: two E4M3 values) and summed in
+// FP32.  No operand is dequantized.
+template <int RMAX, int NST, bool kA16 = false, bool kRow1 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_decode_lds(GemmParams p)
 {
     static_assert(NST == 3 || NST == 4, "three or four ring stages");
+    static_assert(!kRow1 || (RMAX == 1 && !kA16), "single activation row, NVFP4");
     constexpr int NA = NST - 1;
     constexpr int AW = kA16 ? 4 : 1;             // 16-byte activation loads per row tile
     constexpr int kAOps = RMAX * (AW + (kA16 ? 0 : 1));  // activation loads per chunk
@@ -305,7 +326,8 @@ void k_gemm_decode_lds(GemmParams p)
             aso[r] = 0;
         } else {
             aco[r] = (int)(m * (K / 2)) + 64 * wave + 16 * g;
-            aso[r] = (int)((p.a2d ? m / 16 : m) * (K / 16)) + 8 * wave + 2 * g;
+            aso[r] = (int)((p.a2d ? m / 16 : m) * (K / 16)) + 8 * wave +
+                     (kRow1 ? 4 * (g & 1) : 2 * g);
         }
     }
     // chunks start at a per-workgroup offset so the workgroups do not all
@@ -345,7 +367,9 @@ void k_gemm_decode_lds(GemmParams p)
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, aco[r] + 16 * h,
                                                                  kA16 ? 2 * kc : kc / 2, 0));
         __builtin_amdgcn_sched_barrier(0);  // the same load order in the prologue and the loop
-        if constexpr (!kA16) {
+        if constexpr (kRow1) {
+            sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, aso[0], kc / 16, 0);
+        } else if constexpr (!kA16) {
 #pragma unroll
             for (int r = 0; r < RMAX; ++r)
                 sc[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, aso[r], kc / 16, 0);
@@ -356,9 +380,52 @@ void k_gemm_decode_lds(GemmParams p)
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < RMAX; ++r) acc[t][r] = float4_t{0.f, 0.f, 0.f, 0.f};
+    // kRow1: the lane's running sum for weight row n0 + 16 t + lr (blocks
+    // 4 g .. 4 g + 3 of each wave's 8; lane groups 2 and 3 hold zero rows)
+    float ysum[4] = {0.f, 0.f, 0.f, 0.f};
+    // kRow1: which half of the lane's 32 activation codes its operand row
+    // keeps (row lr is block lr: codes 0-15 of lane group lr / 2)
+    const bool keep_lo = lr == 2 * g, keep_hi = lr == 2 * g + 1;
     // chunk i from ring stage st with the activation registers of chunk i
     auto compute = [&](int st, const u32x4 (&ac)[RMAX][AW], const uint32_t (&as)[RMAX]) {
         const uint8_t* base = lds + st * kDlStage;
+        if constexpr (kRow1) {
+            u32x4 bc[4];
+            uint32_t bs[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int row = 16 * t + lr;
+                bc[t] = *reinterpret_cast<const u32x4*>(base + row * 256 +
+                                                        16 * ((4 * wave + g) ^ (row & 15)));
+                // scale bytes of blocks 8 w + 4 (g & 1) .. +3 of the chunk
+                bs[t] = *reinterpret_cast<const uint32_t*>(base + kDlCodes + row * 32 + 8 * wave +
+                                                           4 * (g & 1));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x4 a = ac[0][0];
+            v8i_t af;
+            af[0] = keep_lo ? (int)a[0] : 0;
+            af[1] = keep_lo ? (int)a[1] : 0;
+            af[2] = keep_hi ? (int)a[2] : 0;
+            af[3] = keep_hi ? (int)a[3] : 0;
+            af[4] = 0; af[5] = 0; af[6] = 0; af[7] = 0;
+            float sa[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sa[e] = e4m3_value(as[0], e);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                v8i_t bf;
+                bf[0] = (int)bc[t][0]; bf[1] = (int)bc[t][1];
+                bf[2] = (int)bc[t][2]; bf[3] = (int)bc[t][3];
+                bf[4] = 0; bf[5] = 0; bf[6] = 0; bf[7] = 0;
+                const float4_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    af, bf, float4_t{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, 127, 0, 127);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ysum[t] = __builtin_fmaf(d[e], sa[e] * e4m3_value(bs[t], e), ysum[t]);
+            }
+            return;
+        } else {
         u32x4 bc[4];
         uint32_t bs[4];
 #pragma unroll
@@ -438,6 +505,7 @@ void k_gemm_decode_lds(GemmParams p)
             __builtin_amdgcn_sched_barrier(0);
         }
         }
+        }
     };
     // Issue order: copy(0), A(0), copy(1), A(1), ... (the activations of chunk
     // j right after the copies of chunk j, before those of chunk j + 1): the
@@ -490,6 +558,15 @@ void k_gemm_decode_lds(GemmParams p)
     NVFP4_WAIT_VMCNT(0);
     NVFP4_WAIT_LGKMCNT0();
     __builtin_amdgcn_s_barrier();
+    if constexpr (kRow1) {
+        // lane groups 0 and 1 hold blocks 0-3 and 4-7: their sum is the
+        // partial of row 0 (partial tile row 4 g + j = 0: group 0, j = 0)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float o = __shfl_xor(ysum[t], 16);
+            acc[t][0] = float4_t{g == 0 ? ysum[t] + o : 0.f, 0.f, 0.f, 0.f};
+        }
+    }
     float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -524,16 +601,17 @@ bool gemm_decode_shape(int64_t M, int64_t N, int64_t K)
 hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s)
 {
     dim3 g((unsigned)((p.N + kSkN - 1) / kSkN));
-#define NVFP4_DECODE_LDS(RMAX, NST)                                                            \
+#define NVFP4_DECODE_LDS(RMAX, NST, ROW1)                                                      \
     {                                                                                          \
-        auto kern = k_gemm_decode_lds<RMAX, NST>;                                              \
+        auto kern = k_gemm_decode_lds<RMAX, NST, false, ROW1>;                                 \
         const int lds = decode_lds_bytes(RMAX, NST);                                           \
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
     }
-    if (p.M <= 16) NVFP4_DECODE_LDS(1, 3)
-    else if (p.M <= 32) NVFP4_DECODE_LDS(2, 3)
-    else NVFP4_DECODE_LDS(4, 3)
+    if (p.M == 1) NVFP4_DECODE_LDS(1, 3, true)
+    else if (p.M <= 16) NVFP4_DECODE_LDS(1, 3, false)
+    else if (p.M <= 32) NVFP4_DECODE_LDS(2, 3, false)
+    else NVFP4_DECODE_LDS(4, 3, false)
 #undef NVFP4_DECODE_LDS
     return hipGetLastError();
 }

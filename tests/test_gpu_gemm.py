@@ -221,7 +221,8 @@ def test_nt_kmajor_odd_rows(nv):
 # kernel (512-K chunks through a three-stage LDS ring, its chunk loop runs in
 # pairs; 1, 2 or 4 activation row tiles).  M and N ragged (partial last
 # workgroup), one, an odd and an even number of chunks, 2D weight blocks.
-SKINNY = [(1, 64, 2048, False), (5, 100, 4096, True), (16, 1000, 2048, False),
+SKINNY = [(1, 64, 2048, False), (1, 1000, 512, True), (1, 130, 8192, False), (1, 4100, 1024, True),
+          (5, 100, 4096, True), (16, 1000, 2048, False),
           (17, 200, 1024, True), (32, 77, 3072, False), (33, 130, 1536, False),
           (64, 96, 512, True), (64, 64, 8192, False), (1, 300, 2560, False),
           (7, 48, 512, True), (12, 4200, 1536, False), (20, 130, 512, False),
