@@ -424,7 +424,7 @@ def run_step_bench(torch, ms, steps, warmup, dev, isolated=True):
                       "isolated_frac_of_hbm": round(qbytes[name] / (it * 1e-6) / 1e9
                                                     / HBM_PEAK_GBPS, 4)})
         if counters is not None and name in counters:
-            c["bound"] = counters[name]["bound"]
+            c["bound"] = counters[name].get("bound")
             c["counters"] = counters[name]
         q_calls[name] = c
     q_bytes = sum(qbytes.values()) * steps
