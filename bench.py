@@ -219,6 +219,10 @@ def main():
     ms.free_buffers()
     torch.cuda.empty_cache()
     if not args.step_only:
+        # the decode shapes are a workload of their own: measured after the
+        # GPU has idled out of the training step's power transient (right
+        # after a 20 s GEMM load they ran 1-2 us slower, 3 s later as cold)
+        time.sleep(3.0)
         line["decode"] = decode_bench(torch, nv, workloads)
         line["mxfp4"] = mxfp4_bench(torch, nv, X, W_gu)
         line["kv_cache"] = kv_bench(torch, nv, workloads)
@@ -568,7 +572,10 @@ def decode_bench(torch, nv, workloads):
     both 1x16 RNE.  HBM-bound on the packed weights (codes + scales).  Four
     copies of the quantized weights (4 x 132 MB, twice the 256 MB Infinity
     Cache) are cycled through 40 back-to-back launches, so every launch reads
-    weights evicted by the three before it; `us` is the mean per launch.
+    weights evicted by the three before it; `us` is the mean per launch
+    (HIP events around the 40), `us_graph` the same 40 launches captured in
+    one HIP graph and replayed (a decode loop's way to launch; w4a16_us is
+    timed that way too).
     `us_isolated` is the median of 10 single launches, each after a 1 GiB read
     that evicts the cache (HIP events around one launch also count its
     dispatch)."""
@@ -582,20 +589,46 @@ def decode_bench(torch, nv, workloads):
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     wbytes = N * K * (0.5 + 1 / 16)
     out = {}
+    reps = 40
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def graph_time(launch):
+        """Mean seconds per launch of `reps` launches captured in one HIP graph
+        and replayed (twice untimed, then three timed replays)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(4):
+                launch(i)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                launch(i)
+        g.replay()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(3):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e-3 / (3 * reps)
+
     for M in cfg["ms"]:
         a = nv.quantize(x[:M].contiguous())
         y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
         for i in range(4):
             nv.gemm("NT", a, ws[i], out=y)
-        reps = 40
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(reps):
             nv.gemm("NT", a, ws[i % 4], out=y)
         e1.record()
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) * 1e-3 / reps
+        t_graph = graph_time(lambda i: nv.gemm("NT", a, ws[i % 4], out=y))
         iso = []
         for it in range(12):
             flush.sum()
@@ -611,13 +644,9 @@ def decode_bench(torch, nv, workloads):
         ab = x[:M].contiguous()
         for i in range(4):
             nv.gemm_w4a16(ab, ws[i], out=y)
-        e0.record()
-        for i in range(reps):
-            nv.gemm_w4a16(ab, ws[i % 4], out=y)
-        e1.record()
-        torch.cuda.synchronize()
-        t16 = e0.elapsed_time(e1) * 1e-3 / reps
+        t16 = graph_time(lambda i: nv.gemm_w4a16(ab, ws[i % 4], out=y))
         out["M%d" % M] = {"us": round(t * 1e6, 2),
+                          "us_graph": round(t_graph * 1e6, 2),
                           "w4a16_us": round(t16 * 1e6, 2),
                           "weights_GBps": round(wbytes / t / 1e9, 1),
                           "frac_of_hbm": round(wbytes / t / 1e9 / HBM_PEAK_GBPS, 4),
@@ -627,8 +656,9 @@ def decode_bench(torch, nv, workloads):
     return {"shape": "M x 28672 x 8192, weights 1x16 along K (w4a16_us: BF16 activations)",
             "weight_bytes": int(wbytes),
             "timing": "mean of 40 back-to-back launches over 4 weight copies (528 MB, "
-                      "cache-cold each launch); us_isolated: median of 10 single launches "
-                      "after a cache-evicting read", **out}
+                      "cache-cold each launch; us_graph, w4a16_us: the 40 captured in one HIP "
+                      "graph); us_isolated: median of 10 single launches after a "
+                      "cache-evicting read", **out}
 
 
 def mxfp4_bench(torch, nv, X, W):

@@ -593,6 +593,21 @@ void k_gemm_decode_lds(GemmParams p)
     }
 }
 
+// The dynamic-LDS limit of kernel Kern, raised once per device (not a stream
+// operation: repeating it per launch only costs host time, which the short
+// decode launches feel, and keeps it out of graph captures after the first
+// eager launch).
+template <auto Kern>
+static void set_lds_limit(int bytes)
+{
+    static bool done[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+    if (dev >= 0 && done[dev]) return;
+    hipFuncSetAttribute((const void*)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (dev >= 0) done[dev] = true;
+}
+
 bool gemm_decode_shape(int64_t M, int64_t N, int64_t K)
 {
     return M <= 64 && K % 512 == 0 && (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);
@@ -603,9 +618,9 @@ hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s)
     dim3 g((unsigned)((p.N + kSkN - 1) / kSkN));
 #define NVFP4_DECODE_LDS(RMAX, NST, ROW1)                                                      \
     {                                                                                          \
-        auto kern = k_gemm_decode_lds<RMAX, NST, false, ROW1>;                                 \
+        constexpr auto kern = k_gemm_decode_lds<RMAX, NST, false, ROW1>;                       \
         const int lds = decode_lds_bytes(RMAX, NST);                                           \
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
+        set_lds_limit<kern>(lds);                                                              \
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
     }
     if (p.M == 1) NVFP4_DECODE_LDS(1, 3, true)
@@ -637,17 +652,17 @@ hipError_t launch_gemm_w4a16(int64_t M, int64_t N, int64_t K, const uint16_t* a,
     // loads are few); with more rows they cost more than the skinny kernel's
     // shared LDS copy of the activations (measured at 32 and 64 rows)
     if (M <= 16) {
-        auto kern = k_gemm_decode_lds<1, 3, true>;
+        constexpr auto kern = k_gemm_decode_lds<1, 3, true>;
         const int lds = decode_lds_bytes(1, 3);
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        set_lds_limit<kern>(lds);
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);
         return hipGetLastError();
     }
 #define NVFP4_SKINNY16(RMAX)                                                                   \
     {                                                                                          \
-        auto kern = k_gemm_w4a16<512, RMAX>;                                                   \
+        constexpr auto kern = k_gemm_w4a16<512, RMAX>;                                         \
         const int lds = RMAX * 16 * (512 * 2 + 64);                                            \
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
+        set_lds_limit<kern>(lds);                                                              \
         hipLaunchKernelGGL(kern, g, dim3(256), lds, s, p);                                     \
     }
     if (M <= 32) NVFP4_SKINNY16(2)

@@ -368,3 +368,45 @@ def test_multi_round_grids(nv, rounds, K, b2d):
     ns.append(rng.integers(0, N, 2048))
     pairs = (np.concatenate(ms).astype(np.int64), np.concatenate(ns).astype(np.int64))
     run_and_check(nv, "NT", M, N, K, a_or, a_g, b_or, b_g, pairs=pairs)
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_decode_gemms_in_graph(nv, M):
+    """The decode GEMMs captured in a HIP graph, as the decode bench times
+    them (NVFP4 activations and the weight-only BF16 form), replayed three
+    times; before each replay eager work writes new activations into the
+    captured inputs, and after it every output equals the eager GEMM on the
+    same inputs, bit for bit."""
+    N, K = 1000, 2048
+    w = nv.quantize(workloads.weights(N, K, 11, device="cuda"))
+    x = workloads.activations(M, K, 12, device="cuda")
+    a = nv.quantize(x)
+    ab = x.clone()
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    y16 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        nv.gemm("NT", a, w, out=y)
+        nv.gemm_w4a16(ab, w, out=y16)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv.gemm("NT", a, w, out=y)
+        nv.gemm_w4a16(ab, w, out=y16)
+    for rep in range(3):
+        xn = workloads.activations(M, K, 100 + rep, device="cuda")
+        an = nv.quantize(xn)
+        a.codes.copy_(an.codes)
+        a.scales.copy_(an.scales)
+        a.tensor_scale.copy_(an.tensor_scale)
+        ab.copy_(xn)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = nv.gemm("NT", an, w, out_dtype=torch.bfloat16)
+        ref16 = nv.gemm_w4a16(xn, w)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), (M, rep)
+        assert torch.equal(y16, ref16), (M, rep)
