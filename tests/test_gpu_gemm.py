@@ -410,3 +410,41 @@ def test_decode_gemms_in_graph(nv, M):
         torch.cuda.synchronize()
         assert torch.equal(y, ref), (M, rep)
         assert torch.equal(y16, ref16), (M, rep)
+
+
+@pytest.mark.parametrize("N,b2d,const_sign", [(256, False, False), (200, False, True),
+                                              (272, True, False), (160, True, True)])
+def test_decode_single_row_special_blocks(nv, N, b2d, const_sign):
+    """One activation row (the FP4-MFMA path with the block scales applied to
+    its per-block outputs) on constructed blocks: zero scales, the largest
+    (448) and smallest (2^-9) E4M3 scales, all-zero code blocks under
+    nonzero scales, negative zeros, and (const_sign) every code of both
+    operands positive so the sums never cancel, at K = 8192; against the
+    oracle."""
+    M, K = 1, 8192
+    rng = np.random.default_rng(N * 7 + b2d * 3 + const_sign)
+
+    def operand(rows, ts):
+        c = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+        if const_sign:
+            c &= 0x77  # both nibbles positive
+        s = rng.integers(0x20, 0x60, size=nv.scale_shape(rows, K, b2d and rows > 1, 1), dtype=np.uint8)
+        flat = s.reshape(-1)
+        idx = rng.permutation(flat.size)
+        q = flat.size // 16
+        flat[idx[:q]] = 0x00                 # zero scale
+        flat[idx[q:2 * q]] = 0x7E            # 448
+        flat[idx[2 * q:3 * q]] = 0x01        # 2^-9
+        s = flat.reshape(s.shape)
+        # all-zero and negative-zero code blocks under nonzero scales
+        cb = c.reshape(rows, K // 16, 8)
+        blk = rng.integers(0, K // 16, size=(rows, 8))
+        for r in range(rows):
+            cb[r, blk[r, :4]] = 0x00
+            cb[r, blk[r, 4:]] = 0x88
+        c = cb.reshape(rows, K // 2)
+        return (c, s, ts, b2d and rows > 1), to_gpu_tensor(nv, c, s, ts, rows, K, b2d and rows > 1, 1)
+
+    a_or, a_g = operand(M, 0.5)
+    b_or, b_g = operand(N, 0.75)
+    run_and_check(nv, "NT", M, N, K, a_or, a_g, b_or, b_g)
