@@ -386,6 +386,9 @@ void k_gemm_decode_lds(GemmParams p)
     // kRow1: which half of the lane's 32 activation codes its operand row
     // keeps (row lr is block lr: codes 0-15 of lane group lr / 2)
     const bool keep_lo = lr == 2 * g, keep_hi = lr == 2 * g + 1;
+    // fragment address of weight row 16 t + lr in a stage, less 4096 t: piece
+    // 4 w + g sits at slot (4 w + g) ^ lr (the row's low four bits are lr)
+    const int frag_off = lr * 256 + 16 * ((4 * wave + g) ^ lr);
     // chunk i from ring stage st with the activation registers of chunk i
     auto compute = [&](int st, const u32x4 (&ac)[RMAX][AW], const uint32_t (&as)[RMAX]) {
         const uint8_t* base = lds + st * kDlStage;
@@ -394,12 +397,12 @@ void k_gemm_decode_lds(GemmParams p)
             uint32_t bs[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const int row = 16 * t + lr;
-                bc[t] = *reinterpret_cast<const u32x4*>(base + row * 256 +
-                                                        16 * ((4 * wave + g) ^ (row & 15)));
+                // row 16 t + lr (its piece slot depends on lr only): the
+                // lane's address plus a constant per tile
+                bc[t] = *reinterpret_cast<const u32x4*>(base + frag_off + 4096 * t);
                 // scale bytes of blocks 8 w + 4 (g & 1) .. +3 of the chunk
-                bs[t] = *reinterpret_cast<const uint32_t*>(base + kDlCodes + row * 32 + 8 * wave +
-                                                           4 * (g & 1));
+                bs[t] = *reinterpret_cast<const uint32_t*>(base + kDlCodes + lr * 32 + 512 * t +
+                                                           8 * wave + 4 * (g & 1));
             }
             __builtin_amdgcn_sched_barrier(0);
             const u32x4 a = ac[0][0];
@@ -430,10 +433,9 @@ void k_gemm_decode_lds(GemmParams p)
         uint32_t bs[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int row = 16 * t + lr;
-            bc[t] = *reinterpret_cast<const u32x4*>(base + row * 256 +
-                                                    16 * ((4 * wave + g) ^ (row & 15)));
-            bs[t] = *reinterpret_cast<const uint16_t*>(base + kDlCodes + row * 32 + 8 * wave + 2 * g);
+            bc[t] = *reinterpret_cast<const u32x4*>(base + frag_off + 4096 * t);
+            bs[t] = *reinterpret_cast<const uint16_t*>(base + kDlCodes + lr * 32 + 512 * t +
+                                                       8 * wave + 2 * g);
         }
         // all eight LDS reads in flight before the activations' dequantization
         __builtin_amdgcn_sched_barrier(0);
