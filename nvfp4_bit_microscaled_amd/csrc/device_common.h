@@ -21,6 +21,7 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // 6 * 448: largest E2M1 magnitude times largest E4M3 magnitude.
 constexpr float kGlobalDivisor = 2688.0f;
@@ -263,7 +264,10 @@ __device__ __forceinline__ u32x4 sr_words(uint64_t seed, uint32_t stream_id, uin
 // (bit i set -> element i negated), butterflies at distances 1, 2, 4, 8,
 // then the 1/4 scaling.  Same FP32 operation order as the documented
 // convention.
-__device__ __forceinline__ void rht16_inplace(float v[16], uint32_t mask)
+// rht16_butterflies is everything but the 1/4: where only max |y| is wanted,
+// 0.25 * max |v| over the unscaled v equals the max over the scaled values
+// (x -> RN(0.25 x) is monotone), so one multiply per block replaces sixteen.
+__device__ __forceinline__ void rht16_butterflies(float v[16], uint32_t mask)
 {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -278,6 +282,11 @@ __device__ __forceinline__ void rht16_inplace(float v[16], uint32_t mask)
             v[j + h] = a - b;
         }
     }
+}
+
+__device__ __forceinline__ void rht16_inplace(float v[16], uint32_t mask)
+{
+    rht16_butterflies(v, mask);
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = 0.25f * v[i];
 }
@@ -291,27 +300,59 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// act = BF16(BF16(silu(g)) * u) for BF16-valued g (gate) and u (up), with
-// silu(g) = g / (1 + exp(-g)) in FP32: the rounding points of a BF16
-// framework's silu and multiply.  The reciprocal unit (1 ulp) stands in for a
-// correctly rounded division, as the result only feeds a BF16 rounding; its
-// output flushes below 2^-126, so denominators from 2^126 up (g < -87.3) take
-// the IEEE division.  The standalone SwiGLU pass and the GEMM epilogue that
-// fuses it both use this, so their outputs agree bit for bit.
-// kMayDivide = false leaves the division out: valid when g >= -87 (then
-// 1 + exp(-g) <= 1 + exp(87) < 2^126), which callers check for a whole wave
-// with swiglu_low (a per-lane select would compute the division always).
-template <bool kMayDivide>
-__device__ __forceinline__ uint32_t swiglu_bf16_bits(float g, float u)
+// BF16 bits of two FP32 values rounded to nearest even, a in the low half:
+// one v_cvt_pk_bf16_f32, the same bits as f32_to_bf16_bits on each finite
+// value (these kernels keep FP32 denormals, so those round like any other).
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b)
 {
-    const float den = 1.0f + expf(-g);
-    float sg = g * __builtin_amdgcn_rcpf(den);
-    if (kMayDivide && den >= 8.5070592e37f) sg = g / den;  // 2^126
-    const float sb = __uint_as_float(f32_to_bf16_bits(sg) << 16);
-    return f32_to_bf16_bits(sb * u);
+    const float2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// True where swiglu_bf16_bits may need its division.
+// silu(g) = g / (1 + exp(-g)) in FP32 for a BF16-valued gate g: silu_den,
+// then silu_rcp.  The reciprocal unit (1 ulp) stands in for a correctly
+// rounded division, as the result only feeds a BF16 rounding; its output
+// flushes below 2^-126, so denominators from 2^126 up (g < -87.3) need the
+// IEEE division, which silu_fix applies.  That never happens for g >= -87
+// (1 + exp(87) < 2^126), which callers check for a whole wave (swiglu_low,
+// or the denominators themselves), so the common path has no division.
+__device__ __forceinline__ float silu_den(float g) { return 1.0f + expf(-g); }
+__device__ __forceinline__ float silu_rcp(float g, float den)
+{
+    return g * __builtin_amdgcn_rcpf(den);
+}
+__device__ __forceinline__ bool silu_needs_division(float den) { return den >= 8.5070592e37f; }
+__device__ __forceinline__ float silu_fix(float g, float den, float s)
+{
+    return silu_needs_division(den) ? g / den : s;
+}
+
+// act = BF16(BF16(s) * u) for two gate/up pairs, s = silu(g) from the steps
+// above, as packed BF16 bits (the first pair in the low half): the rounding
+// points of a BF16 framework's silu and multiply.  The standalone SwiGLU pass
+// and the GEMM epilogue that fuses it both end here, so their outputs agree
+// bit for bit.
+__device__ __forceinline__ uint32_t swiglu_pack(float s0, float u0, float s1, float u1)
+{
+    const uint32_t sb = bf16_pair(s0, s1);
+    return bf16_pair(__uint_as_float(sb << 16) * u0, __uint_as_float(sb & 0xFFFF0000u) * u1);
+}
+
+// The same from the gate values; kMayDivide = false leaves the division out
+// (for waves whose gates are all >= -87).
+template <bool kMayDivide>
+__device__ __forceinline__ uint32_t swiglu_pair_bits(float g0, float u0, float g1, float u1)
+{
+    const float d0 = silu_den(g0), d1 = silu_den(g1);
+    float s0 = silu_rcp(g0, d0), s1 = silu_rcp(g1, d1);
+    if (kMayDivide) {
+        s0 = silu_fix(g0, d0, s0);
+        s1 = silu_fix(g1, d1, s1);
+    }
+    return swiglu_pack(s0, u0, s1, u1);
+}
+
+// True where silu may need its division (a gate below -87).
 __device__ __forceinline__ bool swiglu_low(float g) { return g < -87.0f; }
 
 // ---------------------------------------------------------------- reductions

@@ -609,9 +609,11 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmParams& p, float16_t (
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                acc[i][j][r] = __uint_as_float(f32_to_bf16_bits(acc[i][j][r] * sab) << 16);
-                if (j < 2) low |= swiglu_low(acc[i][j][r]);
+            for (int r = 0; r < 16; r += 2) {
+                const uint32_t w = bf16_pair(acc[i][j][r] * sab, acc[i][j][r + 1] * sab);
+                acc[i][j][r] = bf16_lo(w);
+                acc[i][j][r + 1] = bf16_hi(w);
+                if (j < 2) low |= swiglu_low(acc[i][j][r]) | swiglu_low(acc[i][j][r + 1]);
             }
     auto act_of = [&](auto may_divide) {
         constexpr bool kDiv = decltype(may_divide)::value;
@@ -620,11 +622,13 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmParams& p, float16_t (
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float a = __uint_as_float(
-                        swiglu_bf16_bits<kDiv>(acc[i][j][r], acc[i][j + 2][r]) << 16);
-                    acc[i][j][r] = a;
-                    m_plain = __builtin_fmaxf(m_plain, __builtin_fabsf(a));
+                for (int r = 0; r < 16; r += 2) {
+                    const uint32_t w = swiglu_pair_bits<kDiv>(acc[i][j][r], acc[i][j + 2][r],
+                                                              acc[i][j][r + 1], acc[i][j + 2][r + 1]);
+                    acc[i][j][r] = bf16_lo(w);
+                    acc[i][j][r + 1] = bf16_hi(w);
+                    m_plain = __builtin_fmaxf(m_plain, __builtin_fmaxf(__builtin_fabsf(bf16_lo(w)),
+                                                                       __builtin_fabsf(bf16_hi(w))));
                 }
     };
     if (__builtin_amdgcn_ballot_w64(low) != 0)
@@ -632,9 +636,10 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmParams& p, float16_t (
     else
         act_of(std::integral_constant<bool, false>{});
     if (wave_ok) {
-        // d_i x_i, butterflies (x_j + x_{j+h}, x_j - x_{j+h}) for j & h == 0,
-        // then 1/4: the lane at group row i & h == 0 keeps the sum, its
-        // partner the difference, in the transform's FP32 operation order
+        // d_i x_i, butterflies (x_j + x_{j+h}, x_j - x_{j+h}) for j & h == 0:
+        // the lane at group row i & h == 0 keeps the sum, its partner the
+        // difference, in the transform's FP32 operation order (the 1/4 is
+        // applied to the maximum)
         const uint32_t sgn = ((p.rht_mask >> (lr & 15)) & 1u) << 31;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -648,8 +653,10 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmParams& p, float16_t (
                         const float pv = __shfl_xor(v, h, 64);
                         v = (lr & h) ? pv - v : v + pv;
                     }
-                    m_rht = __builtin_fmaxf(m_rht, __builtin_fabsf(0.25f * v));
+                    m_rht = __builtin_fmaxf(m_rht, __builtin_fabsf(v));
                 }
+        // the transform's 1/4, once: RN(0.25 x) is monotone in x
+        m_rht = 0.25f * m_rht;
     } else {
         m_plain = 0.0f;
     }

@@ -10,16 +10,6 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// BF16 bits of two FP32 values rounded to nearest even, a in the low half:
-// one v_cvt_pk_bf16_f32 (these kernels keep FP32 denormals, so those round
-// like any other value).
-__device__ __forceinline__ uint32_t bf16_pair(float a, float b)
-{
-    const float2_t v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
 
 struct GemmParams {
     int64_t M, N, K;

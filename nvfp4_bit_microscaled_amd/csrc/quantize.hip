@@ -351,14 +351,14 @@ __global__ __launch_bounds__(256) void k_amax_dual(QuantParams p)
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            rht16_inplace(v[j], p.mask);
+            rht16_butterflies(v[j], p.mask);
 #pragma unroll
             for (int i = 0; i < 16; ++i) m_rht = __builtin_fmaxf(m_rht, __builtin_fabsf(v[j][i]));
         }
     }
     block_reduce_max_store(m_plain, p.partials + blockIdx.x);
     __syncthreads();  // the reduction's shared slots are reused
-    block_reduce_max_store(m_rht, p.partials + kMaxAmaxPartials + blockIdx.x);
+    block_reduce_max_store(0.25f * m_rht, p.partials + kMaxAmaxPartials + blockIdx.x);
 }
 
 // ------------------------------------------------------------ SwiGLU + amaxes
@@ -396,32 +396,41 @@ __global__ __launch_bounds__(256) void k_swiglu_amax(const uint8_t* h, int64_t l
                                 bf16_hi(graw[i][1])};
             const float u[4] = {bf16_lo(uraw[i][0]), bf16_hi(uraw[i][0]), bf16_lo(uraw[i][1]),
                                 bf16_hi(uraw[i][1])};
-            uint32_t b[4];
+            float den[4], sg[4];
+            bool need_div = false;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                // per-lane select of the division: a wave-wide check of the
-                // gate values would need the tile's code twice, and the
-                // registers it costs lose more than the division here
-                b[j] = swiglu_bf16_bits<true>(g[j], u[j]);
-                float a = __uint_as_float(b[j] << 16);
+                den[j] = silu_den(g[j]);
+                sg[j] = silu_rcp(g[j], den[j]);
+                need_div |= silu_needs_division(den[j]);
+            }
+            // the division only in waves with a gate below -87.3
+            if (__builtin_amdgcn_ballot_w64(need_div) != 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sg[j] = silu_fix(g[j], den[j], sg[j]);
+            }
+            u32x2 w;
+            w[0] = swiglu_pack(sg[0], u[0], sg[1], u[1]);
+            w[1] = swiglu_pack(sg[2], u[2], sg[3], u[3]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a = (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
                 v[j][i] = a;
                 m_plain = __builtin_fmaxf(m_plain, __builtin_fabsf(a));
             }
-            u32x2 w;
-            w[0] = b[0] | (b[1] << 16);
-            w[1] = b[2] | (b[3] << 16);
             *reinterpret_cast<u32x2*>(act + ((r0 + i) * ld_a + c0) * 2) = w;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            rht16_inplace(v[j], mask);
+            rht16_butterflies(v[j], mask);
 #pragma unroll
             for (int i = 0; i < 16; ++i) m_rht = __builtin_fmaxf(m_rht, __builtin_fabsf(v[j][i]));
         }
     }
     block_reduce_max_store(m_plain, partials + blockIdx.x);
     __syncthreads();  // the reduction's shared slots are reused
-    block_reduce_max_store(m_rht, partials + kMaxAmaxPartials + blockIdx.x);
+    // the transform's 1/4 on the maximum (RN(0.25 x) is monotone in x)
+    block_reduce_max_store(0.25f * m_rht, partials + kMaxAmaxPartials + blockIdx.x);
 }
 
 // fp4_pack2 into byte `sel` of `old` (sel is a constant once loops unroll)
