@@ -935,12 +935,7 @@ __device__ __forceinline__ void dequant8_store(uint32_t w, const float e[8], flo
     if (kOutBF16) {
         u32x4 o;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t a = __float_as_uint(v[2 * j]), b = __float_as_uint(v[2 * j + 1]);
-            a += 0x7FFFu + ((a >> 16) & 1u);  // round to nearest even (finite inputs)
-            b += 0x7FFFu + ((b >> 16) & 1u);
-            o[j] = (a >> 16) | (b & 0xFFFF0000u);
-        }
+        for (int j = 0; j < 4; ++j) o[j] = bf16_pair(v[2 * j], v[2 * j + 1]);
         // a wave's 64 stores are 1 KB of consecutive bytes: streaming stores,
         // which skip the caches (the output is written once per call)
         __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst));
