@@ -316,7 +316,25 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b)
 // IEEE division, which silu_fix applies.  That never happens for g >= -87
 // (1 + exp(87) < 2^126), which callers check for a whole wave (swiglu_low,
 // or the denominators themselves), so the common path has no division.
-__device__ __forceinline__ float silu_den(float g) { return 1.0f + expf(-g); }
+// exp(-g) for BF16-valued g: Cody-Waite reduction onto the hardware 2^x
+// (v_exp_f32, 1 ulp on [-0.5, 0.5]): with t = -g log2(e) carried as ph + pl
+// (log2(e) split into its FP32 rounding and the rest), exp(-g) =
+// 2^((ph - e) + pl) * 2^e for e = rint(ph).  Out of range the scaling itself
+// saturates: 2^e from e = 128 overflows to infinity (g <= -89 on the BF16
+// grid), and from e <= -150 leaves at most a denormal (g >= 104), where
+// 1 + exp(-g) is 1 either way.
+__device__ __forceinline__ float exp_neg(float g)
+{
+    constexpr float kLog2e = 1.44269502e+00f;     // log2(e) rounded to FP32
+    constexpr float kLog2eLo = 1.92596299e-08f;   // log2(e) - kLog2e
+    const float ph = g * -kLog2e;
+    float pl = __builtin_fmaf(g, -kLog2e, -ph);
+    pl = __builtin_fmaf(g, -kLog2eLo, pl);
+    const float e = __builtin_rintf(ph);
+    const float a = (ph - e) + pl;
+    return __builtin_ldexpf(__builtin_amdgcn_exp2f(a), (int)e);
+}
+__device__ __forceinline__ float silu_den(float g) { return 1.0f + exp_neg(g); }
 __device__ __forceinline__ float silu_rcp(float g, float den)
 {
     return g * __builtin_amdgcn_rcpf(den);
