@@ -89,7 +89,8 @@ __device__ __forceinline__ float div_markstein(float ax, float d, float r)
 // Per-block quotient context: d = RN(e * s_g) and r = RN(1/d).
 struct BlockDiv {
     float d, r;
-    bool fast;  // d far from the FP32 range ends, so Markstein applies to non-tiny |x|
+    bool fast;        // d far from the FP32 range ends, so Markstein applies to non-tiny |x|
+    bool codes_fast;  // d >= 2^-40 as well: codes need no per-element test (quotients_codes)
 };
 
 __device__ __forceinline__ BlockDiv make_block_div(float d)
@@ -98,6 +99,7 @@ __device__ __forceinline__ BlockDiv make_block_div(float d)
     b.d = d;
     b.r = 1.0f / d;
     b.fast = (d >= 0x1p-60f) && (d <= 0x1p60f);
+    b.codes_fast = (d >= 0x1p-40f) && (d <= 0x1p60f);
     return b;
 }
 
@@ -139,6 +141,26 @@ __device__ __forceinline__ void quotients(const float* x, const BlockDiv& b, flo
         y[i] = __uint_as_float(__float_as_uint(y[i]) | (__float_as_uint(x[i]) & 0x80000000u));
 }
 
+// The same where only the E2M1 codes (round to nearest) of the quotients
+// matter.  In a block with d >= 2^-40 an element below 2^-60 has |x| / d <
+// 2^-20, far under the first rounding boundary 0.25, and Markstein's
+// intermediates on it, denormal or not, stay that small, so its code is the
+// signed zero either way; every other element meets Markstein's conditions.
+// Such blocks skip the per-element test; the rest take quotients().
+template <int n>
+__device__ __forceinline__ void quotients_codes(const float* x, const BlockDiv& b, float* y)
+{
+    if (b.codes_fast) {
+#pragma unroll
+        for (int i = 0; i < n; ++i) {
+            const float q = div_markstein(__builtin_fabsf(x[i]), b.d, b.r);
+            y[i] = __uint_as_float(__float_as_uint(q) | (__float_as_uint(x[i]) & 0x80000000u));
+        }
+    } else {
+        quotients<n>(x, b, y);
+    }
+}
+
 // True when y (FP32 bits u, either sign) lies within 8 units in the last
 // place of a number whose significand has at most 3 bits (the low 21 bits of
 // its mantissa field are 0).  Every E2M1 rounding boundary (0.25, 0.75, 1.25,
@@ -174,7 +196,7 @@ __device__ __forceinline__ void quotients_rne(const float* x, const BlockDiv& b,
         y[i] = x[i] * b.r;
         exact |= near_e2m1_boundary(__float_as_uint(y[i]));
     }
-    if (__builtin_amdgcn_ballot_w64(exact) != 0) quotients<n>(x, b, y);
+    if (__builtin_amdgcn_ballot_w64(exact) != 0) quotients_codes<n>(x, b, y);
 }
 
 // Single quotient (block-scale computation).

@@ -86,6 +86,7 @@ __device__ __forceinline__ uint32_t block_scale(float aB, const TensorScale& ts,
     bd.d = 1.0f;
     bd.r = 1.0f;
     bd.fast = true;
+    bd.codes_fast = true;
     if (!(aB > 0.0f)) return 0u;
     float t = quotient(aB, ts.d6);  // RN(a_B / RN(6 s_g))
     uint32_t e = e4m3_encode(t);
@@ -146,7 +147,7 @@ __device__ __forceinline__ uint32_t encode8(const float v[8], const BlockDiv& bd
     } else if (kRHT) {
         quotients_rne<8>(v, bd, y);
     } else {
-        quotients<8>(v, bd, y);
+        quotients_codes<8>(v, bd, y);
     }
     return pack8_rne(y);
 }
@@ -300,6 +301,7 @@ __global__ __launch_bounds__(256) void k_quant_cols(QuantParams p)
                 for (int i = 0; i < 16; ++i) y[j][i] = 0.0f;
             } else {
                 if (!kSR && kRHT) quotients_rne<16>(v[j], bd, y[j]);
+                else if (!kSR) quotients_codes<16>(v[j], bd, y[j]);
                 else quotients<16>(v[j], bd, y[j]);
             }
         }
@@ -534,6 +536,7 @@ void k_quant_t(QuantParams p)
                 } else {
                     float y[16];
                     if (!kSR && kRHT) quotients_rne<16>(v[j], bd, y);
+                    else if (!kSR) quotients_codes<16>(v[j], bd, y);
                     else quotients<16>(v[j], bd, y);
 #pragma unroll
                     for (int i = 0; i < 16; ++i) v[j][i] = y[i];
