@@ -483,6 +483,9 @@ void k_quant_t(QuantParams p)
     const int64_t rows = p.rows, cols = p.cols;
     const int64_t out_ld = rows / 2;     // bytes per transposed code row
     const int64_t sc_ld = rows / 16;     // bytes per transposed scale row
+    // every transposed code row starts 16-byte aligned (tiles start at
+    // multiples of 128 bytes of a row)
+    const bool codes16 = ((uintptr_t)p.codes & 15) == 0 && (out_ld & 15) == 0;
     for (uint32_t tile = blockIdx.x; tile < p.items; tile += gridDim.x) {
         const uint32_t tr = fdiv(tile, p.div);
         const uint32_t tc = tile - tr * p.div.d;
@@ -578,7 +581,8 @@ void k_quant_t(QuantParams p)
             }
         }
         __syncthreads();
-        // codes: transposed row cl gets its 16 slots (row blocks) in order
+        // codes: transposed row cl gets its 16 slots (row blocks) in order,
+        // two slots per 16-byte store where the rows allow it
         const int nrb = (int)((rows - R0) / 16 < 16 ? (rows - R0) / 16 : 16);
 #pragma unroll 1
         for (int pass = 0; pass < 8; ++pass) {
@@ -586,22 +590,33 @@ void k_quant_t(QuantParams p)
             if (C0 + cl >= cols) continue;
             const int s = (cl >> 2) & 15;
             uint8_t* dst = p.codes + (C0 + cl) * out_ld + R0 / 2 + 16 * ch;
+            const uint8_t* row = lds_codes + cl * kTCodeRow;
+            if (codes16 && 2 * ch + 1 < nrb) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(row + 8 * ((2 * ch) ^ s));
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 8 * ((2 * ch + 1) ^ s));
+                *reinterpret_cast<u32x4*>(dst) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                continue;
+            }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int rb = 2 * ch + h;
                 if (rb < nrb)
                     *reinterpret_cast<u32x2*>(dst + 8 * h) =
-                        *reinterpret_cast<const u32x2*>(lds_codes + cl * kTCodeRow + 8 * (rb ^ s));
+                        *reinterpret_cast<const u32x2*>(row + 8 * (rb ^ s));
             }
         }
-        // scales: one 16-byte row per transposed scale row
+        // scales: one 16-byte row per transposed scale row (one store when
+        // the row is whole and 16-byte aligned, else byte by byte)
         const int nsr = k2D ? 16 : 256;
         if (t < nsr) {
             const int64_t orow = k2D ? C0 / 16 + t : C0 + t;
             if (orow < (k2D ? cols / 16 : cols)) {
                 uint8_t* dst = p.scales + orow * sc_ld + R0 / 16;
                 const uint8_t* src = lds_scales + t * 16;
-                for (int b = 0; b < nrb; ++b) dst[b] = src[b];
+                if (nrb == 16 && ((uintptr_t)dst & 15) == 0)
+                    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+                else
+                    for (int b = 0; b < nrb; ++b) dst[b] = src[b];
             }
         }
         __syncthreads();
