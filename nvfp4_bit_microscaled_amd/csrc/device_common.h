@@ -341,14 +341,16 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b)
 // exp(-g) for BF16-valued g: Cody-Waite reduction onto the hardware 2^x
 // (v_exp_f32, 1 ulp on [-0.5, 0.5]): with t = -g log2(e) carried as ph + pl
 // (log2(e) split into its FP32 rounding and the rest), exp(-g) =
-// 2^((ph - e) + pl) * 2^e for e = rint(ph).  Out of range the scaling itself
-// saturates: 2^e from e = 128 overflows to infinity (g <= -89 on the BF16
-// grid), and from e <= -150 leaves at most a denormal (g >= 104), where
-// 1 + exp(-g) is 1 either way.
+// 2^((ph - e) + pl) * 2^e for e = rint(ph).  g is first clamped to
+// [-100, 110], which keeps e and the reduced argument in range (for large |g|
+// the rounding error of ph alone would exceed it) and changes nothing that
+// matters: from g <= -89 on the BF16 grid 2^e overflows to infinity anyway,
+// and from g >= 104 it leaves at most a denormal, where 1 + exp(-g) is 1.
 __device__ __forceinline__ float exp_neg(float g)
 {
     constexpr float kLog2e = 1.44269502e+00f;     // log2(e) rounded to FP32
     constexpr float kLog2eLo = 1.92596299e-08f;   // log2(e) - kLog2e
+    g = __builtin_amdgcn_fmed3f(g, -100.0f, 110.0f);
     const float ph = g * -kLog2e;
     float pl = __builtin_fmaf(g, -kLog2e, -ph);
     pl = __builtin_fmaf(g, -kLog2eLo, pl);

@@ -99,3 +99,34 @@ def test_act_against_the_oracle(nv, rows, F):
     act, a, ar = nv.swiglu_amax(h.cuda(), mask)
     torch.cuda.synchronize()
     check_act_against_oracle(h, act.cpu(), "swiglu %dx%d" % (rows, F))
+
+
+@pytest.mark.parametrize("up", ["one", "mixed"])
+def test_every_bf16_gate(nv, up):
+    """Every finite BF16 gate value once (65280 of them, [16, 4080]): the
+    reciprocal path, the division where 1 + exp(-g) reaches 2^126 (g below
+    -87.3), exp(-g) overflowing (g <= -89) and underflowing (g >= 104), signed
+    zeros and denormal gates, against the oracle's SwiGLU under the same flip
+    rule; up is 1, or a mix of signs and magnitudes up to 1 (products that
+    underflow BF16 included; larger ones would overflow act or its column
+    transform for the largest gates).  The amaxes equal the oracle's on act."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    g = torch.from_numpy(bits[finite].astype(np.int32).astype(np.int16)).view(torch.bfloat16)
+    assert g.numel() == 16 * 4080
+    g = g.reshape(16, 4080)
+    if up == "one":
+        u = torch.ones_like(g)
+    else:
+        rng = np.random.default_rng(5)
+        pool = np.array([1.0, -1.0, 0.375, -7.0e-3, 1.0e-30, -0.75, 2.0 ** -100, -0.9921875],
+                        dtype=np.float32)
+        u = torch.from_numpy(pool[rng.integers(0, len(pool), size=g.shape)]).to(torch.bfloat16)
+    h = torch.cat([g, u], dim=1)
+    mask = workloads.sign_mask(77)
+    act, a, ar = nv.swiglu_amax(h.cuda(), mask)
+    torch.cuda.synchronize()
+    check_act_against_oracle(h, act.cpu(), "every BF16 gate, up=%s" % up)
+    xo = to_oracle_input(act.cpu())
+    assert a.item() == oracle.amax(xo)
+    assert ar.item() == oracle.amax(xo, rht=True, axis=0, mask=mask)
