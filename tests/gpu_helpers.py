@@ -85,3 +85,24 @@ def check_act_against_oracle(h: torch.Tensor, act: torch.Tensor, what: str = "")
         mid = (float(sbf[r, c]) + other) / 2.0
         assert abs(float(sg) - mid) <= 4 * float(np.spacing(np.abs(sg))), (what, g[r, c], sg, mid)
     return int((~same).sum())
+
+
+def every_bf16_below(exp2: int) -> torch.Tensor:
+    """Every finite BF16 value of magnitude at most M = 2^exp2 (both signs,
+    denormals and zeros included), as BF16 [rows, 16] 1x16 blocks whose first
+    element is M: the block maximum and the tensor amax, so every block gets
+    the largest E4M3 scale and d = RN(448 * RN(M / 2688)), about M / 6.
+    rows is a multiple of 16 (zero-padded)."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    vals = torch.from_numpy(bits[finite].astype(np.int32).astype(np.int16)).view(torch.bfloat16)
+    m = float(2.0 ** exp2)
+    vals = vals[vals.float().abs() <= m]
+    nblk = (vals.numel() + 14) // 15
+    rows = (nblk + 15) // 16 * 16
+    x = torch.zeros(rows, 16, dtype=torch.bfloat16)
+    x[:, 0] = m
+    body = torch.zeros(rows * 15, dtype=torch.bfloat16)
+    body[:vals.numel()] = vals
+    x[:, 1:] = body.reshape(rows, 15)
+    return x

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import to_oracle_input
+from gpu_helpers import every_bf16_below, to_oracle_input
 
 pytestmark = pytest.mark.gpu
 
@@ -290,3 +290,21 @@ def test_quotients_around_every_e2m1_boundary(nv, s_g, mode):
         assert np.array_equal(tq, oq.T) and np.array_equal(q.scales.cpu().numpy(), osc.T)
         return
     compare(nv, x, "rows" if axis == 1 else "cols", rht=True, mask=mask)
+
+
+@pytest.mark.parametrize("exp2", [0, -30, -37, -38, 60, 100, 127])
+def test_every_bf16_element_value(nv, exp2):
+    """Every finite BF16 value up to M = 2^exp2 as an element of blocks whose
+    maximum is M (d about M / 6): round-to-nearest codes of denormal and tiny
+    elements (below 2^-60) where d >= 2^-40 (M up to 2^-37 and 2^60, which
+    skip the per-element tiny-operand test), where d is below it (2^-38) or
+    beyond Markstein's range (2^100, 2^127), and of every other magnitude;
+    rows, columns (the same blocks down the columns) and 16x16 blocks, BF16
+    and FP32 input, plus stochastic rounding on the rows.  Bit-exact against
+    the oracle."""
+    x = every_bf16_below(exp2)
+    compare(nv, x, "rows")
+    compare(nv, x.float(), "rows")
+    compare(nv, x.t().contiguous(), "cols")
+    compare(nv, x, "2d")
+    compare(nv, x, "rows", sr=True, seed=9)

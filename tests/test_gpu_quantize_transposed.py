@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import to_oracle_input
+from gpu_helpers import every_bf16_below, to_oracle_input
 
 pytestmark = pytest.mark.gpu
 
@@ -120,3 +120,13 @@ def test_transposed_operands_give_the_nt_gemm(nv):
     # the same products summed in a different K order: equal within FP32 accumulation
     ref = y_tn.double()
     assert torch.allclose(y_nt.double(), ref, rtol=0, atol=1e-5 * float(ref.abs().max()))
+
+
+@pytest.mark.parametrize("exp2", [0, -37, -38, 127])
+def test_every_bf16_element_value_transposed(nv, exp2):
+    """The transposed-storage kernel on every finite BF16 value up to
+    M = 2^exp2 in blocks (down the columns) whose maximum is M: round to
+    nearest and stochastic rounding, bit-exact against the oracle."""
+    x = every_bf16_below(exp2).t().contiguous()
+    check(nv, x, block2d=False)
+    check(nv, x, block2d=False, sr=True, seed=4, stream_id=1)
