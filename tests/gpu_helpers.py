@@ -106,3 +106,23 @@ def every_bf16_below(exp2: int) -> torch.Tensor:
     body[:vals.numel()] = vals
     x[:, 1:] = body.reshape(rows, 15)
     return x
+
+
+def every_bf16_block_max(exp2: int) -> torch.Tensor:
+    """One 1x16 block per finite BF16 value v with |v| <= M = 2^exp2 (both
+    signs, zeros and denormals included): v first, then v times 15 fractions
+    in [-1, 1] rounded to BF16 (never above |v|), so v is the block maximum;
+    the first block holds M, the tensor amax.  BF16 [rows, 16], rows a
+    multiple of 16 (padding rows are zero blocks)."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    vals = torch.from_numpy(bits[finite].astype(np.int32).astype(np.int16)).view(torch.bfloat16)
+    m = float(2.0 ** exp2)
+    vals = torch.cat([torch.tensor([m], dtype=torch.bfloat16), vals[vals.float().abs() <= m]])
+    rows = (vals.numel() + 15) // 16 * 16
+    frac = torch.tensor([-1.0, 0.875, -0.5, 0.3, -0.1, 0.05, -0.01, 1e-3, -1e-5, 1e-9, -0.7,
+                         0.99, -0.26, 0.74, 0.0], dtype=torch.float32)
+    x = torch.zeros(rows, 16, dtype=torch.bfloat16)
+    x[:vals.numel(), 0] = vals
+    x[:vals.numel(), 1:] = (vals.float()[:, None] * frac[None, :]).to(torch.bfloat16)
+    return x

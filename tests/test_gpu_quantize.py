@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import every_bf16_below, to_oracle_input
+from gpu_helpers import every_bf16_block_max, every_bf16_below, to_oracle_input
 
 pytestmark = pytest.mark.gpu
 
@@ -308,3 +308,17 @@ def test_every_bf16_element_value(nv, exp2):
     compare(nv, x.t().contiguous(), "cols")
     compare(nv, x, "2d")
     compare(nv, x, "rows", sr=True, seed=9)
+
+
+@pytest.mark.parametrize("exp2", [0, -100, 127])
+def test_every_bf16_block_max(nv, exp2):
+    """Every finite BF16 value up to M = 2^exp2 as the maximum of a block of
+    its own under the tensor amax M: block scales across the whole E4M3 range,
+    its rounding, subnormal scales and the scales that underflow to a zero
+    block, with the block's codes; rows, columns, 16x16 blocks (four maxima
+    share a 16x16 block there), RNE and SR.  Bit-exact against the oracle."""
+    x = every_bf16_block_max(exp2)
+    compare(nv, x, "rows")
+    compare(nv, x.t().contiguous(), "cols")
+    compare(nv, x, "2d")
+    compare(nv, x, "rows", sr=True, seed=12)
