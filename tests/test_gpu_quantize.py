@@ -300,14 +300,22 @@ def test_every_bf16_element_value(nv, exp2):
     skip the per-element tiny-operand test), where d is below it (2^-38) or
     beyond Markstein's range (2^100, 2^127), and of every other magnitude;
     rows, columns (the same blocks down the columns) and 16x16 blocks, BF16
-    and FP32 input, plus stochastic rounding on the rows.  Bit-exact against
-    the oracle."""
+    and FP32 input, plus stochastic rounding on the rows, and the same blocks
+    through the RHT16 (RNE rows, SR columns).  Bit-exact against the
+    oracle."""
     x = every_bf16_below(exp2)
     compare(nv, x, "rows")
     compare(nv, x.float(), "rows")
     compare(nv, x.t().contiguous(), "cols")
     compare(nv, x, "2d")
     compare(nv, x, "rows", sr=True, seed=9)
+    # the same blocks through the transform (RNE takes the reciprocal fast path
+    # there), where its sums of 16 values stay finite: at M = 2^127 they
+    # overflow FP32, an infinite transformed amax, outside the finite-input
+    # contract
+    if exp2 <= 100:
+        compare(nv, x, "rows", rht=True, mask=0x6C1B)
+        compare(nv, x.t().contiguous(), "cols", rht=True, mask=0x6C1B, sr=True, seed=10)
 
 
 @pytest.mark.parametrize("exp2", [0, -100, 127])
