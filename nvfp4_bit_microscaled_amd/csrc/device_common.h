@@ -331,13 +331,6 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// silu(g) = g / (1 + exp(-g)) in FP32 for a BF16-valued gate g: silu_den,
-// then silu_rcp.  The reciprocal unit (1 ulp) stands in for a correctly
-// rounded division, as the result only feeds a BF16 rounding; its output
-// flushes below 2^-126, so denominators from 2^126 up (g < -87.3) need the
-// IEEE division, which silu_fix applies.  That never happens for g >= -87
-// (1 + exp(87) < 2^126), which callers check for a whole wave (swiglu_low,
-// or the denominators themselves), so the common path has no division.
 // exp(-g) for BF16-valued g: Cody-Waite reduction onto the hardware 2^x
 // (v_exp_f32, 1 ulp on [-0.5, 0.5]): with t = -g log2(e) carried as ph + pl
 // (log2(e) split into its FP32 rounding and the rest), exp(-g) =
@@ -358,6 +351,14 @@ __device__ __forceinline__ float exp_neg(float g)
     const float a = (ph - e) + pl;
     return __builtin_ldexpf(__builtin_amdgcn_exp2f(a), (int)e);
 }
+
+// silu(g) = g / (1 + exp(-g)) in FP32 for a BF16-valued gate g: silu_den,
+// then silu_rcp.  The reciprocal unit (1 ulp) stands in for a correctly
+// rounded division, as the result only feeds a BF16 rounding; its output
+// flushes below 2^-126, so denominators from 2^126 up (g < -87.3) need the
+// IEEE division, which silu_fix applies.  That never happens for g >= -87
+// (1 + exp(87) < 2^126), which callers check for a whole wave (swiglu_low,
+// or the denominators themselves), so the common path has no division.
 __device__ __forceinline__ float silu_den(float g) { return 1.0f + exp_neg(g); }
 __device__ __forceinline__ float silu_rcp(float g, float den)
 {
