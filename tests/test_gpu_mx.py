@@ -180,3 +180,45 @@ def test_mx_error_larger_than_nvfp4_on_activations(nv):
     mse_nv = ((xn - xf) ** 2).mean().item()
     print("mse mx %.4g nvfp4 %.4g ratio %.3f" % (mse_mx, mse_nv, mse_nv / mse_mx))
     assert mse_nv < mse_mx
+
+
+def _finite_bf16():
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    return torch.from_numpy(bits[finite].astype(np.int32).astype(np.int16)).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("layout", ["maxima", "elements"])
+def test_mx_quantize_every_bf16_value(nv, layout):
+    """Every finite BF16 value as the maximum of a 32-block of its own
+    ("maxima": the block is v and v times 31 fractions in [-1, 1], rounded to
+    BF16, so every E8M0 scale the rule can give, zero blocks and denormal
+    maxima included), or as an element beside block maxima 2^-126, 1 and
+    2^127 ("elements"): codes and scales bit-exact against the oracle."""
+    vals = _finite_bf16()
+    if layout == "maxima":
+        frac = torch.linspace(-1.0, 1.0, 31, dtype=torch.float32)
+        x = torch.empty(vals.numel(), 32, dtype=torch.bfloat16)
+        x[:, 0] = vals
+        x[:, 1:] = (vals.float()[:, None] * frac[None, :]).to(torch.bfloat16)
+    else:
+        parts = []
+        for m in (2.0 ** -126, 1.0, 2.0 ** 127):
+            v = vals[vals.float().abs() <= m]
+            nb = (v.numel() + 30) // 31
+            blk = torch.zeros(nb, 32, dtype=torch.bfloat16)
+            blk[:, 0] = m
+            body = torch.zeros(nb * 31, dtype=torch.bfloat16)
+            body[:v.numel()] = v
+            blk[:, 1:] = body.reshape(nb, 31)
+            parts.append(blk)
+        x = torch.cat(parts)
+    rows = (x.shape[0] + 3) // 4
+    xx = torch.zeros(rows * 4, 32, dtype=torch.bfloat16)
+    xx[:x.shape[0]] = x
+    xx = xx.reshape(rows, 128)                 # four blocks per row
+    t = nv.mx_quantize(xx.cuda())
+    torch.cuda.synchronize()
+    codes, scales = oracle.mx_quantize(to_oracle_input(xx))
+    assert np.array_equal(t.scales.cpu().numpy(), scales)
+    assert np.array_equal(t.codes.cpu().numpy(), codes)
