@@ -188,3 +188,29 @@ def test_kv_cache_full_size_llama8b_layer(nv):
     got = out[torch.from_numpy(rows).cuda()].cpu().view(torch.int16).numpy().view(np.uint16)
     _, b = oracle.kv_cache_read(*ref, amax, rslots.numpy()[rows])
     assert np.array_equal(got, b)
+
+
+@pytest.mark.parametrize("amax", [1.0, 2.0 ** -100, 3.0e38])
+def test_kv_write_every_bf16_value(nv, amax):
+    """Every finite BF16 value as a feature of a token row (4080 features per
+    row, 16 rows), written under calibration amaxes 1, 2^-100 and 3e38: the
+    saturation of values past amax_cal, blocks whose scale underflows, signed
+    zeros and denormals; the cache bytes and the read-back (BF16 and FP32)
+    bit-exact against the oracle."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    x = torch.from_numpy(bits[finite].astype(np.int32).astype(np.int16)).view(torch.bfloat16)
+    x = x.reshape(16, 4080)
+    T, C, S = 16, 4080, 40
+    slots = np.array([3, 39, 0, 17, 8, 25, 30, 1, 12, 33, 5, 21, 38, 9, 14, 27], dtype=np.int64)
+    cache, ref = make_caches(nv, S, C, amax)
+    nv.kv_cache_write(cache, x.cuda(), torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    oracle.kv_cache_write(to_oracle_input(x), slots, amax, *ref)
+    check_cache(cache, ref, "kv write every BF16 value, amax %g" % amax)
+    rd = np.concatenate([slots[::-1], [-1, S]]).astype(np.int64)
+    f, b = oracle.kv_cache_read(ref[0], ref[1], amax, rd)
+    outf = nv.kv_cache_read(cache, torch.from_numpy(rd).cuda(), torch.float32).cpu()
+    outb = nv.kv_cache_read(cache, torch.from_numpy(rd).cuda(), torch.bfloat16).cpu()
+    assert np.array_equal(outf.numpy().view(np.uint32), f.view(np.uint32))
+    assert np.array_equal(outb.view(torch.int16).numpy().view(np.uint16), b)
