@@ -330,3 +330,31 @@ def test_every_bf16_block_max(nv, exp2):
     compare(nv, x.t().contiguous(), "cols")
     compare(nv, x, "2d")
     compare(nv, x, "rows", sr=True, seed=12)
+
+
+@pytest.mark.parametrize("s_g", [1.0, 1.7e-5, 2.0 ** -110, 1.2e35])
+@pytest.mark.parametrize("mode", list(MODES))
+def test_dequantize_every_code_and_scale(nv, s_g, mode):
+    """Every code byte (two E2M1 codes) under every finite positive E4M3 scale
+    byte (0x00-0x7E, subnormals included), in each block layout, under tensor
+    scales 1, an arbitrary 1.7e-5, 2^-110 (products in FP32's denormal range)
+    and 1.2e35 (about the largest any tensor amax gives, 3.4e38 / 2688: the
+    largest products near FP32's and BF16's top): FP32 and BF16 outputs
+    bit-exact against the oracle."""
+    from nvfp4_bit_microscaled_amd import scale_shape
+    R, C = 256, 4096
+    codes = np.tile(np.arange(256, dtype=np.uint8), (R, C // 2 // 256))
+    codes = np.roll(codes, 7, axis=1) ^ (np.arange(R, dtype=np.uint8)[:, None] * 37).astype(np.uint8)
+    sr, sc = scale_shape(R, C, MODES[mode]["block2d"], MODES[mode]["axis"])
+    scales = ((np.arange(sr)[:, None] * 5 + np.arange(sc)[None, :]) % 127).astype(np.uint8)
+    ts = np.float32(s_g)
+    t = nv.NVFP4Tensor(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                       torch.tensor([ts], dtype=torch.float32, device="cuda"),
+                       torch.zeros(1, device="cuda"), R, C, MODES[mode]["block2d"],
+                       MODES[mode]["axis"])
+    f = nv.dequantize(t, torch.float32)
+    b = nv.dequantize(t, torch.bfloat16)
+    torch.cuda.synchronize()
+    rf, rb = oracle.dequantize(codes, scales, float(ts), R, C, **MODES[mode])
+    assert np.array_equal(f.cpu().numpy().view(np.uint32), rf.view(np.uint32))
+    assert np.array_equal(b.cpu().view(torch.int16).numpy().view(np.uint16), rb)
